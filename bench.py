@@ -1,0 +1,254 @@
+#!/usr/bin/env python3
+"""Throughput of the MoE dispatch/combine hot path on one MI355X.
+
+One step = the whole path over one batch of synthetic input already resident
+in HBM: ep_dispatch_layout -> ep_dispatch -> (expert stage of the workload,
+if any) -> ep_combine, all on one stream.  W untimed warmup steps, then K
+timed steps bracketed by stream synchronisation and HIP events; the per-call
+durations come from events recorded on the same stream between the calls.
+
+Prints one JSON line:
+  value         algorithmic HBM bytes of the step / step time (GB/s)
+  tokens_per_s  tokens of the batch / step time
+  roofline      the longest-running call against the 8 TB/s HBM peak, with
+                hardware byte counts when they were measured for this kernel
+  cpu_baseline  the CPU oracle (single thread) on the same workload
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "dispatch+combine HBM GB/s and tokens/s at T=4096,H=7168,E=256,top-8"
+HBM_PEAK_GBS = 8000.0   # MI355X HBM3E, published peak
+
+# Hardware byte counters (rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE) per launch of
+# the dominant kernel, scaled by the same counters' reading on a plain copy of
+# known size; filled in from the committed profiles for the kernel build they
+# were taken on (None = not measured for the current kernels).
+MEASURED_TRAFFIC = {}
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="prefill2n")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--graph", action="store_true", help="also time K steps replayed from one HIP graph")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="only run the plain copy kernel on this many MiB, --steps times (counter calibration)")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(json.dumps({"error": "this build measures one GPU's share of the exchange; "
+                                   "runs on more than one GPU are not part of it (use --gpus 1)"}))
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from combine_dispatch_layout_02_amd import ep, workloads
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    ep.load()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+
+    if args.calib_copy_mib:
+        n = args.calib_copy_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty(n, dtype=torch.uint8, device=dev)
+        for _ in range(args.steps):
+            ep.ep_calib_copy(src, dst, n)
+        torch.cuda.synchronize()
+        print(json.dumps({"calib_copy_bytes": n, "launches": args.steps}))
+        return
+
+    inp = workloads.make_inputs(args.workload)
+    T, H, E, R, N, k = (inp[n] for n in ("T", "H", "E", "R", "N", "k"))
+    fp8 = inp["x_fmt"] == "fp8"
+    shape = ep.make_shape(T, H, E, R, N, k, ep.EP_FMT_FP8_S128 if fp8 else ep.EP_FMT_BF16,
+                          ep.EP_FMT_MXFP8 if fp8 else ep.EP_FMT_BF16)
+    ws = ep.Workspace(shape, dev)
+
+    # inputs resident in HBM before timing
+    x = torch.from_numpy(inp["x"].view(np.int16)).to(dev).view(torch.bfloat16)
+    idx = torch.from_numpy(inp["topk_idx"]).to(dev)
+    w = torch.from_numpy(inp["topk_w"]).to(dev)
+    factor = None if inp["expert_factor"] is None else torch.from_numpy(inp["expert_factor"]).to(dev)
+    if fp8:   # input quantization is outside the timed step
+        xin, xs = ep.quant_fp8_s128(x)
+    else:
+        xin, xs = x, None
+
+    # every output allocated once, outside the timed region
+    lay = dict(r=torch.empty(R, dtype=torch.int32, device=dev), e=torch.empty(E, dtype=torch.int32, device=dev),
+               m=torch.empty((T, R), dtype=torch.uint8, device=dev), n=torch.empty(N, dtype=torch.int32, device=dev),
+               a=torch.empty(1, dtype=torch.int64, device=dev))
+    recv_x = torch.empty((T * k, H), dtype=xin.dtype, device=dev)
+    recv_s = torch.empty((T * k, H // 128), dtype=torch.float32, device=dev) if fp8 else None
+    src = torch.empty(T * k, dtype=torch.int32, device=dev)
+    rw = torch.empty(T * k, dtype=torch.float32, device=dev)
+    slot = torch.empty((T, k), dtype=torch.int32, device=dev)
+    off = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    if fp8:
+        eo = torch.empty((T * k, H), dtype=torch.uint8, device=dev)
+        eos = torch.empty((T * k, H // 32), dtype=torch.uint8, device=dev)
+    elif inp["expert"] == "scale":
+        eo, eos = torch.empty_like(recv_x), None
+    else:
+        eo, eos = recv_x, None   # identity expert: combine reads the receive buffer itself
+    y = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+
+    def layout():
+        ep.ep_dispatch_layout(shape, idx, lay["r"], lay["e"], lay["m"], lay["n"], lay["a"], ws)
+
+    def dispatch():
+        ep.ep_dispatch(shape, xin, xs, idx, w, recv_x, recv_s, src, rw, slot, off, ws)
+
+    def expert():
+        if fp8:
+            ep.ep_expert_requant_mxfp8(shape, off, factor, recv_x, recv_s, eo, eos)
+        elif inp["expert"] == "scale":
+            ep.ep_expert_scale_bf16(shape, off, factor, recv_x, eo)
+
+    def combine():
+        ep.ep_combine(shape, eo, eos, slot, w, y)
+
+    has_expert = fp8 or inp["expert"] == "scale"
+    phases = [("layout", layout), ("dispatch", dispatch)] + ([("expert", expert)] if has_expert else []) \
+        + [("combine", combine)]
+
+    for _ in range(args.warmup):
+        for _, fn in phases:
+            fn()
+    ws.check()
+    torch.cuda.synchronize()
+    V = int(off[-1].item())
+
+    # timed region: K steps, events between the calls on the launch stream
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(phases) + 1)] for _ in range(K)]
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record(stream)
+    for s in range(K):
+        ev[s][0].record(stream)
+        for i, (_, fn) in enumerate(phases):
+            fn()
+            ev[s][i + 1].record(stream)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms_step = t0.elapsed_time(t1) / K
+    phase_us = {name: 1000.0 * sum(ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(K)) / K
+                for i, (name, _) in enumerate(phases)}
+    ws.check()
+
+    graph_ms = None
+    if args.graph:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _, fn in phases:
+                fn()
+        y_eager = y.clone()
+        g.replay()
+        torch.cuda.synchronize()
+        if not torch.equal(y.view(torch.int16), y_eager.view(torch.int16)):
+            raise RuntimeError("graph replay differs from the eager step")
+        ga, gb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ga.record(stream)
+        for _ in range(K):
+            g.replay()
+        gb.record(stream)
+        torch.cuda.synchronize()
+        graph_ms = ga.elapsed_time(gb) / K
+        if not torch.equal(y.view(torch.int16), y_eager.view(torch.int16)):
+            raise RuntimeError("graph replays differ from the eager step")
+
+    # algorithmic bytes (library accounting on host copies of the layout)
+    acc = ep.ep_accounting(shape, 0, lay["r"].cpu().numpy(), lay["n"].cpu().numpy(), int(lay["a"].item()), V)
+    algo_bytes = {"layout": acc["hbm_layout_bytes"], "dispatch": acc["hbm_dispatch_bytes"],
+                  "combine": acc["hbm_combine_bytes"]}
+    if has_expert:
+        # expert stage: reads and writes V rows (plus scales)
+        row_in = H + 4 * H // 128 if fp8 else 2 * H
+        row_out = H + H // 32 if fp8 else 2 * H
+        algo_bytes["expert"] = V * (row_in + row_out) + 4.0 * (E + 1)
+    step_bytes = sum(algo_bytes.values())
+    step_s = ms_step / 1000.0
+    dom = max(("dispatch", "combine"), key=lambda p: phase_us[p])
+    kernels = {"dispatch": "ep_slot_count_kernel + ep_dispatch_copy_kernel", "combine": "ep_combine_" +
+               ("mxfp8" if fp8 else "bf16") + "_kernel"}
+    achieved = algo_bytes[dom] / (phase_us[dom] * 1e-6) / 1e9
+    traffic = MEASURED_TRAFFIC.get((args.workload, dom))
+
+    out = {
+        "metric": METRIC,
+        "value": round(step_bytes / step_s / 1e9, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8/mxfp8" if fp8 else "bf16",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "tokens": T, "hidden": H, "experts": E, "virtual_ranks": R,
+                   "virtual_nodes": N, "topk": k, "routing": inp["routing"], "expert": inp["expert"],
+                   "x_format": inp["x_fmt"], "valid_pairs": V},
+        "tokens_per_s": round(T / step_s, 1),
+        "phase_us": {p: round(v, 2) for p, v in phase_us.items()},
+        "step_algorithmic_bytes": int(step_bytes),
+        "graph_ms_per_step": None if graph_ms is None else round(graph_ms, 4),
+        "roofline": {"bound": "hbm", "kernel": kernels[dom], "achieved": round(achieved, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic, "algorithmic_bytes_per_launch": int(algo_bytes[dom])},
+        "pages_accounting": {"rdma_algo_tokens": acc["rdma_algo_tokens"],
+                             "rdma_physical_tokens": acc["rdma_physical_tokens"],
+                             "nvl_tokens": acc["nvl_tokens"],
+                             "dispatch_rdma_bytes_bf16": acc["dispatch_rdma_bytes_bf16"],
+                             "dispatch_nvl_bytes_bf16": acc["dispatch_nvl_bytes_bf16"]},
+    }
+
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds, step_bytes)
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(inp, seconds, step_bytes):
+    """The CPU oracle as it stands (plain C, one thread) on the same workload:
+    whole passes (layout, slots, dispatch rows, expert stage, combine) repeated
+    until `seconds` of CPU work, at least one pass."""
+    import oracle
+
+    reps, t_start = 0, time.perf_counter()
+    while True:
+        oracle.run_path(inp)
+        reps += 1
+        if time.perf_counter() - t_start >= seconds:
+            break
+    dt = (time.perf_counter() - t_start) / reps
+    return {"value": round(inp["T"] / dt, 1), "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "gbs": round(step_bytes / dt / 1e9, 3),
+            "sample": f"{reps} full passes of workload {inp['name']} (T={inp['T']}), {dt:.3f} s per pass"}
+
+
+if __name__ == "__main__":
+    main()

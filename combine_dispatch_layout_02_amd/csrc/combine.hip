@@ -1,0 +1,210 @@
+// combine.hip -- top-k weighted gather-reduce on gfx950.
+//
+// What it computes (MORI-EP Benchmark, "Combine": the reverse of dispatch;
+// MSCCL++ PR 860: each expert returns one row per dispatched (token, expert)
+// pair, and combine consumes the receiver-side layout that dispatch
+// returned): for every token t and element h,
+//     acc = -0.0f;  for j = 0..k-1 with s = token_slot[t,j] >= 0:
+//         acc = fmaf(topk_w[t,j], value(s, h), acc)
+//     y[t,h] = bf16_rne(acc)          (+0.0 for a token with no valid slot)
+// i.e. fp32 accumulation in top-k slot order and one rounding to bf16.
+// value() is the bf16 element, or for mxfp8 rows e4m3(q) * 2^(e8m0 - 127)
+// (exact in binary32).
+//
+// How: one wave per (token, row part).  Lanes 0..k-1 read the token's slots
+// and weights, which readlane moves into scalar registers, so every branch on
+// a slot is uniform.  Each lane owns 16-byte column vectors of the row; per
+// batch of up to 8 slots it issues all the batch's loads before the first
+// FMA, keeping 8 rows in flight per wave, then applies v_fma_f32 in slot
+// order.  Nothing is reduced across lanes, so the result does not depend on
+// the launch shape.
+#include "ep_device.h"
+#include "ep_internal.h"
+
+namespace ep {
+namespace {
+
+struct CombineArgs {
+    const char *eo;             // [T*k][row_bytes]
+    const uint8_t *eo_scales;   // [T*k][H/32] e8m0, mxfp8 only
+    const int32_t *token_slot;  // [T][k]
+    const float *topk_w;        // [T][k]
+    char *y;                    // [T][2H]
+    int64_t T;
+    int k, H;
+    int64_t row_bytes;          // 2H (bf16) or H (mxfp8)
+    int nvec;                   // 16-byte vectors per payload row
+    int S;                      // waves per token
+};
+
+constexpr int kSlotBatch = 8;
+
+// bf16 rows: a 16-byte vector holds 8 elements; C vectors per lane per pass.
+template <int C>
+__global__ __launch_bounds__(256) void ep_combine_bf16_kernel(CombineArgs a) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int64_t gw = (int64_t)blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
+    const int64_t t = gw / a.S;
+    const int sub = (int)(gw - t * a.S);
+    if (t >= a.T) return;
+
+    int32_t slot = -1;
+    float wt = 0.0f;
+    if (lane < a.k) {
+        slot = a.token_slot[t * a.k + lane];
+        wt = a.topk_w[t * a.k + lane];
+        if ((uint64_t)slot >= (uint64_t)(a.T * a.k)) slot = -1;   // outside the receive rows: masked
+    }
+    const bool any_valid = __ballot(lane < a.k && slot >= 0) != 0;
+    char *yrow = a.y + t * (int64_t)a.H * 2;
+    const int stride = kWave * a.S;
+
+    for (int v0 = lane + kWave * sub; v0 < a.nvec; v0 += stride * C) {
+        float acc[C][8];
+#pragma unroll
+        for (int i = 0; i < C; ++i)
+#pragma unroll
+            for (int q = 0; q < 8; ++q) acc[i][q] = -0.0f;
+
+        for (int jb = 0; jb < a.k; jb += kSlotBatch) {
+            vec16 buf[kSlotBatch][C];
+#pragma unroll
+            for (int jj = 0; jj < kSlotBatch; ++jj) {
+                const int j = jb + jj;
+                if (j >= a.k) break;
+                const int32_t s = readlane(slot, j);
+                if (s < 0) continue;
+                const char *row = a.eo + (int64_t)s * a.row_bytes;
+#pragma unroll
+                for (int i = 0; i < C; ++i) {
+                    const int v = v0 + i * stride;
+                    if (v < a.nvec) buf[jj][i] = ld16(row + (int64_t)v * 16);
+                }
+            }
+#pragma unroll
+            for (int jj = 0; jj < kSlotBatch; ++jj) {
+                const int j = jb + jj;
+                if (j >= a.k) break;
+                const int32_t s = readlane(slot, j);
+                if (s < 0) continue;
+                const float w = readlane(wt, j);
+#pragma unroll
+                for (int i = 0; i < C; ++i) {
+                    const vec16 b = buf[jj][i];
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        acc[i][2 * q] = __builtin_fmaf(w, bf16_lo(b[q]), acc[i][2 * q]);
+                        acc[i][2 * q + 1] = __builtin_fmaf(w, bf16_hi(b[q]), acc[i][2 * q + 1]);
+                    }
+                }
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < C; ++i) {
+            const int v = v0 + i * stride;
+            if (v >= a.nvec) continue;
+            vec16 o;
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                o[q] = any_valid ? pack_bf16x2(acc[i][2 * q], acc[i][2 * q + 1]) : 0u;
+            st16(yrow + (int64_t)v * 16, o);
+        }
+    }
+}
+
+// mxfp8 rows: a 16-byte vector holds 16 e4m3 elements, half of a 32-element
+// scale group; the y row vectors for it are two 16-byte bf16 vectors.
+__global__ __launch_bounds__(256) void ep_combine_mxfp8_kernel(CombineArgs a) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int64_t gw = (int64_t)blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
+    const int64_t t = gw / a.S;
+    const int sub = (int)(gw - t * a.S);
+    if (t >= a.T) return;
+
+    int32_t slot = -1;
+    float wt = 0.0f;
+    if (lane < a.k) {
+        slot = a.token_slot[t * a.k + lane];
+        wt = a.topk_w[t * a.k + lane];
+        if ((uint64_t)slot >= (uint64_t)(a.T * a.k)) slot = -1;   // outside the receive rows: masked
+    }
+    const bool any_valid = __ballot(lane < a.k && slot >= 0) != 0;
+    char *yrow = a.y + t * (int64_t)a.H * 2;
+    const int stride = kWave * a.S;
+    const int G32 = a.H / 32;
+
+    for (int v = lane + kWave * sub; v < a.nvec; v += stride) {
+        float acc[16];
+#pragma unroll
+        for (int q = 0; q < 16; ++q) acc[q] = -0.0f;
+        for (int jb = 0; jb < a.k; jb += kSlotBatch) {
+            vec16 buf[kSlotBatch];
+            uint32_t sc[kSlotBatch];
+#pragma unroll
+            for (int jj = 0; jj < kSlotBatch; ++jj) {
+                const int j = jb + jj;
+                if (j >= a.k) break;
+                const int32_t s = readlane(slot, j);
+                if (s < 0) continue;
+                buf[jj] = ld16(a.eo + (int64_t)s * a.row_bytes + (int64_t)v * 16);
+                sc[jj] = a.eo_scales[(int64_t)s * G32 + (v >> 1)];
+            }
+#pragma unroll
+            for (int jj = 0; jj < kSlotBatch; ++jj) {
+                const int j = jb + jj;
+                if (j >= a.k) break;
+                const int32_t s = readlane(slot, j);
+                if (s < 0) continue;
+                const float w = readlane(wt, j);
+                const float scale = e8m0_to_f32(sc[jj]);
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+#pragma unroll
+                    for (int b = 0; b < 4; ++b) {
+                        const float val = e4m3_to_f32((buf[jj][q] >> (8 * b)) & 0xFFu) * scale;
+                        acc[4 * q + b] = __builtin_fmaf(w, val, acc[4 * q + b]);
+                    }
+                }
+            }
+        }
+        vec16 o0, o1;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            o0[q] = any_valid ? pack_bf16x2(acc[2 * q], acc[2 * q + 1]) : 0u;
+            o1[q] = any_valid ? pack_bf16x2(acc[8 + 2 * q], acc[8 + 2 * q + 1]) : 0u;
+        }
+        st16(yrow + (int64_t)v * 32, o0);
+        st16(yrow + (int64_t)v * 32 + 16, o1);
+    }
+}
+
+}  // namespace
+
+hipError_t launch_combine(const Shape &s, const void *expert_out, const uint8_t *expert_scales,
+                          const int32_t *token_slot, const float *topk_w, void *y,
+                          hipStream_t stream) {
+    if (s.T == 0) return hipSuccess;
+    CombineArgs a;
+    a.eo = static_cast<const char *>(expert_out);
+    a.eo_scales = expert_scales;
+    a.token_slot = token_slot;
+    a.topk_w = topk_w;
+    a.y = static_cast<char *>(y);
+    a.T = s.T;
+    a.k = s.k;
+    a.H = s.H;
+    const bool mx = (s.y_fmt == 2);
+    a.row_bytes = mx ? (int64_t)s.H : 2 * (int64_t)s.H;
+    a.nvec = (int)(a.row_bytes / 16);
+    a.S = waves_per_token(s.T, a.nvec);
+    const int64_t waves = s.T * a.S;
+    const dim3 grid((unsigned)((waves + 3) / 4)), block(256);
+    if (mx) {
+        hipLaunchKernelGGL(ep_combine_mxfp8_kernel, grid, block, 0, stream, a);
+    } else {
+        hipLaunchKernelGGL(ep_combine_bf16_kernel<2>, grid, block, 0, stream, a);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace ep

@@ -1,0 +1,142 @@
+// ep_device.h -- device-side helpers shared by the gfx950 kernels of libep_hip.
+//
+// Number formats (bit-exact definitions, written for the hardware's integer
+// and IEEE float units; no fast-math, no flush-to-zero):
+//   bf16   : top 16 bits of a binary32; narrowing rounds to nearest even,
+//            NaN becomes 0x7FC0.
+//   e4m3   : OCP 8-bit float "E4M3" (fn variant): bias 7, 3 mantissa bits,
+//            S.1111.111 = NaN, no infinities, largest finite 448.  Encoding
+//            rounds to nearest even and saturates finite overflow and
+//            infinities to +-448.
+//   e8m0   : OCP Microscaling scale, 2^(e - 127); 0xFF = NaN.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ep {
+
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------------- bit casts
+
+__device__ __forceinline__ float u2f(uint32_t u) { return __uint_as_float(u); }
+__device__ __forceinline__ uint32_t f2u(float f) { return __float_as_uint(f); }
+
+// ---------------------------------------------------------------- bf16
+
+__device__ __forceinline__ float bf16_lo(uint32_t pair) { return u2f(pair << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t pair) { return u2f(pair & 0xFFFF0000u); }
+
+// binary32 -> bf16 bits, round to nearest even; NaN -> 0x7FC0.
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
+    uint32_t u = f2u(f);
+    uint32_t r = (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+    return ((u & 0x7FFFFFFFu) > 0x7F800000u) ? 0x7FC0u : r;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    return f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
+}
+
+// ---------------------------------------------------------------- e4m3
+
+// binary32 -> e4m3 byte (RNE, saturating).
+//   |f| >= 448 (or inf)       -> 0x7E with sign
+//   normal e4m3 range (>=2^-6): drop 20 mantissa bits with RNE on the integer
+//                               pattern (a carry moves into the exponent),
+//                               rebias 127 -> 7 (subtract 120 << 3)
+//   below 2^-6                 -> subnormal steps of 2^-9: rint(|f| * 512)
+//                               (the scaling is exact; 8 is the smallest
+//                               normal code 0x08)
+__device__ __forceinline__ uint32_t f32_to_e4m3(float f) {
+    const uint32_t u = f2u(f);
+    const uint32_t sign = (u >> 24) & 0x80u;
+    const uint32_t a = u & 0x7FFFFFFFu;
+    uint32_t code;
+    if (a > 0x7F800000u) {
+        code = 0x7Fu;
+    } else if (a >= 0x43E00000u) {        // 448.0f
+        code = 0x7Eu;
+    } else if (a >= 0x3C800000u) {        // 2^-6
+        uint32_t r = a + 0x7FFFFu + ((a >> 20) & 1u);
+        code = (r >> 20) - (120u << 3);
+    } else {
+        code = (uint32_t)__builtin_rintf(u2f(a) * 512.0f);
+    }
+    return sign | code;
+}
+
+// e4m3 byte -> binary32 (exact).  The byte's exponent+mantissa bits placed at
+// binary32 bits 20..26 read as a float equal to value * 2^-120 for normals and
+// subnormals alike; multiplying by 2^120 is exact.
+__device__ __forceinline__ float e4m3_to_f32(uint32_t b) {
+    const uint32_t mag = b & 0x7Fu;
+    float v = u2f(mag << 20) * 0x1p120f;
+    v = (mag == 0x7Fu) ? __builtin_nanf("") : v;
+    return (b & 0x80u) ? -v : v;
+}
+
+// ---------------------------------------------------------------- e8m0
+
+// 2^(e - 127) as a binary32 (exact; e = 0 gives the subnormal 2^-127).
+__device__ __forceinline__ float e8m0_to_f32(uint32_t e) {
+    float v = (e == 0u) ? u2f(0x00400000u) : u2f(e << 23);
+    return (e == 0xFFu) ? __builtin_nanf("") : v;
+}
+
+// Shared exponent X of an mxfp8 32-group with largest magnitude amax:
+// clamp(floor(log2 amax) - 8, -127, 127); -127 for amax == 0 or a binary32
+// subnormal amax (whose floor(log2) is below -126).
+__device__ __forceinline__ int mx_shared_exp(float amax) {
+    const uint32_t a = f2u(amax) & 0x7FFFFFFFu;
+    if (a < 0x00800000u) return -127;
+    const int x = (int)(a >> 23) - 127 - 8;
+    return x < -127 ? -127 : (x > 127 ? 127 : x);
+}
+
+// 2^-X as a binary32 for X in [-127, 127] (exact).
+__device__ __forceinline__ float pow2_neg(int X) {
+    const int e = 127 - X;   // biased exponent of 2^-X
+    return (e <= 0) ? u2f(0x00400000u) : u2f((uint32_t)e << 23);
+}
+
+// ---------------------------------------------------------------- wave helpers
+
+__device__ __forceinline__ int lane_id() { return __lane_id(); }
+
+__device__ __forceinline__ uint64_t lanemask_lt() {
+    const int l = lane_id();
+    return (l == 0) ? 0ull : (~0ull >> (64 - l));
+}
+
+template <typename T>
+__device__ __forceinline__ T readlane(T v, int lane);
+
+template <>
+__device__ __forceinline__ int readlane<int>(int v, int lane) {
+    return __builtin_amdgcn_readlane(v, lane);
+}
+template <>
+__device__ __forceinline__ float readlane<float>(float v, int lane) {
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
+}
+
+// 16-byte vector type used for every row copy (one global_load/store_dwordx4).
+typedef uint32_t vec16 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ vec16 ld16(const void *p) {
+    return *reinterpret_cast<const vec16 *>(p);
+}
+__device__ __forceinline__ void st16(void *p, vec16 v) {
+    *reinterpret_cast<vec16 *>(p) = v;
+}
+// Non-temporal variants: streamed data that is not re-read by this kernel.
+__device__ __forceinline__ vec16 ld16_nt(const void *p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const vec16 *>(p));
+}
+__device__ __forceinline__ void st16_nt(void *p, vec16 v) {
+    __builtin_nontemporal_store(v, reinterpret_cast<vec16 *>(p));
+}
+
+}  // namespace ep

@@ -1,0 +1,78 @@
+// ep_internal.h -- launcher interface between the C ABI (ep_abi.hip) and the
+// kernels.  Not installed; callers use include/ep.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace ep {
+
+// Workspace layout (bytes from the workspace base; every region 256-aligned).
+//   ctrl        : u32[64]   [0] error flags, [1] layout ticket, [2] slot ticket
+//   partial     : i32[layout_blocks][R + N + E]   per-block layout counts
+//   tile_count  : i32[slot_tiles][E]   per-tile expert counts, then (after the
+//                 single-pass scan) the exclusive prefix of expert e over
+//                 earlier tiles
+//   local_rank  : i32[T * k]   rank of pair p among the same-expert pairs of
+//                 its tile that precede it (-1 for masked / invalid pairs)
+struct WsLayout {
+    size_t ctrl, partial, tile_count, local_rank, total;
+    int layout_blocks;   // blocks of kLayoutTokens tokens
+    int slot_tiles;      // tiles of slot_tile entries
+    int slot_waves;      // waves per slot tile
+    int slot_tile;       // entries per slot tile (slot_waves * 64)
+};
+
+constexpr int kLayoutTokens = 256;   // tokens (lanes) per layout block
+constexpr int kCtrlWords = 64;
+constexpr uint32_t kErrBadExpert = 0x1u;
+constexpr uint32_t kErrBadSlot = 0x2u;   // internal consistency check of the slot scan
+
+struct Shape {
+    int64_t T;
+    int H, E, R, N, k;
+    int x_fmt, y_fmt;
+};
+
+WsLayout ws_layout(const Shape &s);
+
+// Kernel launchers; every one enqueues on `stream` and returns the launch status.
+hipError_t launch_ws_init(uint32_t *ws, size_t words, hipStream_t stream);
+
+hipError_t launch_layout(const Shape &s, const WsLayout &L, const int64_t *topk_idx,
+                         int32_t *per_rank, int32_t *per_expert, uint8_t *in_rank,
+                         int32_t *per_node, int64_t *algo, char *ws, hipStream_t stream);
+
+hipError_t launch_slot_count(const Shape &s, const WsLayout &L, const int64_t *topk_idx,
+                             int32_t *expert_offset, char *ws, hipStream_t stream);
+
+hipError_t launch_dispatch_copy(const Shape &s, const WsLayout &L, const void *x,
+                                const float *x_scales, const int64_t *topk_idx,
+                                const float *topk_w, void *recv_x, float *recv_x_scales,
+                                int32_t *recv_src_idx, float *recv_topk_w, int32_t *token_slot,
+                                const int32_t *expert_offset, char *ws, hipStream_t stream);
+
+hipError_t launch_combine(const Shape &s, const void *expert_out, const uint8_t *expert_scales,
+                          const int32_t *token_slot, const float *topk_w, void *y,
+                          hipStream_t stream);
+
+hipError_t launch_quant_fp8(int64_t rows, int H, const uint16_t *x, uint8_t *q, float *scales,
+                            hipStream_t stream);
+
+hipError_t launch_expert_scale_bf16(const Shape &s, const int32_t *expert_offset,
+                                    const float *factor, const uint16_t *recv, uint16_t *out,
+                                    hipStream_t stream);
+
+hipError_t launch_expert_requant_mxfp8(const Shape &s, const int32_t *expert_offset,
+                                       const float *factor, const uint8_t *recv_q,
+                                       const float *recv_scales, uint8_t *out_q,
+                                       uint8_t *out_e8m0, hipStream_t stream);
+
+hipError_t launch_calib_copy(const void *src, void *dst, size_t bytes, hipStream_t stream);
+
+// Waves per token for the row kernels: enough waves to cover the chip when T
+// is small, never so many that a wave has fewer than 64 row vectors.
+int waves_per_token(int64_t T, int64_t row_vectors);
+
+}  // namespace ep

@@ -1,0 +1,250 @@
+/*
+ * ep.h -- C ABI of the MI355X (gfx950) MoE expert-parallel dispatch / combine
+ * library (libep_hip.so).
+ *
+ * One GPU's share of the exchange at its real shape: one source's T tokens are
+ * routed to E experts spread over R virtual ranks grouped into N virtual
+ * nodes.  Every destination is a contiguous region of ONE receive allocation:
+ * expert segments lie back to back in expert order, a virtual rank's region
+ * is the union of its experts' segments, a virtual node's region the union of
+ * its ranks' regions.
+ *
+ * Sources (web pages; sections named, no line numbers):
+ *   [MORI]  "MORI-EP Benchmark": "Bandwidth Computation" (RDMA bandwidth, Algo
+ *           BW vs Physical BW, NVL / XGMI bandwidth), "Why DeepEP and Mori RDMA
+ *           token counts are equivalent" (Steps 1-3), "Combine", and the
+ *           reference script print_bw_values.py (rank layout, fp8 factor).
+ *   [MEB]   "MoE-EP Benchmark" README, "Environment reference"
+ *           (MEGA_COMBINE_DTYPE: mxfp8 = 32 e4m3 + e8m0 scale).
+ *   [PR860] MSCCL++ pull request 860: get_dispatch_layout / dispatch /
+ *           combine(handle) surface (PR body, "Scope"); combine consumes the
+ *           receiver-side layout returned by dispatch (internode combine
+ *           fix commit); TOKEN_MAJOR compacted prefix offsets (RANK_MAJOR
+ *           commit); one copy per dispatched token per expert (LL combine
+ *           byte commit); capacity-sized buffers instead of a CPU wait for
+ *           exact receive counts (DeepEP V2 graph-capture comment).
+ *
+ * Conventions for every call:
+ *   - Data pointers are DEVICE pointers owned by the caller, except where a
+ *     parameter says "host".  The library never allocates device memory,
+ *     never synchronizes (except ep_check), and enqueues work only on
+ *     `stream` (a hipStream_t; NULL = the null stream).
+ *   - Calls return EP_OK (0) or a negative ep_status; argument errors are
+ *     detected on the host before anything is enqueued.  No exception
+ *     crosses the ABI.
+ *   - topk_idx is [T, k] int64 row-major; a negative id marks a masked slot
+ *     and is skipped everywhere ([MORI] script pads -1 entries); an id >= E
+ *     is invalid: it is treated as masked and raises EP_ERRFLAG_BAD_EXPERT in
+ *     the workspace's error word (read back with ep_check).
+ *   - bf16 values are raw 16-bit patterns; e4m3 (OCP "fn") and e8m0 are bytes.
+ *   - Calls that share one workspace must be ordered (same stream, or
+ *     explicit events); two concurrent calls on one workspace race.
+ */
+#ifndef EP_HIP_H
+#define EP_HIP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define EP_ABI_VERSION 1
+
+/* Status codes. */
+enum ep_status {
+    EP_OK = 0,
+    EP_EINVAL = -1,      /* shape or argument out of the supported range */
+    EP_EALIGN = -2,      /* a row buffer is not 16-byte aligned */
+    EP_EWORKSPACE = -3,  /* workspace missing or smaller than ep_workspace_bytes */
+    EP_EHIP = -4,        /* a HIP runtime call or kernel launch failed */
+    EP_EDEVICE = -5      /* a kernel flagged bad input (ep_check) */
+};
+
+/* Bits of the device error word. */
+#define EP_ERRFLAG_BAD_EXPERT 0x1u
+#define EP_ERRFLAG_BAD_SLOT   0x2u   /* internal: a computed slot fell outside [0, T*k) (skipped) */
+
+/* Payload formats. */
+enum ep_format {
+    EP_FMT_BF16 = 0,         /* 2 bytes per element */
+    EP_FMT_FP8_S128 = 1,     /* e4m3 bytes + one fp32 scale per 128 elements ([MORI] script's fp8 factor) */
+    EP_FMT_MXFP8 = 2         /* e4m3 bytes + one e8m0 byte per 32 elements ([MEB]) */
+};
+
+/* Problem shape.  Supported range (else EP_EINVAL):
+ *   0 <= num_tokens, num_tokens * num_topk < 2^31;
+ *   1 <= num_topk <= 32;
+ *   1 <= num_experts <= 4096, num_experts % num_ranks == 0;
+ *   1 <= num_ranks <= 64, 1 <= num_nodes <= num_ranks, num_ranks % num_nodes == 0;
+ *   hidden >= 8, hidden % 8 == 0 (16-byte bf16 row vectors);
+ *   fp8 / mxfp8 formats: hidden % 128 == 0;
+ *   x_format in {BF16, FP8_S128}; y_format in {BF16, MXFP8}. */
+typedef struct ep_shape {
+    int64_t num_tokens;   /* T: tokens of this source */
+    int32_t hidden;       /* H: elements per token row */
+    int32_t num_experts;  /* E */
+    int32_t num_ranks;    /* R: virtual ranks; expert e lives on rank e / (E/R) */
+    int32_t num_nodes;    /* N: virtual nodes; expert e lives on node e / (E/N) */
+    int32_t num_topk;     /* k */
+    int32_t x_format;     /* format of dispatched rows: EP_FMT_BF16 | EP_FMT_FP8_S128 */
+    int32_t y_format;     /* format of the rows combine reads: EP_FMT_BF16 | EP_FMT_MXFP8 */
+} ep_shape;
+
+/* Version of this ABI (EP_ABI_VERSION). */
+int ep_abi_version(void);
+
+/* Human-readable text of a status code (static storage). */
+const char *ep_strerror(int status);
+
+/* Host-only check of a shape against the supported range. */
+int ep_validate_shape(const ep_shape *shape);
+
+/* Host-only: bytes of device workspace ep_dispatch_layout / ep_dispatch need
+ * for this shape (written to *bytes).  The workspace holds the error word,
+ * the single-pass reduction tickets, per-block partial counts, per-tile
+ * expert counts and per-pair ranks inside a tile. */
+int ep_workspace_bytes(const ep_shape *shape, size_t *bytes);
+
+/* Zero a workspace (a fill kernel on `stream`, no memset node).  Required
+ * once after allocation; afterwards every call leaves the tickets at zero. */
+int ep_workspace_init(void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Layout pass ([MORI] "Why ... equivalent" Steps 1-3, "Algo BW vs Physical
+ * BW"; [PR860] get_dispatch_layout).  For each token: the set of ranks and
+ * the set of nodes its valid experts live on (rank = e / (E/R), node =
+ * e / (E/N)), duplicates collapsed.  Outputs (device, written in full):
+ *   num_tokens_per_rank   [R] int32: tokens whose rank set contains r
+ *   num_tokens_per_expert [E] int32: valid (t, j) pairs routed to e
+ *   is_token_in_rank      [T, R] uint8 (0/1) row-major
+ *   num_tokens_per_node   [N] int32: tokens whose node set contains n
+ *   rdma_algo_token_count [1] int64: deduplicated (token, node) pairs, local
+ *                         node included (= sum of num_tokens_per_node)
+ * The physical count algo * (N-1)/N and the exact per-source count are host
+ * arithmetic (ep_accounting).  Deterministic: integer counts only.
+ */
+int ep_dispatch_layout(const ep_shape *shape, const int64_t *topk_idx,
+                       int32_t *num_tokens_per_rank, int32_t *num_tokens_per_expert,
+                       uint8_t *is_token_in_rank, int32_t *num_tokens_per_node,
+                       int64_t *rdma_algo_token_count,
+                       void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Dispatch: slot assignment plus the row permutation ([PR860] TOKEN_MAJOR
+ * compacted prefix offsets; [MORI] "NVL / XGMI bandwidth": received rows are
+ * token rows).  Every valid pair (t, j) with expert e gets slot
+ *     token_slot[t,j] = expert_offset[e] + #{valid (t',j') before (t,j) in
+ *                       row-major order with expert e}
+ * (a stable counting sort: expert segments in expert order, ascending t
+ * inside a segment), and recv_x[slot] is a bitwise copy of row t.  Capacity
+ * is T*k rows, so no receive count has to reach the host first.
+ *   x             [T, H] bf16 (x_format BF16) or [T, H] e4m3 (FP8_S128)
+ *   x_scales      [T, H/128] fp32 for FP8_S128, else NULL
+ *   topk_idx      [T, k] int64
+ *   topk_w        [T, k] fp32 (copied bitwise into recv_topk_w)
+ *   recv_x        [T*k, H] same element type as x (16-byte aligned); rows at
+ *                 or beyond expert_offset[E] are left untouched
+ *   recv_x_scales [T*k, H/128] fp32 for FP8_S128, else NULL
+ *   recv_src_idx  [T*k] int32: source token of each slot
+ *   recv_topk_w   [T*k] fp32: weight of each slot's pair
+ *   token_slot    [T, k] int32: slot of each pair, -1 if masked (handle)
+ *   expert_offset [E+1] int32: segment starts, expert_offset[E] = valid
+ *                 pairs (handle); rank r's region is
+ *                 [expert_offset[r*E/R], expert_offset[(r+1)*E/R]).
+ * Deterministic: no order-dependent atomics.
+ */
+int ep_dispatch(const ep_shape *shape, const void *x, const float *x_scales,
+                const int64_t *topk_idx, const float *topk_w,
+                void *recv_x, float *recv_x_scales, int32_t *recv_src_idx, float *recv_topk_w,
+                int32_t *token_slot, int32_t *expert_offset,
+                void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Combine: the top-k weighted gather-reduce back into token order ([MORI]
+ * "Combine": reverse of dispatch; [PR860] one copy per dispatched token per
+ * expert, combine consumes the receiver-side layout from dispatch):
+ *     acc = -0.0f; for j = 0..k-1 with s = token_slot[t,j] >= 0:
+ *         acc = fmaf(topk_w[t,j], value(expert_out[s, h]), acc)
+ *     y[t,h] = bf16_rne(acc)   (+0.0 if token t has no valid slot)
+ * fp32 accumulation in top-k slot order, one rounding to bf16.
+ *   expert_out        [T*k, H]: bf16 (y_format BF16) or e4m3 (MXFP8), 16-byte aligned
+ *   expert_out_scales [T*k, H/32] e8m0 bytes for MXFP8
+ *                     (value = e4m3 * 2^(e8m0 - 127)), else NULL
+ *   token_slot, topk_w: from the dispatch handle / the caller ([T, k]); a
+ *                     slot outside [0, T*k) is treated as masked
+ *   y                 [T, H] bf16, 16-byte aligned
+ */
+int ep_combine(const ep_shape *shape, const void *expert_out, const uint8_t *expert_out_scales,
+               const int32_t *token_slot, const float *topk_w, void *y, void *stream);
+
+/* Synchronize `stream`, read and clear the workspace error word; returns
+ * EP_EDEVICE if any kernel flagged bad input (e.g. an expert id >= E), and
+ * writes the flags to *flags (host) when flags is not NULL. */
+int ep_check(void *ws, size_t ws_bytes, void *stream, uint32_t *flags);
+
+/* ---- payload conversion and the workloads' expert stage ------------------ */
+
+/* fp8 rows for dispatch ([MORI] script's fp8 factor: one byte per element and
+ * one fp32 scale per 128).  Per (row, 128-group): amax = max |x|, scale =
+ * amax / 448 (IEEE division; 1 for an all-zero group), q = e4m3_rne_sat(x /
+ * scale).  x [rows, H] bf16; q [rows, H] bytes; scales [rows, H/128] fp32.
+ * Requires H % 128 == 0. */
+int ep_quant_fp8_s128(int64_t rows, int32_t hidden, const uint16_t *x, uint8_t *q,
+                      float *scales, void *stream);
+
+/* Expert stage of the workloads (outside dispatch and combine).  Rows
+ * [0, expert_offset[E]) of a receive buffer with capacity T*k; row s belongs
+ * to the expert whose segment holds s.
+ *   scale_bf16: out[s] = bf16_rne(f32(recv[s]) * factor[e(s)]).
+ *   requant_mxfp8: v = e4m3(q[s]) * scales128[s] (times factor[e(s)] when
+ *     factor != NULL); per 32-group X = clamp(floor(log2 amax) - 8, -127,
+ *     127) (-127 for an all-zero group, OCP Microscaling shared exponent),
+ *     out_q = e4m3_rne_sat(v * 2^-X), out_e8m0 = X + 127 ([MEB]). */
+int ep_expert_scale_bf16(const ep_shape *shape, const int32_t *expert_offset,
+                         const float *factor, const uint16_t *recv, uint16_t *out, void *stream);
+int ep_expert_requant_mxfp8(const ep_shape *shape, const int32_t *expert_offset,
+                            const float *factor, const uint8_t *recv_q, const float *recv_scales,
+                            uint8_t *out_q, uint8_t *out_e8m0, void *stream);
+
+/* ---- accounting (host arithmetic on host copies of the layout counts) ---- */
+
+/* [MORI] "Bandwidth Computation": RDMA algo tokens include the local node;
+ * physical = algo * (N-1)/N; the exact per-source physical count drops pairs
+ * whose node is own_node; NVL rows of one source = its (token, rank) pairs;
+ * bytes = tokens * H * element size (2 for bf16); combine mirrors dispatch;
+ * fp8 factor (1 + 4/128)/2.  hbm_* are the minimum HBM bytes of one
+ * dispatch and one combine call on this shape (rows moved plus index and
+ * weight metadata), given the valid pair count. */
+typedef struct ep_accounting_t {
+    int64_t rdma_algo_tokens;
+    double rdma_physical_tokens;
+    int64_t rdma_physical_tokens_exact;
+    int64_t nvl_tokens;
+    double dispatch_rdma_bytes_bf16;
+    double dispatch_nvl_bytes_bf16;
+    double combine_rdma_bytes_bf16;
+    double combine_nvl_bytes_bf16;
+    double fp8_factor;
+    double dispatch_rdma_bytes_fp8;
+    double dispatch_nvl_bytes_fp8;
+    double hbm_layout_bytes;
+    double hbm_dispatch_bytes;
+    double hbm_combine_bytes;
+} ep_accounting_t;
+
+int ep_accounting(const ep_shape *shape, int32_t own_node, const int32_t *num_tokens_per_rank,
+                  const int32_t *num_tokens_per_node, int64_t rdma_algo_token_count,
+                  int64_t valid_pairs, ep_accounting_t *out);
+
+/* ---- measurement helper --------------------------------------------------- */
+
+/* Plain device copy of `bytes` bytes (16-byte aligned pointers, bytes % 16
+ * == 0): a known-size reference for scaling hardware byte counters. */
+int ep_calib_copy(const void *src, void *dst, size_t bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* EP_HIP_H */
