@@ -17,7 +17,8 @@
 // batch of up to 8 slots it issues all the batch's loads before the first
 // FMA, keeping 8 rows in flight per wave, then applies v_fma_f32 in slot
 // order.  Nothing is reduced across lanes, so the result does not depend on
-// the launch shape.
+// the launch shape.  The gathered rows are read once: the loads carry the
+// non-temporal hint so they do not evict what the caches still hold.
 #include "ep_device.h"
 #include "ep_internal.h"
 
@@ -78,7 +79,7 @@ __global__ __launch_bounds__(256) void ep_combine_bf16_kernel(CombineArgs a) {
 #pragma unroll
                 for (int i = 0; i < C; ++i) {
                     const int v = v0 + i * stride;
-                    if (v < a.nvec) buf[jj][i] = ld16(row + (int64_t)v * 16);
+                    if (v < a.nvec) buf[jj][i] = ld16_nt(row + (int64_t)v * 16);
                 }
             }
 #pragma unroll
@@ -146,7 +147,7 @@ __global__ __launch_bounds__(256) void ep_combine_mxfp8_kernel(CombineArgs a) {
                 if (j >= a.k) break;
                 const int32_t s = readlane(slot, j);
                 if (s < 0) continue;
-                buf[jj] = ld16(a.eo + (int64_t)s * a.row_bytes + (int64_t)v * 16);
+                buf[jj] = ld16_nt(a.eo + (int64_t)s * a.row_bytes + (int64_t)v * 16);
                 sc[jj] = a.eo_scales[(int64_t)s * G32 + (v >> 1)];
             }
 #pragma unroll
@@ -202,7 +203,7 @@ hipError_t launch_combine(const Shape &s, const void *expert_out, const uint8_t 
     if (mx) {
         hipLaunchKernelGGL(ep_combine_mxfp8_kernel, grid, block, 0, stream, a);
     } else {
-        hipLaunchKernelGGL(ep_combine_bf16_kernel<2>, grid, block, 0, stream, a);
+        hipLaunchKernelGGL(ep_combine_bf16_kernel<4>, grid, block, 0, stream, a);
     }
     return hipGetLastError();
 }

@@ -51,25 +51,27 @@ namespace ep {
 
 WsLayout ws_layout(const Shape &s) {
     WsLayout L;
-    L.layout_blocks = (int)((s.T + kLayoutTokens - 1) / kLayoutTokens);
-    if (L.layout_blocks < 1) L.layout_blocks = 1;
-    // waves per slot tile: the LDS masks (W * E * 8 bytes) stay under 48 KiB
-    int W = 16;
-    while (W > 1 && (size_t)W * (size_t)s.E * 8 > 48 * 1024) W >>= 1;
-    L.slot_waves = W;
-    L.slot_tile = W * 64;   // 64-lane wavefronts
+    // pair masks of one tile (tile_waves * E * 8 bytes) stay within 48 KiB
+    int wmax = 16;
+    while (wmax > 1 && (size_t)wmax * (size_t)s.E * 8 > 48 * 1024) wmax >>= 1;
+    L.tile_tokens = (wmax * 64) / s.k;
+    if (L.tile_tokens < 1) L.tile_tokens = 1;
+    L.tile_waves = (L.tile_tokens * s.k + 63) / 64;
+    L.count_threads = L.tile_waves * 64;
+    L.tiles = (int)((s.T + L.tile_tokens - 1) / L.tile_tokens);
+    if (L.tiles < 1) L.tiles = 1;
     const int64_t TK = s.T * s.k;
-    L.slot_tiles = (int)((TK + L.slot_tile - 1) / L.slot_tile);
-    if (L.slot_tiles < 1) L.slot_tiles = 1;
     size_t off = 0;
     L.ctrl = off;
     off = align256(off + kCtrlWords * sizeof(uint32_t));
-    L.partial = off;
-    off = align256(off + sizeof(int32_t) * (size_t)L.layout_blocks * (size_t)(s.R + s.N + s.E));
     L.tile_count = off;
-    off = align256(off + sizeof(int32_t) * (size_t)L.slot_tiles * (size_t)s.E);
+    off = align256(off + sizeof(int32_t) * (size_t)L.tiles * (size_t)s.E);
+    L.rn_count = off;
+    off = align256(off + sizeof(int32_t) * (size_t)L.tiles * (size_t)(s.R + s.N));
     L.local_rank = off;
     off = align256(off + sizeof(int32_t) * (size_t)(TK > 0 ? TK : 1));
+    L.plan_offset = off;
+    off = align256(off + sizeof(int32_t) * (size_t)(s.E + 1));
     L.total = off;
     return L;
 }
@@ -125,36 +127,73 @@ int ep_dispatch_layout(const ep_shape *shape, const int64_t *topk_idx, int32_t *
     const WsLayout L = ep::ws_layout(s);
     if (!ws || ws_bytes < L.total) return EP_EWORKSPACE;
     if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0) return EP_EALIGN;
-    return hip_status(ep::launch_layout(s, L, topk_idx, num_tokens_per_rank, num_tokens_per_expert,
-                                        is_token_in_rank, num_tokens_per_node, rdma_algo_token_count,
-                                        static_cast<char *>(ws), static_cast<hipStream_t>(stream)));
+    return hip_status(ep::launch_plan(s, L, topk_idx, num_tokens_per_rank, num_tokens_per_expert,
+                                      is_token_in_rank, num_tokens_per_node, rdma_algo_token_count,
+                                      static_cast<char *>(ws), static_cast<hipStream_t>(stream)));
 }
+
+}  // extern "C"
+
+namespace {
+
+int check_dispatch_args(const ep_shape *shape, Shape *s, const void *x, const float *x_scales,
+                        const int64_t *topk_idx, const float *topk_w, const void *recv_x,
+                        const float *recv_x_scales, const int32_t *recv_src_idx,
+                        const float *recv_topk_w, const int32_t *token_slot,
+                        const int32_t *expert_offset, const void *ws, size_t ws_bytes,
+                        WsLayout *L) {
+    int rc = check_shape(shape, s);
+    if (rc != EP_OK) return rc;
+    if (!expert_offset) return EP_EINVAL;
+    if (s->T > 0 && (!x || !topk_idx || !topk_w || !recv_x || !recv_src_idx || !recv_topk_w ||
+                     !token_slot))
+        return EP_EINVAL;
+    const bool fp8 = s->x_fmt == EP_FMT_FP8_S128;
+    if (fp8 && s->T > 0 && (!x_scales || !recv_x_scales)) return EP_EINVAL;
+    if (!fp8 && (x_scales || recv_x_scales)) return EP_EINVAL;
+    if (s->T > 0 && (!aligned16(x) || !aligned16(recv_x))) return EP_EALIGN;
+    *L = ep::ws_layout(*s);
+    if (!ws || ws_bytes < L->total) return EP_EWORKSPACE;
+    if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0) return EP_EALIGN;
+    return EP_OK;
+}
+
+}  // namespace
+
+extern "C" {
 
 int ep_dispatch(const ep_shape *shape, const void *x, const float *x_scales,
                 const int64_t *topk_idx, const float *topk_w, void *recv_x, float *recv_x_scales,
                 int32_t *recv_src_idx, float *recv_topk_w, int32_t *token_slot,
                 int32_t *expert_offset, void *ws, size_t ws_bytes, void *stream) {
     Shape s;
-    int rc = check_shape(shape, &s);
+    WsLayout L;
+    int rc = check_dispatch_args(shape, &s, x, x_scales, topk_idx, topk_w, recv_x, recv_x_scales,
+                                 recv_src_idx, recv_topk_w, token_slot, expert_offset, ws, ws_bytes, &L);
     if (rc != EP_OK) return rc;
-    if (!expert_offset) return EP_EINVAL;
-    if (s.T > 0 && (!x || !topk_idx || !topk_w || !recv_x || !recv_src_idx || !recv_topk_w ||
-                    !token_slot))
-        return EP_EINVAL;
-    const bool fp8 = s.x_fmt == EP_FMT_FP8_S128;
-    if (fp8 && s.T > 0 && (!x_scales || !recv_x_scales)) return EP_EINVAL;
-    if (!fp8 && (x_scales || recv_x_scales)) return EP_EINVAL;
-    if (s.T > 0 && (!aligned16(x) || !aligned16(recv_x))) return EP_EALIGN;
-    const WsLayout L = ep::ws_layout(s);
-    if (!ws || ws_bytes < L.total) return EP_EWORKSPACE;
-    if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0) return EP_EALIGN;
     hipStream_t st = static_cast<hipStream_t>(stream);
     char *w = static_cast<char *>(ws);
-    hipError_t e = ep::launch_slot_count(s, L, topk_idx, expert_offset, w, st);
+    hipError_t e = ep::launch_plan(s, L, topk_idx, nullptr, nullptr, nullptr, nullptr, nullptr, w, st);
     if (e != hipSuccess) return EP_EHIP;
     e = ep::launch_dispatch_copy(s, L, x, x_scales, topk_idx, topk_w, recv_x, recv_x_scales,
                                  recv_src_idx, recv_topk_w, token_slot, expert_offset, w, st);
     return hip_status(e);
+}
+
+int ep_dispatch_from_layout(const ep_shape *shape, const void *x, const float *x_scales,
+                            const int64_t *topk_idx, const float *topk_w, void *recv_x,
+                            float *recv_x_scales, int32_t *recv_src_idx, float *recv_topk_w,
+                            int32_t *token_slot, int32_t *expert_offset, void *ws, size_t ws_bytes,
+                            void *stream) {
+    Shape s;
+    WsLayout L;
+    int rc = check_dispatch_args(shape, &s, x, x_scales, topk_idx, topk_w, recv_x, recv_x_scales,
+                                 recv_src_idx, recv_topk_w, token_slot, expert_offset, ws, ws_bytes, &L);
+    if (rc != EP_OK) return rc;
+    return hip_status(ep::launch_dispatch_copy(s, L, x, x_scales, topk_idx, topk_w, recv_x,
+                                               recv_x_scales, recv_src_idx, recv_topk_w, token_slot,
+                                               expert_offset, static_cast<char *>(ws),
+                                               static_cast<hipStream_t>(stream)));
 }
 
 int ep_combine(const ep_shape *shape, const void *expert_out, const uint8_t *expert_out_scales,

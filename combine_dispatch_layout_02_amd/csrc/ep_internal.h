@@ -9,25 +9,27 @@
 namespace ep {
 
 // Workspace layout (bytes from the workspace base; every region 256-aligned).
-//   ctrl        : u32[64]   [0] error flags, [1] layout ticket, [2] slot ticket
-//   partial     : i32[layout_blocks][R + N + E]   per-block layout counts
-//   tile_count  : i32[slot_tiles][E]   per-tile expert counts, then (after the
-//                 single-pass scan) the exclusive prefix of expert e over
-//                 earlier tiles
-//   local_rank  : i32[T * k]   rank of pair p among the same-expert pairs of
-//                 its tile that precede it (-1 for masked / invalid pairs)
+//   ctrl        : u32[64]            [0] error flags
+//   tile_count  : i32[tiles][E]      per-tile expert pair counts, then (after
+//                                    the scan) the exclusive prefix of expert e
+//                                    over earlier tiles
+//   rn_count    : i32[tiles][R + N]  per-tile rank / node token counts
+//   local_rank  : i32[T * k]         rank of a pair among the same-expert pairs
+//                                    of its tile that precede it (-1: masked)
+//   plan_offset : i32[E + 1]         expert segment starts
+// A tile holds tile_tokens whole tokens (tile_tokens * k <= count_threads
+// pairs, one thread per pair).
 struct WsLayout {
-    size_t ctrl, partial, tile_count, local_rank, total;
-    int layout_blocks;   // blocks of kLayoutTokens tokens
-    int slot_tiles;      // tiles of slot_tile entries
-    int slot_waves;      // waves per slot tile
-    int slot_tile;       // entries per slot tile (slot_waves * 64)
+    size_t ctrl, tile_count, rn_count, local_rank, plan_offset, total;
+    int tiles;           // ceil(T / tile_tokens)
+    int tile_tokens;
+    int tile_waves;      // ceil(tile_tokens * k / 64): waves that own pair masks
+    int count_threads;   // tile_waves * 64
 };
 
-constexpr int kLayoutTokens = 256;   // tokens (lanes) per layout block
 constexpr int kCtrlWords = 64;
 constexpr uint32_t kErrBadExpert = 0x1u;
-constexpr uint32_t kErrBadSlot = 0x2u;   // internal consistency check of the slot scan
+constexpr uint32_t kErrBadSlot = 0x2u;   // internal consistency check of the plan
 
 struct Shape {
     int64_t T;
@@ -40,18 +42,16 @@ WsLayout ws_layout(const Shape &s);
 // Kernel launchers; every one enqueues on `stream` and returns the launch status.
 hipError_t launch_ws_init(uint32_t *ws, size_t words, hipStream_t stream);
 
-hipError_t launch_layout(const Shape &s, const WsLayout &L, const int64_t *topk_idx,
-                         int32_t *per_rank, int32_t *per_expert, uint8_t *in_rank,
-                         int32_t *per_node, int64_t *algo, char *ws, hipStream_t stream);
-
-hipError_t launch_slot_count(const Shape &s, const WsLayout &L, const int64_t *topk_idx,
-                             int32_t *expert_offset, char *ws, hipStream_t stream);
+// Layout counts (outputs may be null) and the dispatch plan in the workspace.
+hipError_t launch_plan(const Shape &s, const WsLayout &L, const int64_t *topk_idx,
+                       int32_t *per_rank, int32_t *per_expert, uint8_t *in_rank,
+                       int32_t *per_node, int64_t *algo, char *ws, hipStream_t stream);
 
 hipError_t launch_dispatch_copy(const Shape &s, const WsLayout &L, const void *x,
                                 const float *x_scales, const int64_t *topk_idx,
                                 const float *topk_w, void *recv_x, float *recv_x_scales,
                                 int32_t *recv_src_idx, float *recv_topk_w, int32_t *token_slot,
-                                const int32_t *expert_offset, char *ws, hipStream_t stream);
+                                int32_t *expert_offset, char *ws, hipStream_t stream);
 
 hipError_t launch_combine(const Shape &s, const void *expert_out, const uint8_t *expert_scales,
                           const int32_t *token_slot, const float *topk_w, void *y,

@@ -1,0 +1,317 @@
+// plan.hip -- the layout pass and the dispatch plan on gfx950.
+//
+// What it computes:
+//  * layout (MORI-EP Benchmark, "Why DeepEP and Mori RDMA token counts are
+//    equivalent", Steps 1-3; the reference script's per-rank counts): per
+//    token the set of virtual ranks and of virtual nodes its valid experts
+//    live on (rank = e / (E/R), node = e / (E/N)), repeats collapsed; per-rank
+//    and per-node token counts, per-expert pair counts, the token-in-rank map
+//    and the RDMA algo count (deduplicated (token, node) pairs, local node
+//    included);
+//  * the dispatch plan (MSCCL++ PR 860, RANK_MAJOR commit: the default layout
+//    places tokens at compacted prefix offsets): a stable counting sort of
+//    the valid (t, j) pairs by expert -- expert segments back to back in
+//    expert order, pairs in row-major (t, j) order inside a segment.
+//
+// How (two launches; the kernel boundary publishes the first one's results,
+// so no cross-block fence or ticket is needed):
+//  ep_plan_count_kernel  one block per tile of TT whole tokens.  The tile's
+//      topk_idx is staged in LDS once.
+//      - pairs (lane = pair): bit `lane` of an LDS 64-bit mask per (wave,
+//        expert) is set with an atomic OR (order-independent); a pair's rank
+//        among the tile's earlier pairs of the same expert is the popcount of
+//        that expert's masks of earlier waves plus its own wave's mask below
+//        the lane.  Per-tile expert counts are popcounts of the masks.
+//      - tokens (lane = token): the token's ranks and nodes are OR-ed into two
+//        64-bit masks in registers (a repeated rank / node is a no-op), the
+//        token-in-rank row is written from the rank mask, and per-rank /
+//        per-node counts are wavefront ballots of one mask bit plus popcount.
+//  ep_plan_scan_kernel   one block: per expert the exclusive prefix of the
+//      tile counts over tiles (in place) and the total; the exclusive scan of
+//      the totals over experts (segment starts); per rank / node the sum over
+//      tiles.  Integer sums only: the plan and the counts are deterministic.
+#include "ep_device.h"
+#include "ep_internal.h"
+
+namespace ep {
+namespace {
+
+struct CountArgs {
+    const int64_t *topk_idx;
+    int64_t T;
+    int k, E, R, N, epr, epn;
+    int TT;                   // tokens per tile
+    int W;                    // waves whose masks exist (pairs per tile / 64, rounded up)
+    uint8_t *in_rank;         // [T][R] or null
+    int32_t *tile_count;      // [ntiles][E]
+    int32_t *rn_count;        // [ntiles][R + N]
+    int32_t *local_rank;      // [T * k]
+    uint32_t *ctrl;
+};
+
+__global__ __launch_bounds__(1024) void ep_plan_count_kernel(CountArgs a) {
+    extern __shared__ uint64_t lds[];
+    uint64_t *masks = lds;                                            // [W][E]
+    int32_t *ids = reinterpret_cast<int32_t *>(masks + (size_t)a.W * a.E);   // [TT * k]
+    int32_t *rn = ids + a.TT * a.k;                                   // [R + N]
+    const int tid = threadIdx.x, nt = blockDim.x;
+    const int lane = tid & (kWave - 1), w = tid / kWave;
+    const int E = a.E, k = a.k;
+    const int64_t t0 = (int64_t)blockIdx.x * a.TT;
+    const int ntok = (int)min<int64_t>(a.TT, a.T - t0);
+    const int npairs = ntok * k;
+
+    for (int i = tid; i < a.W * E; i += nt) masks[i] = 0ull;
+    for (int i = tid; i < a.R + a.N; i += nt) rn[i] = 0;
+    bool bad = false;
+    for (int q = tid; q < npairs; q += nt) {   // stage ids; invalid ids become masked
+        const int64_t v = a.topk_idx[t0 * k + q];
+        bad |= (v >= E);
+        ids[q] = (v >= 0 && v < E) ? (int32_t)v : -1;
+    }
+    __syncthreads();
+
+    // ---- pairs: ranks inside the tile
+    int e = -1;
+    if (tid < npairs) {
+        e = ids[tid];
+        if (e >= 0) atomicOr((unsigned long long *)&masks[w * E + e], 1ull << lane);
+    }
+    __syncthreads();
+    if (tid < npairs) {
+        int32_t r = -1;
+        if (e >= 0) {
+            r = (int32_t)__popcll(masks[w * E + e] & lanemask_lt());
+            for (int w2 = 0; w2 < w; ++w2) r += (int32_t)__popcll(masks[w2 * E + e]);
+        }
+        a.local_rank[t0 * k + tid] = r;
+    }
+    int32_t *tc = a.tile_count + (size_t)blockIdx.x * E;
+    for (int e2 = tid; e2 < E; e2 += nt) {
+        int32_t c = 0;
+        for (int w2 = 0; w2 < a.W; ++w2) c += (int32_t)__popcll(masks[w2 * E + e2]);
+        tc[e2] = c;
+    }
+
+    // ---- tokens: rank / node sets in registers
+    for (int tb = 0; tb < a.TT; tb += nt) {   // one pass unless TT > blockDim
+        const int tl = tb + tid;
+        uint64_t rmask = 0, nmask = 0;
+        if (tl < ntok) {
+            for (int j = 0; j < k; ++j) {
+                const int ej = ids[tl * k + j];
+                if (ej < 0) continue;
+                rmask |= 1ull << (ej / a.epr);
+                nmask |= 1ull << (ej / a.epn);
+            }
+            if (a.in_rank) {
+                uint8_t *out = a.in_rank + (t0 + tl) * a.R;
+                if ((a.R & 15) == 0) {
+                    for (int r0 = 0; r0 < a.R; r0 += 16) {
+                        vec16 v;
+                        for (int q = 0; q < 4; ++q) {
+                            uint32_t wd = 0;
+                            for (int b = 0; b < 4; ++b)
+                                wd |= (uint32_t)((rmask >> (r0 + 4 * q + b)) & 1u) << (8 * b);
+                            v[q] = wd;
+                        }
+                        st16(out + r0, v);
+                    }
+                } else if ((a.R & 3) == 0) {
+                    for (int r0 = 0; r0 < a.R; r0 += 4) {
+                        uint32_t wd = 0;
+                        for (int b = 0; b < 4; ++b) wd |= (uint32_t)((rmask >> (r0 + b)) & 1u) << (8 * b);
+                        *reinterpret_cast<uint32_t *>(out + r0) = wd;
+                    }
+                } else {
+                    for (int r = 0; r < a.R; ++r) out[r] = (uint8_t)((rmask >> r) & 1u);
+                }
+            }
+        }
+        // waves holding no token of this pass skip the ballots (wave-uniform)
+        if (tb + w * kWave < ntok) {
+            for (int r = 0; r < a.R; ++r) {
+                const uint64_t b = __ballot((rmask >> r) & 1u);
+                if (lane == 0 && b) atomicAdd(&rn[r], (int)__popcll(b));
+            }
+            for (int n = 0; n < a.N; ++n) {
+                const uint64_t b = __ballot((nmask >> n) & 1u);
+                if (lane == 0 && b) atomicAdd(&rn[a.R + n], (int)__popcll(b));
+            }
+        }
+    }
+    if (__ballot(bad) && lane == 0) atomicOr(&a.ctrl[0], kErrBadExpert);
+    __syncthreads();
+    int32_t *rc = a.rn_count + (size_t)blockIdx.x * (a.R + a.N);
+    for (int i = tid; i < a.R + a.N; i += nt) rc[i] = rn[i];
+}
+
+// Exclusive scan of n ints held in LDS (`in`), written to `out` (n + 1
+// entries, out[n] = total).  Called by every thread of the block.
+__device__ void block_exclusive_scan(const int32_t *in, int32_t *out, int n, int32_t *tmp) {
+    const int nt = blockDim.x, tid = threadIdx.x;
+    const int lane = tid & (kWave - 1), wid = tid / kWave, nw = (nt + kWave - 1) / kWave;
+    const int chunk = (n + nt - 1) / nt;
+    const int b = min(tid * chunk, n), e = min(b + chunk, n);
+    int32_t s = 0;
+    for (int i = b; i < e; ++i) s += in[i];
+    int32_t v = s;
+    for (int off = 1; off < kWave; off <<= 1) {
+        const int32_t u = __shfl_up(v, off);
+        if (lane >= off) v += u;
+    }
+    if (lane == kWave - 1) tmp[wid] = v;
+    __syncthreads();
+    if (tid == 0) {
+        int32_t run = 0;
+        for (int i = 0; i < nw; ++i) {
+            const int32_t x = tmp[i];
+            tmp[i] = run;
+            run += x;
+        }
+        tmp[nw] = run;
+    }
+    __syncthreads();
+    int32_t excl = tmp[wid] + v - s;
+    for (int i = b; i < e; ++i) {
+        const int32_t x = in[i];
+        out[i] = excl;
+        excl += x;
+    }
+    if (tid == 0) out[n] = tmp[nw];
+    __syncthreads();
+}
+
+struct ScanArgs {
+    int E, R, N, ntiles;
+    int32_t *tile_count;      // [ntiles][E] -> exclusive prefix over tiles
+    const int32_t *rn_count;  // [ntiles][R + N]
+    int32_t *plan_offset;     // [E + 1] segment starts (workspace copy)
+    int32_t *per_expert;      // [E] or null
+    int32_t *per_rank;        // [R] or null
+    int32_t *per_node;        // [N] or null
+    int64_t *algo;            // [1] or null
+};
+
+constexpr int kScanMaxE = 4096;
+constexpr int kScanBatch = 16;
+
+__global__ __launch_bounds__(1024) void ep_plan_scan_kernel(ScanArgs a) {
+    __shared__ int32_t part[kScanMaxE + 1];
+    __shared__ int32_t tmp[1024 / kWave + 1];
+    const int tid = threadIdx.x, nt = blockDim.x, E = a.E;
+    // Q threads share an expert's tiles (E < blockDim); each owns `chunk` tiles
+    const int Q = (nt >= E) ? nt / E : 1;
+    const int chunk = (a.ntiles + Q - 1) / Q;
+    for (int idx = tid; idx < E * Q; idx += nt) {
+        const int ee = idx % E, q = idx / E;
+        const int ta = min(q * chunk, a.ntiles), tb = min(ta + chunk, a.ntiles);
+        const int32_t *col = a.tile_count + ee;
+        int32_t s = 0;
+        for (int t = ta; t < tb; t += kScanBatch) {
+            int32_t c[kScanBatch];
+#pragma unroll
+            for (int u = 0; u < kScanBatch; ++u) c[u] = (t + u < tb) ? col[(size_t)(t + u) * E] : 0;
+#pragma unroll
+            for (int u = 0; u < kScanBatch; ++u) s += c[u];
+        }
+        part[idx] = s;   // idx = q * E + ee
+    }
+    __syncthreads();
+    for (int idx = tid; idx < E * Q; idx += nt) {
+        const int ee = idx % E, q = idx / E;
+        int32_t run = 0;
+        for (int q2 = 0; q2 < q; ++q2) run += part[q2 * E + ee];
+        const int ta = min(q * chunk, a.ntiles), tb = min(ta + chunk, a.ntiles);
+        int32_t *col = a.tile_count + ee;
+        for (int t = ta; t < tb; t += kScanBatch) {
+            int32_t c[kScanBatch];
+#pragma unroll
+            for (int u = 0; u < kScanBatch; ++u) c[u] = (t + u < tb) ? col[(size_t)(t + u) * E] : 0;
+#pragma unroll
+            for (int u = 0; u < kScanBatch; ++u) {
+                if (t + u < tb) col[(size_t)(t + u) * E] = run;
+                run += c[u];
+            }
+        }
+    }
+    __syncthreads();
+    for (int ee = tid; ee < E; ee += nt) {
+        int32_t s = 0;
+        for (int q = 0; q < Q; ++q) s += part[q * E + ee];
+        part[ee] = s;   // column ee is read and written by this thread only
+        if (a.per_expert) a.per_expert[ee] = s;
+    }
+    __syncthreads();
+    block_exclusive_scan(part, a.plan_offset, E, tmp);
+
+    // rank / node token counts: sums over tiles
+    const int RN = a.R + a.N;
+    if (a.per_rank) {
+        for (int i = tid; i < RN; i += nt) {
+            int32_t s = 0;
+            for (int t = 0; t < a.ntiles; t += kScanBatch) {
+                int32_t c[kScanBatch];
+#pragma unroll
+                for (int u = 0; u < kScanBatch; ++u)
+                    c[u] = (t + u < a.ntiles) ? a.rn_count[(size_t)(t + u) * RN + i] : 0;
+#pragma unroll
+                for (int u = 0; u < kScanBatch; ++u) s += c[u];
+            }
+            if (i < a.R) a.per_rank[i] = s; else a.per_node[i - a.R] = s;
+            part[i] = s;
+        }
+        __syncthreads();
+        if (tid == 0) {
+            int64_t al = 0;
+            for (int n = 0; n < a.N; ++n) al += part[a.R + n];
+            *a.algo = al;
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_plan(const Shape &s, const WsLayout &L, const int64_t *topk_idx,
+                       int32_t *per_rank, int32_t *per_expert, uint8_t *in_rank,
+                       int32_t *per_node, int64_t *algo, char *ws, hipStream_t stream) {
+    CountArgs c;
+    c.topk_idx = topk_idx;
+    c.T = s.T;
+    c.k = s.k;
+    c.E = s.E;
+    c.R = s.R;
+    c.N = s.N;
+    c.epr = s.E / s.R;
+    c.epn = s.E / s.N;
+    c.TT = L.tile_tokens;
+    c.W = L.tile_waves;
+    c.in_rank = in_rank;
+    c.tile_count = reinterpret_cast<int32_t *>(ws + L.tile_count);
+    c.rn_count = reinterpret_cast<int32_t *>(ws + L.rn_count);
+    c.local_rank = reinterpret_cast<int32_t *>(ws + L.local_rank);
+    c.ctrl = reinterpret_cast<uint32_t *>(ws + L.ctrl);
+    if (s.T > 0) {
+        const size_t lds = sizeof(uint64_t) * (size_t)L.tile_waves * s.E +
+                           sizeof(int32_t) * ((size_t)L.tile_tokens * s.k + s.R + s.N);
+        hipLaunchKernelGGL(ep_plan_count_kernel, dim3(L.tiles), dim3(L.count_threads), lds, stream, c);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    ScanArgs a;
+    a.E = s.E;
+    a.R = s.R;
+    a.N = s.N;
+    a.ntiles = s.T > 0 ? L.tiles : 0;
+    a.tile_count = c.tile_count;
+    a.rn_count = c.rn_count;
+    a.plan_offset = reinterpret_cast<int32_t *>(ws + L.plan_offset);
+    a.per_expert = per_expert;
+    a.per_rank = per_rank;
+    a.per_node = per_node;
+    a.algo = algo;
+    hipLaunchKernelGGL(ep_plan_scan_kernel, dim3(1), dim3(1024), 0, stream, a);
+    return hipGetLastError();
+}
+
+}  // namespace ep

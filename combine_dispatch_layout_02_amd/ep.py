@@ -27,7 +27,8 @@ EP_OK, EP_EINVAL, EP_EALIGN, EP_EWORKSPACE, EP_EHIP, EP_EDEVICE = 0, -1, -2, -3,
 # every symbol include/ep.h declares
 EXPORTED = (
     "ep_abi_version", "ep_strerror", "ep_validate_shape", "ep_workspace_bytes", "ep_workspace_init",
-    "ep_dispatch_layout", "ep_dispatch", "ep_combine", "ep_check", "ep_quant_fp8_s128",
+    "ep_dispatch_layout", "ep_dispatch", "ep_dispatch_from_layout", "ep_combine", "ep_check",
+    "ep_quant_fp8_s128",
     "ep_expert_scale_bf16", "ep_expert_requant_mxfp8", "ep_accounting", "ep_calib_copy",
 )
 
@@ -89,6 +90,7 @@ def load():
         "ep_workspace_init": (ctypes.c_int, [P, sz, P]),
         "ep_dispatch_layout": (ctypes.c_int, [SP, P, P, P, P, P, P, P, sz, P]),
         "ep_dispatch": (ctypes.c_int, [SP, P, P, P, P, P, P, P, P, P, P, P, sz, P]),
+        "ep_dispatch_from_layout": (ctypes.c_int, [SP, P, P, P, P, P, P, P, P, P, P, P, sz, P]),
         "ep_combine": (ctypes.c_int, [SP, P, P, P, P, P, P]),
         "ep_check": (ctypes.c_int, [P, sz, P, ctypes.POINTER(ctypes.c_uint32)]),
         "ep_quant_fp8_s128": (ctypes.c_int, [i64, i32, P, P, P, P]),
@@ -156,6 +158,7 @@ class Workspace:
         self._buf = torch.empty(self.nbytes + 256, dtype=torch.uint8, device=dev)
         off = (-self._buf.data_ptr()) % 256
         self.tensor = self._buf[off:off + self.nbytes]
+        self.planned_for = None   # (topk_idx pointer, shape fields) of the last layout call
         _ok(lib.ep_workspace_init(_ptr(self.tensor), self.nbytes, _stream(stream)), "ep_workspace_init")
 
     @property
@@ -187,10 +190,17 @@ def ep_dispatch_layout(shape, topk_idx, num_tokens_per_rank, num_tokens_per_expe
                                   _ptr(num_tokens_per_expert), _ptr(is_token_in_rank),
                                   _ptr(num_tokens_per_node), _ptr(rdma_algo_token_count), ws.ptr,
                                   ws.nbytes, _stream(stream)), "ep_dispatch_layout")
+    ws.planned_for = (topk_idx.data_ptr(), _shape_key(shape))
+
+
+def _shape_key(shape):
+    return tuple(getattr(shape, f) for f, _ in shape._fields_)
 
 
 def ep_dispatch(shape, x, x_scales, topk_idx, topk_w, recv_x, recv_x_scales, recv_src_idx, recv_topk_w,
-                token_slot, expert_offset, ws: Workspace, stream=None):
+                token_slot, expert_offset, ws: Workspace, stream=None, from_layout=False):
+    """from_layout=True calls ep_dispatch_from_layout: the plan of the preceding
+    ep_dispatch_layout call on this workspace and this topk_idx is reused."""
     T, k, H, E = shape.num_tokens, shape.num_topk, shape.hidden, shape.num_experts
     fp8 = shape.x_format == EP_FMT_FP8_S128
     _need(x, torch.uint8 if fp8 else torch.bfloat16, (T, H), "x")
@@ -204,10 +214,18 @@ def ep_dispatch(shape, x, x_scales, topk_idx, topk_w, recv_x, recv_x_scales, rec
     _need(recv_topk_w, torch.float32, (T * k,), "recv_topk_w")
     _need(token_slot, torch.int32, (T, k), "token_slot")
     _need(expert_offset, torch.int32, (E + 1,), "expert_offset")
-    _ok(load().ep_dispatch(ctypes.byref(shape), _ptr(x), _ptr(x_scales), _ptr(topk_idx), _ptr(topk_w),
-                           _ptr(recv_x), _ptr(recv_x_scales), _ptr(recv_src_idx), _ptr(recv_topk_w),
-                           _ptr(token_slot), _ptr(expert_offset), ws.ptr, ws.nbytes, _stream(stream)),
-        "ep_dispatch")
+    fn = load().ep_dispatch
+    if from_layout:
+        if ws.planned_for != (topk_idx.data_ptr(), _shape_key(shape)):
+            raise RuntimeError("ep_dispatch_from_layout needs a preceding ep_dispatch_layout on this "
+                               "workspace with the same topk_idx and shape")
+        fn = load().ep_dispatch_from_layout
+    else:
+        ws.planned_for = None   # ep_dispatch rewrites the plan (same content for the same topk_idx)
+    _ok(fn(ctypes.byref(shape), _ptr(x), _ptr(x_scales), _ptr(topk_idx), _ptr(topk_w),
+           _ptr(recv_x), _ptr(recv_x_scales), _ptr(recv_src_idx), _ptr(recv_topk_w),
+           _ptr(token_slot), _ptr(expert_offset), ws.ptr, ws.nbytes, _stream(stream)),
+        "ep_dispatch_from_layout" if from_layout else "ep_dispatch")
 
 
 def ep_combine(shape, expert_out, expert_out_scales, token_slot, topk_w, y, stream=None):
@@ -288,7 +306,7 @@ def dispatch_layout(topk_idx, shape, ws: Workspace, stream=None) -> dict:
     return out
 
 
-def dispatch(x, topk_idx, topk_w, shape, ws: Workspace, x_scales=None, stream=None):
+def dispatch(x, topk_idx, topk_w, shape, ws: Workspace, x_scales=None, stream=None, from_layout=False):
     """Returns recv_x, recv_x_scales (None for bf16), recv_src_idx, recv_topk_w, handle."""
     dev = x.device
     T, k, H, E = shape.num_tokens, shape.num_topk, shape.hidden, shape.num_experts
@@ -300,7 +318,7 @@ def dispatch(x, topk_idx, topk_w, shape, ws: Workspace, x_scales=None, stream=No
     token_slot = torch.empty((T, k), dtype=torch.int32, device=dev)
     expert_offset = torch.empty(E + 1, dtype=torch.int32, device=dev)
     ep_dispatch(shape, x, x_scales, topk_idx, topk_w, recv_x, recv_x_scales, recv_src_idx, recv_topk_w,
-                token_slot, expert_offset, ws, stream)
+                token_slot, expert_offset, ws, stream, from_layout)
     return recv_x, recv_x_scales, recv_src_idx, recv_topk_w, Handle(shape, token_slot, expert_offset, topk_w)
 
 

@@ -103,12 +103,12 @@ int ep_validate_shape(const ep_shape *shape);
 
 /* Host-only: bytes of device workspace ep_dispatch_layout / ep_dispatch need
  * for this shape (written to *bytes).  The workspace holds the error word,
- * the single-pass reduction tickets, per-block partial counts, per-tile
- * expert counts and per-pair ranks inside a tile. */
+ * per-tile expert / rank / node counts, each pair's rank inside its tile and
+ * the expert segment starts (the dispatch plan). */
 int ep_workspace_bytes(const ep_shape *shape, size_t *bytes);
 
-/* Zero a workspace (a fill kernel on `stream`, no memset node).  Required
- * once after allocation; afterwards every call leaves the tickets at zero. */
+/* Zero a workspace (a fill kernel on `stream`, no memset node): clears the
+ * error word.  Call once after allocation. */
 int ep_workspace_init(void *ws, size_t ws_bytes, void *stream);
 
 /*
@@ -124,6 +124,9 @@ int ep_workspace_init(void *ws, size_t ws_bytes, void *stream);
  *                         node included (= sum of num_tokens_per_node)
  * The physical count algo * (N-1)/N and the exact per-source count are host
  * arithmetic (ep_accounting).  Deterministic: integer counts only.
+ * The call also leaves the dispatch plan of this topk_idx (expert segment
+ * starts, per-tile prefixes, ranks inside tiles) in the workspace, where
+ * ep_dispatch_from_layout uses it.
  */
 int ep_dispatch_layout(const ep_shape *shape, const int64_t *topk_idx,
                        int32_t *num_tokens_per_rank, int32_t *num_tokens_per_expert,
@@ -160,6 +163,21 @@ int ep_dispatch(const ep_shape *shape, const void *x, const float *x_scales,
                 void *recv_x, float *recv_x_scales, int32_t *recv_src_idx, float *recv_topk_w,
                 int32_t *token_slot, int32_t *expert_offset,
                 void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Dispatch that reuses the plan the preceding ep_dispatch_layout call on the
+ * SAME workspace and the SAME topk_idx left there (stream-ordered before
+ * this call): same arguments and results as ep_dispatch, minus the planning
+ * launches.  The pages' cached dispatch ([PR860] cached_notify /
+ * previous_handle) reuses a layout the same way.  Calling it without that
+ * preceding layout call, or with a different topk_idx, gives unspecified
+ * slots (the kernel still never writes outside [0, T*k) rows).
+ */
+int ep_dispatch_from_layout(const ep_shape *shape, const void *x, const float *x_scales,
+                            const int64_t *topk_idx, const float *topk_w,
+                            void *recv_x, float *recv_x_scales, int32_t *recv_src_idx,
+                            float *recv_topk_w, int32_t *token_slot, int32_t *expert_offset,
+                            void *ws, size_t ws_bytes, void *stream);
 
 /*
  * Combine: the top-k weighted gather-reduce back into token order ([MORI]

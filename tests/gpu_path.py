@@ -19,7 +19,9 @@ def bf16_bits(t: torch.Tensor) -> np.ndarray:
     return t.view(torch.int16).cpu().numpy().view(np.uint16)
 
 
-def run(inp: dict, dev="cuda", check=True) -> dict:
+def run(inp: dict, dev="cuda", check=True, from_layout=True) -> dict:
+    """from_layout: dispatch reuses the layout call's plan (ep_dispatch_from_layout);
+    otherwise the standalone ep_dispatch plans again."""
     T, H, E, R, N, k = (inp[n] for n in ("T", "H", "E", "R", "N", "k"))
     fp8 = inp.get("x_fmt", "bf16") == "fp8"
     shape = ep.make_shape(T, H, E, R, N, k, ep.EP_FMT_FP8_S128 if fp8 else ep.EP_FMT_BF16,
@@ -32,7 +34,7 @@ def run(inp: dict, dev="cuda", check=True) -> dict:
     lay = ep.dispatch_layout(idx, shape, ws)
     if fp8:
         q, s = ep.quant_fp8_s128(x)
-        recv_x, recv_s, src, rw, h = ep.dispatch(q, idx, w, shape, ws, x_scales=s)
+        recv_x, recv_s, src, rw, h = ep.dispatch(q, idx, w, shape, ws, x_scales=s, from_layout=from_layout)
         factor = inp.get("expert_factor")
         f = None if factor is None else torch.from_numpy(factor).to(dev)
         eq = torch.zeros((T * k, H), dtype=torch.uint8, device=dev)
@@ -42,7 +44,7 @@ def run(inp: dict, dev="cuda", check=True) -> dict:
         out.update(x_q=q.cpu().numpy(), x_scales=s.cpu().numpy(), recv_x=recv_x.cpu().numpy(),
                    recv_x_scales=recv_s.cpu().numpy(), expert_q=eq.cpu().numpy(), expert_e8m0=ee.cpu().numpy())
     else:
-        recv_x, _, src, rw, h = ep.dispatch(x, idx, w, shape, ws)
+        recv_x, _, src, rw, h = ep.dispatch(x, idx, w, shape, ws, from_layout=from_layout)
         if inp.get("expert") == "scale":
             eo = torch.zeros_like(recv_x)
             f = torch.from_numpy(inp["expert_factor"]).to(dev)

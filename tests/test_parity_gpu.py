@@ -26,19 +26,20 @@ def _gpu():
     ep.load()  # fails loudly if the HIP library is missing
 
 
-def _run_both(inp):
+def _run_both(inp, from_layout=True):
     import gpu_path
     print(f"case {inp.get('name')} T={inp['T']} H={inp['H']} E={inp['E']} R={inp['R']} N={inp['N']} "
-          f"k={inp['k']} seed={inp.get('seed')}", flush=True)
-    g = gpu_path.run(inp)
+          f"k={inp['k']} seed={inp.get('seed')} from_layout={from_layout}", flush=True)
+    g = gpu_path.run(inp, from_layout=from_layout)
     r = oracle.run_path(inp)
     ndiff = gpu_path.compare(g, r, inp.get("x_fmt") == "fp8")
     return g, r, ndiff
 
 
+@pytest.mark.parametrize("from_layout", [True, False], ids=["from_layout", "standalone"])
 @pytest.mark.parametrize("name", list(W.WORKLOADS))
-def test_workload_full_size(name):
-    g, r, ndiff = _run_both(W.make_inputs(name))
+def test_workload_full_size(name, from_layout):
+    g, r, ndiff = _run_both(W.make_inputs(name), from_layout)
     assert ndiff == 0
     if W.WORKLOADS[name]["x_fmt"] == "bf16" and W.WORKLOADS[name]["expert"] == "identity":
         inp = W.make_inputs(name)
@@ -57,14 +58,17 @@ def test_ragged_token_counts(T):
     dict(E=64, R=64, N=8, k=8), dict(E=4096, R=64, N=64, k=32, T=300), dict(H=8, T=100),
     dict(H=7176, T=130)])
 def test_edge_cases_bf16(kw):
+    kw = dict(kw)
     base = dict(T=kw.pop("T", 700), H=kw.pop("H", 512))
     base.update(kw)
-    _, _, ndiff = _run_both(W.make_inputs("tiny", **base))
-    assert ndiff == 0
+    for from_layout in (True, False):
+        _, _, ndiff = _run_both(W.make_inputs("tiny", **base), from_layout)
+        assert ndiff == 0
 
 
 @pytest.mark.parametrize("kw", [dict(mask_frac=0.25), dict(routing="replace", T=333), dict(E=32, R=8, N=2)])
 def test_edge_cases_quantized(kw):
+    kw = dict(kw)
     base = dict(T=kw.pop("T", 500), H=1024)
     base.update(kw)
     _, _, ndiff = _run_both(W.make_inputs("quant", **base))
@@ -76,10 +80,11 @@ def test_scaled_expert_with_masks():
     assert ndiff == 0
 
 
-def test_empty_batch():
+@pytest.mark.parametrize("from_layout", [True, False])
+def test_empty_batch(from_layout):
     import gpu_path
     inp = W.make_inputs("tiny", T=0)
-    g = gpu_path.run(inp)
+    g = gpu_path.run(inp, from_layout=from_layout)
     assert g["layout"]["rdma_algo_token_count"] == 0
     assert (g["layout"]["num_tokens_per_rank"] == 0).all()
     assert (g["layout"]["num_tokens_per_expert"] == 0).all()
@@ -111,8 +116,9 @@ def test_repeat_calls_are_deterministic():
 
 
 def test_workspace_reuse_across_calls():
-    """The single-pass tickets return to zero after every call: three calls on
-    one workspace with different routings all match the oracle."""
+    """Every layout / standalone dispatch call rewrites the plan in the
+    workspace: three rounds on one workspace with different routings, mixing
+    both dispatch entry points, all match the oracle."""
     from combine_dispatch_layout_02_amd import ep
     import gpu_path
     inp = W.make_inputs("prefill2n", T=777, H=256)
@@ -124,10 +130,23 @@ def test_workspace_reuse_across_calls():
         w = torch.from_numpy(inp["topk_w"]).cuda()
         x = gpu_path.to_dev_bf16(inp["x"])
         lay = ep.dispatch_layout(idx, shape, ws)
-        recv_x, _, src, rw, h = ep.dispatch(x, idx, w, shape, ws)
+        recv_x, _, src, rw, h = ep.dispatch(x, idx, w, shape, ws, from_layout=seed % 2 == 0)
         y = ep.combine(recv_x, h)
         ws.check()
         r = oracle.run_path(inp)
         assert int(lay["rdma_algo_token_count"].item()) == r["layout"]["rdma_algo_token_count"]
         np.testing.assert_array_equal(h.token_slot.cpu().numpy(), r["slots"]["token_slot"])
         np.testing.assert_array_equal(gpu_path.bf16_bits(y), r["y"])
+
+
+def test_from_layout_requires_a_layout_call():
+    from combine_dispatch_layout_02_amd import ep
+    import gpu_path
+    inp = W.make_inputs("tiny")
+    shape = ep.make_shape(inp["T"], inp["H"], inp["E"], inp["R"], inp["N"], inp["k"])
+    ws = ep.Workspace(shape)
+    idx = torch.from_numpy(inp["topk_idx"]).cuda()
+    w = torch.from_numpy(inp["topk_w"]).cuda()
+    x = gpu_path.to_dev_bf16(inp["x"])
+    with pytest.raises(RuntimeError, match="preceding ep_dispatch_layout"):
+        ep.dispatch(x, idx, w, shape, ws, from_layout=True)
