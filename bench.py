@@ -4,9 +4,11 @@
 One step = the whole path over one batch of synthetic input already resident
 in HBM: ep_dispatch_layout (layout counts and the dispatch plan) ->
 ep_dispatch_from_layout (the row permutation) -> (expert stage of the
-workload, if any) -> ep_combine, all on one stream.  W untimed warmup steps, then K
-timed steps bracketed by stream synchronisation and HIP events; the per-call
-durations come from events recorded on the same stream between the calls.
+workload, if any) -> ep_combine, all on one stream.  W untimed warmup steps,
+then K timed steps bracketed by stream synchronisation and HIP events, three
+ways: replayed from HIP graphs of 10 captured steps (the reported
+ms_per_step), eager back to back (eager_ms_per_step), and eager with events
+between the calls (the per-call durations in phase_us).
 
 Prints one JSON line:
   value         algorithmic HBM bytes of the step / step time (GB/s)
@@ -35,6 +37,7 @@ HBM_PEAK_GBS = 8000.0   # MI355X HBM3E, published peak
 # known size; filled in from the committed profiles for the kernel build they
 # were taken on (None = not measured for the current kernels).
 MEASURED_TRAFFIC = {}
+GRAPH_STEPS = 10   # steps captured per HIP graph
 
 
 def parse():
@@ -45,7 +48,8 @@ def parse():
     ap.add_argument("--workload", default="prefill2n")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
-    ap.add_argument("--graph", action="store_true", help="also time K steps replayed from one HIP graph")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="time the eager loop only (default: K steps replayed from HIP graphs of %d steps)" % GRAPH_STEPS)
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="only run the plain copy kernel on this many MiB, --steps times (counter calibration)")
     return ap.parse_args()
@@ -59,16 +63,14 @@ def main():
                                    "runs on more than one GPU are not part of it (use --gpus 1)"}))
         sys.exit(2)
 
-    import numpy as np
     import torch
 
-    from combine_dispatch_layout_02_amd import ep, workloads
+    from combine_dispatch_layout_02_amd import ep
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     ep.load()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    stream = torch.cuda.current_stream()
 
     if args.calib_copy_mib:
         n = args.calib_copy_mib << 20
@@ -80,7 +82,23 @@ def main():
         print(json.dumps({"calib_copy_bytes": n, "launches": args.steps}))
         return
 
-    inp = workloads.make_inputs(args.workload)
+    out = measure(args.workload, args.steps, args.warmup, not args.no_graph)
+    inp = out.pop("_inp")
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds, out["step_algorithmic_bytes"])
+    print(json.dumps(out), flush=True)
+
+
+def measure(workload: str, steps: int, warmup: int, graph: bool = False) -> dict:
+    """Time `steps` steps of the path on `workload` (inputs resident in HBM)."""
+    import numpy as np
+    import torch
+
+    from combine_dispatch_layout_02_amd import ep, workloads
+
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    inp = workloads.make_inputs(workload)
     T, H, E, R, N, k = (inp[n] for n in ("T", "H", "E", "R", "N", "k"))
     fp8 = inp["x_fmt"] == "fp8"
     shape = ep.make_shape(T, H, E, R, N, k, ep.EP_FMT_FP8_S128 if fp8 else ep.EP_FMT_BF16,
@@ -135,51 +153,72 @@ def main():
     phases = [("layout", layout), ("dispatch", dispatch)] + ([("expert", expert)] if has_expert else []) \
         + [("combine", combine)]
 
-    for _ in range(args.warmup):
+    def step():
         for _, fn in phases:
             fn()
+
+    for _ in range(warmup):
+        step()
     ws.check()
     torch.cuda.synchronize()
     V = int(off[-1].item())
+    y_ref = y.clone()   # every step recomputes the same y from the same inputs
 
-    # timed region: K steps, events between the calls on the launch stream
-    K = args.steps
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(phases) + 1)] for _ in range(K)]
-    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    def timed(run_steps) -> float:
+        """ms per step of `steps` steps, stream-synchronised on both sides."""
+        a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a0.record(stream)
+        run_steps()
+        a1.record(stream)
+        torch.cuda.synchronize()
+        return a0.elapsed_time(a1) / steps
+
+    # (1) eager: K steps back to back on the stream
+    def eager():
+        for _ in range(steps):
+            step()
+    eager_ms = timed(eager)
+    ws.check()
+
+    # (2) per-call durations: K more steps with events between the calls
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(phases) + 1)] for _ in range(steps)]
     torch.cuda.synchronize()
-    t0.record(stream)
-    for s in range(K):
+    for s in range(steps):
         ev[s][0].record(stream)
         for i, (_, fn) in enumerate(phases):
             fn()
             ev[s][i + 1].record(stream)
-    t1.record(stream)
     torch.cuda.synchronize()
-    ms_step = t0.elapsed_time(t1) / K
-    phase_us = {name: 1000.0 * sum(ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(K)) / K
+    phase_us = {name: 1000.0 * sum(ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(steps)) / steps
                 for i, (name, _) in enumerate(phases)}
-    ws.check()
 
-    graph_ms = None
-    if args.graph:
+    # (3) HIP graph: G steps captured once, replayed K/G times (launch gaps
+    # between steps vanish inside a graph, as in a captured serving loop)
+    graph_ms, G = None, 0
+    if graph:
+        G = max(1, min(GRAPH_STEPS, steps))
+        while steps % G:
+            G -= 1
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
-            for _, fn in phases:
-                fn()
-        y_eager = y.clone()
-        g.replay()
-        torch.cuda.synchronize()
-        if not torch.equal(y.view(torch.int16), y_eager.view(torch.int16)):
-            raise RuntimeError("graph replay differs from the eager step")
-        ga, gb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        ga.record(stream)
-        for _ in range(K):
+            for _ in range(G):
+                step()
+        for _ in range(2):   # replays, with eager work and syncs in between, must match the eager result
             g.replay()
-        gb.record(stream)
-        torch.cuda.synchronize()
-        graph_ms = ga.elapsed_time(gb) / K
-        if not torch.equal(y.view(torch.int16), y_eager.view(torch.int16)):
+            torch.cuda.synchronize()
+            if not torch.equal(y.view(torch.int16), y_ref.view(torch.int16)):
+                raise RuntimeError("graph replay differs from the eager step")
+            step()
+            torch.cuda.synchronize()
+
+        def replays():
+            for _ in range(steps // G):
+                g.replay()
+        graph_ms = timed(replays)
+        if not torch.equal(y.view(torch.int16), y_ref.view(torch.int16)):
             raise RuntimeError("graph replays differ from the eager step")
+    ms_step = graph_ms if graph_ms is not None else eager_ms
 
     # algorithmic bytes (library accounting on host copies of the layout)
     acc = ep.ep_accounting(shape, 0, lay["r"].cpu().numpy(), lay["n"].cpu().numpy(), int(lay["a"].item()), V)
@@ -196,7 +235,7 @@ def main():
     kernels = {"dispatch": "ep_dispatch_copy_kernel", "combine": "ep_combine_" +
                ("mxfp8" if fp8 else "bf16") + "_kernel"}
     achieved = algo_bytes[dom] / (phase_us[dom] * 1e-6) / 1e9
-    traffic = MEASURED_TRAFFIC.get((args.workload, dom))
+    traffic = MEASURED_TRAFFIC.get((workload, dom))
 
     out = {
         "metric": METRIC,
@@ -204,20 +243,21 @@ def main():
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": K,
-        "warmup": args.warmup,
+        "warmup": warmup,
         "ms_per_step": round(ms_step, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "fp8/mxfp8" if fp8 else "bf16",
         "data": "synthetic",
-        "config": {"workload": args.workload, "tokens": T, "hidden": H, "experts": E, "virtual_ranks": R,
+        "config": {"workload": workload, "tokens": T, "hidden": H, "experts": E, "virtual_ranks": R,
                    "virtual_nodes": N, "topk": k, "routing": inp["routing"], "expert": inp["expert"],
                    "x_format": inp["x_fmt"], "valid_pairs": V},
         "tokens_per_s": round(T / step_s, 1),
         "phase_us": {p: round(v, 2) for p, v in phase_us.items()},
         "step_algorithmic_bytes": int(step_bytes),
-        "graph_ms_per_step": None if graph_ms is None else round(graph_ms, 4),
+        "eager_ms_per_step": round(eager_ms, 4),
+        "timing": ("steps replayed from a HIP graph of %d steps" % G) if graph_ms is not None else "eager",
         "roofline": {"bound": "hbm", "kernel": kernels[dom], "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "algorithmic_bytes_per_launch": int(algo_bytes[dom])},
@@ -227,10 +267,8 @@ def main():
                              "dispatch_rdma_bytes_bf16": acc["dispatch_rdma_bytes_bf16"],
                              "dispatch_nvl_bytes_bf16": acc["dispatch_nvl_bytes_bf16"]},
     }
-
-    if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds, step_bytes)
-    print(json.dumps(out), flush=True)
+    out["_inp"] = inp
+    return out
 
 
 def cpu_baseline(inp, seconds, step_bytes):

@@ -12,11 +12,11 @@
 // (exact in binary32).
 //
 // How: one wave per (token, row part).  Lanes 0..k-1 read the token's slots
-// and weights, which readlane moves into scalar registers, so every branch on
-// a slot is uniform.  Each lane owns 16-byte column vectors of the row; per
-// batch of up to 8 slots it issues all the batch's loads before the first
-// FMA, keeping 8 rows in flight per wave, then applies v_fma_f32 in slot
-// order.  Nothing is reduced across lanes, so the result does not depend on
+// and weights, which readlane moves into scalar registers, so every decision
+// on a slot is uniform.  Each lane owns 16-byte column vectors of the row;
+// per batch of slots (all k when k is a compile-time constant) it issues
+// every load of the batch before the first FMA, then applies v_fma_f32 in
+// slot order.  Nothing is reduced across lanes, so the result does not depend on
 // the launch shape.  The gathered rows are read once: the loads carry the
 // non-temporal hint so they do not evict what the caches still hold.
 #include "ep_device.h"
@@ -40,23 +40,47 @@ struct CombineArgs {
 
 constexpr int kSlotBatch = 8;
 
-// bf16 rows: a 16-byte vector holds 8 elements; C vectors per lane per pass.
-template <int C>
+#ifndef EP_COMBINE_VECS
+#define EP_COMBINE_VECS 4      // 16-byte vectors per lane per pass (bf16 rows)
+#endif
+#ifndef EP_COMBINE_WAVES
+#define EP_COMBINE_WAVES 16384   // waves the combine aims for (16 per CU)
+#endif
+#ifndef EP_COMBINE_Y_NT
+#define EP_COMBINE_Y_NT 0      // non-temporal stores for y
+#endif
+
+__device__ __forceinline__ void store_y(char *p, vec16 v) {
+    if (EP_COMBINE_Y_NT) st16_nt(p, v); else st16(p, v);
+}
+
+// Slot j of the token in a scalar register; lanes >= k hold -1, so any j < 64
+// past the token's slots reads as masked.  A masked slot's load is pointed at
+// row 0 (always allocated, and cache-resident when several slots are masked)
+// so every load of a batch is unconditional and issued back to back; its
+// FMAs are skipped, which keeps the masked-slot semantics exact.
+__device__ __forceinline__ int64_t row_of(int32_t s) { return s >= 0 ? (int64_t)s : 0; }
+
+// bf16 rows: a 16-byte vector holds 8 elements; C vectors per lane per pass,
+// KB slots per batch (k itself when k is a compile-time constant KC).
+template <int C, int KC>
 __global__ __launch_bounds__(256) void ep_combine_bf16_kernel(CombineArgs a) {
+    constexpr int KB = KC > 0 ? KC : kSlotBatch;
     const int lane = threadIdx.x & (kWave - 1);
     const int64_t gw = (int64_t)blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
     const int64_t t = gw / a.S;
     const int sub = (int)(gw - t * a.S);
     if (t >= a.T) return;
+    const int k = KC > 0 ? KC : a.k;
 
     int32_t slot = -1;
     float wt = 0.0f;
-    if (lane < a.k) {
-        slot = a.token_slot[t * a.k + lane];
-        wt = a.topk_w[t * a.k + lane];
-        if ((uint64_t)slot >= (uint64_t)(a.T * a.k)) slot = -1;   // outside the receive rows: masked
+    if (lane < k) {
+        slot = a.token_slot[t * k + lane];
+        wt = a.topk_w[t * k + lane];
+        if ((uint64_t)slot >= (uint64_t)(a.T * k)) slot = -1;   // outside the receive rows: masked
     }
-    const bool any_valid = __ballot(lane < a.k && slot >= 0) != 0;
+    const bool any_valid = __ballot(lane < k && slot >= 0) != 0;
     char *yrow = a.y + t * (int64_t)a.H * 2;
     const int stride = kWave * a.S;
 
@@ -67,15 +91,11 @@ __global__ __launch_bounds__(256) void ep_combine_bf16_kernel(CombineArgs a) {
 #pragma unroll
             for (int q = 0; q < 8; ++q) acc[i][q] = -0.0f;
 
-        for (int jb = 0; jb < a.k; jb += kSlotBatch) {
-            vec16 buf[kSlotBatch][C];
+        for (int jb = 0; jb < k; jb += KB) {
+            vec16 buf[KB][C];
 #pragma unroll
-            for (int jj = 0; jj < kSlotBatch; ++jj) {
-                const int j = jb + jj;
-                if (j >= a.k) break;
-                const int32_t s = readlane(slot, j);
-                if (s < 0) continue;
-                const char *row = a.eo + (int64_t)s * a.row_bytes;
+            for (int jj = 0; jj < KB; ++jj) {
+                const char *row = a.eo + row_of(readlane(slot, jb + jj)) * a.row_bytes;
 #pragma unroll
                 for (int i = 0; i < C; ++i) {
                     const int v = v0 + i * stride;
@@ -83,21 +103,16 @@ __global__ __launch_bounds__(256) void ep_combine_bf16_kernel(CombineArgs a) {
                 }
             }
 #pragma unroll
-            for (int jj = 0; jj < kSlotBatch; ++jj) {
-                const int j = jb + jj;
-                if (j >= a.k) break;
-                const int32_t s = readlane(slot, j);
-                if (s < 0) continue;
-                const float w = readlane(wt, j);
+            for (int jj = 0; jj < KB; ++jj) {
+                if (readlane(slot, jb + jj) < 0) continue;   // masked (or past k): uniform skip
+                const float w = readlane(wt, jb + jj);
 #pragma unroll
-                for (int i = 0; i < C; ++i) {
-                    const vec16 b = buf[jj][i];
+                for (int i = 0; i < C; ++i)
 #pragma unroll
                     for (int q = 0; q < 4; ++q) {
-                        acc[i][2 * q] = __builtin_fmaf(w, bf16_lo(b[q]), acc[i][2 * q]);
-                        acc[i][2 * q + 1] = __builtin_fmaf(w, bf16_hi(b[q]), acc[i][2 * q + 1]);
+                        acc[i][2 * q] = __builtin_fmaf(w, bf16_lo(buf[jj][i][q]), acc[i][2 * q]);
+                        acc[i][2 * q + 1] = __builtin_fmaf(w, bf16_hi(buf[jj][i][q]), acc[i][2 * q + 1]);
                     }
-                }
             }
         }
 #pragma unroll
@@ -108,28 +123,31 @@ __global__ __launch_bounds__(256) void ep_combine_bf16_kernel(CombineArgs a) {
 #pragma unroll
             for (int q = 0; q < 4; ++q)
                 o[q] = any_valid ? pack_bf16x2(acc[i][2 * q], acc[i][2 * q + 1]) : 0u;
-            st16(yrow + (int64_t)v * 16, o);
+            store_y(yrow + (int64_t)v * 16, o);
         }
     }
 }
 
 // mxfp8 rows: a 16-byte vector holds 16 e4m3 elements, half of a 32-element
 // scale group; the y row vectors for it are two 16-byte bf16 vectors.
+template <int KC>
 __global__ __launch_bounds__(256) void ep_combine_mxfp8_kernel(CombineArgs a) {
+    constexpr int KB = KC > 0 ? KC : kSlotBatch;
     const int lane = threadIdx.x & (kWave - 1);
     const int64_t gw = (int64_t)blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
     const int64_t t = gw / a.S;
     const int sub = (int)(gw - t * a.S);
     if (t >= a.T) return;
+    const int k = KC > 0 ? KC : a.k;
 
     int32_t slot = -1;
     float wt = 0.0f;
-    if (lane < a.k) {
-        slot = a.token_slot[t * a.k + lane];
-        wt = a.topk_w[t * a.k + lane];
-        if ((uint64_t)slot >= (uint64_t)(a.T * a.k)) slot = -1;   // outside the receive rows: masked
+    if (lane < k) {
+        slot = a.token_slot[t * k + lane];
+        wt = a.topk_w[t * k + lane];
+        if ((uint64_t)slot >= (uint64_t)(a.T * k)) slot = -1;   // outside the receive rows: masked
     }
-    const bool any_valid = __ballot(lane < a.k && slot >= 0) != 0;
+    const bool any_valid = __ballot(lane < k && slot >= 0) != 0;
     char *yrow = a.y + t * (int64_t)a.H * 2;
     const int stride = kWave * a.S;
     const int G32 = a.H / 32;
@@ -138,34 +156,27 @@ __global__ __launch_bounds__(256) void ep_combine_mxfp8_kernel(CombineArgs a) {
         float acc[16];
 #pragma unroll
         for (int q = 0; q < 16; ++q) acc[q] = -0.0f;
-        for (int jb = 0; jb < a.k; jb += kSlotBatch) {
-            vec16 buf[kSlotBatch];
-            uint32_t sc[kSlotBatch];
+        for (int jb = 0; jb < k; jb += KB) {
+            vec16 buf[KB];
+            uint32_t sc[KB];
 #pragma unroll
-            for (int jj = 0; jj < kSlotBatch; ++jj) {
-                const int j = jb + jj;
-                if (j >= a.k) break;
-                const int32_t s = readlane(slot, j);
-                if (s < 0) continue;
-                buf[jj] = ld16_nt(a.eo + (int64_t)s * a.row_bytes + (int64_t)v * 16);
-                sc[jj] = a.eo_scales[(int64_t)s * G32 + (v >> 1)];
+            for (int jj = 0; jj < KB; ++jj) {
+                const int64_t r = row_of(readlane(slot, jb + jj));
+                buf[jj] = ld16_nt(a.eo + r * a.row_bytes + (int64_t)v * 16);
+                sc[jj] = a.eo_scales[r * G32 + (v >> 1)];
             }
 #pragma unroll
-            for (int jj = 0; jj < kSlotBatch; ++jj) {
-                const int j = jb + jj;
-                if (j >= a.k) break;
-                const int32_t s = readlane(slot, j);
-                if (s < 0) continue;
-                const float w = readlane(wt, j);
+            for (int jj = 0; jj < KB; ++jj) {
+                if (readlane(slot, jb + jj) < 0) continue;
+                const float w = readlane(wt, jb + jj);
                 const float scale = e8m0_to_f32(sc[jj]);
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
+                for (int q = 0; q < 4; ++q)
 #pragma unroll
                     for (int b = 0; b < 4; ++b) {
                         const float val = e4m3_to_f32((buf[jj][q] >> (8 * b)) & 0xFFu) * scale;
                         acc[4 * q + b] = __builtin_fmaf(w, val, acc[4 * q + b]);
                     }
-                }
             }
         }
         vec16 o0, o1;
@@ -174,8 +185,8 @@ __global__ __launch_bounds__(256) void ep_combine_mxfp8_kernel(CombineArgs a) {
             o0[q] = any_valid ? pack_bf16x2(acc[2 * q], acc[2 * q + 1]) : 0u;
             o1[q] = any_valid ? pack_bf16x2(acc[8 + 2 * q], acc[8 + 2 * q + 1]) : 0u;
         }
-        st16(yrow + (int64_t)v * 32, o0);
-        st16(yrow + (int64_t)v * 32 + 16, o1);
+        store_y(yrow + (int64_t)v * 32, o0);
+        store_y(yrow + (int64_t)v * 32 + 16, o1);
     }
 }
 
@@ -197,13 +208,15 @@ hipError_t launch_combine(const Shape &s, const void *expert_out, const uint8_t 
     const bool mx = (s.y_fmt == 2);
     a.row_bytes = mx ? (int64_t)s.H : 2 * (int64_t)s.H;
     a.nvec = (int)(a.row_bytes / 16);
-    a.S = waves_per_token(s.T, a.nvec);
+    a.S = waves_per_token(s.T, a.nvec, EP_COMBINE_WAVES);
     const int64_t waves = s.T * a.S;
     const dim3 grid((unsigned)((waves + 3) / 4)), block(256);
     if (mx) {
-        hipLaunchKernelGGL(ep_combine_mxfp8_kernel, grid, block, 0, stream, a);
+        if (s.k == 8) hipLaunchKernelGGL(ep_combine_mxfp8_kernel<8>, grid, block, 0, stream, a);
+        else hipLaunchKernelGGL(ep_combine_mxfp8_kernel<0>, grid, block, 0, stream, a);
     } else {
-        hipLaunchKernelGGL(ep_combine_bf16_kernel<4>, grid, block, 0, stream, a);
+        if (s.k == 8) hipLaunchKernelGGL((ep_combine_bf16_kernel<EP_COMBINE_VECS, 8>), grid, block, 0, stream, a);
+        else hipLaunchKernelGGL((ep_combine_bf16_kernel<EP_COMBINE_VECS, 0>), grid, block, 0, stream, a);
     }
     return hipGetLastError();
 }

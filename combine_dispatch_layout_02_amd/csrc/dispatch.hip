@@ -21,6 +21,13 @@
 namespace ep {
 namespace {
 
+#ifndef EP_DISPATCH_NT_STORE
+#define EP_DISPATCH_NT_STORE 0   // non-temporal stores for the receive rows
+#endif
+#ifndef EP_DISPATCH_WAVES
+#define EP_DISPATCH_WAVES 4096   // waves the copy aims for (4 per CU)
+#endif
+
 struct CopyArgs {
     const char *x;            // [T][row_bytes]
     const float *x_scales;    // [T][G] or null
@@ -33,11 +40,12 @@ struct CopyArgs {
     int32_t *token_slot;
     const int32_t *plan_offset;   // [E + 1] segment starts (workspace)
     int32_t *expert_offset;       // [E + 1] handle copy of plan_offset
-    const int32_t *tile_prefix;   // [ntiles][E]
+    const int32_t *tile_prefix;   // [ntiles][E + R + N] (expert columns first)
     const int32_t *local_rank;    // [T*k]
     uint32_t *ctrl;               // error word
     int64_t T;
     int k, E, TT;             // TT: tokens per plan tile
+    int cols;                 // columns of the tile matrix: E + R + N
     int64_t row_bytes;        // payload bytes per row (multiple of 16)
     int nvec;                 // row_bytes / 16
     int G;                    // fp32 scales per row (0 for bf16 rows)
@@ -62,7 +70,7 @@ __global__ __launch_bounds__(256) void ep_dispatch_copy_kernel(CopyArgs a) {
         const int32_t lr = a.local_rank[p];
         if (lr >= 0) {
             const int e = (int)a.topk_idx[p];
-            slot = a.plan_offset[e] + a.tile_prefix[(t / a.TT) * a.E + e] + lr;
+            slot = a.plan_offset[e] + a.tile_prefix[(t / a.TT) * a.cols + e] + lr;
             if ((uint64_t)slot >= (uint64_t)(a.T * a.k)) {   // cannot happen; never write outside
                 atomicOr(&a.ctrl[0], kErrBadSlot);
                 slot = -1;
@@ -105,7 +113,10 @@ __global__ __launch_bounds__(256) void ep_dispatch_copy_kernel(CopyArgs a) {
 #pragma unroll
             for (int i = 0; i < VPL; ++i) {
                 const int v = v0 + i * stride;
-                if (v < a.nvec) st16(dst + (int64_t)v * 16, buf[i]);
+                if (v < a.nvec) {
+                    if (EP_DISPATCH_NT_STORE) st16_nt(dst + (int64_t)v * 16, buf[i]);
+                    else st16(dst + (int64_t)v * 16, buf[i]);
+                }
             }
         }
     }
@@ -113,10 +124,10 @@ __global__ __launch_bounds__(256) void ep_dispatch_copy_kernel(CopyArgs a) {
 
 }  // namespace
 
-int waves_per_token(int64_t T, int64_t row_vectors) {
-    // aim for >= 16384 waves (16 per CU), keep >= 64 row vectors per wave
+int waves_per_token(int64_t T, int64_t row_vectors, int64_t target) {
+    // aim for `target` waves, keep >= 64 row vectors per wave
     int S = 1;
-    while (T * S < 16384 && (row_vectors / (2 * S)) >= kWave && S < 64) S *= 2;
+    while (T * S < target && (row_vectors / (2 * S)) >= kWave && S < 64) S *= 2;
     return S;
 }
 
@@ -144,11 +155,12 @@ hipError_t launch_dispatch_copy(const Shape &s, const WsLayout &L, const void *x
     a.k = s.k;
     a.E = s.E;
     a.TT = L.tile_tokens;
+    a.cols = s.E + s.R + s.N;
     const bool fp8 = (s.x_fmt == 1);
     a.row_bytes = fp8 ? (int64_t)s.H : 2 * (int64_t)s.H;
     a.nvec = (int)(a.row_bytes / 16);
     a.G = fp8 ? s.H / 128 : 0;
-    a.S = waves_per_token(s.T, a.nvec);
+    a.S = waves_per_token(s.T, a.nvec, EP_DISPATCH_WAVES);
     const int per_lane = (a.nvec + kWave * a.S - 1) / (kWave * a.S);
     const int64_t waves = s.T * a.S;
     int64_t blocks = (waves + 3) / 4;

@@ -65,9 +65,7 @@ WsLayout ws_layout(const Shape &s) {
     L.ctrl = off;
     off = align256(off + kCtrlWords * sizeof(uint32_t));
     L.tile_count = off;
-    off = align256(off + sizeof(int32_t) * (size_t)L.tiles * (size_t)s.E);
-    L.rn_count = off;
-    off = align256(off + sizeof(int32_t) * (size_t)L.tiles * (size_t)(s.R + s.N));
+    off = align256(off + sizeof(int32_t) * (size_t)L.tiles * (size_t)(s.E + s.R + s.N));
     L.local_rank = off;
     off = align256(off + sizeof(int32_t) * (size_t)(TK > 0 ? TK : 1));
     L.plan_offset = off;

@@ -10,17 +10,17 @@ namespace ep {
 
 // Workspace layout (bytes from the workspace base; every region 256-aligned).
 //   ctrl        : u32[64]            [0] error flags
-//   tile_count  : i32[tiles][E]      per-tile expert pair counts, then (after
-//                                    the scan) the exclusive prefix of expert e
-//                                    over earlier tiles
-//   rn_count    : i32[tiles][R + N]  per-tile rank / node token counts
+//   tile_count  : i32[tiles][E+R+N]  per tile: expert pair counts (then, after
+//                                    the scan, the exclusive prefix of expert e
+//                                    over earlier tiles), rank and node token
+//                                    counts
 //   local_rank  : i32[T * k]         rank of a pair among the same-expert pairs
 //                                    of its tile that precede it (-1: masked)
 //   plan_offset : i32[E + 1]         expert segment starts
 // A tile holds tile_tokens whole tokens (tile_tokens * k <= count_threads
 // pairs, one thread per pair).
 struct WsLayout {
-    size_t ctrl, tile_count, rn_count, local_rank, plan_offset, total;
+    size_t ctrl, tile_count, local_rank, plan_offset, total;
     int tiles;           // ceil(T / tile_tokens)
     int tile_tokens;
     int tile_waves;      // ceil(tile_tokens * k / 64): waves that own pair masks
@@ -71,8 +71,9 @@ hipError_t launch_expert_requant_mxfp8(const Shape &s, const int32_t *expert_off
 
 hipError_t launch_calib_copy(const void *src, void *dst, size_t bytes, hipStream_t stream);
 
-// Waves per token for the row kernels: enough waves to cover the chip when T
-// is small, never so many that a wave has fewer than 64 row vectors.
-int waves_per_token(int64_t T, int64_t row_vectors);
+// Waves per token for the row kernels: the smallest power of two that gives
+// `target` waves in all, never so many that a wave has fewer than 64 row
+// vectors.
+int waves_per_token(int64_t T, int64_t row_vectors, int64_t target);
 
 }  // namespace ep

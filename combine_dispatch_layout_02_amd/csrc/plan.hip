@@ -43,8 +43,7 @@ struct CountArgs {
     int TT;                   // tokens per tile
     int W;                    // waves whose masks exist (pairs per tile / 64, rounded up)
     uint8_t *in_rank;         // [T][R] or null
-    int32_t *tile_count;      // [ntiles][E]
-    int32_t *rn_count;        // [ntiles][R + N]
+    int32_t *tile_count;      // [ntiles][E + R + N]: experts, ranks, nodes
     int32_t *local_rank;      // [T * k]
     uint32_t *ctrl;
 };
@@ -86,7 +85,7 @@ __global__ __launch_bounds__(1024) void ep_plan_count_kernel(CountArgs a) {
         }
         a.local_rank[t0 * k + tid] = r;
     }
-    int32_t *tc = a.tile_count + (size_t)blockIdx.x * E;
+    int32_t *tc = a.tile_count + (size_t)blockIdx.x * (E + a.R + a.N);
     for (int e2 = tid; e2 < E; e2 += nt) {
         int32_t c = 0;
         for (int w2 = 0; w2 < a.W; ++w2) c += (int32_t)__popcll(masks[w2 * E + e2]);
@@ -142,8 +141,7 @@ __global__ __launch_bounds__(1024) void ep_plan_count_kernel(CountArgs a) {
     }
     if (__ballot(bad) && lane == 0) atomicOr(&a.ctrl[0], kErrBadExpert);
     __syncthreads();
-    int32_t *rc = a.rn_count + (size_t)blockIdx.x * (a.R + a.N);
-    for (int i = tid; i < a.R + a.N; i += nt) rc[i] = rn[i];
+    for (int i = tid; i < a.R + a.N; i += nt) tc[E + i] = rn[i];
 }
 
 // Exclusive scan of n ints held in LDS (`in`), written to `out` (n + 1
@@ -184,8 +182,7 @@ __device__ void block_exclusive_scan(const int32_t *in, int32_t *out, int n, int
 
 struct ScanArgs {
     int E, R, N, ntiles;
-    int32_t *tile_count;      // [ntiles][E] -> exclusive prefix over tiles
-    const int32_t *rn_count;  // [ntiles][R + N]
+    int32_t *tile_count;      // [ntiles][E + R + N]; expert columns -> exclusive prefix over tiles
     int32_t *plan_offset;     // [E + 1] segment starts (workspace copy)
     int32_t *per_expert;      // [E] or null
     int32_t *per_rank;        // [R] or null
@@ -193,81 +190,86 @@ struct ScanArgs {
     int64_t *algo;            // [1] or null
 };
 
-constexpr int kScanMaxE = 4096;
-constexpr int kScanBatch = 16;
+constexpr int kScanMaxCols = 4096 + 128;
+constexpr int kScanRegs = 16;   // tiles a thread keeps in registers
 
 __global__ __launch_bounds__(1024) void ep_plan_scan_kernel(ScanArgs a) {
-    __shared__ int32_t part[kScanMaxE + 1];
+    __shared__ int32_t part[kScanMaxCols + 1];
     __shared__ int32_t tmp[1024 / kWave + 1];
     const int tid = threadIdx.x, nt = blockDim.x, E = a.E;
-    // Q threads share an expert's tiles (E < blockDim); each owns `chunk` tiles
-    const int Q = (nt >= E) ? nt / E : 1;
+    const int cols = E + a.R + a.N;
+    // Q threads share one column's tiles (columns < blockDim); each owns `chunk` tiles
+    const int Q = (nt >= cols) ? nt / cols : 1;
     const int chunk = (a.ntiles + Q - 1) / Q;
-    for (int idx = tid; idx < E * Q; idx += nt) {
-        const int ee = idx % E, q = idx / E;
+    // block-uniform choice: every thread owns at most one (column, part) and
+    // at most kScanRegs tiles -> one batch of loads kept in registers
+    const bool in_regs = (cols * Q <= nt) && (chunk <= kScanRegs);
+    if (in_regs) {
+        const bool live = tid < cols * Q;
+        const int c = tid % cols, q = tid / cols;
         const int ta = min(q * chunk, a.ntiles), tb = min(ta + chunk, a.ntiles);
-        const int32_t *col = a.tile_count + ee;
+        int32_t *col = a.tile_count + c;
+        int32_t v[kScanRegs];
         int32_t s = 0;
-        for (int t = ta; t < tb; t += kScanBatch) {
-            int32_t c[kScanBatch];
 #pragma unroll
-            for (int u = 0; u < kScanBatch; ++u) c[u] = (t + u < tb) ? col[(size_t)(t + u) * E] : 0;
-#pragma unroll
-            for (int u = 0; u < kScanBatch; ++u) s += c[u];
+        for (int u = 0; u < kScanRegs; ++u) {
+            v[u] = (live && ta + u < tb) ? col[(size_t)(ta + u) * cols] : 0;
+            s += v[u];
         }
-        part[idx] = s;   // idx = q * E + ee
-    }
-    __syncthreads();
-    for (int idx = tid; idx < E * Q; idx += nt) {
-        const int ee = idx % E, q = idx / E;
-        int32_t run = 0;
-        for (int q2 = 0; q2 < q; ++q2) run += part[q2 * E + ee];
-        const int ta = min(q * chunk, a.ntiles), tb = min(ta + chunk, a.ntiles);
-        int32_t *col = a.tile_count + ee;
-        for (int t = ta; t < tb; t += kScanBatch) {
-            int32_t c[kScanBatch];
+        if (live) part[tid] = s;   // tid = q * cols + c
+        __syncthreads();
+        if (live && c < E) {
+            int32_t run = 0;
+            for (int q2 = 0; q2 < q; ++q2) run += part[q2 * cols + c];
 #pragma unroll
-            for (int u = 0; u < kScanBatch; ++u) c[u] = (t + u < tb) ? col[(size_t)(t + u) * E] : 0;
-#pragma unroll
-            for (int u = 0; u < kScanBatch; ++u) {
-                if (t + u < tb) col[(size_t)(t + u) * E] = run;
-                run += c[u];
+            for (int u = 0; u < kScanRegs; ++u) {
+                if (ta + u < tb) col[(size_t)(ta + u) * cols] = run;
+                run += v[u];
             }
         }
-    }
-    __syncthreads();
-    for (int ee = tid; ee < E; ee += nt) {
-        int32_t s = 0;
-        for (int q = 0; q < Q; ++q) s += part[q * E + ee];
-        part[ee] = s;   // column ee is read and written by this thread only
-        if (a.per_expert) a.per_expert[ee] = s;
-    }
-    __syncthreads();
-    block_exclusive_scan(part, a.plan_offset, E, tmp);
-
-    // rank / node token counts: sums over tiles
-    const int RN = a.R + a.N;
-    if (a.per_rank) {
-        for (int i = tid; i < RN; i += nt) {
+    } else {
+        for (int idx = tid; idx < cols * Q; idx += nt) {
+            const int c = idx % cols, q = idx / cols;
+            const int ta = min(q * chunk, a.ntiles), tb = min(ta + chunk, a.ntiles);
+            const int32_t *col = a.tile_count + c;
             int32_t s = 0;
-            for (int t = 0; t < a.ntiles; t += kScanBatch) {
-                int32_t c[kScanBatch];
-#pragma unroll
-                for (int u = 0; u < kScanBatch; ++u)
-                    c[u] = (t + u < a.ntiles) ? a.rn_count[(size_t)(t + u) * RN + i] : 0;
-#pragma unroll
-                for (int u = 0; u < kScanBatch; ++u) s += c[u];
-            }
-            if (i < a.R) a.per_rank[i] = s; else a.per_node[i - a.R] = s;
-            part[i] = s;
+            for (int t = ta; t < tb; ++t) s += col[(size_t)t * cols];
+            part[idx] = s;
         }
         __syncthreads();
-        if (tid == 0) {
-            int64_t al = 0;
-            for (int n = 0; n < a.N; ++n) al += part[a.R + n];
-            *a.algo = al;
+        for (int idx = tid; idx < cols * Q; idx += nt) {
+            const int c = idx % cols, q = idx / cols;
+            if (c >= E) continue;
+            const int ta = min(q * chunk, a.ntiles), tb = min(ta + chunk, a.ntiles);
+            int32_t *col = a.tile_count + c;
+            int32_t run = 0;
+            for (int q2 = 0; q2 < q; ++q2) run += part[q2 * cols + c];
+            for (int t = ta; t < tb; ++t) {
+                const int32_t x = col[(size_t)t * cols];
+                col[(size_t)t * cols] = run;
+                run += x;
+            }
         }
     }
+    __syncthreads();
+    // column totals into part[0..cols) (row q = 0), summing the Q partials
+    for (int c = tid; c < cols; c += nt) {
+        int32_t s = 0;
+        for (int q = 0; q < Q; ++q) s += part[q * cols + c];
+        part[c] = s;   // column c is read and written by this thread only
+        if (c < E) {
+            if (a.per_expert) a.per_expert[c] = s;
+        } else if (a.per_rank) {
+            if (c < E + a.R) a.per_rank[c - E] = s; else a.per_node[c - E - a.R] = s;
+        }
+    }
+    __syncthreads();
+    if (a.algo && tid == 0) {
+        int64_t al = 0;
+        for (int n = 0; n < a.N; ++n) al += part[E + a.R + n];
+        *a.algo = al;
+    }
+    block_exclusive_scan(part, a.plan_offset, E, tmp);
 }
 
 }  // namespace
@@ -288,7 +290,6 @@ hipError_t launch_plan(const Shape &s, const WsLayout &L, const int64_t *topk_id
     c.W = L.tile_waves;
     c.in_rank = in_rank;
     c.tile_count = reinterpret_cast<int32_t *>(ws + L.tile_count);
-    c.rn_count = reinterpret_cast<int32_t *>(ws + L.rn_count);
     c.local_rank = reinterpret_cast<int32_t *>(ws + L.local_rank);
     c.ctrl = reinterpret_cast<uint32_t *>(ws + L.ctrl);
     if (s.T > 0) {
@@ -304,7 +305,6 @@ hipError_t launch_plan(const Shape &s, const WsLayout &L, const int64_t *topk_id
     a.N = s.N;
     a.ntiles = s.T > 0 ? L.tiles : 0;
     a.tile_count = c.tile_count;
-    a.rn_count = c.rn_count;
     a.plan_offset = reinterpret_cast<int32_t *>(ws + L.plan_offset);
     a.per_expert = per_expert;
     a.per_rank = per_rank;
