@@ -34,12 +34,47 @@ sys.path.insert(0, ROOT)
 METRIC = "dispatch+combine HBM GB/s and tokens/s at T=4096,H=7168,E=256,top-8"
 HBM_PEAK_GBS = 8000.0   # MI355X HBM3E, published peak
 
-# Hardware byte counters (rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE) per launch of
-# the dominant kernel, scaled by the same counters' reading on a plain copy of
-# known size; filled in from the committed profiles for the kernel build they
-# were taken on (None = not measured for the current kernels).
-MEASURED_TRAFFIC = {}
 GRAPH_STEPS = 10   # steps captured per HIP graph
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def kernel_source_hash() -> str:
+    """sha256 over the HIP sources and headers of the library."""
+    import glob
+    import hashlib
+
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "combine_dispatch_layout_02_amd", "csrc")
+    for path in sorted(glob.glob(os.path.join(csrc, "*.hip")) + glob.glob(os.path.join(csrc, "*.h"))
+                       + [os.path.join(ROOT, "include", "ep.h")]):
+        h.update(os.path.basename(path).encode())
+        h.update(open(path, "rb").read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload: str, kernel: str):
+    """HBM bytes per launch of `kernel` from the committed counter summary
+    (rocprofv3 FETCH_SIZE / WRITE_SIZE, each scaled by its reading on a plain
+    copy of known size), or None when there is none for this workload or the
+    kernel sources changed since the counters were taken."""
+    path = os.path.join(PROFILES, f"counters_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    for line in open(path):
+        if line.startswith("#") or "=" not in line:
+            continue
+        parts = dict(p.split("=", 1) for p in line.split())
+        if "kernel" in parts:
+            fields[parts["kernel"]] = parts
+        else:
+            fields.update(parts)
+    if fields.get("kernel_sources_sha256") != kernel_source_hash():
+        return None
+    for name, parts in fields.items():
+        if isinstance(parts, dict) and name.startswith(kernel):
+            return int(float(parts["traffic_bytes"]))
+    return None
 
 
 class HipEvents:
@@ -286,7 +321,7 @@ def measure(workload: str, steps: int, warmup: int, graph: bool = False) -> dict
     kernels = {"dispatch": "ep_dispatch_copy_kernel", "combine": "ep_combine_" +
                ("mxfp8" if fp8 else "bf16") + "_kernel"}
     achieved = algo_bytes[dom] / (phase_us[dom] * 1e-6) / 1e9
-    traffic = MEASURED_TRAFFIC.get((workload, dom))
+    traffic = measured_traffic(workload, kernels[dom])
 
     out = {
         "metric": METRIC,
