@@ -63,6 +63,18 @@ __global__ __launch_bounds__(256) void ep_dispatch_copy_kernel(CopyArgs a) {
     if (g <= a.E) a.expert_offset[g] = a.plan_offset[g];   // handle copy of the segment starts
     if (t >= a.T) return;   // wave-uniform
 
+    // the first pass of row t does not depend on the slots: issue its loads
+    // before the slot lookups so the two latencies overlap
+    const char *src = a.x + t * a.row_bytes;
+    const int stride = kWave * a.S;            // vectors between a lane's consecutive vectors
+    const int v_first = lane + kWave * sub;
+    vec16 buf[VPL];
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) {
+        const int v = v_first + i * stride;
+        if (v < a.nvec) buf[i] = ld16(src + (int64_t)v * 16);
+    }
+
     // lanes 0..k-1: the token's slots
     int32_t slot = -1;
     if (lane < a.k) {
@@ -84,27 +96,26 @@ __global__ __launch_bounds__(256) void ep_dispatch_copy_kernel(CopyArgs a) {
             }
         }
     }
-    if (__ballot(slot >= 0) == 0) return;   // no valid slot: the row is not read
+    if (__ballot(slot >= 0) == 0) return;   // no valid slot: nothing to store
 
     // fp32 scale rows (fp8 payload): lanes spread over the waves of the token
     if (a.G > 0) {
-        for (int g = lane + kWave * sub; g < a.G; g += kWave * a.S) {
-            const float sc = a.x_scales[t * a.G + g];
+        for (int gi = lane + kWave * sub; gi < a.G; gi += kWave * a.S) {
+            const float sc = a.x_scales[t * a.G + gi];
             for (int j = 0; j < a.k; ++j) {
                 const int32_t s = readlane(slot, j);
-                if (s >= 0) a.recv_scales[(int64_t)s * a.G + g] = sc;
+                if (s >= 0) a.recv_scales[(int64_t)s * a.G + gi] = sc;
             }
         }
     }
 
-    const char *src = a.x + t * a.row_bytes;
-    const int stride = kWave * a.S;            // vectors between a lane's consecutive vectors
-    for (int v0 = lane + kWave * sub; v0 < a.nvec; v0 += stride * VPL) {
-        vec16 buf[VPL];
+    for (int v0 = v_first; v0 < a.nvec; v0 += stride * VPL) {
+        if (v0 != v_first) {
 #pragma unroll
-        for (int i = 0; i < VPL; ++i) {
-            const int v = v0 + i * stride;
-            if (v < a.nvec) buf[i] = ld16(src + (int64_t)v * 16);
+            for (int i = 0; i < VPL; ++i) {
+                const int v = v0 + i * stride;
+                if (v < a.nvec) buf[i] = ld16(src + (int64_t)v * 16);
+            }
         }
         for (int j = 0; j < a.k; ++j) {
             const int32_t s = readlane(slot, j);

@@ -7,6 +7,10 @@
 
 #include <hip/hip_runtime.h>
 
+#ifndef EP_PLAN_WAVES
+#define EP_PLAN_WAVES 16   // waves (64 pairs each) per plan tile, at most
+#endif
+
 namespace {
 
 using ep::Shape;
@@ -52,7 +56,7 @@ namespace ep {
 WsLayout ws_layout(const Shape &s) {
     WsLayout L;
     // pair masks of one tile (tile_waves * E * 8 bytes) stay within 48 KiB
-    int wmax = 16;
+    int wmax = EP_PLAN_WAVES;
     while (wmax > 1 && (size_t)wmax * (size_t)s.E * 8 > 48 * 1024) wmax >>= 1;
     L.tile_tokens = (wmax * 64) / s.k;
     if (L.tile_tokens < 1) L.tile_tokens = 1;

@@ -40,6 +40,7 @@ struct CountArgs {
     const int64_t *topk_idx;
     int64_t T;
     int k, E, R, N, epr, epn;
+    int epr_shift, epn_shift; // log2 of epr / epn when powers of two, else -1
     int TT;                   // tokens per tile
     int W;                    // waves whose masks exist (pairs per tile / 64, rounded up)
     uint8_t *in_rank;         // [T][R] or null
@@ -100,8 +101,10 @@ __global__ __launch_bounds__(1024) void ep_plan_count_kernel(CountArgs a) {
             for (int j = 0; j < k; ++j) {
                 const int ej = ids[tl * k + j];
                 if (ej < 0) continue;
-                rmask |= 1ull << (ej / a.epr);
-                nmask |= 1ull << (ej / a.epn);
+                const int r = a.epr_shift >= 0 ? ej >> a.epr_shift : ej / a.epr;
+                const int n = a.epn_shift >= 0 ? ej >> a.epn_shift : ej / a.epn;
+                rmask |= 1ull << r;
+                nmask |= 1ull << n;
             }
             if (a.in_rank) {
                 uint8_t *out = a.in_rank + (t0 + tl) * a.R;
@@ -191,7 +194,7 @@ struct ScanArgs {
 };
 
 constexpr int kScanMaxCols = 4096 + 128;
-constexpr int kScanRegs = 16;   // tiles a thread keeps in registers
+constexpr int kScanRegs = 32;   // tiles a thread keeps in registers
 
 __global__ __launch_bounds__(1024) void ep_plan_scan_kernel(ScanArgs a) {
     __shared__ int32_t part[kScanMaxCols + 1];
@@ -286,6 +289,8 @@ hipError_t launch_plan(const Shape &s, const WsLayout &L, const int64_t *topk_id
     c.N = s.N;
     c.epr = s.E / s.R;
     c.epn = s.E / s.N;
+    c.epr_shift = (c.epr & (c.epr - 1)) == 0 ? __builtin_ctz((unsigned)c.epr) : -1;
+    c.epn_shift = (c.epn & (c.epn - 1)) == 0 ? __builtin_ctz((unsigned)c.epn) : -1;
     c.TT = L.tile_tokens;
     c.W = L.tile_waves;
     c.in_rank = in_rank;
