@@ -129,7 +129,12 @@ __global__ __launch_bounds__(256) void ep_combine_bf16_kernel(CombineArgs a) {
 }
 
 // mxfp8 rows: a 16-byte vector holds 16 e4m3 elements, half of a 32-element
-// scale group; the y row vectors for it are two 16-byte bf16 vectors.
+// scale group; the y row vectors for it are two 16-byte bf16 vectors.  The
+// element value e4m3(q) * 2^(e8m0 - 127) comes from gfx950's
+// v_cvt_scalef32_pk_f32_fp8 (two elements per instruction).  That product is
+// exact in binary32, and the instruction returns exactly it -- NaN codes,
+// subnormal codes and the subnormal scale 2^-127 included -- which the GPU
+// parity test over every (code, scale) pair checks through this kernel.
 template <int KC>
 __global__ __launch_bounds__(256) void ep_combine_mxfp8_kernel(CombineArgs a) {
     constexpr int KB = KC > 0 ? KC : kSlotBatch;
@@ -171,12 +176,15 @@ __global__ __launch_bounds__(256) void ep_combine_mxfp8_kernel(CombineArgs a) {
                 const float w = readlane(wt, jb + jj);
                 const float scale = e8m0_to_f32(sc[jj]);
 #pragma unroll
-                for (int q = 0; q < 4; ++q)
-#pragma unroll
-                    for (int b = 0; b < 4; ++b) {
-                        const float val = e4m3_to_f32((buf[jj][q] >> (8 * b)) & 0xFFu) * scale;
-                        acc[4 * q + b] = __builtin_fmaf(w, val, acc[4 * q + b]);
-                    }
+                for (int q = 0; q < 4; ++q) {
+                    // e4m3 bytes 0,1 and 2,3 of the dword, each times the scale
+                    const f32x2 lo = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(buf[jj][q], scale, false);
+                    const f32x2 hi = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(buf[jj][q], scale, true);
+                    acc[4 * q + 0] = __builtin_fmaf(w, lo.x, acc[4 * q + 0]);
+                    acc[4 * q + 1] = __builtin_fmaf(w, lo.y, acc[4 * q + 1]);
+                    acc[4 * q + 2] = __builtin_fmaf(w, hi.x, acc[4 * q + 2]);
+                    acc[4 * q + 3] = __builtin_fmaf(w, hi.y, acc[4 * q + 3]);
+                }
             }
         }
         vec16 o0, o1;

@@ -122,6 +122,8 @@ __device__ __forceinline__ float readlane<float>(float v, int lane) {
     return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
 }
 
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
 // 16-byte vector type used for every row copy (one global_load/store_dwordx4).
 typedef uint32_t vec16 __attribute__((ext_vector_type(4)));
 

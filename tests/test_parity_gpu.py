@@ -150,3 +150,24 @@ def test_from_layout_requires_a_layout_call():
     x = gpu_path.to_dev_bf16(inp["x"])
     with pytest.raises(RuntimeError, match="preceding ep_dispatch_layout"):
         ep.dispatch(x, idx, w, shape, ws, from_layout=True)
+
+
+def test_mxfp8_combine_every_code_and_scale():
+    """k = 1, w = 1: y = bf16(e4m3(q) * 2^(e8m0 - 127)) for every e4m3 code and
+    every e8m0 byte (row r uses scale byte r for all its groups), through
+    ep_combine against the oracle."""
+    from combine_dispatch_layout_02_amd import ep
+    import gpu_path
+    T, H, k = 256, 256, 1
+    q = np.tile(np.arange(256, dtype=np.uint8), (T, 1))
+    e = np.repeat(np.arange(T, dtype=np.uint8)[:, None], H // 32, axis=1)
+    e[255] = 254                   # 0xFF is NaN as a scale; the rows cover every finite one
+    slot = np.arange(T, dtype=np.int32).reshape(T, 1)
+    w = np.ones((T, k), np.float32)
+    ref = oracle.combine_mxfp8(q, e, slot, w)
+    shape = ep.make_shape(T, H, 1, 1, 1, k, ep.EP_FMT_BF16, ep.EP_FMT_MXFP8)
+    y = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
+    ep.ep_combine(shape, torch.from_numpy(q).cuda(), torch.from_numpy(e).cuda(),
+                  torch.from_numpy(slot).cuda(), torch.from_numpy(w).cuda(), y)
+    got = gpu_path.bf16_bits(y)
+    np.testing.assert_array_equal(got, ref)
