@@ -74,6 +74,12 @@ __global__ __launch_bounds__(256) void ep_dispatch_copy_kernel(CopyArgs a) {
         const int v = v_first + i * stride;
         if (v < a.nvec) buf[i] = ld16(src + (int64_t)v * 16);
     }
+    // fp32 scales of an fp8 row (one per 128 elements): this wave's share,
+    // loaded with the row (G <= 64 * S, one value per lane, in every shape the
+    // ABI accepts with hidden <= 8192 * S; larger rows loop below)
+    const int g_first = lane + kWave * sub;
+    float sc0 = 0.0f;
+    if (g_first < a.G) sc0 = a.x_scales[t * a.G + g_first];
 
     // lanes 0..k-1: the token's slots
     int32_t slot = -1;
@@ -100,8 +106,8 @@ __global__ __launch_bounds__(256) void ep_dispatch_copy_kernel(CopyArgs a) {
 
     // fp32 scale rows (fp8 payload): lanes spread over the waves of the token
     if (a.G > 0) {
-        for (int gi = lane + kWave * sub; gi < a.G; gi += kWave * a.S) {
-            const float sc = a.x_scales[t * a.G + gi];
+        for (int gi = g_first; gi < a.G; gi += kWave * a.S) {
+            const float sc = (gi == g_first) ? sc0 : a.x_scales[t * a.G + gi];
             for (int j = 0; j < a.k; ++j) {
                 const int32_t s = readlane(slot, j);
                 if (s >= 0) a.recv_scales[(int64_t)s * a.G + gi] = sc;
