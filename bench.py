@@ -8,7 +8,7 @@ workload, if any) -> ep_combine, all on one stream.  W untimed warmup steps,
 then K timed steps bracketed by stream synchronisation and HIP events, three
 ways: replayed from HIP graphs of 10 captured steps (the reported
 ms_per_step), eager back to back (eager_ms_per_step), and eager with events
-between the calls (the per-call durations in phase_us).  The workloads'
+between the calls (the per-call durations in phase_us: median over steps).  The workloads'
 expert stage (identity, per-expert scaling, or fp8 -> mxfp8 re-encoding)
 runs during warmup and is not part of the timed step.
 
@@ -25,6 +25,7 @@ from __future__ import annotations
 import argparse
 import json
 import os
+import statistics
 import sys
 import time
 
@@ -131,6 +132,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-graph", action="store_true",
                     help="time the eager loop only (default: K steps replayed from HIP graphs of %d steps)" % GRAPH_STEPS)
+    ap.add_argument("--sweep", action="store_true",
+                    help="time the step at T = 1, 2, 4, ..., 8192 tokens (the workload's other sizes fixed) "
+                         "and print one JSON line with the series")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="only run the plain copy kernel on this many MiB, --steps times (counter calibration)")
     return ap.parse_args()
@@ -163,6 +167,16 @@ def main():
         print(json.dumps({"calib_copy_bytes": n, "launches": args.steps}))
         return
 
+    if args.sweep:
+        series = []
+        for T in [2 ** i for i in range(14)]:
+            o = measure(args.workload, args.steps, args.warmup, not args.no_graph, T=T)
+            o.pop("_inp")
+            series.append({"tokens": T, "us_per_step": round(o["ms_per_step"] * 1000, 2),
+                           "tokens_per_s": o["tokens_per_s"], "gbs": o["value"], "phase_us": o["phase_us"]})
+        print(json.dumps({"metric": "step time vs tokens per source (" + args.workload + " shape)",
+                          "unit": "us", "series": series}), flush=True)
+        return
     out = measure(args.workload, args.steps, args.warmup, not args.no_graph)
     inp = out.pop("_inp")
     if not args.no_cpu_baseline:
@@ -170,8 +184,9 @@ def main():
     print(json.dumps(out), flush=True)
 
 
-def measure(workload: str, steps: int, warmup: int, graph: bool = False) -> dict:
-    """Time `steps` steps of the path on `workload` (inputs resident in HBM)."""
+def measure(workload: str, steps: int, warmup: int, graph: bool = False, **overrides) -> dict:
+    """Time `steps` steps of the path on `workload` (inputs resident in HBM);
+    keyword overrides change the workload's shape (e.g. T=...)."""
     import numpy as np
     import torch
 
@@ -179,7 +194,7 @@ def measure(workload: str, steps: int, warmup: int, graph: bool = False) -> dict
 
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream()
-    inp = workloads.make_inputs(workload)
+    inp = workloads.make_inputs(workload, **overrides)
     T, H, E, R, N, k = (inp[n] for n in ("T", "H", "E", "R", "N", "k"))
     fp8 = inp["x_fmt"] == "fp8"
     shape = ep.make_shape(T, H, E, R, N, k, ep.EP_FMT_FP8_S128 if fp8 else ep.EP_FMT_BF16,
@@ -279,7 +294,10 @@ def measure(workload: str, steps: int, warmup: int, graph: bool = False) -> dict
             fn()
             hev.record(ev[s][i + 1], stream)
     torch.cuda.synchronize()
-    phase_us = {name: 1000.0 * sum(hev.ms(ev[s][i], ev[s][i + 1]) for s in range(steps)) / steps
+    # median over the steps: a host-side submission stall (e.g. a pause of the
+    # interpreter) leaves the GPU idle between two events and inflates one
+    # sample; the median keeps the kernel's own duration
+    phase_us = {name: 1000.0 * statistics.median(hev.ms(ev[s][i], ev[s][i + 1]) for s in range(steps))
                 for i, (name, _) in enumerate(phases)}
     for e in ev:
         hev.destroy(e)

@@ -30,11 +30,49 @@
 //      tile counts over tiles (in place) and the total; the exclusive scan of
 //      the totals over experts (segment starts); per rank / node the sum over
 //      tiles.  Integer sums only: the plan and the counts are deterministic.
+//  A batch that fits one tile (T * k <= 1024 pairs at E <= 384) is planned by
+//  the count kernel alone: its block holds every count and scans them in LDS.
 #include "ep_device.h"
 #include "ep_internal.h"
 
 namespace ep {
 namespace {
+
+// Exclusive scan of n ints held in LDS (`in`), written to `out` (n + 1
+// entries, out[n] = total).  Called by every thread of the block.
+__device__ void block_exclusive_scan(const int32_t *in, int32_t *out, int n, int32_t *tmp) {
+    const int nt = blockDim.x, tid = threadIdx.x;
+    const int lane = tid & (kWave - 1), wid = tid / kWave, nw = (nt + kWave - 1) / kWave;
+    const int chunk = (n + nt - 1) / nt;
+    const int b = min(tid * chunk, n), e = min(b + chunk, n);
+    int32_t s = 0;
+    for (int i = b; i < e; ++i) s += in[i];
+    int32_t v = s;
+    for (int off = 1; off < kWave; off <<= 1) {
+        const int32_t u = __shfl_up(v, off);
+        if (lane >= off) v += u;
+    }
+    if (lane == kWave - 1) tmp[wid] = v;
+    __syncthreads();
+    if (tid == 0) {
+        int32_t run = 0;
+        for (int i = 0; i < nw; ++i) {
+            const int32_t x = tmp[i];
+            tmp[i] = run;
+            run += x;
+        }
+        tmp[nw] = run;
+    }
+    __syncthreads();
+    int32_t excl = tmp[wid] + v - s;
+    for (int i = b; i < e; ++i) {
+        const int32_t x = in[i];
+        out[i] = excl;
+        excl += x;
+    }
+    if (tid == 0) out[n] = tmp[nw];
+    __syncthreads();
+}
 
 struct CountArgs {
     const int64_t *topk_idx;
@@ -47,6 +85,10 @@ struct CountArgs {
     int32_t *tile_count;      // [ntiles][E + R + N]: experts, ranks, nodes
     int32_t *local_rank;      // [T * k]
     uint32_t *ctrl;
+    // single-tile batches (one block) finish the plan in the same launch:
+    int32_t *plan_offset;     // [E + 1]
+    int32_t *per_expert, *per_rank, *per_node;   // layout outputs or null
+    int64_t *algo;
 };
 
 __global__ __launch_bounds__(1024) void ep_plan_count_kernel(CountArgs a) {
@@ -87,10 +129,16 @@ __global__ __launch_bounds__(1024) void ep_plan_count_kernel(CountArgs a) {
         a.local_rank[t0 * k + tid] = r;
     }
     int32_t *tc = a.tile_count + (size_t)blockIdx.x * (E + a.R + a.N);
+    const bool single = gridDim.x == 1;   // the whole batch is this tile
+    int32_t *cnt = rn + a.R + a.N;        // [E] tile counts (single-tile finish)
     for (int e2 = tid; e2 < E; e2 += nt) {
         int32_t c = 0;
         for (int w2 = 0; w2 < a.W; ++w2) c += (int32_t)__popcll(masks[w2 * E + e2]);
-        tc[e2] = c;
+        tc[e2] = single ? 0 : c;          // single tile: no earlier tiles, prefix 0
+        if (single) {
+            cnt[e2] = c;
+            if (a.per_expert) a.per_expert[e2] = c;
+        }
     }
 
     // ---- tokens: rank / node sets in registers
@@ -145,42 +193,20 @@ __global__ __launch_bounds__(1024) void ep_plan_count_kernel(CountArgs a) {
     if (__ballot(bad) && lane == 0) atomicOr(&a.ctrl[0], kErrBadExpert);
     __syncthreads();
     for (int i = tid; i < a.R + a.N; i += nt) tc[E + i] = rn[i];
-}
+    if (!single) return;   // block-uniform
 
-// Exclusive scan of n ints held in LDS (`in`), written to `out` (n + 1
-// entries, out[n] = total).  Called by every thread of the block.
-__device__ void block_exclusive_scan(const int32_t *in, int32_t *out, int n, int32_t *tmp) {
-    const int nt = blockDim.x, tid = threadIdx.x;
-    const int lane = tid & (kWave - 1), wid = tid / kWave, nw = (nt + kWave - 1) / kWave;
-    const int chunk = (n + nt - 1) / nt;
-    const int b = min(tid * chunk, n), e = min(b + chunk, n);
-    int32_t s = 0;
-    for (int i = b; i < e; ++i) s += in[i];
-    int32_t v = s;
-    for (int off = 1; off < kWave; off <<= 1) {
-        const int32_t u = __shfl_up(v, off);
-        if (lane >= off) v += u;
-    }
-    if (lane == kWave - 1) tmp[wid] = v;
-    __syncthreads();
-    if (tid == 0) {
-        int32_t run = 0;
-        for (int i = 0; i < nw; ++i) {
-            const int32_t x = tmp[i];
-            tmp[i] = run;
-            run += x;
+    // ---- single-tile batch: segment starts and layout outputs right here
+    block_exclusive_scan(cnt, a.plan_offset, E, reinterpret_cast<int32_t *>(cnt + E));
+    if (a.per_rank) {
+        for (int i = tid; i < a.R + a.N; i += nt) {
+            if (i < a.R) a.per_rank[i] = rn[i]; else a.per_node[i - a.R] = rn[i];
         }
-        tmp[nw] = run;
+        if (tid == 0) {
+            int64_t al = 0;
+            for (int n = 0; n < a.N; ++n) al += rn[a.R + n];
+            *a.algo = al;
+        }
     }
-    __syncthreads();
-    int32_t excl = tmp[wid] + v - s;
-    for (int i = b; i < e; ++i) {
-        const int32_t x = in[i];
-        out[i] = excl;
-        excl += x;
-    }
-    if (tid == 0) out[n] = tmp[nw];
-    __syncthreads();
 }
 
 struct ScanArgs {
@@ -297,12 +323,19 @@ hipError_t launch_plan(const Shape &s, const WsLayout &L, const int64_t *topk_id
     c.tile_count = reinterpret_cast<int32_t *>(ws + L.tile_count);
     c.local_rank = reinterpret_cast<int32_t *>(ws + L.local_rank);
     c.ctrl = reinterpret_cast<uint32_t *>(ws + L.ctrl);
+    c.plan_offset = reinterpret_cast<int32_t *>(ws + L.plan_offset);
+    c.per_expert = per_expert;
+    c.per_rank = per_rank;
+    c.per_node = per_node;
+    c.algo = algo;
     if (s.T > 0) {
+        // masks, staged ids, rank/node counts, and (single tile) expert counts + scan scratch
         const size_t lds = sizeof(uint64_t) * (size_t)L.tile_waves * s.E +
-                           sizeof(int32_t) * ((size_t)L.tile_tokens * s.k + s.R + s.N);
+                           sizeof(int32_t) * ((size_t)L.tile_tokens * s.k + s.R + s.N + s.E + 1 +
+                                              1024 / kWave + 1);
         hipLaunchKernelGGL(ep_plan_count_kernel, dim3(L.tiles), dim3(L.count_threads), lds, stream, c);
         const hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
+        if (e != hipSuccess || L.tiles == 1) return e;   // one tile: the plan is complete
     }
     ScanArgs a;
     a.E = s.E;
