@@ -34,6 +34,7 @@ struct CombineArgs {
     int64_t T;
     int k, H;
     int64_t row_bytes;          // 2H (bf16) or H (mxfp8)
+    int64_t rows;               // receive rows (T*k, or R*M for RANK_MAJOR)
     int nvec;                   // 16-byte vectors per payload row
     int S;                      // waves per token
 };
@@ -78,7 +79,7 @@ __global__ __launch_bounds__(256) void ep_combine_bf16_kernel(CombineArgs a) {
     if (lane < k) {
         slot = a.token_slot[t * k + lane];
         wt = a.topk_w[t * k + lane];
-        if ((uint64_t)slot >= (uint64_t)(a.T * k)) slot = -1;   // outside the receive rows: masked
+        if ((uint64_t)slot >= (uint64_t)a.rows) slot = -1;   // outside the receive rows: masked
     }
     const bool any_valid = __ballot(lane < k && slot >= 0) != 0;
     char *yrow = a.y + t * (int64_t)a.H * 2;
@@ -150,7 +151,7 @@ __global__ __launch_bounds__(256) void ep_combine_mxfp8_kernel(CombineArgs a) {
     if (lane < k) {
         slot = a.token_slot[t * k + lane];
         wt = a.topk_w[t * k + lane];
-        if ((uint64_t)slot >= (uint64_t)(a.T * k)) slot = -1;   // outside the receive rows: masked
+        if ((uint64_t)slot >= (uint64_t)a.rows) slot = -1;   // outside the receive rows: masked
     }
     const bool any_valid = __ballot(lane < k && slot >= 0) != 0;
     char *yrow = a.y + t * (int64_t)a.H * 2;
@@ -213,6 +214,7 @@ hipError_t launch_combine(const Shape &s, const void *expert_out, const uint8_t 
     a.T = s.T;
     a.k = s.k;
     a.H = s.H;
+    a.rows = s.rows();
     const bool mx = (s.y_fmt == 2);
     a.row_bytes = mx ? (int64_t)s.H : 2 * (int64_t)s.H;
     a.nvec = (int)(a.row_bytes / 16);

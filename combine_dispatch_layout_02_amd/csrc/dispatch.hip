@@ -45,6 +45,9 @@ struct CopyArgs {
     uint32_t *ctrl;               // error word
     int64_t T;
     int k, E, TT;             // TT: tokens per plan tile
+    int M;                    // rank_capacity (0: compacted layout)
+    int epr, epr_shift;       // experts per rank, its log2 (or -1)
+    int64_t rows;             // receive rows
     int cols;                 // columns of the tile matrix: E + R + N
     int64_t row_bytes;        // payload bytes per row (multiple of 16)
     int nvec;                 // row_bytes / 16
@@ -89,7 +92,17 @@ __global__ __launch_bounds__(256) void ep_dispatch_copy_kernel(CopyArgs a) {
         if (lr >= 0) {
             const int e = (int)a.topk_idx[p];
             slot = a.plan_offset[e] + a.tile_prefix[(t / a.TT) * a.cols + e] + lr;
-            if ((uint64_t)slot >= (uint64_t)(a.T * a.k)) {   // cannot happen; never write outside
+            if (a.M > 0) {   // RANK_MAJOR: the same place inside the rank, at the rank's fixed block
+                const int r = a.epr_shift >= 0 ? e >> a.epr_shift : e / a.epr;
+                const int32_t in_rank = slot - a.plan_offset[r * a.epr];
+                if (in_rank < a.M) {
+                    slot = r * a.M + in_rank;
+                } else {
+                    atomicOr(&a.ctrl[0], kErrRankOverflow);
+                    slot = -1;
+                }
+            }
+            if (slot >= 0 && (uint64_t)slot >= (uint64_t)a.rows) {   // cannot happen; never write outside
                 atomicOr(&a.ctrl[0], kErrBadSlot);
                 slot = -1;
             }
@@ -173,6 +186,10 @@ hipError_t launch_dispatch_copy(const Shape &s, const WsLayout &L, const void *x
     a.E = s.E;
     a.TT = L.tile_tokens;
     a.cols = s.E + s.R + s.N;
+    a.M = s.M;
+    a.epr = s.E / s.R;
+    a.epr_shift = (a.epr & (a.epr - 1)) == 0 ? __builtin_ctz((unsigned)a.epr) : -1;
+    a.rows = s.rows();
     const bool fp8 = (s.x_fmt == 1);
     a.row_bytes = fp8 ? (int64_t)s.H : 2 * (int64_t)s.H;
     a.nvec = (int)(a.row_bytes / 16);

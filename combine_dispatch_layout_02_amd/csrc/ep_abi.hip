@@ -34,6 +34,7 @@ int check_shape(const ep_shape *sh, Shape *out) {
     if (sh->y_format != EP_FMT_BF16 && sh->y_format != EP_FMT_MXFP8) return EP_EINVAL;
     if ((sh->x_format == EP_FMT_FP8_S128 || sh->y_format == EP_FMT_MXFP8) && H % 128 != 0)
         return EP_EINVAL;
+    if (sh->rank_capacity < 0 || (int64_t)R * sh->rank_capacity >= (int64_t(1) << 31)) return EP_EINVAL;
     if (out) {
         out->T = T;
         out->H = H;
@@ -43,6 +44,7 @@ int check_shape(const ep_shape *sh, Shape *out) {
         out->k = k;
         out->x_fmt = sh->x_format;
         out->y_fmt = sh->y_format;
+        out->M = sh->rank_capacity;
     }
     return EP_OK;
 }
@@ -241,6 +243,7 @@ int ep_expert_scale_bf16(const ep_shape *shape, const int32_t *expert_offset, co
     Shape s;
     int rc = check_shape(shape, &s);
     if (rc != EP_OK) return rc;
+    if (s.M != 0) return EP_EINVAL;
     if (s.T == 0) return EP_OK;
     if (!expert_offset || !factor || !recv || !out) return EP_EINVAL;
     if (!aligned16(recv) || !aligned16(out)) return EP_EALIGN;
@@ -254,7 +257,7 @@ int ep_expert_requant_mxfp8(const ep_shape *shape, const int32_t *expert_offset,
     Shape s;
     int rc = check_shape(shape, &s);
     if (rc != EP_OK) return rc;
-    if (s.H % 128 != 0) return EP_EINVAL;
+    if (s.H % 128 != 0 || s.M != 0) return EP_EINVAL;
     if (s.T == 0) return EP_OK;
     if (!expert_offset || !recv_q || !recv_scales || !out_q || !out_e8m0) return EP_EINVAL;
     if (!aligned16(recv_q) || !aligned16(out_q)) return EP_EALIGN;

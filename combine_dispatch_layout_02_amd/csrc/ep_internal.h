@@ -30,11 +30,14 @@ struct WsLayout {
 constexpr int kCtrlWords = 64;
 constexpr uint32_t kErrBadExpert = 0x1u;
 constexpr uint32_t kErrBadSlot = 0x2u;   // internal consistency check of the plan
+constexpr uint32_t kErrRankOverflow = 0x4u;
 
 struct Shape {
     int64_t T;
     int H, E, R, N, k;
     int x_fmt, y_fmt;
+    int M;   // rank_capacity: 0 compacted layout, > 0 RANK_MAJOR
+    int64_t rows() const { return M > 0 ? (int64_t)R * M : T * k; }   // receive rows
 };
 
 WsLayout ws_layout(const Shape &s);

@@ -43,7 +43,15 @@ class ep_shape(ctypes.Structure):
         ("num_topk", ctypes.c_int32),
         ("x_format", ctypes.c_int32),
         ("y_format", ctypes.c_int32),
+        ("rank_capacity", ctypes.c_int32),
     ]
+
+    @property
+    def rows(self) -> int:
+        """Receive rows: T*k (compacted) or R * rank_capacity (RANK_MAJOR)."""
+        if self.rank_capacity > 0:
+            return self.num_ranks * self.rank_capacity
+        return self.num_tokens * self.num_topk
 
 
 class ep_accounting_t(ctypes.Structure):
@@ -118,8 +126,9 @@ def _ok(rc: int, what: str):
         raise RuntimeError(f"{what} failed: {strerror(rc)} ({rc})")
 
 
-def make_shape(T, H, E, R, N, k, x_format=EP_FMT_BF16, y_format=EP_FMT_BF16) -> ep_shape:
-    return ep_shape(int(T), int(H), int(E), int(R), int(N), int(k), int(x_format), int(y_format))
+def make_shape(T, H, E, R, N, k, x_format=EP_FMT_BF16, y_format=EP_FMT_BF16, rank_capacity=0) -> ep_shape:
+    return ep_shape(int(T), int(H), int(E), int(R), int(N), int(k), int(x_format), int(y_format),
+                    int(rank_capacity))
 
 
 def _ptr(t):
@@ -206,12 +215,13 @@ def ep_dispatch(shape, x, x_scales, topk_idx, topk_w, recv_x, recv_x_scales, rec
     _need(x, torch.uint8 if fp8 else torch.bfloat16, (T, H), "x")
     _need(topk_idx, torch.int64, (T, k), "topk_idx")
     _need(topk_w, torch.float32, (T, k), "topk_w")
-    _need(recv_x, x.dtype, (T * k, H), "recv_x")
+    rows = shape.rows
+    _need(recv_x, x.dtype, (rows, H), "recv_x")
     if fp8:
         _need(x_scales, torch.float32, (T, H // 128), "x_scales")
-        _need(recv_x_scales, torch.float32, (T * k, H // 128), "recv_x_scales")
-    _need(recv_src_idx, torch.int32, (T * k,), "recv_src_idx")
-    _need(recv_topk_w, torch.float32, (T * k,), "recv_topk_w")
+        _need(recv_x_scales, torch.float32, (rows, H // 128), "recv_x_scales")
+    _need(recv_src_idx, torch.int32, (rows,), "recv_src_idx")
+    _need(recv_topk_w, torch.float32, (rows,), "recv_topk_w")
     _need(token_slot, torch.int32, (T, k), "token_slot")
     _need(expert_offset, torch.int32, (E + 1,), "expert_offset")
     fn = load().ep_dispatch
@@ -231,9 +241,9 @@ def ep_dispatch(shape, x, x_scales, topk_idx, topk_w, recv_x, recv_x_scales, rec
 def ep_combine(shape, expert_out, expert_out_scales, token_slot, topk_w, y, stream=None):
     T, k, H = shape.num_tokens, shape.num_topk, shape.hidden
     mx = shape.y_format == EP_FMT_MXFP8
-    _need(expert_out, torch.uint8 if mx else torch.bfloat16, (T * k, H), "expert_out")
+    _need(expert_out, torch.uint8 if mx else torch.bfloat16, (shape.rows, H), "expert_out")
     if mx:
-        _need(expert_out_scales, torch.uint8, (T * k, H // 32), "expert_out_scales")
+        _need(expert_out_scales, torch.uint8, (shape.rows, H // 32), "expert_out_scales")
     _need(token_slot, torch.int32, (T, k), "token_slot")
     _need(topk_w, torch.float32, (T, k), "topk_w")
     _need(y, torch.bfloat16, (T, H), "y")
@@ -311,10 +321,11 @@ def dispatch(x, topk_idx, topk_w, shape, ws: Workspace, x_scales=None, stream=No
     dev = x.device
     T, k, H, E = shape.num_tokens, shape.num_topk, shape.hidden, shape.num_experts
     fp8 = shape.x_format == EP_FMT_FP8_S128
-    recv_x = torch.empty((T * k, H), dtype=x.dtype, device=dev)
-    recv_x_scales = torch.empty((T * k, H // 128), dtype=torch.float32, device=dev) if fp8 else None
-    recv_src_idx = torch.empty(T * k, dtype=torch.int32, device=dev)
-    recv_topk_w = torch.empty(T * k, dtype=torch.float32, device=dev)
+    rows = shape.rows
+    recv_x = torch.empty((rows, H), dtype=x.dtype, device=dev)
+    recv_x_scales = torch.empty((rows, H // 128), dtype=torch.float32, device=dev) if fp8 else None
+    recv_src_idx = torch.empty(rows, dtype=torch.int32, device=dev)
+    recv_topk_w = torch.empty(rows, dtype=torch.float32, device=dev)
     token_slot = torch.empty((T, k), dtype=torch.int32, device=dev)
     expert_offset = torch.empty(E + 1, dtype=torch.int32, device=dev)
     ep_dispatch(shape, x, x_scales, topk_idx, topk_w, recv_x, recv_x_scales, recv_src_idx, recv_topk_w,

@@ -64,7 +64,8 @@ enum ep_status {
 
 /* Bits of the device error word. */
 #define EP_ERRFLAG_BAD_EXPERT 0x1u
-#define EP_ERRFLAG_BAD_SLOT   0x2u   /* internal: a computed slot fell outside [0, T*k) (skipped) */
+#define EP_ERRFLAG_BAD_SLOT   0x2u   /* internal: a computed slot fell outside the receive rows (skipped) */
+#define EP_ERRFLAG_RANK_OVERFLOW 0x4u /* RANK_MAJOR: a rank received more pairs than rank_capacity (dropped) */
 
 /* Payload formats. */
 enum ep_format {
@@ -80,7 +81,10 @@ enum ep_format {
  *   1 <= num_ranks <= 64, 1 <= num_nodes <= num_ranks, num_ranks % num_nodes == 0;
  *   hidden >= 8, hidden % 8 == 0 (16-byte bf16 row vectors);
  *   fp8 / mxfp8 formats: hidden % 128 == 0;
- *   x_format in {BF16, FP8_S128}; y_format in {BF16, MXFP8}. */
+ *   x_format in {BF16, FP8_S128}; y_format in {BF16, MXFP8};
+ *   rank_capacity >= 0, num_ranks * rank_capacity < 2^31.
+ * Receive rows ("rows" below): T*k for the compacted layout (rank_capacity
+ * 0), num_ranks * rank_capacity for the RANK_MAJOR layout. */
 typedef struct ep_shape {
     int64_t num_tokens;   /* T: tokens of this source */
     int32_t hidden;       /* H: elements per token row */
@@ -90,6 +94,10 @@ typedef struct ep_shape {
     int32_t num_topk;     /* k */
     int32_t x_format;     /* format of dispatched rows: EP_FMT_BF16 | EP_FMT_FP8_S128 */
     int32_t y_format;     /* format of the rows combine reads: EP_FMT_BF16 | EP_FMT_MXFP8 */
+    int32_t rank_capacity;/* 0: compacted (token-major) receive layout; M > 0: RANK_MAJOR,
+                             rank r owns receive rows [r*M, (r+1)*M) ([PR860] RANK_MAJOR
+                             commit: a fixed [num_ranks, max_tokens_per_rank, hidden]
+                             slot instead of the compacted prefix offset) */
 } ep_shape;
 
 /* Version of this ABI (EP_ABI_VERSION). */
@@ -143,15 +151,21 @@ int ep_dispatch_layout(const ep_shape *shape, const int64_t *topk_idx,
  * (a stable counting sort: expert segments in expert order, ascending t
  * inside a segment), and recv_x[slot] is a bitwise copy of row t.  Capacity
  * is T*k rows, so no receive count has to reach the host first.
+ * RANK_MAJOR (rank_capacity M > 0): the same order inside each rank, but rank
+ * r's rows start at r*M instead of expert_offset[r*E/R]; a pair whose place
+ * inside its rank is >= M is dropped (token_slot -1) and raises
+ * EP_ERRFLAG_RANK_OVERFLOW.  expert_offset keeps the compacted segment
+ * starts, so expert e's rows in rank r's block start at
+ * r*M + expert_offset[e] - expert_offset[r*E/R].
  *   x             [T, H] bf16 (x_format BF16) or [T, H] e4m3 (FP8_S128)
  *   x_scales      [T, H/128] fp32 for FP8_S128, else NULL
  *   topk_idx      [T, k] int64
  *   topk_w        [T, k] fp32 (copied bitwise into recv_topk_w)
- *   recv_x        [T*k, H] same element type as x (16-byte aligned); rows at
- *                 or beyond expert_offset[E] are left untouched
- *   recv_x_scales [T*k, H/128] fp32 for FP8_S128, else NULL
- *   recv_src_idx  [T*k] int32: source token of each slot
- *   recv_topk_w   [T*k] fp32: weight of each slot's pair
+ *   recv_x        [rows, H] same element type as x (16-byte aligned); rows no
+ *                 pair lands in are left untouched
+ *   recv_x_scales [rows, H/128] fp32 for FP8_S128, else NULL
+ *   recv_src_idx  [rows] int32: source token of each slot
+ *   recv_topk_w   [rows] fp32: weight of each slot's pair
  *   token_slot    [T, k] int32: slot of each pair, -1 if masked (handle)
  *   expert_offset [E+1] int32: segment starts, expert_offset[E] = valid
  *                 pairs (handle); rank r's region is
@@ -187,11 +201,14 @@ int ep_dispatch_from_layout(const ep_shape *shape, const void *x, const float *x
  *         acc = fmaf(topk_w[t,j], value(expert_out[s, h]), acc)
  *     y[t,h] = bf16_rne(acc)   (+0.0 if token t has no valid slot)
  * fp32 accumulation in top-k slot order, one rounding to bf16.
- *   expert_out        [T*k, H]: bf16 (y_format BF16) or e4m3 (MXFP8), 16-byte aligned
- *   expert_out_scales [T*k, H/32] e8m0 bytes for MXFP8
+ * Combine does not depend on the receive layout: RANK_MAJOR and compacted
+ * slots give bit-identical y ([PR860] RANK_MAJOR commit: the combine path is
+ * layout-agnostic).
+ *   expert_out        [rows, H]: bf16 (y_format BF16) or e4m3 (MXFP8), 16-byte aligned
+ *   expert_out_scales [rows, H/32] e8m0 bytes for MXFP8
  *                     (value = e4m3 * 2^(e8m0 - 127)), else NULL
  *   token_slot, topk_w: from the dispatch handle / the caller ([T, k]); a
- *                     slot outside [0, T*k) is treated as masked
+ *                     slot outside [0, rows) is treated as masked
  *   y                 [T, H] bf16, 16-byte aligned
  */
 int ep_combine(const ep_shape *shape, const void *expert_out, const uint8_t *expert_out_scales,
@@ -212,9 +229,10 @@ int ep_check(void *ws, size_t ws_bytes, void *stream, uint32_t *flags);
 int ep_quant_fp8_s128(int64_t rows, int32_t hidden, const uint16_t *x, uint8_t *q,
                       float *scales, void *stream);
 
-/* Expert stage of the workloads (outside dispatch and combine).  Rows
- * [0, expert_offset[E]) of a receive buffer with capacity T*k; row s belongs
- * to the expert whose segment holds s.
+/* Expert stage of the workloads (outside dispatch and combine), compacted
+ * layout only (rank_capacity 0, else EP_EINVAL).  Rows [0, expert_offset[E])
+ * of a receive buffer with capacity T*k; row s belongs to the expert whose
+ * segment holds s.
  *   scale_bf16: out[s] = bf16_rne(f32(recv[s]) * factor[e(s)]).
  *   requant_mxfp8: v = e4m3(q[s]) * scales128[s] (times factor[e(s)] when
  *     factor != NULL); per 32-group X = clamp(floor(log2 amax) - 8, -127,

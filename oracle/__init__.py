@@ -79,6 +79,7 @@ def _load():
         "oracle_algo_by_presence": (i64, [i64, i32, i32, i32, P, P]),
         "oracle_accounting": (None, [i32, i32, i32, i32, P, P, i64, ctypes.POINTER(Accounting)]),
         "oracle_slots": (None, [i64, i32, i32, P, P, P, P, P, P]),
+        "oracle_slots_rank_major": (i64, [i64, i32, i32, i32, i32, P, P, P, P, P]),
         "oracle_dispatch_rows": (None, [i64, i32, i64, P, P, P]),
         "oracle_combine_bf16": (None, [i64, i32, i32, P, P, P, P]),
         "oracle_combine_mxfp8": (None, [i64, i32, i32, P, P, P, P, P]),
@@ -191,13 +192,30 @@ def slots(topk_idx: np.ndarray, topk_w: np.ndarray, E: int) -> dict:
     return out
 
 
-def dispatch_rows(src: np.ndarray, token_slot: np.ndarray, fill=0) -> np.ndarray:
-    """recv[token_slot[t, j]] = src[t] bitwise; capacity T*k rows."""
+def slots_rank_major(topk_idx: np.ndarray, topk_w: np.ndarray, E: int, R: int, M: int) -> dict:
+    """RANK_MAJOR fixed-slot layout (PR 860, RANK_MAJOR commit): rank r owns rows
+    [r*M, (r+1)*M); pairs past a rank's capacity are dropped (slot -1)."""
+    lib = _load()
+    idx = _c(topk_idx, np.int64)
+    w = _c(topk_w, np.float32)
+    T, k = idx.shape
+    out = {
+        "token_slot": np.empty((T, k), np.int32),
+        "recv_src_idx": np.full(R * M, -1, np.int32),
+        "recv_topk_w": np.zeros(R * M, np.float32),
+    }
+    out["dropped"] = int(lib.oracle_slots_rank_major(T, k, E, R, M, _p(idx), _p(w), _p(out["token_slot"]),
+                                                     _p(out["recv_src_idx"]), _p(out["recv_topk_w"])))
+    return out
+
+
+def dispatch_rows(src: np.ndarray, token_slot: np.ndarray, fill=0, rows=None) -> np.ndarray:
+    """recv[token_slot[t, j]] = src[t] bitwise; capacity `rows` (default T*k) rows."""
     lib = _load()
     src = np.ascontiguousarray(src)
     ts = _c(token_slot, np.int32)
     T, k = ts.shape
-    recv = np.full((T * k,) + src.shape[1:], fill, dtype=src.dtype)
+    recv = np.full(((T * k) if rows is None else rows,) + src.shape[1:], fill, dtype=src.dtype)
     row_bytes = src.dtype.itemsize * int(np.prod(src.shape[1:], dtype=np.int64))
     lib.oracle_dispatch_rows(T, k, row_bytes, _p(src), _p(ts), _p(recv))
     return recv
@@ -329,20 +347,27 @@ def run_path(inputs: dict) -> dict:
     idx, w = inputs["topk_idx"], inputs["topk_w"]
     out = {"layout": layout(idx, E, R, N)}
     sl = slots(idx, w, E)
+    M = int(inputs.get("rank_capacity", 0))
+    rows = None
+    if M > 0:   # RANK_MAJOR: same expert_offset (compacted starts), slots at fixed rank blocks
+        rm = slots_rank_major(idx, w, E, R, M)
+        sl = dict(sl, token_slot=rm["token_slot"], recv_src_idx=rm["recv_src_idx"],
+                  recv_topk_w=rm["recv_topk_w"], dropped=rm["dropped"])
+        rows = R * M
     out["slots"] = sl
     ts = sl["token_slot"]
     expert = inputs.get("expert", "identity")
     if inputs.get("x_fmt", "bf16") == "fp8":
         q, s = quant_fp8_s128(inputs["x"])
         out["x_q"], out["x_scales"] = q, s
-        rq = dispatch_rows(q, ts)
-        rs = dispatch_rows(s, ts)
+        rq = dispatch_rows(q, ts, rows=rows)
+        rs = dispatch_rows(s, ts, rows=rows)
         out["recv_x"], out["recv_x_scales"] = rq, rs
         eq, ee = expert_requant_mxfp8(rq, rs, sl["expert_offset"], inputs.get("expert_factor"))
         out["expert_q"], out["expert_e8m0"] = eq, ee
         out["y"] = combine_mxfp8(eq, ee, ts, w)
     else:
-        rx = dispatch_rows(inputs["x"], ts)
+        rx = dispatch_rows(inputs["x"], ts, rows=rows)
         out["recv_x"] = rx
         if expert == "scale":
             eo = expert_scale_bf16(rx, sl["expert_offset"], inputs["expert_factor"])

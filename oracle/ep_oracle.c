@@ -210,6 +210,33 @@ void oracle_slots(int64_t T, int32_t k, int32_t E, const int64_t *topk_idx,
     free(fill);
 }
 
+/* RANK_MAJOR: rows grouped by destination rank at fixed offsets r * M; the
+ * order inside a rank's block is expert, then (t, j).  Written as a direct
+ * walk over each rank's experts and the pairs routed to them. */
+int64_t oracle_slots_rank_major(int64_t T, int32_t k, int32_t E, int32_t R, int32_t M,
+                                const int64_t *topk_idx, const float *topk_w,
+                                int32_t *token_slot, int32_t *recv_src_idx, float *recv_topk_w)
+{
+    const int32_t experts_per_rank = E / R;
+    int64_t dropped = 0;
+    for (int64_t i = 0; i < T * k; ++i) token_slot[i] = -1;
+    for (int32_t r = 0; r < R; ++r) {
+        int64_t filled = 0;
+        for (int32_t e = r * experts_per_rank; e < (r + 1) * experts_per_rank; ++e)
+            for (int64_t t = 0; t < T; ++t)
+                for (int32_t j = 0; j < k; ++j) {
+                    if (topk_idx[t * k + j] != e) continue;
+                    if (filled >= M) { ++dropped; continue; }
+                    const int64_t s = (int64_t)r * M + filled;
+                    filled += 1;
+                    token_slot[t * k + j] = (int32_t)s;
+                    recv_src_idx[s] = (int32_t)t;
+                    recv_topk_w[s] = topk_w[t * k + j];
+                }
+    }
+    return dropped;
+}
+
 /* Dispatch moves bytes only: each valid (t, j) pair receives a copy of row t
  * ([MORI] "NVL / XGMI bandwidth": the received tensor holds token rows). */
 void oracle_dispatch_rows(int64_t T, int32_t k, int64_t row_bytes, const void *src,

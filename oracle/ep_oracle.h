@@ -92,6 +92,17 @@ void oracle_slots(int64_t T, int32_t k, int32_t E, const int64_t *topk_idx,
                   int32_t *recv_src_idx,  /* [T*k] */
                   float *recv_topk_w);    /* [T*k] */
 
+/* RANK_MAJOR fixed-slot layout ([PR860] RANK_MAJOR commit: each dispatched
+ * token at a fixed [num_ranks, max_tokens_per_rank, hidden] slot instead of a
+ * compacted prefix offset).  For one source: virtual rank r owns receive rows
+ * [r*M, (r+1)*M); inside, the rank's expert segments in expert order, pairs
+ * in row-major (t, j) order.  Pairs past a rank's capacity M get slot -1 and
+ * are counted in the return value.  recv_src_idx / recv_topk_w have R*M
+ * entries; rows a rank does not fill are left untouched. */
+int64_t oracle_slots_rank_major(int64_t T, int32_t k, int32_t E, int32_t R, int32_t M,
+                                const int64_t *topk_idx, const float *topk_w,
+                                int32_t *token_slot, int32_t *recv_src_idx, float *recv_topk_w);
+
 /* recv[token_slot[t,j]] = src[t] for every valid pair: a bitwise copy of
  * row_bytes bytes per row (works for bf16 rows, e4m3 rows and scale rows). */
 void oracle_dispatch_rows(int64_t T, int32_t k, int64_t row_bytes, const void *src,

@@ -58,6 +58,19 @@ def test_validate_rejects(lib, bad):
     assert lib.ep_workspace_bytes(ctypes.byref(sh), ctypes.byref(n)) == ep.EP_EINVAL
 
 
+def test_rank_capacity_limits(lib):
+    sh = ep.make_shape(64, 256, 16, 4, 1, 2, rank_capacity=-1)
+    assert lib.ep_validate_shape(ctypes.byref(sh)) == ep.EP_EINVAL
+    sh = ep.make_shape(64, 256, 16, 4, 1, 2, rank_capacity=2 ** 29)
+    assert lib.ep_validate_shape(ctypes.byref(sh)) == ep.EP_EINVAL
+    sh = ep.make_shape(64, 256, 16, 4, 1, 2, rank_capacity=100)
+    assert lib.ep_validate_shape(ctypes.byref(sh)) == ep.EP_OK
+    assert sh.rows == 400
+    fake = ctypes.c_void_p(0x1000)
+    # the expert stage handles the compacted layout only
+    assert lib.ep_expert_scale_bf16(ctypes.byref(sh), fake, fake, fake, fake, None) == ep.EP_EINVAL
+
+
 @pytest.mark.parametrize("p", [GOOD, dict(T=0, H=8, E=1, R=1, N=1, k=1), dict(T=64, H=256, E=16, R=4, N=1, k=2),
                                dict(T=8192, H=7168, E=4096, R=64, N=64, k=32)])
 def test_validate_accepts_and_sizes_workspace(lib, p):

@@ -89,3 +89,53 @@ def test_dispatch_rows_bitwise():
     scales = np.arange(inp["T"] * 2, dtype=np.float32).reshape(inp["T"], 2)
     rs = oracle.dispatch_rows(scales, sl["token_slot"])
     np.testing.assert_array_equal(rs[:V], scales[sl["recv_src_idx"][:V]])
+
+
+def _brute_rank_major(idx, E, R, M):
+    T, k = idx.shape
+    epr = E // R
+    slot = -np.ones((T, k), np.int64)
+    dropped = 0
+    for r in range(R):
+        pairs = sorted((int(idx[t, j]), t, j) for t in range(T) for j in range(k)
+                       if r * epr <= idx[t, j] < (r + 1) * epr)
+        for pos, (_, t, j) in enumerate(pairs):
+            if pos < M:
+                slot[t, j] = r * M + pos
+            else:
+                dropped += 1
+    return slot, dropped
+
+
+@pytest.mark.parametrize("M", [1, 7, 30, 64])
+def test_rank_major_brute_force(M):
+    """RANK_MAJOR (MSCCL++ PR 860, RANK_MAJOR commit): rank r owns rows
+    [r*M, (r+1)*M); inside, expert then (t, j) order; pairs past M dropped."""
+    rng = np.random.default_rng(9)
+    E, R, k, T = 16, 4, 3, 40
+    idx = rng.integers(-1, E, (T, k)).astype(np.int64)
+    w = rng.random((T, k), dtype=np.float32)
+    rm = oracle.slots_rank_major(idx, w, E, R, M)
+    ref, dropped = _brute_rank_major(idx, E, R, M)
+    np.testing.assert_array_equal(rm["token_slot"], ref)
+    assert rm["dropped"] == dropped
+    tt, jj = np.nonzero(ref >= 0)
+    np.testing.assert_array_equal(rm["recv_src_idx"][ref[tt, jj]], tt)
+
+
+def test_rank_major_reduces_bitwise_to_token_major():
+    """The page states the combine over RANK_MAJOR slots reduces bit-exactly
+    to the token-major result (the combine is layout-agnostic)."""
+    inp = W.make_inputs("prefill2n", T=256, H=512, mask_frac=0.1)
+    tm = oracle.run_path(inp)
+    M = int(max(np.diff(tm["slots"]["expert_offset"][:: inp["E"] // inp["R"]])))
+    rm = oracle.run_path(dict(inp, rank_capacity=M))
+    assert rm["slots"]["dropped"] == 0
+    np.testing.assert_array_equal(rm["y"], tm["y"])
+    # same place inside each rank's block
+    epr = inp["E"] // inp["R"]
+    off = tm["slots"]["expert_offset"]
+    ts_tm, ts_rm = tm["slots"]["token_slot"], rm["slots"]["token_slot"]
+    r = np.where(inp["topk_idx"] >= 0, inp["topk_idx"] // epr, 0)
+    valid = inp["topk_idx"] >= 0
+    np.testing.assert_array_equal((ts_rm - r * M)[valid], (ts_tm - off[r * epr])[valid])

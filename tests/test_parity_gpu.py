@@ -171,3 +171,29 @@ def test_mxfp8_combine_every_code_and_scale():
                   torch.from_numpy(slot).cuda(), torch.from_numpy(w).cuda(), y)
     got = gpu_path.bf16_bits(y)
     np.testing.assert_array_equal(got, ref)
+
+
+@pytest.mark.parametrize("slack", [0, 37])
+def test_rank_major_full_size(slack):
+    """RANK_MAJOR layout at the prefill shape: parity with the oracle, and y
+    bit-identical to the compacted layout's y (PR 860: the combine reduces
+    bit-exactly to the token-major result)."""
+    import gpu_path
+    inp = W.make_inputs("prefill2n")
+    off = oracle.slots(inp["topk_idx"], inp["topk_w"], inp["E"])["expert_offset"]
+    M = int(max(np.diff(off[:: inp["E"] // inp["R"]]))) + slack
+    g_tm = gpu_path.run(inp)
+    g, r, ndiff = _run_both(dict(inp, rank_capacity=M))
+    assert ndiff == 0
+    np.testing.assert_array_equal(g["y"], g_tm["y"])
+
+
+def test_rank_major_overflow_is_flagged_and_dropped():
+    import gpu_path
+    inp = dict(W.make_inputs("tiny", T=500, H=256), rank_capacity=100)
+    g = gpu_path.run(inp, check=False)
+    with pytest.raises(RuntimeError, match="flags 0x4"):
+        g["ws"].check()
+    r = oracle.run_path(inp)
+    assert r["slots"]["dropped"] > 0
+    gpu_path.compare(g, r, False)
