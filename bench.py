@@ -197,8 +197,9 @@ def measure(workload: str, steps: int, warmup: int, graph: bool = False, **overr
     inp = workloads.make_inputs(workload, **overrides)
     T, H, E, R, N, k = (inp[n] for n in ("T", "H", "E", "R", "N", "k"))
     fp8 = inp["x_fmt"] == "fp8"
-    shape = ep.make_shape(T, H, E, R, N, k, ep.EP_FMT_FP8_S128 if fp8 else ep.EP_FMT_BF16,
-                          ep.EP_FMT_MXFP8 if fp8 else ep.EP_FMT_BF16)
+    nv = inp.get("y_fmt") == "nvfp4"
+    yf = ep.EP_FMT_NVFP4 if nv else (ep.EP_FMT_MXFP8 if fp8 else ep.EP_FMT_BF16)
+    shape = ep.make_shape(T, H, E, R, N, k, ep.EP_FMT_FP8_S128 if fp8 else ep.EP_FMT_BF16, yf)
     ws = ep.Workspace(shape, dev)
 
     # inputs resident in HBM before timing
@@ -224,6 +225,9 @@ def measure(workload: str, steps: int, warmup: int, graph: bool = False, **overr
     if fp8:
         eo = torch.empty((T * k, H), dtype=torch.uint8, device=dev)
         eos = torch.empty((T * k, H // 32), dtype=torch.uint8, device=dev)
+    elif nv:
+        eo = torch.empty((T * k, H // 2), dtype=torch.uint8, device=dev)
+        eos = torch.empty((T * k, H // 16), dtype=torch.int16, device=dev)
     elif inp["expert"] == "scale":
         eo, eos = torch.empty_like(recv_x), None
     else:
@@ -239,13 +243,15 @@ def measure(workload: str, steps: int, warmup: int, graph: bool = False, **overr
     def expert():
         if fp8:
             ep.ep_expert_requant_mxfp8(shape, off, factor, recv_x, recv_s, eo, eos)
+        elif nv:
+            ep.ep_expert_requant_nvfp4(shape, off, factor, recv_x, eo, eos)
         elif inp["expert"] == "scale":
             ep.ep_expert_scale_bf16(shape, off, factor, recv_x, eo)
 
     def combine():
         ep.ep_combine(shape, eo, eos, slot, w, y)
 
-    has_expert = fp8 or inp["expert"] == "scale"
+    has_expert = fp8 or nv or inp["expert"] == "scale"
     # the expert stage stands in for the expert computation between dispatch
     # and combine: it runs in warmup (its output does not change from step to
     # step, the inputs being the same) and stays out of the timed step
@@ -337,7 +343,7 @@ def measure(workload: str, steps: int, warmup: int, graph: bool = False, **overr
     step_s = ms_step / 1000.0
     dom = max(("dispatch", "combine"), key=lambda p: phase_us[p])
     kernels = {"dispatch": "ep_dispatch_copy_kernel", "combine": "ep_combine_" +
-               ("mxfp8" if fp8 else "bf16") + "_kernel"}
+               ("mxfp8" if fp8 else ("nvfp4" if nv else "bf16")) + "_kernel"}
     achieved = algo_bytes[dom] / (phase_us[dom] * 1e-6) / 1e9
     traffic = measured_traffic(workload, kernels[dom])
 
@@ -352,7 +358,7 @@ def measure(workload: str, steps: int, warmup: int, graph: bool = False, **overr
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp8/mxfp8" if fp8 else "bf16",
+        "dtype": "fp8/mxfp8" if fp8 else ("bf16/nvfp4" if nv else "bf16"),
         "data": "synthetic",
         "config": {"workload": workload, "tokens": T, "hidden": H, "experts": E, "virtual_ranks": R,
                    "virtual_nodes": N, "topk": k, "routing": inp["routing"], "expert": inp["expert"],

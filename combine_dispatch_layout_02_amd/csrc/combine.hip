@@ -199,6 +199,79 @@ __global__ __launch_bounds__(256) void ep_combine_mxfp8_kernel(CombineArgs a) {
     }
 }
 
+// nvfp4 rows: a 16-byte vector holds 32 e2m1 elements (two 16-element scale
+// groups, one bf16 scale each); the y row vectors for it are four 16-byte
+// bf16 vectors.  Elements decode with v_cvt_scalef32_pk_f32_fp4 at scale 1.0
+// (exact), then one fp32 multiply by the group's bf16 scale (exact: a 2-bit
+// times an 8-bit significand).  The instruction's own scale operand is not
+// used: it honours only the exponent of a scale, and these scales are not
+// powers of two.
+template <int KC>
+__global__ __launch_bounds__(256) void ep_combine_nvfp4_kernel(CombineArgs a) {
+    constexpr int KB = KC > 0 ? KC : kSlotBatch;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int64_t gw = (int64_t)blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
+    const int64_t t = gw / a.S;
+    const int sub = (int)(gw - t * a.S);
+    if (t >= a.T) return;
+    const int k = KC > 0 ? KC : a.k;
+
+    int32_t slot = -1;
+    float wt = 0.0f;
+    if (lane < k) {
+        slot = a.token_slot[t * k + lane];
+        wt = a.topk_w[t * k + lane];
+        if ((uint64_t)slot >= (uint64_t)a.rows) slot = -1;   // outside the receive rows: masked
+    }
+    const bool any_valid = __ballot(lane < k && slot >= 0) != 0;
+    char *yrow = a.y + t * (int64_t)a.H * 2;
+    const int stride = kWave * a.S;
+    const int G16 = a.H / 16;
+    const uint16_t *scales = reinterpret_cast<const uint16_t *>(a.eo_scales);
+
+    for (int v = lane + kWave * sub; v < a.nvec; v += stride) {
+        float acc[32];
+#pragma unroll
+        for (int q = 0; q < 32; ++q) acc[q] = -0.0f;
+        for (int jb = 0; jb < k; jb += KB) {
+            vec16 buf[KB];
+            uint32_t sc[KB];
+#pragma unroll
+            for (int jj = 0; jj < KB; ++jj) {
+                const int64_t r = row_of(readlane(slot, jb + jj));
+                buf[jj] = ld16_nt(a.eo + r * a.row_bytes + (int64_t)v * 16);
+                sc[jj] = *reinterpret_cast<const uint32_t *>(scales + r * G16 + 2 * v);   // two bf16
+            }
+#pragma unroll
+            for (int jj = 0; jj < KB; ++jj) {
+                if (readlane(slot, jb + jj) < 0) continue;
+                const float w = readlane(wt, jb + jj);
+                const float s_lo = bf16_lo(sc[jj]), s_hi = bf16_hi(sc[jj]);
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const float s = q < 2 ? s_lo : s_hi;   // dwords 0-1: group 2v, 2-3: group 2v+1
+                    // byte b of the dword holds elements 2b (low nibble) and 2b + 1
+                    const f32x2 e0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(buf[jj][q], 1.0f, 0);
+                    const f32x2 e1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(buf[jj][q], 1.0f, 1);
+                    const f32x2 e2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(buf[jj][q], 1.0f, 2);
+                    const f32x2 e3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(buf[jj][q], 1.0f, 3);
+                    const float ev[8] = {e0.x, e0.y, e1.x, e1.y, e2.x, e2.y, e3.x, e3.y};
+#pragma unroll
+                    for (int b = 0; b < 8; ++b) acc[8 * q + b] = __builtin_fmaf(w, ev[b] * s, acc[8 * q + b]);
+                }
+            }
+        }
+#pragma unroll
+        for (int o = 0; o < 4; ++o) {
+            vec16 out;
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                out[q] = any_valid ? pack_bf16x2(acc[8 * o + 2 * q], acc[8 * o + 2 * q + 1]) : 0u;
+            store_y(yrow + (int64_t)v * 64 + 16 * o, out);
+        }
+    }
+}
+
 }  // namespace
 
 hipError_t launch_combine(const Shape &s, const void *expert_out, const uint8_t *expert_scales,
@@ -215,13 +288,16 @@ hipError_t launch_combine(const Shape &s, const void *expert_out, const uint8_t 
     a.k = s.k;
     a.H = s.H;
     a.rows = s.rows();
-    const bool mx = (s.y_fmt == 2);
-    a.row_bytes = mx ? (int64_t)s.H : 2 * (int64_t)s.H;
+    const bool mx = (s.y_fmt == 2), nv = (s.y_fmt == 3);
+    a.row_bytes = nv ? (int64_t)s.H / 2 : (mx ? (int64_t)s.H : 2 * (int64_t)s.H);
     a.nvec = (int)(a.row_bytes / 16);
     a.S = waves_per_token(s.T, a.nvec, EP_COMBINE_WAVES);
     const int64_t waves = s.T * a.S;
     const dim3 grid((unsigned)((waves + 3) / 4)), block(256);
-    if (mx) {
+    if (nv) {
+        if (s.k == 8) hipLaunchKernelGGL(ep_combine_nvfp4_kernel<8>, grid, block, 0, stream, a);
+        else hipLaunchKernelGGL(ep_combine_nvfp4_kernel<0>, grid, block, 0, stream, a);
+    } else if (mx) {
         if (s.k == 8) hipLaunchKernelGGL(ep_combine_mxfp8_kernel<8>, grid, block, 0, stream, a);
         else hipLaunchKernelGGL(ep_combine_mxfp8_kernel<0>, grid, block, 0, stream, a);
     } else {

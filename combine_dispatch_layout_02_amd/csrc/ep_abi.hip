@@ -31,8 +31,9 @@ int check_shape(const ep_shape *sh, Shape *out) {
     if (E % R != 0 || R % N != 0) return EP_EINVAL;
     if (H < 8 || H % 8 != 0) return EP_EINVAL;
     if (sh->x_format != EP_FMT_BF16 && sh->x_format != EP_FMT_FP8_S128) return EP_EINVAL;
-    if (sh->y_format != EP_FMT_BF16 && sh->y_format != EP_FMT_MXFP8) return EP_EINVAL;
-    if ((sh->x_format == EP_FMT_FP8_S128 || sh->y_format == EP_FMT_MXFP8) && H % 128 != 0)
+    if (sh->y_format != EP_FMT_BF16 && sh->y_format != EP_FMT_MXFP8 && sh->y_format != EP_FMT_NVFP4)
+        return EP_EINVAL;
+    if ((sh->x_format != EP_FMT_BF16 || sh->y_format != EP_FMT_BF16) && H % 128 != 0)
         return EP_EINVAL;
     if (sh->rank_capacity < 0 || (int64_t)R * sh->rank_capacity >= (int64_t(1) << 31)) return EP_EINVAL;
     if (out) {
@@ -207,10 +208,12 @@ int ep_combine(const ep_shape *shape, const void *expert_out, const uint8_t *exp
     if (rc != EP_OK) return rc;
     if (s.T == 0) return EP_OK;
     if (!expert_out || !token_slot || !topk_w || !y) return EP_EINVAL;
-    const bool mx = s.y_fmt == EP_FMT_MXFP8;
-    if (mx && !expert_out_scales) return EP_EINVAL;
-    if (!mx && expert_out_scales) return EP_EINVAL;
+    const bool scaled = s.y_fmt != EP_FMT_BF16;
+    if (scaled && !expert_out_scales) return EP_EINVAL;
+    if (!scaled && expert_out_scales) return EP_EINVAL;
     if (!aligned16(expert_out) || !aligned16(y)) return EP_EALIGN;
+    if (s.y_fmt == EP_FMT_NVFP4 && (reinterpret_cast<uintptr_t>(expert_out_scales) & 3u) != 0)
+        return EP_EALIGN;
     return hip_status(ep::launch_combine(s, expert_out, expert_out_scales, token_slot, topk_w, y,
                                          static_cast<hipStream_t>(stream)));
 }
@@ -266,6 +269,20 @@ int ep_expert_requant_mxfp8(const ep_shape *shape, const int32_t *expert_offset,
                                                       static_cast<hipStream_t>(stream)));
 }
 
+int ep_expert_requant_nvfp4(const ep_shape *shape, const int32_t *expert_offset, const float *factor,
+                            const uint16_t *recv, uint8_t *out_q, uint16_t *out_scales,
+                            void *stream) {
+    Shape s;
+    int rc = check_shape(shape, &s);
+    if (rc != EP_OK) return rc;
+    if (s.H % 128 != 0 || s.M != 0) return EP_EINVAL;
+    if (s.T == 0) return EP_OK;
+    if (!expert_offset || !recv || !out_q || !out_scales) return EP_EINVAL;
+    if (!aligned16(recv) || (reinterpret_cast<uintptr_t>(out_q) & 7u) != 0) return EP_EALIGN;
+    return hip_status(ep::launch_expert_requant_nvfp4(s, expert_offset, factor, recv, out_q, out_scales,
+                                                      static_cast<hipStream_t>(stream)));
+}
+
 int ep_accounting(const ep_shape *shape, int32_t own_node, const int32_t *num_tokens_per_rank,
                   const int32_t *num_tokens_per_node, int64_t rdma_algo_token_count,
                   int64_t valid_pairs, ep_accounting_t *out) {
@@ -292,7 +309,8 @@ int ep_accounting(const ep_shape *shape, int32_t own_node, const int32_t *num_to
     // minimum HBM traffic of one call each (payload rows + index/weight metadata)
     const double T = (double)s.T, TK = (double)s.T * s.k, V = (double)valid_pairs;
     const double xrow = (s.x_fmt == EP_FMT_FP8_S128) ? H + 4.0 * H / 128.0 : 2.0 * H;
-    const double yrow = (s.y_fmt == EP_FMT_MXFP8) ? H + H / 32.0 : 2.0 * H;
+    const double yrow = (s.y_fmt == EP_FMT_MXFP8) ? H + H / 32.0
+                        : (s.y_fmt == EP_FMT_NVFP4) ? H / 2.0 + 2.0 * H / 16.0 : 2.0 * H;
     out->hbm_layout_bytes = TK * 8.0 + T * s.R + 4.0 * (s.R + s.N + s.E) + 8.0;
     out->hbm_dispatch_bytes = T * xrow + V * xrow             // rows: read once, written per pair
                               + TK * (8.0 + 4.0 + 4.0)        // topk_idx, topk_w read; token_slot written

@@ -77,6 +77,30 @@ __device__ __forceinline__ float e4m3_to_f32(uint32_t b) {
     return (b & 0x80u) ? -v : v;
 }
 
+// ---------------------------------------------------------------- e2m1
+
+// binary32 -> e2m1 code (OCP 4-bit E2M1: bias 1, one mantissa bit,
+// magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6), RNE, saturating to +-6.
+//   |f| >= 6 (or inf / NaN) -> 0x7 with sign
+//   [1, 6): keep one of 23 mantissa bits with RNE on the integer pattern,
+//           rebias 127 -> 1 (a carry moves into the exponent)
+//   below 1: steps of 0.5: rint(|f| * 2) (2 is the code of 1.0)
+__device__ __forceinline__ uint32_t f32_to_e2m1(float f) {
+    const uint32_t u = f2u(f);
+    const uint32_t sign = (u >> 28) & 0x8u;
+    const uint32_t a = u & 0x7FFFFFFFu;
+    uint32_t code;
+    if (a >= 0x40C00000u) {            // 6.0f, inf, NaN
+        code = 0x7u;
+    } else if (a >= 0x3F800000u) {     // 1.0f
+        const uint32_t r = a + 0x1FFFFFu + ((a >> 22) & 1u);
+        code = (r >> 22) - (126u << 1);
+    } else {
+        code = (uint32_t)__builtin_rintf(u2f(a) * 2.0f);
+    }
+    return sign | code;
+}
+
 // ---------------------------------------------------------------- e8m0
 
 // 2^(e - 127) as a binary32 (exact; e = 0 gives the subnormal 2^-127).

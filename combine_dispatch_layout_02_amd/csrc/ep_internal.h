@@ -72,6 +72,10 @@ hipError_t launch_expert_requant_mxfp8(const Shape &s, const int32_t *expert_off
                                        const float *recv_scales, uint8_t *out_q,
                                        uint8_t *out_e8m0, hipStream_t stream);
 
+hipError_t launch_expert_requant_nvfp4(const Shape &s, const int32_t *expert_offset,
+                                       const float *factor, const uint16_t *recv, uint8_t *out_q,
+                                       uint16_t *out_scales, hipStream_t stream);
+
 hipError_t launch_calib_copy(const void *src, void *dst, size_t bytes, hipStream_t stream);
 
 // Waves per token for the row kernels: the smallest power of two that gives

@@ -131,6 +131,50 @@ __global__ __launch_bounds__(256) void ep_expert_requant_kernel(const int32_t *o
     if ((lane & 1) == 0) oe[s * (H / 32) + h / 32] = (uint8_t)(X + 127);
 }
 
+// nvfp4 re-encode of bf16 rows: a lane holds one 16-element group (two
+// 16-byte loads); one wave per (row, 1024 elements).
+__global__ __launch_bounds__(256) void ep_expert_requant_nvfp4_kernel(const int32_t *off, int E, int H,
+                                                                      int64_t rows_cap,
+                                                                      const float *factor,
+                                                                      const uint16_t *recv,
+                                                                      uint8_t *oq, uint16_t *os) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int parts = (H + 1023) / 1024;
+    const int64_t gw = (int64_t)blockIdx.x * 4 + threadIdx.x / kWave;
+    const int64_t s = gw / parts;
+    const int part = (int)(gw - s * parts);
+    if (s >= rows_cap || s >= off[E]) return;   // wave-uniform
+    const int h = part * 1024 + lane * 16;
+    if (h >= H) return;
+    const float f = factor ? factor[expert_of_row(off, E, s)] : 1.0f;
+    const vec16 b0 = ld16(recv + s * H + h), b1 = ld16(recv + s * H + h + 8);
+    float v[16];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        v[2 * q] = bf16_lo(b0[q]);
+        v[2 * q + 1] = bf16_hi(b0[q]);
+        v[8 + 2 * q] = bf16_lo(b1[q]);
+        v[8 + 2 * q + 1] = bf16_hi(b1[q]);
+    }
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        if (factor) v[i] = v[i] * f;
+        amax = fmaxf(amax, fabsf(v[i]));
+    }
+    uint32_t sb = f32_to_bf16(amax / 6.0f);
+    if ((sb & 0x7FFFu) == 0u) sb = 0x3F80u;   // zero scale -> 1.0
+    const float sf = u2f(sb << 16);
+    uint2 packed = {0u, 0u};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const uint32_t byte = f32_to_e2m1(v[2 * i] / sf) | (f32_to_e2m1(v[2 * i + 1] / sf) << 4);
+        if (i < 4) packed.x |= byte << (8 * i); else packed.y |= byte << (8 * (i - 4));
+    }
+    *reinterpret_cast<uint2 *>(oq + s * (H / 2) + h / 2) = packed;
+    os[s * (H / 16) + h / 16] = (uint16_t)sb;
+}
+
 __global__ __launch_bounds__(256) void ep_fill_zero_kernel(uint32_t *p, size_t words) {
     for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < words;
          i += (size_t)gridDim.x * blockDim.x)
@@ -176,6 +220,17 @@ hipError_t launch_expert_requant_mxfp8(const Shape &s, const int32_t *expert_off
     hipLaunchKernelGGL(ep_expert_requant_kernel, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0,
                        stream, expert_offset, s.E, s.H, rows, factor, recv_q, recv_scales, out_q,
                        out_e8m0);
+    return hipGetLastError();
+}
+
+hipError_t launch_expert_requant_nvfp4(const Shape &s, const int32_t *expert_offset,
+                                       const float *factor, const uint16_t *recv, uint8_t *out_q,
+                                       uint16_t *out_scales, hipStream_t stream) {
+    const int64_t rows = s.T * s.k;
+    if (rows == 0) return hipSuccess;
+    const int64_t waves = rows * ((s.H + 1023) / 1024);
+    hipLaunchKernelGGL(ep_expert_requant_nvfp4_kernel, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0,
+                       stream, expert_offset, s.E, s.H, rows, factor, recv, out_q, out_scales);
     return hipGetLastError();
 }
 

@@ -21,7 +21,7 @@ import torch
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libep_hip.so")
 
-EP_FMT_BF16, EP_FMT_FP8_S128, EP_FMT_MXFP8 = 0, 1, 2
+EP_FMT_BF16, EP_FMT_FP8_S128, EP_FMT_MXFP8, EP_FMT_NVFP4 = 0, 1, 2, 3
 EP_OK, EP_EINVAL, EP_EALIGN, EP_EWORKSPACE, EP_EHIP, EP_EDEVICE = 0, -1, -2, -3, -4, -5
 
 # every symbol include/ep.h declares
@@ -29,7 +29,8 @@ EXPORTED = (
     "ep_abi_version", "ep_strerror", "ep_validate_shape", "ep_workspace_bytes", "ep_workspace_init",
     "ep_dispatch_layout", "ep_dispatch", "ep_dispatch_from_layout", "ep_combine", "ep_check",
     "ep_quant_fp8_s128",
-    "ep_expert_scale_bf16", "ep_expert_requant_mxfp8", "ep_accounting", "ep_calib_copy",
+    "ep_expert_scale_bf16", "ep_expert_requant_mxfp8", "ep_expert_requant_nvfp4", "ep_accounting",
+    "ep_calib_copy",
 )
 
 
@@ -104,6 +105,7 @@ def load():
         "ep_quant_fp8_s128": (ctypes.c_int, [i64, i32, P, P, P, P]),
         "ep_expert_scale_bf16": (ctypes.c_int, [SP, P, P, P, P, P]),
         "ep_expert_requant_mxfp8": (ctypes.c_int, [SP, P, P, P, P, P, P, P]),
+        "ep_expert_requant_nvfp4": (ctypes.c_int, [SP, P, P, P, P, P, P]),
         "ep_accounting": (ctypes.c_int, [SP, i32, P, P, i64, i64, ctypes.POINTER(ep_accounting_t)]),
         "ep_calib_copy": (ctypes.c_int, [P, P, sz, P]),
     }
@@ -240,10 +242,17 @@ def ep_dispatch(shape, x, x_scales, topk_idx, topk_w, recv_x, recv_x_scales, rec
 
 def ep_combine(shape, expert_out, expert_out_scales, token_slot, topk_w, y, stream=None):
     T, k, H = shape.num_tokens, shape.num_topk, shape.hidden
-    mx = shape.y_format == EP_FMT_MXFP8
-    _need(expert_out, torch.uint8 if mx else torch.bfloat16, (shape.rows, H), "expert_out")
-    if mx:
+    fmt = shape.y_format
+    if fmt == EP_FMT_MXFP8:
+        _need(expert_out, torch.uint8, (shape.rows, H), "expert_out")
         _need(expert_out_scales, torch.uint8, (shape.rows, H // 32), "expert_out_scales")
+    elif fmt == EP_FMT_NVFP4:
+        _need(expert_out, torch.uint8, (shape.rows, H // 2), "expert_out")
+        if expert_out_scales is None or expert_out_scales.dtype not in (torch.int16, torch.bfloat16) \
+                or tuple(expert_out_scales.shape) != (shape.rows, H // 16):
+            raise ValueError("expert_out_scales: expected bf16 bits [rows, H/16]")
+    else:
+        _need(expert_out, torch.bfloat16, (shape.rows, H), "expert_out")
     _need(token_slot, torch.int32, (T, k), "token_slot")
     _need(topk_w, torch.float32, (T, k), "topk_w")
     _need(y, torch.bfloat16, (T, H), "y")
@@ -270,6 +279,12 @@ def ep_expert_requant_mxfp8(shape, expert_offset, factor, recv_q, recv_scales, o
     _ok(load().ep_expert_requant_mxfp8(ctypes.byref(shape), _ptr(expert_offset), _ptr(factor),
                                        _ptr(recv_q), _ptr(recv_scales), _ptr(out_q), _ptr(out_e8m0),
                                        _stream(stream)), "ep_expert_requant_mxfp8")
+
+
+def ep_expert_requant_nvfp4(shape, expert_offset, factor, recv, out_q, out_scales, stream=None):
+    _ok(load().ep_expert_requant_nvfp4(ctypes.byref(shape), _ptr(expert_offset), _ptr(factor), _ptr(recv),
+                                       _ptr(out_q), _ptr(out_scales), _stream(stream)),
+        "ep_expert_requant_nvfp4")
 
 
 def ep_accounting(shape, own_node, num_tokens_per_rank, num_tokens_per_node, rdma_algo_token_count,

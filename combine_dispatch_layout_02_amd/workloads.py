@@ -17,6 +17,8 @@ rank, two nodes of eight ranks for the RDMA accounting):
               over a seeded expert permutation, without replacement
   quant       T=4096, H=7168, E=256, R=8,  N=1, k=8, uniform; rows travel
               as fp8 e4m3 + fp32 scale per 128, the expert returns mxfp8
+  nvfp4       as quant, but bf16 rows out and an nvfp4 payload back (16
+              e2m1 + one bf16 scale per 16 elements)
 
 Draw order from one numpy PCG64 stream per workload (seed 0 unless given):
 x, routing, weight logits, expert factors.  bf16 rows are the round-to-
@@ -38,6 +40,8 @@ WORKLOADS = {
                    expert="identity", x_fmt="bf16"),
     "quant": dict(T=4096, H=7168, E=256, R=8, N=1, k=8, routing="uniform", expert="identity",
                   x_fmt="fp8"),
+    "nvfp4": dict(T=4096, H=7168, E=256, R=8, N=1, k=8, routing="uniform", expert="identity",
+                  x_fmt="bf16", y_fmt="nvfp4"),
 }
 
 

@@ -71,7 +71,9 @@ enum ep_status {
 enum ep_format {
     EP_FMT_BF16 = 0,         /* 2 bytes per element */
     EP_FMT_FP8_S128 = 1,     /* e4m3 bytes + one fp32 scale per 128 elements ([MORI] script's fp8 factor) */
-    EP_FMT_MXFP8 = 2         /* e4m3 bytes + one e8m0 byte per 32 elements ([MEB]) */
+    EP_FMT_MXFP8 = 2,        /* e4m3 bytes + one e8m0 byte per 32 elements ([MEB]) */
+    EP_FMT_NVFP4 = 3         /* e2m1 nibbles (2 per byte, even element low) + one bf16 scale
+                                per 16 elements ([MEB] "16e2m1xbf16") */
 };
 
 /* Problem shape.  Supported range (else EP_EINVAL):
@@ -80,8 +82,8 @@ enum ep_format {
  *   1 <= num_experts <= 4096, num_experts % num_ranks == 0;
  *   1 <= num_ranks <= 64, 1 <= num_nodes <= num_ranks, num_ranks % num_nodes == 0;
  *   hidden >= 8, hidden % 8 == 0 (16-byte bf16 row vectors);
- *   fp8 / mxfp8 formats: hidden % 128 == 0;
- *   x_format in {BF16, FP8_S128}; y_format in {BF16, MXFP8};
+ *   fp8 / mxfp8 / nvfp4 formats: hidden % 128 == 0;
+ *   x_format in {BF16, FP8_S128}; y_format in {BF16, MXFP8, NVFP4};
  *   rank_capacity >= 0, num_ranks * rank_capacity < 2^31.
  * Receive rows ("rows" below): T*k for the compacted layout (rank_capacity
  * 0), num_ranks * rank_capacity for the RANK_MAJOR layout. */
@@ -93,7 +95,7 @@ typedef struct ep_shape {
     int32_t num_nodes;    /* N: virtual nodes; expert e lives on node e / (E/N) */
     int32_t num_topk;     /* k */
     int32_t x_format;     /* format of dispatched rows: EP_FMT_BF16 | EP_FMT_FP8_S128 */
-    int32_t y_format;     /* format of the rows combine reads: EP_FMT_BF16 | EP_FMT_MXFP8 */
+    int32_t y_format;     /* format of the rows combine reads: EP_FMT_BF16 | EP_FMT_MXFP8 | EP_FMT_NVFP4 */
     int32_t rank_capacity;/* 0: compacted (token-major) receive layout; M > 0: RANK_MAJOR,
                              rank r owns receive rows [r*M, (r+1)*M) ([PR860] RANK_MAJOR
                              commit: a fixed [num_ranks, max_tokens_per_rank, hidden]
@@ -204,9 +206,11 @@ int ep_dispatch_from_layout(const ep_shape *shape, const void *x, const float *x
  * Combine does not depend on the receive layout: RANK_MAJOR and compacted
  * slots give bit-identical y ([PR860] RANK_MAJOR commit: the combine path is
  * layout-agnostic).
- *   expert_out        [rows, H]: bf16 (y_format BF16) or e4m3 (MXFP8), 16-byte aligned
- *   expert_out_scales [rows, H/32] e8m0 bytes for MXFP8
- *                     (value = e4m3 * 2^(e8m0 - 127)), else NULL
+ *   expert_out        [rows, H] bf16 (y_format BF16), [rows, H] e4m3 (MXFP8) or
+ *                     [rows, H/2] packed e2m1 (NVFP4); 16-byte aligned
+ *   expert_out_scales [rows, H/32] e8m0 bytes for MXFP8 (value = e4m3 *
+ *                     2^(e8m0 - 127)); [rows, H/16] bf16 bit patterns for NVFP4
+ *                     (value = e2m1 * bf16, 4-byte aligned); NULL for BF16
  *   token_slot, topk_w: from the dispatch handle / the caller ([T, k]); a
  *                     slot outside [0, rows) is treated as masked
  *   y                 [T, H] bf16, 16-byte aligned
@@ -238,6 +242,14 @@ int ep_quant_fp8_s128(int64_t rows, int32_t hidden, const uint16_t *x, uint8_t *
  *     factor != NULL); per 32-group X = clamp(floor(log2 amax) - 8, -127,
  *     127) (-127 for an all-zero group, OCP Microscaling shared exponent),
  *     out_q = e4m3_rne_sat(v * 2^-X), out_e8m0 = X + 127 ([MEB]). */
+/* nvfp4 re-encode of bf16 receive rows (the expert stage for an NVFP4
+ * combine payload): v = f32(recv[s]) (times factor[e(s)] when factor !=
+ * NULL); per 16-group s = bf16_rne(amax / 6), 1.0 when that is zero;
+ * element e2m1_rne_sat(v / s).  out_q [rows, H/2], out_scales [rows, H/16]
+ * bf16 bits.  Compacted layout only; requires H % 128 == 0. */
+int ep_expert_requant_nvfp4(const ep_shape *shape, const int32_t *expert_offset,
+                            const float *factor, const uint16_t *recv, uint8_t *out_q,
+                            uint16_t *out_scales, void *stream);
 int ep_expert_scale_bf16(const ep_shape *shape, const int32_t *expert_offset,
                          const float *factor, const uint16_t *recv, uint16_t *out, void *stream);
 int ep_expert_requant_mxfp8(const ep_shape *shape, const int32_t *expert_offset,

@@ -92,6 +92,11 @@ def _load():
         "oracle_quant_fp8_s128": (None, [i64, i32, P, P, P]),
         "oracle_quant_mxfp8": (None, [i64, i32, P, P, P]),
         "oracle_expert_scale_bf16": (None, [i32, i32, P, P, P, P]),
+        "oracle_f32_to_e2m1": (ctypes.c_uint8, [ctypes.c_float]),
+        "oracle_e2m1_to_f32": (ctypes.c_float, [ctypes.c_uint8]),
+        "oracle_quant_nvfp4": (None, [i64, i32, P, P, P]),
+        "oracle_combine_nvfp4": (None, [i64, i32, i32, P, P, P, P, P]),
+        "oracle_expert_requant_nvfp4": (None, [i32, i32, P, P, P, P, P]),
         "oracle_expert_requant_mxfp8": (None, [i32, i32, P, P, P, P, P, P]),
     }
     for name, (res, args) in sig.items():
@@ -313,6 +318,54 @@ def quant_mxfp8(v: np.ndarray):
     return q, e
 
 
+def f32_to_e2m1(x) -> np.ndarray:
+    lib = _load()
+    a = np.asarray(x, np.float32).ravel()
+    return np.array([lib.oracle_f32_to_e2m1(float(v)) for v in a], np.uint8).reshape(np.shape(x))
+
+
+def e2m1_to_f32(q) -> np.ndarray:
+    lib = _load()
+    a = np.asarray(q, np.uint8).ravel()
+    return np.array([lib.oracle_e2m1_to_f32(int(v)) for v in a], np.float32).reshape(np.shape(q))
+
+
+def quant_nvfp4(v: np.ndarray):
+    lib = _load()
+    a = _c(v, np.float32)
+    rows, H = a.shape
+    q = np.empty((rows, H // 2), np.uint8)
+    s = np.empty((rows, H // 16), np.uint16)
+    lib.oracle_quant_nvfp4(rows, H, _p(a), _p(q), _p(s))
+    return q, s
+
+
+def combine_nvfp4(expert_q, expert_scales, token_slot, topk_w) -> np.ndarray:
+    lib = _load()
+    q = _c(expert_q, np.uint8)
+    sc = _c(expert_scales, np.uint16)
+    ts = _c(token_slot, np.int32)
+    w = _c(topk_w, np.float32)
+    T, k = ts.shape
+    H = q.shape[1] * 2
+    y = np.empty((T, H), np.uint16)
+    lib.oracle_combine_nvfp4(T, k, H, _p(q), _p(sc), _p(ts), _p(w), _p(y))
+    return y
+
+
+def expert_requant_nvfp4(recv: np.ndarray, expert_offset: np.ndarray, factor=None):
+    lib = _load()
+    r = _c(recv, np.uint16)
+    off = _c(expert_offset, np.int32)
+    f = None if factor is None else _c(factor, np.float32)
+    E = off.shape[0] - 1
+    rows, H = r.shape
+    out_q = np.zeros((rows, H // 2), np.uint8)
+    out_s = np.zeros((rows, H // 16), np.uint16)
+    lib.oracle_expert_requant_nvfp4(E, H, _p(off), _p(f), _p(r), _p(out_q), _p(out_s))
+    return out_q, out_s
+
+
 def expert_scale_bf16(recv: np.ndarray, expert_offset: np.ndarray, factor: np.ndarray) -> np.ndarray:
     lib = _load()
     r = _c(recv, np.uint16)
@@ -369,6 +422,11 @@ def run_path(inputs: dict) -> dict:
     else:
         rx = dispatch_rows(inputs["x"], ts, rows=rows)
         out["recv_x"] = rx
+        if inputs.get("y_fmt") == "nvfp4":
+            eq, es = expert_requant_nvfp4(rx, sl["expert_offset"], inputs.get("expert_factor"))
+            out["expert_q"], out["expert_scales"] = eq, es
+            out["y"] = combine_nvfp4(eq, es, ts, w)
+            return out
         if expert == "scale":
             eo = expert_scale_bf16(rx, sl["expert_offset"], inputs["expert_factor"])
         else:

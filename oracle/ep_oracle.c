@@ -321,6 +321,36 @@ float oracle_e8m0_to_f32(uint8_t e)
 }
 
 /*
+ * OCP 4-bit floating point, E2M1: 1 sign, 2 exponent bits with bias 1, 1
+ * mantissa bit; exponent field 0 holds the subnormal 0.5 * m; no NaN, no
+ * infinity; magnitudes {0, 0.5, 1, 1.5, 2, 3, 4, 6}.  Encoding rounds to
+ * nearest, ties to the even code, and saturates to +-6.
+ */
+uint8_t oracle_f32_to_e2m1(float f)
+{
+    const uint8_t sign = signbit(f) ? 0x8 : 0x0;
+    if (isnan(f)) return sign | 0x7;   /* no NaN code: saturate */
+    double a = fabs((double)f);
+    if (a >= 6.0) return sign | 0x7;
+    if (a < 1.0) {
+        double m = nearbyint(a * 2.0);   /* steps of 0.5; 2 means 1.0 = code 2 */
+        return sign | (uint8_t)m;
+    }
+    int e = ilogb(a);                    /* 0, 1 or 2 */
+    double m = nearbyint(ldexp(a, 1 - e));   /* significand * 2, in [2, 4] */
+    if (m == 4.0) { m = 2.0; e += 1; }
+    if (e + 1 > 3) return sign | 0x7;
+    return sign | (uint8_t)(((e + 1) << 1) | ((int)m - 2));
+}
+
+float oracle_e2m1_to_f32(uint8_t q)
+{
+    const int s = (q >> 3) & 1, ex = (q >> 1) & 3, m = q & 1;
+    double v = (ex == 0) ? 0.5 * m : ldexp(1.0 + 0.5 * m, ex - 1);
+    return (float)(s ? -v : v);
+}
+
+/*
  * fp8 dispatch rows: one e4m3 byte per element and one fp32 scale per 128
  * channels ([MORI] Reference script's fp8 factor).  The pages fix only the
  * format; the rule taken: amax of the group, scale = amax / 448 (IEEE
@@ -380,6 +410,50 @@ void oracle_quant_mxfp8(int64_t rows, int32_t H, const float *v, uint8_t *q, uin
         }
 }
 
+/*
+ * nvfp4 ([MEB] MEGA_COMBINE_DTYPE: "16e2m1xbf16").  The pages fix the shape
+ * only; the rule taken: s = bf16_rne(amax / 6) (6 = largest e2m1), 1.0 when
+ * that is zero, element e2m1(v / s) with saturation.
+ */
+void oracle_quant_nvfp4(int64_t rows, int32_t H, const float *v, uint8_t *q, uint16_t *scales)
+{
+    const int32_t groups = H / 16;
+    for (int64_t r = 0; r < rows; ++r)
+        for (int32_t g = 0; g < groups; ++g) {
+            const float *vs = v + r * H + g * 16;
+            float amax = 0.0f;
+            for (int32_t i = 0; i < 16; ++i) {
+                float a = fabsf(vs[i]);
+                if (a > amax) amax = a;
+            }
+            uint16_t sb = oracle_f32_to_bf16(amax / 6.0f);
+            if (oracle_bf16_to_f32(sb) == 0.0f) sb = 0x3F80;
+            const float s = oracle_bf16_to_f32(sb);
+            scales[r * groups + g] = sb;
+            for (int32_t i = 0; i < 16; i += 2) {
+                uint8_t lo = oracle_f32_to_e2m1(vs[i] / s);
+                uint8_t hi = oracle_f32_to_e2m1(vs[i + 1] / s);
+                q[r * (H / 2) + (g * 16 + i) / 2] = (uint8_t)(lo | (hi << 4));
+            }
+        }
+}
+
+void oracle_expert_requant_nvfp4(int32_t E, int32_t H, const int32_t *expert_offset,
+                                 const float *factor, const uint16_t *recv, uint8_t *out_q,
+                                 uint16_t *out_scales)
+{
+    float *v = (float *)malloc(sizeof(float) * (size_t)H);
+    for (int32_t e = 0; e < E; ++e)
+        for (int64_t s = expert_offset[e]; s < expert_offset[e + 1]; ++s) {
+            for (int32_t h = 0; h < H; ++h) {
+                v[h] = oracle_bf16_to_f32(recv[s * H + h]);
+                if (factor) v[h] = v[h] * factor[e];
+            }
+            oracle_quant_nvfp4(1, H, v, out_q + s * (H / 2), out_scales + s * (H / 16));
+        }
+    free(v);
+}
+
 /* ======================================================================== */
 /* Combine                                                                   */
 /* ======================================================================== */
@@ -436,6 +510,35 @@ void oracle_combine_mxfp8(int64_t T, int32_t k, int32_t H, const uint8_t *expert
             const uint8_t *sc = expert_e8m0 + (int64_t)s * groups;
             for (int32_t h = 0; h < H; ++h) {
                 float v = oracle_e4m3_to_f32(row[h]) * oracle_e8m0_to_f32(sc[h / 32]);
+                acc[h] = fmaf(w, v, acc[h]);
+            }
+        }
+        for (int32_t h = 0; h < H; ++h)
+            y[t * H + h] = nvalid ? oracle_f32_to_bf16(acc[h]) : (uint16_t)0;
+    }
+    free(acc);
+}
+
+/* nvfp4 payload: element value = e2m1 * f32(bf16 scale), exact in binary32
+ * (a 2-bit significand times an 8-bit one). */
+void oracle_combine_nvfp4(int64_t T, int32_t k, int32_t H, const uint8_t *expert_q,
+                          const uint16_t *expert_scales, const int32_t *token_slot,
+                          const float *topk_w, uint16_t *y)
+{
+    float *acc = (float *)malloc(sizeof(float) * (size_t)H);
+    for (int64_t t = 0; t < T; ++t) {
+        int32_t nvalid = 0;
+        for (int32_t h = 0; h < H; ++h) acc[h] = -0.0f;
+        for (int32_t j = 0; j < k; ++j) {
+            int32_t s = token_slot[t * k + j];
+            if (s < 0) continue;
+            ++nvalid;
+            const float w = topk_w[t * k + j];
+            const uint8_t *row = expert_q + (int64_t)s * (H / 2);
+            const uint16_t *sc = expert_scales + (int64_t)s * (H / 16);
+            for (int32_t h = 0; h < H; ++h) {
+                uint8_t code = (uint8_t)((row[h / 2] >> (4 * (h & 1))) & 0xF);
+                float v = oracle_e2m1_to_f32(code) * oracle_bf16_to_f32(sc[h / 16]);
                 acc[h] = fmaf(w, v, acc[h]);
             }
         }

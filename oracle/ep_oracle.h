@@ -134,6 +134,9 @@ uint8_t  oracle_f32_to_e4m3(float f);        /* RNE, saturate to +-448, NaN -> 0
 float    oracle_e4m3_to_f32(uint8_t q);
 float    oracle_e8m0_to_f32(uint8_t e);      /* 2^(e-127); 255 -> NaN */
 
+uint8_t  oracle_f32_to_e2m1(float f);        /* 4-bit code: RNE, saturate to +-6 */
+float    oracle_e2m1_to_f32(uint8_t q);      /* low 4 bits */
+
 /* fp8 rows: per (row, 128-channel group) amax, scale = amax/448 (1 if 0),
  * q = e4m3(x / scale). */
 void oracle_quant_fp8_s128(int64_t rows, int32_t H, const uint16_t *x_bf16,
@@ -142,6 +145,23 @@ void oracle_quant_fp8_s128(int64_t rows, int32_t H, const uint16_t *x_bf16,
 /* mxfp8 encode of fp32 rows: per 32-group X = clamp(floor(log2 amax) - 8,
  * -127, 127) (-127 for an all-zero group), q = e4m3(v * 2^-X), byte X + 127. */
 void oracle_quant_mxfp8(int64_t rows, int32_t H, const float *v, uint8_t *q, uint8_t *e8m0);
+
+/* nvfp4 ([MEB] MEGA_COMBINE_DTYPE: 16 e2m1 elements share one bf16 scale).
+ * Per 16-group: s = bf16_rne(amax / 6) (1.0 when that is zero), element
+ * e2m1_rne_sat(v / s); two elements per byte, the even element in the low
+ * nibble.  q is [rows, H/2] bytes, scales [rows, H/16] bf16 bits. */
+void oracle_quant_nvfp4(int64_t rows, int32_t H, const float *v, uint8_t *q, uint16_t *scales);
+
+/* Combine over nvfp4 rows: value = e2m1 * f32(scale bf16). */
+void oracle_combine_nvfp4(int64_t T, int32_t k, int32_t H, const uint8_t *expert_q,
+                          const uint16_t *expert_scales, const int32_t *token_slot,
+                          const float *topk_w, uint16_t *y);
+
+/* Expert stage for the nvfp4 payload: out = nvfp4(f32(recv[s]) * factor[e(s)])
+ * (factor may be NULL: identity). */
+void oracle_expert_requant_nvfp4(int32_t E, int32_t H, const int32_t *expert_offset,
+                                 const float *factor, const uint16_t *recv, uint8_t *out_q,
+                                 uint16_t *out_scales);
 
 /* Expert stage used by the workloads (not part of dispatch or combine):
  *  scale_bf16:  out[s] = bf16( f32(recv[s]) * factor[e(s)] )

@@ -24,8 +24,10 @@ def run(inp: dict, dev="cuda", check=True, from_layout=True) -> dict:
     otherwise the standalone ep_dispatch plans again."""
     T, H, E, R, N, k = (inp[n] for n in ("T", "H", "E", "R", "N", "k"))
     fp8 = inp.get("x_fmt", "bf16") == "fp8"
-    shape = ep.make_shape(T, H, E, R, N, k, ep.EP_FMT_FP8_S128 if fp8 else ep.EP_FMT_BF16,
-                          ep.EP_FMT_MXFP8 if fp8 else ep.EP_FMT_BF16, inp.get("rank_capacity", 0))
+    nv = inp.get("y_fmt") == "nvfp4"
+    yf = ep.EP_FMT_NVFP4 if nv else (ep.EP_FMT_MXFP8 if fp8 else ep.EP_FMT_BF16)
+    shape = ep.make_shape(T, H, E, R, N, k, ep.EP_FMT_FP8_S128 if fp8 else ep.EP_FMT_BF16, yf,
+                          inp.get("rank_capacity", 0))
     ws = ep.Workspace(shape, dev)
     x = to_dev_bf16(inp["x"], dev)
     idx = torch.from_numpy(np.ascontiguousarray(inp["topk_idx"])).to(dev)
@@ -43,6 +45,16 @@ def run(inp: dict, dev="cuda", check=True, from_layout=True) -> dict:
         y = ep.combine(eq, h, ee)
         out.update(x_q=q.cpu().numpy(), x_scales=s.cpu().numpy(), recv_x=recv_x.cpu().numpy(),
                    recv_x_scales=recv_s.cpu().numpy(), expert_q=eq.cpu().numpy(), expert_e8m0=ee.cpu().numpy())
+    elif nv:
+        recv_x, _, src, rw, h = ep.dispatch(x, idx, w, shape, ws, from_layout=from_layout)
+        factor = inp.get("expert_factor")
+        f = None if factor is None else torch.from_numpy(factor).to(dev)
+        eq = torch.zeros((shape.rows, H // 2), dtype=torch.uint8, device=dev)
+        es = torch.zeros((shape.rows, H // 16), dtype=torch.int16, device=dev)
+        ep.ep_expert_requant_nvfp4(shape, h.expert_offset, f, recv_x, eq, es)
+        y = ep.combine(eq, h, es)
+        out.update(recv_x=bf16_bits(recv_x), expert_q=eq.cpu().numpy(),
+                   expert_scales=es.cpu().numpy().view(np.uint16))
     else:
         recv_x, _, src, rw, h = ep.dispatch(x, idx, w, shape, ws, from_layout=from_layout)
         if inp.get("expert") == "scale":
@@ -74,7 +86,7 @@ def ulp_distance(a_bits, b_bits):
     return np.abs(ordered(a_bits) - ordered(b_bits))
 
 
-def compare(gpu: dict, ref: dict, fp8: bool):
+def compare(gpu: dict, ref: dict, fp8: bool, nvfp4: bool = False):
     """Element-by-element parity: integer and byte outputs bit-exact, y <= 1 bf16 ulp.
     Receive rows are compared where a pair landed (every layout).  Returns the
     number of y elements that differ at all (expected 0)."""
@@ -98,6 +110,10 @@ def compare(gpu: dict, ref: dict, fp8: bool):
                                       ref["recv_x_scales"][used].view(np.uint32), err_msg="recv_x_scales")
         np.testing.assert_array_equal(gpu["expert_q"][used], ref["expert_q"][used], err_msg="expert_q")
         np.testing.assert_array_equal(gpu["expert_e8m0"][used], ref["expert_e8m0"][used], err_msg="expert_e8m0")
+    elif nvfp4:
+        np.testing.assert_array_equal(gpu["expert_q"][used], ref["expert_q"][used], err_msg="expert_q nvfp4")
+        np.testing.assert_array_equal(gpu["expert_scales"][used], ref["expert_scales"][used],
+                                      err_msg="expert_scales nvfp4")
     else:
         np.testing.assert_array_equal(gpu["expert_out"][used], ref["expert_out"][used], err_msg="expert_out")
     d = ulp_distance(gpu["y"], ref["y"])

@@ -181,3 +181,89 @@ def test_inherent_quantization_error_on_normal_rows():
     assert abs(_rel_l2(deq8, xf) - 0.026) < 0.003
     assert abs(_rel_l2(deqmx, xf) - 0.029) < 0.003
     assert abs(_rel_l2(chain, xf) - 0.039) < 0.003
+
+
+# ---------------------------------------------------------------- e2m1 / nvfp4
+
+def e2m1_value(code: int) -> Fraction:
+    """OCP E2M1 from its definition: bias 1, one mantissa bit, field 0 subnormal."""
+    s, e, m = (code >> 3) & 1, (code >> 1) & 3, code & 1
+    mag = Fraction(m, 2) if e == 0 else (1 + Fraction(m, 2)) * Fraction(2) ** (e - 1)
+    return -mag if s else mag
+
+
+def e2m1_nearest(x: float) -> int:
+    """Brute force: the code whose value is nearest to x; ties go to the code
+    with an even mantissa bit; beyond the largest magnitude, saturate."""
+    fx = Fraction(float(x))
+    best = None
+    for c in range(16):
+        if (c & 8) != (8 if np.signbit(x) else 0):
+            continue
+        d = abs(e2m1_value(c) - fx)
+        if best is None or d < best[0] or (d == best[0] and c % 2 == 0):
+            best = (d, c)
+    return best[1]
+
+
+def test_e2m1_decode_all_codes():
+    dec = oracle.e2m1_to_f32(np.arange(16, dtype=np.uint8))
+    assert [Fraction(float(v)) for v in dec] == [e2m1_value(c) for c in range(16)]
+    assert sorted({abs(float(v)) for v in dec}) == [0, 0.5, 1, 1.5, 2, 3, 4, 6]
+
+
+def test_e2m1_encode_against_brute_force():
+    grid = np.concatenate([np.linspace(-7, 7, 2801), [0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, -5.0, 6.0, 1e30,
+                                                      -1e-30, -0.0]]).astype(np.float32)
+    np.testing.assert_array_equal(oracle.f32_to_e2m1(grid), [e2m1_nearest(v) for v in grid])
+
+
+def test_quant_nvfp4_rule():
+    import torch
+    rng = np.random.default_rng(6)
+    v = (rng.standard_normal((4, 256)) * np.exp2(rng.integers(-10, 10, (4, 1)))).astype(np.float32)
+    v[0, :16] = 0.0
+    q, s = oracle.quant_nvfp4(v)
+    for r in range(4):
+        for g in range(16):
+            grp = v[r, g * 16:(g + 1) * 16]
+            amax = torch.tensor(float(np.abs(grp).max()), dtype=torch.float32)
+            sb = int((amax / 6.0).to(torch.bfloat16).view(torch.int16)) & 0xFFFF
+            if sb & 0x7FFF == 0:
+                sb = 0x3F80
+            assert s[r, g] == sb
+            sf = np.uint32(sb << 16).view(np.float32)
+            codes = [(q[r, (g * 16 + i) // 2] >> (4 * (i % 2))) & 0xF for i in range(16)]
+            assert codes == [e2m1_nearest(np.float32(x) / sf) for x in grp]
+
+
+def test_nvfp4_combine_matches_fp64_and_representable_rows():
+    inp = W.make_inputs("nvfp4", T=48, H=512, E=32, R=8)
+    out = oracle.run_path(inp)
+    ts, w = out["slots"]["token_slot"], inp["topk_w"]
+    codes = np.stack([(out["expert_q"] >> 0) & 0xF, (out["expert_q"] >> 4) & 0xF], axis=-1).reshape(
+        out["expert_q"].shape[0], -1)
+    deq = oracle.e2m1_to_f32(codes).astype(np.float64)
+    sc = (out["expert_scales"].astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    deq *= np.repeat(sc, 16, axis=1)
+    y64 = np.zeros((ts.shape[0], deq.shape[1]))
+    for t in range(ts.shape[0]):
+        for j in range(ts.shape[1]):
+            y64[t] += float(w[t, j]) * deq[ts[t, j]]
+    import torch
+    ref = torch.from_numpy(y64).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+    def ordered(x):
+        x = np.asarray(x, np.int32)
+        return np.where(x & 0x8000, -(x & 0x7FFF), x)
+    assert np.abs(ordered(out["y"]) - ordered(ref)).max() <= 1
+    # rows made of e2m1 values with a 6 in every group (scale exactly 1) survive
+    rng = np.random.default_rng(8)
+    vals = oracle.e2m1_to_f32(rng.integers(0, 16, (16, 256)).astype(np.uint8))
+    vals[:, ::16] = 6.0
+    x = W.f32_to_bf16_bits(vals)
+    idx = np.argsort(rng.random((16, 8)), 1)[:, :4].astype(np.int64)
+    wt = np.full((16, 4), 0.25, np.float32)
+    res = oracle.run_path(dict(T=16, H=256, E=8, R=4, N=1, k=4, x=x, topk_idx=idx, topk_w=wt,
+                               x_fmt="bf16", y_fmt="nvfp4", expert="identity"))
+    np.testing.assert_array_equal(res["y"], x)

@@ -32,7 +32,7 @@ def _run_both(inp, from_layout=True):
           f"k={inp['k']} seed={inp.get('seed')} from_layout={from_layout}", flush=True)
     g = gpu_path.run(inp, from_layout=from_layout)
     r = oracle.run_path(inp)
-    ndiff = gpu_path.compare(g, r, inp.get("x_fmt") == "fp8")
+    ndiff = gpu_path.compare(g, r, inp.get("x_fmt") == "fp8", inp.get("y_fmt") == "nvfp4")
     return g, r, ndiff
 
 
@@ -41,7 +41,8 @@ def _run_both(inp, from_layout=True):
 def test_workload_full_size(name, from_layout):
     g, r, ndiff = _run_both(W.make_inputs(name), from_layout)
     assert ndiff == 0
-    if W.WORKLOADS[name]["x_fmt"] == "bf16" and W.WORKLOADS[name]["expert"] == "identity":
+    cfg = W.WORKLOADS[name]
+    if cfg["x_fmt"] == "bf16" and cfg.get("y_fmt", "bf16") == "bf16" and cfg["expert"] == "identity":
         inp = W.make_inputs(name)
         np.testing.assert_array_equal(g["y"], inp["x"])   # identity round trip
 
@@ -197,3 +198,33 @@ def test_rank_major_overflow_is_flagged_and_dropped():
     r = oracle.run_path(inp)
     assert r["slots"]["dropped"] > 0
     gpu_path.compare(g, r, False)
+
+
+@pytest.mark.parametrize("kw", [dict(), dict(mask_frac=0.25, T=777), dict(routing="replace", T=300)])
+def test_nvfp4_payload(kw):
+    kw = dict(kw)
+    base = dict(T=kw.pop("T", 500), H=1024)
+    base.update(kw)
+    _, _, ndiff = _run_both(W.make_inputs("nvfp4", **base))
+    assert ndiff == 0
+
+
+def test_nvfp4_combine_every_code_and_scale_kind():
+    """k = 1, w = 1: y = bf16(e2m1 * scale) for every e2m1 code under scales
+    that are powers of two, general bf16 values, tiny and huge, through
+    ep_combine against the oracle."""
+    from combine_dispatch_layout_02_amd import ep
+    import gpu_path
+    rng = np.random.default_rng(4)
+    T, H, k = 64, 256, 1
+    q = np.tile(np.arange(256, dtype=np.uint8), (T, 1))[:, : H // 2]
+    sc = rng.integers(0, 0x7F80, (T, H // 16)).astype(np.uint16)   # finite bf16 scales
+    sc[0], sc[1], sc[2] = 0x3F80, 0x3FC0, 0x0001
+    slot = np.arange(T, dtype=np.int32).reshape(T, 1)
+    w = np.ones((T, k), np.float32)
+    ref = oracle.combine_nvfp4(q, sc, slot, w)
+    shape = ep.make_shape(T, H, 1, 1, 1, k, ep.EP_FMT_BF16, ep.EP_FMT_NVFP4)
+    y = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
+    ep.ep_combine(shape, torch.from_numpy(q).cuda(), torch.from_numpy(sc.view(np.int16)).cuda(),
+                  torch.from_numpy(slot).cuda(), torch.from_numpy(w).cuda(), y)
+    np.testing.assert_array_equal(gpu_path.bf16_bits(y), ref)
