@@ -81,6 +81,9 @@ def _load():
         "oracle_slots": (None, [i64, i32, i32, P, P, P, P, P, P]),
         "oracle_slots_rank_major": (i64, [i64, i32, i32, i32, i32, P, P, P, P, P]),
         "oracle_dispatch_rows": (None, [i64, i32, i64, P, P, P]),
+        "oracle_slots_ranks": (None, [i64, i32, i32, i32, P, P, P, P, P, P, P]),
+        "oracle_expert_reduce_ranks": (None, [i64, i32, i32, i32, i32, P, P, P, P, P, P, P, P, P]),
+        "oracle_combine_ranks": (None, [i64, i32, i32, P, P, P]),
         "oracle_combine_bf16": (None, [i64, i32, i32, P, P, P, P]),
         "oracle_combine_mxfp8": (None, [i64, i32, i32, P, P, P, P, P]),
         "oracle_combine_bf16_f64": (None, [i64, i32, i32, P, P, P, P]),
@@ -212,6 +215,65 @@ def slots_rank_major(topk_idx: np.ndarray, topk_w: np.ndarray, E: int, R: int, M
     out["dropped"] = int(lib.oracle_slots_rank_major(T, k, E, R, M, _p(idx), _p(w), _p(out["token_slot"]),
                                                      _p(out["recv_src_idx"]), _p(out["recv_topk_w"])))
     return out
+
+
+def slots_ranks(topk_idx: np.ndarray, topk_w: np.ndarray, E: int, R: int) -> dict:
+    """(token, rank) receive rows: one row per token per rank it reaches,
+    regions in rank order, ascending t inside a region; plus each row's
+    top-k list as its rank sees it (local ids, -1 / weight 0 elsewhere)."""
+    lib = _load()
+    idx = _c(topk_idx, np.int64)
+    w = _c(topk_w, np.float32)
+    T, k = idx.shape
+    cap = T * min(k, R)
+    out = {
+        "token_rank_slot": np.empty((T, R), np.int32),
+        "rank_offset": np.empty(R + 1, np.int32),
+        "recv_src_idx": np.full(cap, -1, np.int32),
+        "recv_topk_idx": np.full((cap, k), -1, np.int32),
+        "recv_topk_w": np.zeros((cap, k), np.float32),
+    }
+    lib.oracle_slots_ranks(T, k, E, R, _p(idx), _p(w), _p(out["token_rank_slot"]), _p(out["rank_offset"]),
+                           _p(out["recv_src_idx"]), _p(out["recv_topk_idx"]), _p(out["recv_topk_w"]))
+    return out
+
+
+def expert_reduce_ranks(topk_idx, topk_w, E, R, rank_offset, recv_src_idx, recv=None, factor=None,
+                        recv_q=None, recv_scales=None):
+    """Per received (token, rank) row: the weighted sum over the token's
+    experts on that rank of the expert outputs, one bf16 partial row.  The
+    rows are bf16 (`recv`) or e4m3 plus fp32 scales per 128 (`recv_q`,
+    `recv_scales`)."""
+    lib = _load()
+    idx = _c(topk_idx, np.int64)
+    w = _c(topk_w, np.float32)
+    T, k = idx.shape
+    if recv_q is not None:
+        q = _c(recv_q, np.uint8)
+        sc = _c(recv_scales, np.float32)
+        rv = None
+        rows, H = q.shape
+    else:
+        rv = _c(recv, np.uint16)
+        q = sc = None
+        rows, H = rv.shape
+    part = np.zeros((rows, H), np.uint16)
+    f = None if factor is None else _c(factor, np.float32)
+    lib.oracle_expert_reduce_ranks(T, k, E, R, H, _p(idx), _p(w), _p(f), _p(_c(rank_offset, np.int32)),
+                                   _p(_c(recv_src_idx, np.int32)), _p(rv), _p(q), _p(sc), _p(part))
+    return part
+
+
+def combine_ranks(partial: np.ndarray, token_rank_slot: np.ndarray) -> np.ndarray:
+    """y[t] = bf16 of the fp32 sum, in rank order, of the token's partials."""
+    lib = _load()
+    pt = _c(partial, np.uint16)
+    ts = _c(token_rank_slot, np.int32)
+    T, R = ts.shape
+    H = pt.shape[1]
+    y = np.empty((T, H), np.uint16)
+    lib.oracle_combine_ranks(T, R, H, _p(pt), _p(ts), _p(y))
+    return y
 
 
 def dispatch_rows(src: np.ndarray, token_slot: np.ndarray, fill=0, rows=None) -> np.ndarray:
@@ -400,6 +462,28 @@ def run_path(inputs: dict) -> dict:
     idx, w = inputs["topk_idx"], inputs["topk_w"]
     out = {"layout": layout(idx, E, R, N)}
     sl = slots(idx, w, E)
+    expert = inputs.get("expert", "identity")
+    if inputs.get("rank_rows"):   # (token, rank) receive rows with per-rank partials
+        sr = slots_ranks(idx, w, E, R)
+        out["slots"] = dict(sl, **sr)
+        cap = T * min(k, R)
+        fac = inputs.get("expert_factor") if expert == "scale" else None
+        trs = sr["token_rank_slot"]
+        if inputs.get("x_fmt", "bf16") == "fp8":
+            q, s = quant_fp8_s128(inputs["x"])
+            out["x_q"], out["x_scales"] = q, s
+            rq = dispatch_rows(q, trs, rows=cap)
+            rs = dispatch_rows(s, trs, rows=cap)
+            out["recv_x"], out["recv_x_scales"] = rq, rs
+            part = expert_reduce_ranks(idx, w, E, R, sr["rank_offset"], sr["recv_src_idx"], factor=fac,
+                                       recv_q=rq, recv_scales=rs)
+        else:
+            rx = dispatch_rows(inputs["x"], trs, rows=cap)
+            out["recv_x"] = rx
+            part = expert_reduce_ranks(idx, w, E, R, sr["rank_offset"], sr["recv_src_idx"], rx, fac)
+        out["expert_out"] = part
+        out["y"] = combine_ranks(part, trs)
+        return out
     M = int(inputs.get("rank_capacity", 0))
     rows = None
     if M > 0:   # RANK_MAJOR: same expert_offset (compacted starts), slots at fixed rank blocks

@@ -237,6 +237,98 @@ int64_t oracle_slots_rank_major(int64_t T, int32_t k, int32_t E, int32_t R, int3
     return dropped;
 }
 
+/* (token, rank) rows: a token reaches rank r when any of its valid experts
+ * lives there; rank regions in rank order, ascending t inside. */
+void oracle_slots_ranks(int64_t T, int32_t k, int32_t E, int32_t R, const int64_t *topk_idx,
+                        const float *topk_w, int32_t *token_rank_slot, int32_t *rank_offset,
+                        int32_t *recv_src_idx, int32_t *recv_topk_idx, float *recv_topk_w)
+{
+    const int32_t experts_per_rank = E / R;
+    uint8_t *hit = (uint8_t *)calloc((size_t)(T * R > 0 ? T * R : 1), 1);
+    for (int64_t t = 0; t < T; ++t)
+        for (int32_t j = 0; j < k; ++j) {
+            int64_t e = topk_idx[t * k + j];
+            if (e < 0 || e >= E) continue;
+            hit[t * R + e / experts_per_rank] = 1;
+        }
+    rank_offset[0] = 0;
+    for (int32_t r = 0; r < R; ++r) {
+        int32_t n = 0;
+        for (int64_t t = 0; t < T; ++t) n += hit[t * R + r];
+        rank_offset[r + 1] = rank_offset[r] + n;
+    }
+    for (int32_t r = 0; r < R; ++r) {
+        int32_t fill = 0;
+        for (int64_t t = 0; t < T; ++t) {
+            if (!hit[t * R + r]) { token_rank_slot[t * R + r] = -1; continue; }
+            const int32_t s = rank_offset[r] + fill++;
+            token_rank_slot[t * R + r] = s;
+            recv_src_idx[s] = (int32_t)t;
+            /* the token's top-k list as rank r sees it: local expert ids of
+             * the slots on r, -1 (weight 0) for every other slot */
+            for (int32_t j = 0; j < k; ++j) {
+                int64_t e = topk_idx[t * k + j];
+                const int on_r = (e >= 0 && e < E && e / experts_per_rank == r);
+                recv_topk_idx[(int64_t)s * k + j] = on_r ? (int32_t)(e - (int64_t)r * experts_per_rank) : -1;
+                recv_topk_w[(int64_t)s * k + j] = on_r ? topk_w[t * k + j] : 0.0f;
+            }
+        }
+    }
+    free(hit);
+}
+
+void oracle_expert_reduce_ranks(int64_t T, int32_t k, int32_t E, int32_t R, int32_t H,
+                                const int64_t *topk_idx, const float *topk_w, const float *factor,
+                                const int32_t *rank_offset, const int32_t *recv_src_idx,
+                                const uint16_t *recv, const uint8_t *recv_q, const float *recv_scales,
+                                uint16_t *partial)
+{
+    (void)T;
+    const int32_t experts_per_rank = E / R;
+    float *acc = (float *)malloc(sizeof(float) * (size_t)H);
+    for (int32_t r = 0; r < R; ++r)
+        for (int64_t s = rank_offset[r]; s < rank_offset[r + 1]; ++s) {
+            const int64_t t = recv_src_idx[s];
+            for (int32_t h = 0; h < H; ++h) acc[h] = -0.0f;
+            for (int32_t j = 0; j < k; ++j) {
+                int64_t e = topk_idx[t * k + j];
+                if (e < 0 || e >= E || e / experts_per_rank != r) continue;
+                const float w = topk_w[t * k + j];
+                for (int32_t h = 0; h < H; ++h) {
+                    /* the expert's output element: the received value (bf16,
+                     * or e4m3 times its group's scale), times the expert's
+                     * factor, as a bf16 */
+                    float v = recv_q ? oracle_e4m3_to_f32(recv_q[s * H + h]) * recv_scales[s * (H / 128) + h / 128]
+                                     : oracle_bf16_to_f32(recv[s * H + h]);
+                    if (factor) v = v * factor[e];
+                    v = oracle_bf16_to_f32(oracle_f32_to_bf16(v));
+                    acc[h] = fmaf(w, v, acc[h]);
+                }
+            }
+            for (int32_t h = 0; h < H; ++h) partial[s * H + h] = oracle_f32_to_bf16(acc[h]);
+        }
+    free(acc);
+}
+
+void oracle_combine_ranks(int64_t T, int32_t R, int32_t H, const uint16_t *partial,
+                          const int32_t *token_rank_slot, uint16_t *y)
+{
+    float *acc = (float *)malloc(sizeof(float) * (size_t)H);
+    for (int64_t t = 0; t < T; ++t) {
+        int32_t nvalid = 0;
+        for (int32_t h = 0; h < H; ++h) acc[h] = -0.0f;
+        for (int32_t r = 0; r < R; ++r) {
+            const int32_t s = token_rank_slot[t * R + r];
+            if (s < 0) continue;
+            ++nvalid;
+            for (int32_t h = 0; h < H; ++h) acc[h] = acc[h] + oracle_bf16_to_f32(partial[(int64_t)s * H + h]);
+        }
+        for (int32_t h = 0; h < H; ++h)
+            y[t * H + h] = nvalid ? oracle_f32_to_bf16(acc[h]) : (uint16_t)0;
+    }
+    free(acc);
+}
+
 /* Dispatch moves bytes only: each valid (t, j) pair receives a copy of row t
  * ([MORI] "NVL / XGMI bandwidth": the received tensor holds token rows). */
 void oracle_dispatch_rows(int64_t T, int32_t k, int64_t row_bytes, const void *src,

@@ -103,6 +103,41 @@ int64_t oracle_slots_rank_major(int64_t T, int32_t k, int32_t E, int32_t R, int3
                                 const int64_t *topk_idx, const float *topk_w,
                                 int32_t *token_slot, int32_t *recv_src_idx, float *recv_topk_w);
 
+/* (token, rank) receive rows, the high-throughput layout ([PR860]: DeepEP's
+ * expanded receive layout, one row per (token, source rank) pair; [MORI]
+ * "NVL / XGMI bandwidth": one received row per token and rank).  For one
+ * source: a token reaches rank r when one of its valid experts lives on r;
+ * it then gets exactly one row in r's region.  Regions back to back in rank
+ * order (rank_offset = exclusive scan of num_tokens_per_rank), ascending t
+ * inside a region.  token_rank_slot [T, R] (-1 when t does not reach r),
+ * rank_offset [R+1], recv_src_idx [T*min(k,R)].  Per row s, the token's
+ * top-k list as its rank sees it: recv_topk_idx [rows, k] = e - r*EPR for
+ * the slots whose expert lives on r, else -1; recv_topk_w [rows, k] = the
+ * slot's weight there, else 0. */
+void oracle_slots_ranks(int64_t T, int32_t k, int32_t E, int32_t R, const int64_t *topk_idx,
+                        const float *topk_w, int32_t *token_rank_slot, int32_t *rank_offset,
+                        int32_t *recv_src_idx, int32_t *recv_topk_idx, float *recv_topk_w);
+
+/* Expert stage of the (token, rank) layout (the weights are applied on the
+ * destination, which returns one partial row per received row):
+ * partial[s] = bf16_rne( fp32 fma chain over the token's slots j (ascending)
+ * whose expert e lives on row s's rank, from -0.0f:
+ * acc = fmaf(w[t,j], o_e, acc) ), where the expert's output element is
+ * o_e = bf16_rne(v * factor[e]) (factor NULL: bf16_rne(v)) and v is the
+ * received bf16 element (recv_q NULL) or e4m3(recv_q) * its group's fp32
+ * scale (recv_scales [rows, H/128]). */
+void oracle_expert_reduce_ranks(int64_t T, int32_t k, int32_t E, int32_t R, int32_t H,
+                                const int64_t *topk_idx, const float *topk_w, const float *factor,
+                                const int32_t *rank_offset, const int32_t *recv_src_idx,
+                                const uint16_t *recv, const uint8_t *recv_q, const float *recv_scales,
+                                uint16_t *partial);
+
+/* Combine of the (token, rank) layout: y[t] = bf16_rne(sum over the token's
+ * ranks, ascending, of f32(partial[token_rank_slot[t,r]])), fp32 adds from
+ * -0.0f; +0.0 for a token that reaches no rank. */
+void oracle_combine_ranks(int64_t T, int32_t R, int32_t H, const uint16_t *partial,
+                          const int32_t *token_rank_slot, uint16_t *y);
+
 /* recv[token_slot[t,j]] = src[t] for every valid pair: a bitwise copy of
  * row_bytes bytes per row (works for bf16 rows, e4m3 rows and scale rows). */
 void oracle_dispatch_rows(int64_t T, int32_t k, int64_t row_bytes, const void *src,
