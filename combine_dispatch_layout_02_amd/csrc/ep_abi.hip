@@ -36,6 +36,8 @@ int check_shape(const ep_shape *sh, Shape *out) {
     if ((sh->x_format != EP_FMT_BF16 || sh->y_format != EP_FMT_BF16) && H % 128 != 0)
         return EP_EINVAL;
     if (sh->rank_capacity < 0 || (int64_t)R * sh->rank_capacity >= (int64_t(1) << 31)) return EP_EINVAL;
+    if (sh->rank_rows != 0 && sh->rank_rows != 1) return EP_EINVAL;
+    if (sh->rank_rows && T * (int64_t)R >= (int64_t(1) << 31)) return EP_EINVAL;
     if (out) {
         out->T = T;
         out->H = H;
@@ -46,6 +48,7 @@ int check_shape(const ep_shape *sh, Shape *out) {
         out->x_fmt = sh->x_format;
         out->y_fmt = sh->y_format;
         out->M = sh->rank_capacity;
+        out->rank_rows = sh->rank_rows;
     }
     return EP_OK;
 }
@@ -77,6 +80,10 @@ WsLayout ws_layout(const Shape &s) {
     off = align256(off + sizeof(int32_t) * (size_t)(TK > 0 ? TK : 1));
     L.plan_offset = off;
     off = align256(off + sizeof(int32_t) * (size_t)(s.E + 1));
+    L.tr_local = off;
+    off = align256(off + (s.rank_rows ? sizeof(int32_t) * (size_t)(s.T > 0 ? s.T : 1) * (size_t)s.R : 0));
+    L.plan_rank_offset = off;
+    off = align256(off + sizeof(int32_t) * (size_t)(s.R + 1));
     L.total = off;
     return L;
 }
@@ -218,6 +225,63 @@ int ep_combine(const ep_shape *shape, const void *expert_out, const uint8_t *exp
                                          static_cast<hipStream_t>(stream)));
 }
 
+int ep_dispatch_ranks(const ep_shape *shape, const void *x, const float *x_scales,
+                      const int64_t *topk_idx, const float *topk_w, void *recv_x,
+                      float *recv_x_scales, int32_t *recv_src_idx, int32_t *recv_topk_idx,
+                      float *recv_topk_w, int32_t *token_rank_slot, int32_t *rank_offset,
+                      void *ws, size_t ws_bytes, void *stream) {
+    Shape s;
+    int rc = check_shape(shape, &s);
+    if (rc != EP_OK) return rc;
+    if (!s.rank_rows || !rank_offset) return EP_EINVAL;
+    if (s.T > 0 && (!x || !topk_idx || !topk_w || !recv_x || !recv_src_idx || !recv_topk_idx ||
+                    !recv_topk_w || !token_rank_slot))
+        return EP_EINVAL;
+    const bool fp8 = s.x_fmt == EP_FMT_FP8_S128;
+    if (fp8 && s.T > 0 && (!x_scales || !recv_x_scales)) return EP_EINVAL;
+    if (!fp8 && (x_scales || recv_x_scales)) return EP_EINVAL;
+    if (s.T > 0 && (!aligned16(x) || !aligned16(recv_x))) return EP_EALIGN;
+    const WsLayout L = ep::ws_layout(s);
+    if (!ws || ws_bytes < L.total) return EP_EWORKSPACE;
+    if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0) return EP_EALIGN;
+    return hip_status(ep::launch_dispatch_ranks(s, L, x, x_scales, topk_idx, topk_w, recv_x,
+                                                recv_x_scales, recv_src_idx, recv_topk_idx,
+                                                recv_topk_w, token_rank_slot, rank_offset,
+                                                static_cast<char *>(ws),
+                                                static_cast<hipStream_t>(stream)));
+}
+
+int ep_expert_reduce_ranks(const ep_shape *shape, const void *recv_x, const float *recv_x_scales,
+                           const int32_t *rank_offset, const int32_t *recv_topk_idx,
+                           const float *recv_topk_w, const float *factor, uint16_t *partial,
+                           void *stream) {
+    Shape s;
+    int rc = check_shape(shape, &s);
+    if (rc != EP_OK) return rc;
+    if (!s.rank_rows || s.y_fmt != EP_FMT_BF16) return EP_EINVAL;
+    if (s.T == 0) return EP_OK;
+    if (!recv_x || !rank_offset || !recv_topk_idx || !recv_topk_w || !partial) return EP_EINVAL;
+    const bool fp8 = s.x_fmt == EP_FMT_FP8_S128;
+    if (fp8 != (recv_x_scales != nullptr)) return EP_EINVAL;
+    if (!aligned16(recv_x) || !aligned16(partial)) return EP_EALIGN;
+    return hip_status(ep::launch_expert_reduce_ranks(s, recv_x, recv_x_scales, rank_offset,
+                                                     recv_topk_idx, recv_topk_w, factor, partial,
+                                                     static_cast<hipStream_t>(stream)));
+}
+
+int ep_combine_ranks(const ep_shape *shape, const uint16_t *partial,
+                     const int32_t *token_rank_slot, void *y, void *stream) {
+    Shape s;
+    int rc = check_shape(shape, &s);
+    if (rc != EP_OK) return rc;
+    if (!s.rank_rows || s.y_fmt != EP_FMT_BF16) return EP_EINVAL;
+    if (s.T == 0) return EP_OK;
+    if (!partial || !token_rank_slot || !y) return EP_EINVAL;
+    if (!aligned16(partial) || !aligned16(y)) return EP_EALIGN;
+    return hip_status(ep::launch_combine_ranks(s, partial, token_rank_slot, y,
+                                               static_cast<hipStream_t>(stream)));
+}
+
 int ep_check(void *ws, size_t ws_bytes, void *stream, uint32_t *flags) {
     if (!ws || ws_bytes < 256) return EP_EINVAL;
     hipStream_t st = static_cast<hipStream_t>(stream);
@@ -318,6 +382,15 @@ int ep_accounting(const ep_shape *shape, int32_t own_node, const int32_t *num_to
                               + 4.0 * (s.E + 1);              // expert_offset
     out->hbm_combine_bytes = V * yrow + T * 2.0 * H          // rows gathered, y written
                              + TK * (4.0 + 4.0);             // token_slot, topk_w read
+    // (token, rank) rows: one per (t, r) pair, i.e. nvl_tokens rows
+    const double NR = (double)nvl;
+    out->hbm_dispatch_ranks_bytes = T * xrow + NR * xrow       // rows: read once, written per rank
+                                    + TK * (8.0 + 4.0)         // topk_idx, topk_w read
+                                    + T * s.R * 4.0            // token_rank_slot written
+                                    + NR * (4.0 + 8.0 * s.k)   // recv_src_idx, recv_topk_idx / _w
+                                    + 4.0 * (s.R + 1);         // rank_offset
+    out->hbm_combine_ranks_bytes = NR * 2.0 * H + T * 2.0 * H  // partials gathered, y written
+                                   + T * s.R * 4.0;            // token_rank_slot read
     return EP_OK;
 }
 

@@ -17,10 +17,13 @@ namespace ep {
 //   local_rank  : i32[T * k]         rank of a pair among the same-expert pairs
 //                                    of its tile that precede it (-1: masked)
 //   plan_offset : i32[E + 1]         expert segment starts
+//   tr_local    : i32[T * R]         (token, rank) rows only: rank of token t
+//                                    among its tile's tokens reaching rank r
+//   plan_rank_offset : i32[R + 1]    (token, rank) region starts
 // A tile holds tile_tokens whole tokens (tile_tokens * k <= count_threads
 // pairs, one thread per pair).
 struct WsLayout {
-    size_t ctrl, tile_count, local_rank, plan_offset, total;
+    size_t ctrl, tile_count, local_rank, plan_offset, tr_local, plan_rank_offset, total;
     int tiles;           // ceil(T / tile_tokens)
     int tile_tokens;
     int tile_waves;      // ceil(tile_tokens * k / 64): waves that own pair masks
@@ -37,7 +40,9 @@ struct Shape {
     int H, E, R, N, k;
     int x_fmt, y_fmt;
     int M;   // rank_capacity: 0 compacted layout, > 0 RANK_MAJOR
-    int64_t rows() const { return M > 0 ? (int64_t)R * M : T * k; }   // receive rows
+    int rank_rows;   // 1: the layout also plans (token, rank) receive rows
+    int64_t rows() const { return M > 0 ? (int64_t)R * M : T * k; }   // receive rows (pairs)
+    int64_t rank_rows_cap() const { return T * (k < R ? k : R); }      // (token, rank) rows
 };
 
 WsLayout ws_layout(const Shape &s);
@@ -59,6 +64,22 @@ hipError_t launch_dispatch_copy(const Shape &s, const WsLayout &L, const void *x
 hipError_t launch_combine(const Shape &s, const void *expert_out, const uint8_t *expert_scales,
                           const int32_t *token_slot, const float *topk_w, void *y,
                           hipStream_t stream);
+
+// (token, rank) receive layout
+hipError_t launch_dispatch_ranks(const Shape &s, const WsLayout &L, const void *x,
+                                 const float *x_scales, const int64_t *topk_idx,
+                                 const float *topk_w, void *recv_x, float *recv_x_scales,
+                                 int32_t *recv_src_idx, int32_t *recv_topk_idx, float *recv_topk_w,
+                                 int32_t *token_rank_slot, int32_t *rank_offset, const char *ws,
+                                 hipStream_t stream);
+
+hipError_t launch_expert_reduce_ranks(const Shape &s, const void *recv_x, const float *recv_scales,
+                                      const int32_t *rank_offset, const int32_t *recv_topk_idx,
+                                      const float *recv_topk_w, const float *factor,
+                                      uint16_t *partial, hipStream_t stream);
+
+hipError_t launch_combine_ranks(const Shape &s, const uint16_t *partial,
+                                const int32_t *token_rank_slot, void *y, hipStream_t stream);
 
 hipError_t launch_quant_fp8(int64_t rows, int H, const uint16_t *x, uint8_t *q, float *scales,
                             hipStream_t stream);

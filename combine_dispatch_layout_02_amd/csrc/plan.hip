@@ -85,8 +85,11 @@ struct CountArgs {
     int32_t *tile_count;      // [ntiles][E + R + N]: experts, ranks, nodes
     int32_t *local_rank;      // [T * k]
     uint32_t *ctrl;
+    int32_t *tr_local;        // [T][R] rank of token t among the tile's tokens reaching rank r
+                              // (-1: t does not reach r); null unless (token, rank) rows are planned
     // single-tile batches (one block) finish the plan in the same launch:
     int32_t *plan_offset;     // [E + 1]
+    int32_t *plan_rank_offset;   // [R + 1] (token, rank) region starts
     int32_t *per_expert, *per_rank, *per_node;   // layout outputs or null
     int64_t *algo;
 };
@@ -96,6 +99,10 @@ __global__ __launch_bounds__(1024) void ep_plan_count_kernel(CountArgs a) {
     uint64_t *masks = lds;                                            // [W][E]
     int32_t *ids = reinterpret_cast<int32_t *>(masks + (size_t)a.W * a.E);   // [TT * k]
     int32_t *rn = ids + a.TT * a.k;                                   // [R + N]
+    // rank ballots per token wave ((token, rank) rows only), after the
+    // single-tile counts and scan scratch
+    uint64_t *hb = reinterpret_cast<uint64_t *>(
+        (reinterpret_cast<uintptr_t>(rn + a.R + a.N + a.E + 1 + 1024 / kWave + 1) + 7) & ~uintptr_t(7));
     const int tid = threadIdx.x, nt = blockDim.x;
     const int lane = tid & (kWave - 1), w = tid / kWave;
     const int E = a.E, k = a.k;
@@ -183,6 +190,7 @@ __global__ __launch_bounds__(1024) void ep_plan_count_kernel(CountArgs a) {
             for (int r = 0; r < a.R; ++r) {
                 const uint64_t b = __ballot((rmask >> r) & 1u);
                 if (lane == 0 && b) atomicAdd(&rn[r], (int)__popcll(b));
+                if (a.tr_local && lane == 0) hb[w * a.R + r] = b;
             }
             for (int n = 0; n < a.N; ++n) {
                 const uint64_t b = __ballot((nmask >> n) & 1u);
@@ -192,11 +200,37 @@ __global__ __launch_bounds__(1024) void ep_plan_count_kernel(CountArgs a) {
     }
     if (__ballot(bad) && lane == 0) atomicOr(&a.ctrl[0], kErrBadExpert);
     __syncthreads();
-    for (int i = tid; i < a.R + a.N; i += nt) tc[E + i] = rn[i];
+    // single tile: the rank columns hold the prefix over earlier tiles (0)
+    // when (token, rank) rows are planned, else the counts
+    for (int i = tid; i < a.R + a.N; i += nt) tc[E + i] = (single && a.tr_local && i < a.R) ? 0 : rn[i];
+    if (a.tr_local && tid < ntok) {   // token tid's place among the tile's tokens of each rank
+        uint64_t rm = 0;
+        for (int j = 0; j < k; ++j) {
+            const int ej = ids[tid * k + j];
+            if (ej >= 0) rm |= 1ull << (a.epr_shift >= 0 ? ej >> a.epr_shift : ej / a.epr);
+        }
+        int32_t *out = a.tr_local + (t0 + tid) * a.R;
+        for (int r = 0; r < a.R; ++r) {
+            int32_t v = -1;
+            if ((rm >> r) & 1u) {
+                v = (int32_t)__popcll(hb[w * a.R + r] & lanemask_lt());
+                for (int w2 = 0; w2 < w; ++w2) v += (int32_t)__popcll(hb[w2 * a.R + r]);
+            }
+            out[r] = v;
+        }
+    }
     if (!single) return;   // block-uniform
 
     // ---- single-tile batch: segment starts and layout outputs right here
     block_exclusive_scan(cnt, a.plan_offset, E, reinterpret_cast<int32_t *>(cnt + E));
+    if (a.tr_local && tid == 0) {   // (token, rank) region starts
+        int32_t run = 0;
+        for (int r = 0; r < a.R; ++r) {
+            a.plan_rank_offset[r] = run;
+            run += rn[r];
+        }
+        a.plan_rank_offset[a.R] = run;
+    }
     if (a.per_rank) {
         for (int i = tid; i < a.R + a.N; i += nt) {
             if (i < a.R) a.per_rank[i] = rn[i]; else a.per_node[i - a.R] = rn[i];
@@ -213,6 +247,7 @@ struct ScanArgs {
     int E, R, N, ntiles;
     int32_t *tile_count;      // [ntiles][E + R + N]; expert columns -> exclusive prefix over tiles
     int32_t *plan_offset;     // [E + 1] segment starts (workspace copy)
+    int32_t *plan_rank_offset;   // [R + 1] (token, rank) region starts, or null
     int32_t *per_expert;      // [E] or null
     int32_t *per_rank;        // [R] or null
     int32_t *per_node;        // [N] or null
@@ -233,6 +268,9 @@ __global__ __launch_bounds__(1024) void ep_plan_scan_kernel(ScanArgs a) {
     // block-uniform choice: every thread owns at most one (column, part) and
     // at most kScanRegs tiles -> one batch of loads kept in registers
     const bool in_regs = (cols * Q <= nt) && (chunk <= kScanRegs);
+    // columns that need prefixes over tiles: experts, and ranks when (token,
+    // rank) rows are planned
+    const int pcols = E + (a.plan_rank_offset ? a.R : 0);
     if (in_regs) {
         const bool live = tid < cols * Q;
         const int c = tid % cols, q = tid / cols;
@@ -247,7 +285,7 @@ __global__ __launch_bounds__(1024) void ep_plan_scan_kernel(ScanArgs a) {
         }
         if (live) part[tid] = s;   // tid = q * cols + c
         __syncthreads();
-        if (live && c < E) {
+        if (live && c < pcols) {
             int32_t run = 0;
             for (int q2 = 0; q2 < q; ++q2) run += part[q2 * cols + c];
 #pragma unroll
@@ -268,7 +306,7 @@ __global__ __launch_bounds__(1024) void ep_plan_scan_kernel(ScanArgs a) {
         __syncthreads();
         for (int idx = tid; idx < cols * Q; idx += nt) {
             const int c = idx % cols, q = idx / cols;
-            if (c >= E) continue;
+            if (c >= pcols) continue;
             const int ta = min(q * chunk, a.ntiles), tb = min(ta + chunk, a.ntiles);
             int32_t *col = a.tile_count + c;
             int32_t run = 0;
@@ -298,6 +336,14 @@ __global__ __launch_bounds__(1024) void ep_plan_scan_kernel(ScanArgs a) {
         for (int n = 0; n < a.N; ++n) al += part[E + a.R + n];
         *a.algo = al;
     }
+    if (a.plan_rank_offset && tid == 0) {
+        int32_t run = 0;
+        for (int r = 0; r < a.R; ++r) {
+            a.plan_rank_offset[r] = run;
+            run += part[E + r];
+        }
+        a.plan_rank_offset[a.R] = run;
+    }
     block_exclusive_scan(part, a.plan_offset, E, tmp);
 }
 
@@ -324,6 +370,8 @@ hipError_t launch_plan(const Shape &s, const WsLayout &L, const int64_t *topk_id
     c.local_rank = reinterpret_cast<int32_t *>(ws + L.local_rank);
     c.ctrl = reinterpret_cast<uint32_t *>(ws + L.ctrl);
     c.plan_offset = reinterpret_cast<int32_t *>(ws + L.plan_offset);
+    c.tr_local = s.rank_rows ? reinterpret_cast<int32_t *>(ws + L.tr_local) : nullptr;
+    c.plan_rank_offset = reinterpret_cast<int32_t *>(ws + L.plan_rank_offset);
     c.per_expert = per_expert;
     c.per_rank = per_rank;
     c.per_node = per_node;
@@ -332,7 +380,8 @@ hipError_t launch_plan(const Shape &s, const WsLayout &L, const int64_t *topk_id
         // masks, staged ids, rank/node counts, and (single tile) expert counts + scan scratch
         const size_t lds = sizeof(uint64_t) * (size_t)L.tile_waves * s.E +
                            sizeof(int32_t) * ((size_t)L.tile_tokens * s.k + s.R + s.N + s.E + 1 +
-                                              1024 / kWave + 1);
+                                              1024 / kWave + 1) +
+                           8 + sizeof(uint64_t) * (size_t)L.tile_waves * s.R;   // rank ballots
         hipLaunchKernelGGL(ep_plan_count_kernel, dim3(L.tiles), dim3(L.count_threads), lds, stream, c);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess || L.tiles == 1) return e;   // one tile: the plan is complete
@@ -344,6 +393,7 @@ hipError_t launch_plan(const Shape &s, const WsLayout &L, const int64_t *topk_id
     a.ntiles = s.T > 0 ? L.tiles : 0;
     a.tile_count = c.tile_count;
     a.plan_offset = reinterpret_cast<int32_t *>(ws + L.plan_offset);
+    a.plan_rank_offset = s.rank_rows ? reinterpret_cast<int32_t *>(ws + L.plan_rank_offset) : nullptr;
     a.per_expert = per_expert;
     a.per_rank = per_rank;
     a.per_node = per_node;

@@ -1,0 +1,423 @@
+// ranks.hip -- the (token, rank) receive layout on gfx950.
+//
+// What it computes (MSCCL++ PR 860: DeepEP's high-throughput path receives
+// one row per (token, source rank) pair, its "expanded" receive layout;
+// MORI-EP Benchmark, "NVL / XGMI bandwidth": one received row per token and
+// destination rank, which is what num_tokens_per_rank counts): a token that
+// reaches rank r (one of its valid experts lives on r) gets exactly one row
+// in r's region.  Regions lie back to back in rank order, tokens ascending
+// inside a region, so row = rank_offset[r] + (tokens of r in earlier plan
+// tiles) + (rank of t among its tile's tokens of r), all from the plan.
+// The destination applies its own experts' top-k weights and returns one
+// partial row per received row; combine sums a token's partials.
+//
+//   ep_dispatch_ranks_kernel   row t read once, stored once per rank it
+//       reaches; writes the handle (token_rank_slot, rank_offset), the source
+//       index and the token's top-k list as each rank sees it.
+//   ep_expert_reduce_ranks_kernel   the stand-in expert stage: per received
+//       row, the fp32 fma chain over the row's local top-k slots (ascending
+//       j) of w * bf16(v * factor[e]), one bf16 rounding.
+//   ep_combine_ranks_kernel    y[t] = bf16_rne(fp32 sum over the token's
+//       ranks, ascending, of its partials), from -0.0; +0.0 when it reaches
+//       no rank.
+//
+// How: one wave per (token or row, row part), as in the token-major kernels.
+// Lanes 0..R-1 of a token's wave hold its row on each rank; a ballot gives
+// the uniform mask of ranks reached, walked in ascending order with readlane,
+// so every store and every add happens in a fixed order.
+#include "ep_device.h"
+#include "ep_internal.h"
+
+namespace ep {
+namespace {
+
+#ifndef EP_RANKS_WAVES
+#define EP_RANKS_WAVES 4096      // waves the dispatch copy aims for
+#endif
+#ifndef EP_RANKS_COMBINE_WAVES
+#define EP_RANKS_COMBINE_WAVES 16384
+#endif
+
+struct RankCopyArgs {
+    const char *x;                  // [T][row_bytes]
+    const float *x_scales;          // [T][G] or null
+    const int64_t *topk_idx;        // [T][k]
+    const float *topk_w;            // [T][k]
+    char *recv_x;                   // [cap][row_bytes]
+    float *recv_scales;             // [cap][G] or null
+    int32_t *recv_src_idx;          // [cap]
+    int32_t *recv_topk_idx;         // [cap][k]
+    float *recv_topk_w;             // [cap][k]
+    int32_t *token_rank_slot;       // [T][R] handle
+    int32_t *rank_offset;           // [R + 1] handle copy
+    const int32_t *plan_rank_offset;   // [R + 1] (workspace)
+    const int32_t *tile_prefix;     // [ntiles][E + R + N]; rank columns: prefix over tiles
+    const int32_t *tr_local;        // [T][R]
+    uint32_t *ctrl;
+    int64_t T;
+    int k, E, R, TT, cols;
+    int epr, epr_shift;
+    int64_t cap;                    // receive rows: T * min(k, R)
+    int64_t row_bytes;
+    int nvec, G, S;
+};
+
+template <int VPL>
+__global__ __launch_bounds__(256) void ep_dispatch_ranks_kernel(RankCopyArgs a) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int64_t gw = (int64_t)blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
+    const int64_t t = gw / a.S;
+    const int sub = (int)(gw - t * a.S);
+    const int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (g <= a.R) a.rank_offset[g] = a.plan_rank_offset[g];   // handle copy of the region starts
+    if (t >= a.T) return;   // wave-uniform
+
+    const char *src = a.x + t * a.row_bytes;
+    const int stride = kWave * a.S;
+    const int v_first = lane + kWave * sub;
+    vec16 buf[VPL];
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) {
+        const int v = v_first + i * stride;
+        if (v < a.nvec) buf[i] = ld16(src + (int64_t)v * 16);
+    }
+
+    // lanes 0..R-1: the token's row on each rank (-1: not reached)
+    int32_t slot = -1;
+    if (lane < a.R) {
+        const int32_t lr = a.tr_local[t * a.R + lane];
+        if (lr >= 0) {
+            slot = a.plan_rank_offset[lane] + a.tile_prefix[(t / a.TT) * a.cols + a.E + lane] + lr;
+            if ((uint64_t)slot >= (uint64_t)a.cap) {   // cannot happen; never write outside
+                atomicOr(&a.ctrl[0], kErrBadSlot);
+                slot = -1;
+            }
+        }
+        if (sub == 0) a.token_rank_slot[t * a.R + lane] = slot;
+    }
+    const uint64_t live = __ballot(slot >= 0);
+    if (live == 0) return;
+
+    if (sub == 0) {   // source index and the token's top-k list as each rank sees it
+        int e = -1;
+        float w = 0.0f;
+        if (lane < a.k) {
+            const int64_t v = a.topk_idx[t * a.k + lane];
+            e = (v >= 0 && v < a.E) ? (int)v : -1;
+            w = a.topk_w[t * a.k + lane];
+        }
+        const int re = e < 0 ? -1 : (a.epr_shift >= 0 ? e >> a.epr_shift : e / a.epr);
+        for (uint64_t m = live; m; m &= m - 1) {
+            const int r = __builtin_ctzll(m);
+            const int64_t s = readlane(slot, r);
+            if (lane == 0) a.recv_src_idx[s] = (int32_t)t;
+            if (lane < a.k) {
+                const bool on = (re == r);
+                a.recv_topk_idx[s * a.k + lane] = on ? e - r * a.epr : -1;
+                a.recv_topk_w[s * a.k + lane] = on ? w : 0.0f;
+            }
+        }
+    }
+
+    if (a.G > 0) {   // fp32 scale rows of an fp8 payload
+        for (int gi = v_first; gi < a.G; gi += stride) {
+            const float sc = a.x_scales[t * a.G + gi];
+            for (uint64_t m = live; m; m &= m - 1) {
+                const int64_t s = readlane(slot, __builtin_ctzll(m));
+                a.recv_scales[s * a.G + gi] = sc;
+            }
+        }
+    }
+
+    for (int v0 = v_first; v0 < a.nvec; v0 += stride * VPL) {
+        if (v0 != v_first) {
+#pragma unroll
+            for (int i = 0; i < VPL; ++i) {
+                const int v = v0 + i * stride;
+                if (v < a.nvec) buf[i] = ld16(src + (int64_t)v * 16);
+            }
+        }
+        for (uint64_t m = live; m; m &= m - 1) {
+            const int64_t s = readlane(slot, __builtin_ctzll(m));
+            char *dst = a.recv_x + s * a.row_bytes;
+#pragma unroll
+            for (int i = 0; i < VPL; ++i) {
+                const int v = v0 + i * stride;
+                if (v < a.nvec) st16(dst + (int64_t)v * 16, buf[i]);
+            }
+        }
+    }
+}
+
+struct ReduceArgs {
+    const char *recv;               // [cap][row_bytes]: bf16, or e4m3
+    const float *recv_scales;       // [cap][H/128] (e4m3 rows) or null
+    const int32_t *rank_offset;     // [R + 1]
+    const int32_t *recv_topk_idx;   // [cap][k] local expert ids, -1 elsewhere
+    const float *recv_topk_w;       // [cap][k]
+    const float *factor;            // [E] or null (identity expert)
+    uint16_t *partial;              // [cap][H] bf16
+    int64_t cap;
+    int k, R, H, epr;
+    int fp8;
+    int nvec;                       // 16-byte vectors per received row
+    int S;
+};
+
+// value of one received element after the expert: bf16_rne(v * factor)
+__device__ __forceinline__ float expert_value(float v, float f, bool scaled) {
+    if (scaled) v = v * f;
+    return u2f(f32_to_bf16(v) << 16);
+}
+
+__global__ __launch_bounds__(256) void ep_expert_reduce_ranks_kernel(ReduceArgs a) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int64_t gw = (int64_t)blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
+    const int64_t s = gw / a.S;
+    const int sub = (int)(gw - s * a.S);
+    if (s >= a.cap) return;
+    if (s >= a.rank_offset[a.R]) return;   // past the last region (uniform)
+    // the row's rank: the last r with rank_offset[r] <= s (empty regions
+    // before it share its start, those after it start past s)
+    const int32_t ro = lane < a.R ? a.rank_offset[lane] : 0x7FFFFFFF;
+    const int r = (int)__popcll(__ballot(lane < a.R && ro <= s)) - 1;
+    if (r < 0) return;   // rank_offset[0] > s: not a plan's offsets (uniform)
+
+    int le_id = -1;
+    float wt = 0.0f, fac = 1.0f;
+    if (lane < a.k) {
+        le_id = a.recv_topk_idx[s * a.k + lane];
+        if (le_id >= a.epr) le_id = -1;   // not a local expert id: skipped
+        wt = a.recv_topk_w[s * a.k + lane];
+        if (le_id >= 0 && a.factor) fac = a.factor[r * a.epr + le_id];
+    }
+    const bool scaled = a.factor != nullptr;
+    const uint64_t on = __ballot(lane < a.k && le_id >= 0);
+    const char *row = a.recv + s * (int64_t)a.nvec * 16;
+    uint16_t *out = a.partial + s * (int64_t)a.H;
+    for (int v = lane + kWave * sub; v < a.nvec; v += kWave * a.S) {
+        const vec16 in = ld16(row + (int64_t)v * 16);
+        if (!a.fp8) {   // 8 bf16 elements
+            float x[8], acc[8];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                x[2 * q] = bf16_lo(in[q]);
+                x[2 * q + 1] = bf16_hi(in[q]);
+            }
+#pragma unroll
+            for (int i = 0; i < 8; ++i) acc[i] = -0.0f;
+            for (uint64_t m = on; m; m &= m - 1) {
+                const int j = __builtin_ctzll(m);
+                const float w = readlane(wt, j), f = readlane(fac, j);
+#pragma unroll
+                for (int i = 0; i < 8; ++i) acc[i] = __builtin_fmaf(w, expert_value(x[i], f, scaled), acc[i]);
+            }
+            vec16 o;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) o[q] = pack_bf16x2(acc[2 * q], acc[2 * q + 1]);
+            st16(out + (int64_t)v * 8, o);
+        } else {        // 16 e4m3 elements, one fp32 scale per 128
+            const float sc = a.recv_scales[s * (a.H / 128) + v / 8];
+            float x[16], acc[16];
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+#pragma unroll
+                for (int b = 0; b < 4; ++b) x[4 * q + b] = e4m3_to_f32((in[q] >> (8 * b)) & 0xFFu) * sc;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) acc[i] = -0.0f;
+            for (uint64_t m = on; m; m &= m - 1) {
+                const int j = __builtin_ctzll(m);
+                const float w = readlane(wt, j), f = readlane(fac, j);
+#pragma unroll
+                for (int i = 0; i < 16; ++i) acc[i] = __builtin_fmaf(w, expert_value(x[i], f, scaled), acc[i]);
+            }
+            vec16 o0, o1;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                o0[q] = pack_bf16x2(acc[2 * q], acc[2 * q + 1]);
+                o1[q] = pack_bf16x2(acc[8 + 2 * q], acc[8 + 2 * q + 1]);
+            }
+            st16(out + (int64_t)v * 16, o0);
+            st16(out + (int64_t)v * 16 + 8, o1);
+        }
+    }
+}
+
+struct RankCombineArgs {
+    const char *partial;            // [cap][2H]
+    const int32_t *token_rank_slot; // [T][R]
+    char *y;                        // [T][2H]
+    int64_t T, cap;
+    int R, nvec, S;
+};
+
+constexpr int kRankBatch = 8;   // partial rows whose loads are issued together
+
+template <int C>
+__global__ __launch_bounds__(256) void ep_combine_ranks_kernel(RankCombineArgs a) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int64_t gw = (int64_t)blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
+    const int64_t t = gw / a.S;
+    const int sub = (int)(gw - t * a.S);
+    if (t >= a.T) return;
+    int32_t slot = -1;
+    if (lane < a.R) {
+        slot = a.token_rank_slot[t * a.R + lane];
+        if ((uint64_t)slot >= (uint64_t)a.cap) slot = -1;   // outside the receive rows: not reached
+    }
+    const uint64_t live = __ballot(slot >= 0);
+    char *yrow = a.y + t * (int64_t)a.nvec * 16;
+    const int stride = kWave * a.S;
+
+    for (int v0 = lane + kWave * sub; v0 < a.nvec; v0 += stride * C) {
+        float acc[C][8];
+#pragma unroll
+        for (int i = 0; i < C; ++i)
+#pragma unroll
+            for (int q = 0; q < 8; ++q) acc[i][q] = -0.0f;
+        for (uint64_t m = live; m;) {
+            // the next (up to) kRankBatch ranks, ascending
+            int64_t rows[kRankBatch];
+            int nb = 0;
+#pragma unroll
+            for (int jj = 0; jj < kRankBatch; ++jj) {
+                rows[jj] = 0;
+                if (m) {
+                    rows[jj] = readlane(slot, __builtin_ctzll(m));
+                    m &= m - 1;
+                    nb = jj + 1;
+                }
+            }
+            vec16 buf[kRankBatch][C];
+#pragma unroll
+            for (int jj = 0; jj < kRankBatch; ++jj) {
+                if (jj >= nb) break;   // uniform
+                const char *row = a.partial + rows[jj] * (int64_t)a.nvec * 16;
+#pragma unroll
+                for (int i = 0; i < C; ++i) {
+                    const int v = v0 + i * stride;
+                    if (v < a.nvec) buf[jj][i] = ld16_nt(row + (int64_t)v * 16);
+                }
+            }
+#pragma unroll
+            for (int jj = 0; jj < kRankBatch; ++jj) {
+                if (jj >= nb) break;
+#pragma unroll
+                for (int i = 0; i < C; ++i)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        acc[i][2 * q] = acc[i][2 * q] + bf16_lo(buf[jj][i][q]);
+                        acc[i][2 * q + 1] = acc[i][2 * q + 1] + bf16_hi(buf[jj][i][q]);
+                    }
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < C; ++i) {
+            const int v = v0 + i * stride;
+            if (v >= a.nvec) continue;
+            vec16 o;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) o[q] = live ? pack_bf16x2(acc[i][2 * q], acc[i][2 * q + 1]) : 0u;
+            st16(yrow + (int64_t)v * 16, o);
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_dispatch_ranks(const Shape &s, const WsLayout &L, const void *x,
+                                 const float *x_scales, const int64_t *topk_idx,
+                                 const float *topk_w, void *recv_x, float *recv_x_scales,
+                                 int32_t *recv_src_idx, int32_t *recv_topk_idx, float *recv_topk_w,
+                                 int32_t *token_rank_slot, int32_t *rank_offset, const char *ws,
+                                 hipStream_t stream) {
+    RankCopyArgs a;
+    a.x = static_cast<const char *>(x);
+    a.x_scales = x_scales;
+    a.topk_idx = topk_idx;
+    a.topk_w = topk_w;
+    a.recv_x = static_cast<char *>(recv_x);
+    a.recv_scales = recv_x_scales;
+    a.recv_src_idx = recv_src_idx;
+    a.recv_topk_idx = recv_topk_idx;
+    a.recv_topk_w = recv_topk_w;
+    a.token_rank_slot = token_rank_slot;
+    a.rank_offset = rank_offset;
+    a.plan_rank_offset = reinterpret_cast<const int32_t *>(ws + L.plan_rank_offset);
+    a.tile_prefix = reinterpret_cast<const int32_t *>(ws + L.tile_count);
+    a.tr_local = reinterpret_cast<const int32_t *>(ws + L.tr_local);
+    a.ctrl = reinterpret_cast<uint32_t *>(const_cast<char *>(ws) + L.ctrl);
+    a.T = s.T;
+    a.k = s.k;
+    a.E = s.E;
+    a.R = s.R;
+    a.TT = L.tile_tokens;
+    a.cols = s.E + s.R + s.N;
+    a.epr = s.E / s.R;
+    a.epr_shift = (a.epr & (a.epr - 1)) == 0 ? __builtin_ctz((unsigned)a.epr) : -1;
+    a.cap = s.rank_rows_cap();
+    const bool fp8 = (s.x_fmt == 1);
+    a.row_bytes = fp8 ? (int64_t)s.H : 2 * (int64_t)s.H;
+    a.nvec = (int)(a.row_bytes / 16);
+    a.G = fp8 ? s.H / 128 : 0;
+    a.S = waves_per_token(s.T, a.nvec, EP_RANKS_WAVES);
+    const int per_lane = (a.nvec + kWave * a.S - 1) / (kWave * a.S);
+    int64_t blocks = (s.T * a.S + 3) / 4;
+    if (blocks * 256 < s.R + 1) blocks = 1;   // threads to copy rank_offset (R <= 64)
+    const dim3 grid((unsigned)blocks), block(256);
+    if (per_lane <= 2) {
+        hipLaunchKernelGGL(ep_dispatch_ranks_kernel<2>, grid, block, 0, stream, a);
+    } else if (per_lane <= 4) {
+        hipLaunchKernelGGL(ep_dispatch_ranks_kernel<4>, grid, block, 0, stream, a);
+    } else if (per_lane <= 8) {
+        hipLaunchKernelGGL(ep_dispatch_ranks_kernel<8>, grid, block, 0, stream, a);
+    } else {
+        hipLaunchKernelGGL(ep_dispatch_ranks_kernel<16>, grid, block, 0, stream, a);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_expert_reduce_ranks(const Shape &s, const void *recv_x, const float *recv_scales,
+                                      const int32_t *rank_offset, const int32_t *recv_topk_idx,
+                                      const float *recv_topk_w, const float *factor,
+                                      uint16_t *partial, hipStream_t stream) {
+    ReduceArgs a;
+    a.recv = static_cast<const char *>(recv_x);
+    a.recv_scales = recv_scales;
+    a.rank_offset = rank_offset;
+    a.recv_topk_idx = recv_topk_idx;
+    a.recv_topk_w = recv_topk_w;
+    a.factor = factor;
+    a.partial = partial;
+    a.cap = s.rank_rows_cap();
+    a.k = s.k;
+    a.R = s.R;
+    a.H = s.H;
+    a.epr = s.E / s.R;
+    a.fp8 = (s.x_fmt == 1);
+    a.nvec = a.fp8 ? s.H / 16 : s.H / 8;
+    a.S = waves_per_token(a.cap, a.nvec, EP_RANKS_COMBINE_WAVES);
+    const int64_t waves = a.cap * a.S;
+    hipLaunchKernelGGL(ep_expert_reduce_ranks_kernel, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0,
+                       stream, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_combine_ranks(const Shape &s, const uint16_t *partial,
+                                const int32_t *token_rank_slot, void *y, hipStream_t stream) {
+    RankCombineArgs a;
+    a.partial = reinterpret_cast<const char *>(partial);
+    a.token_rank_slot = token_rank_slot;
+    a.y = static_cast<char *>(y);
+    a.T = s.T;
+    a.cap = s.rank_rows_cap();
+    a.R = s.R;
+    a.nvec = s.H / 8;
+    a.S = waves_per_token(s.T, a.nvec, EP_RANKS_COMBINE_WAVES);
+    const int64_t waves = s.T * a.S;
+    hipLaunchKernelGGL(ep_combine_ranks_kernel<4>, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0,
+                       stream, a);
+    return hipGetLastError();
+}
+
+}  // namespace ep

@@ -28,7 +28,7 @@ EP_OK, EP_EINVAL, EP_EALIGN, EP_EWORKSPACE, EP_EHIP, EP_EDEVICE = 0, -1, -2, -3,
 EXPORTED = (
     "ep_abi_version", "ep_strerror", "ep_validate_shape", "ep_workspace_bytes", "ep_workspace_init",
     "ep_dispatch_layout", "ep_dispatch", "ep_dispatch_from_layout", "ep_combine", "ep_check",
-    "ep_quant_fp8_s128",
+    "ep_dispatch_ranks", "ep_expert_reduce_ranks", "ep_combine_ranks", "ep_quant_fp8_s128",
     "ep_expert_scale_bf16", "ep_expert_requant_mxfp8", "ep_expert_requant_nvfp4", "ep_accounting",
     "ep_calib_copy",
 )
@@ -45,6 +45,7 @@ class ep_shape(ctypes.Structure):
         ("x_format", ctypes.c_int32),
         ("y_format", ctypes.c_int32),
         ("rank_capacity", ctypes.c_int32),
+        ("rank_rows", ctypes.c_int32),
     ]
 
     @property
@@ -53,6 +54,11 @@ class ep_shape(ctypes.Structure):
         if self.rank_capacity > 0:
             return self.num_ranks * self.rank_capacity
         return self.num_tokens * self.num_topk
+
+    @property
+    def rank_rows_cap(self) -> int:
+        """Receive rows of the (token, rank) layout: T * min(k, R)."""
+        return self.num_tokens * min(self.num_topk, self.num_ranks)
 
 
 class ep_accounting_t(ctypes.Structure):
@@ -71,6 +77,8 @@ class ep_accounting_t(ctypes.Structure):
         ("hbm_layout_bytes", ctypes.c_double),
         ("hbm_dispatch_bytes", ctypes.c_double),
         ("hbm_combine_bytes", ctypes.c_double),
+        ("hbm_dispatch_ranks_bytes", ctypes.c_double),
+        ("hbm_combine_ranks_bytes", ctypes.c_double),
     ]
 
     def as_dict(self):
@@ -101,6 +109,9 @@ def load():
         "ep_dispatch": (ctypes.c_int, [SP, P, P, P, P, P, P, P, P, P, P, P, sz, P]),
         "ep_dispatch_from_layout": (ctypes.c_int, [SP, P, P, P, P, P, P, P, P, P, P, P, sz, P]),
         "ep_combine": (ctypes.c_int, [SP, P, P, P, P, P, P]),
+        "ep_dispatch_ranks": (ctypes.c_int, [SP, P, P, P, P, P, P, P, P, P, P, P, P, sz, P]),
+        "ep_expert_reduce_ranks": (ctypes.c_int, [SP, P, P, P, P, P, P, P, P]),
+        "ep_combine_ranks": (ctypes.c_int, [SP, P, P, P, P]),
         "ep_check": (ctypes.c_int, [P, sz, P, ctypes.POINTER(ctypes.c_uint32)]),
         "ep_quant_fp8_s128": (ctypes.c_int, [i64, i32, P, P, P, P]),
         "ep_expert_scale_bf16": (ctypes.c_int, [SP, P, P, P, P, P]),
@@ -113,7 +124,7 @@ def load():
         fn = getattr(lib, name)
         fn.restype = res
         fn.argtypes = args
-    if lib.ep_abi_version() != 1:
+    if lib.ep_abi_version() != 2:
         raise RuntimeError("libep_hip ABI version mismatch")
     _lib = lib
     return lib
@@ -128,9 +139,10 @@ def _ok(rc: int, what: str):
         raise RuntimeError(f"{what} failed: {strerror(rc)} ({rc})")
 
 
-def make_shape(T, H, E, R, N, k, x_format=EP_FMT_BF16, y_format=EP_FMT_BF16, rank_capacity=0) -> ep_shape:
+def make_shape(T, H, E, R, N, k, x_format=EP_FMT_BF16, y_format=EP_FMT_BF16, rank_capacity=0,
+               rank_rows=0) -> ep_shape:
     return ep_shape(int(T), int(H), int(E), int(R), int(N), int(k), int(x_format), int(y_format),
-                    int(rank_capacity))
+                    int(rank_capacity), int(rank_rows))
 
 
 def _ptr(t):
@@ -260,6 +272,61 @@ def ep_combine(shape, expert_out, expert_out_scales, token_slot, topk_w, y, stre
                           _ptr(topk_w), _ptr(y), _stream(stream)), "ep_combine")
 
 
+def ep_dispatch_ranks(shape, x, x_scales, topk_idx, topk_w, recv_x, recv_x_scales, recv_src_idx,
+                      recv_topk_idx, recv_topk_w, token_rank_slot, rank_offset, ws: Workspace, stream=None):
+    """(token, rank) rows from the plan of the preceding ep_dispatch_layout on
+    this workspace with this topk_idx (shape.rank_rows must be 1)."""
+    T, k, H, R = shape.num_tokens, shape.num_topk, shape.hidden, shape.num_ranks
+    fp8 = shape.x_format == EP_FMT_FP8_S128
+    cap = shape.rank_rows_cap
+    _need(x, torch.uint8 if fp8 else torch.bfloat16, (T, H), "x")
+    _need(topk_idx, torch.int64, (T, k), "topk_idx")
+    _need(topk_w, torch.float32, (T, k), "topk_w")
+    _need(recv_x, x.dtype, (cap, H), "recv_x")
+    if fp8:
+        _need(x_scales, torch.float32, (T, H // 128), "x_scales")
+        _need(recv_x_scales, torch.float32, (cap, H // 128), "recv_x_scales")
+    _need(recv_src_idx, torch.int32, (cap,), "recv_src_idx")
+    _need(recv_topk_idx, torch.int32, (cap, k), "recv_topk_idx")
+    _need(recv_topk_w, torch.float32, (cap, k), "recv_topk_w")
+    _need(token_rank_slot, torch.int32, (T, R), "token_rank_slot")
+    _need(rank_offset, torch.int32, (R + 1,), "rank_offset")
+    if ws.planned_for != (topk_idx.data_ptr(), _shape_key(shape)):
+        raise RuntimeError("ep_dispatch_ranks needs a preceding ep_dispatch_layout on this workspace "
+                           "with the same topk_idx and shape")
+    _ok(load().ep_dispatch_ranks(ctypes.byref(shape), _ptr(x), _ptr(x_scales), _ptr(topk_idx), _ptr(topk_w),
+                                 _ptr(recv_x), _ptr(recv_x_scales), _ptr(recv_src_idx), _ptr(recv_topk_idx),
+                                 _ptr(recv_topk_w), _ptr(token_rank_slot), _ptr(rank_offset), ws.ptr,
+                                 ws.nbytes, _stream(stream)), "ep_dispatch_ranks")
+
+
+def ep_expert_reduce_ranks(shape, recv_x, recv_x_scales, rank_offset, recv_topk_idx, recv_topk_w, factor,
+                           partial, stream=None):
+    cap, H, k, R = shape.rank_rows_cap, shape.hidden, shape.num_topk, shape.num_ranks
+    fp8 = shape.x_format == EP_FMT_FP8_S128
+    _need(recv_x, torch.uint8 if fp8 else torch.bfloat16, (cap, H), "recv_x")
+    if fp8:
+        _need(recv_x_scales, torch.float32, (cap, H // 128), "recv_x_scales")
+    _need(rank_offset, torch.int32, (R + 1,), "rank_offset")
+    _need(recv_topk_idx, torch.int32, (cap, k), "recv_topk_idx")
+    _need(recv_topk_w, torch.float32, (cap, k), "recv_topk_w")
+    if factor is not None:
+        _need(factor, torch.float32, (shape.num_experts,), "factor")
+    _need(partial, torch.bfloat16, (cap, H), "partial")
+    _ok(load().ep_expert_reduce_ranks(ctypes.byref(shape), _ptr(recv_x), _ptr(recv_x_scales), _ptr(rank_offset),
+                                      _ptr(recv_topk_idx), _ptr(recv_topk_w), _ptr(factor), _ptr(partial),
+                                      _stream(stream)), "ep_expert_reduce_ranks")
+
+
+def ep_combine_ranks(shape, partial, token_rank_slot, y, stream=None):
+    T, H, R = shape.num_tokens, shape.hidden, shape.num_ranks
+    _need(partial, torch.bfloat16, (shape.rank_rows_cap, H), "partial")
+    _need(token_rank_slot, torch.int32, (T, R), "token_rank_slot")
+    _need(y, torch.bfloat16, (T, H), "y")
+    _ok(load().ep_combine_ranks(ctypes.byref(shape), _ptr(partial), _ptr(token_rank_slot), _ptr(y),
+                                _stream(stream)), "ep_combine_ranks")
+
+
 def ep_quant_fp8_s128(x, q, scales, stream=None):
     rows, H = x.shape
     _need(x, torch.bfloat16, (rows, H), "x")
@@ -361,3 +428,52 @@ def quant_fp8_s128(x, stream=None):
     s = torch.empty((rows, H // 128), dtype=torch.float32, device=x.device)
     ep_quant_fp8_s128(x, q, s, stream)
     return q, s
+
+
+@dataclass
+class RankHandle:
+    """What the (token, rank) combine needs from dispatch."""
+    shape: ep_shape
+    token_rank_slot: torch.Tensor   # [T, R] int32
+    rank_offset: torch.Tensor       # [R + 1] int32
+
+
+def dispatch_ranks(x, topk_idx, topk_w, shape, ws: Workspace, x_scales=None, stream=None) -> dict:
+    """(token, rank) dispatch after dispatch_layout on `ws`; returns recv_x,
+    recv_x_scales (None for bf16), recv_src_idx, recv_topk_idx, recv_topk_w
+    and the handle."""
+    dev = x.device
+    T, k, H, R = shape.num_tokens, shape.num_topk, shape.hidden, shape.num_ranks
+    cap = shape.rank_rows_cap
+    fp8 = shape.x_format == EP_FMT_FP8_S128
+    out = dict(
+        recv_x=torch.empty((cap, H), dtype=x.dtype, device=dev),
+        recv_x_scales=torch.empty((cap, H // 128), dtype=torch.float32, device=dev) if fp8 else None,
+        recv_src_idx=torch.empty(cap, dtype=torch.int32, device=dev),
+        recv_topk_idx=torch.empty((cap, k), dtype=torch.int32, device=dev),
+        recv_topk_w=torch.empty((cap, k), dtype=torch.float32, device=dev),
+    )
+    h = RankHandle(shape, torch.empty((T, R), dtype=torch.int32, device=dev),
+                   torch.empty(R + 1, dtype=torch.int32, device=dev))
+    ep_dispatch_ranks(shape, x, x_scales, topk_idx, topk_w, out["recv_x"], out["recv_x_scales"],
+                      out["recv_src_idx"], out["recv_topk_idx"], out["recv_topk_w"], h.token_rank_slot,
+                      h.rank_offset, ws, stream)
+    out["handle"] = h
+    return out
+
+
+def expert_reduce_ranks(d: dict, factor=None, stream=None):
+    """The workloads' expert stage over the rows of dispatch_ranks' result."""
+    h = d["handle"]
+    sh = h.shape
+    part = torch.empty((sh.rank_rows_cap, sh.hidden), dtype=torch.bfloat16, device=d["recv_x"].device)
+    ep_expert_reduce_ranks(sh, d["recv_x"], d["recv_x_scales"], h.rank_offset, d["recv_topk_idx"],
+                           d["recv_topk_w"], factor, part, stream)
+    return part
+
+
+def combine_ranks(partial, handle: RankHandle, stream=None):
+    sh = handle.shape
+    y = torch.empty((sh.num_tokens, sh.hidden), dtype=torch.bfloat16, device=partial.device)
+    ep_combine_ranks(sh, partial, handle.token_rank_slot, y, stream)
+    return y

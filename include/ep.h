@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define EP_ABI_VERSION 1
+#define EP_ABI_VERSION 2
 
 /* Status codes. */
 enum ep_status {
@@ -84,9 +84,11 @@ enum ep_format {
  *   hidden >= 8, hidden % 8 == 0 (16-byte bf16 row vectors);
  *   fp8 / mxfp8 / nvfp4 formats: hidden % 128 == 0;
  *   x_format in {BF16, FP8_S128}; y_format in {BF16, MXFP8, NVFP4};
- *   rank_capacity >= 0, num_ranks * rank_capacity < 2^31.
+ *   rank_capacity >= 0, num_ranks * rank_capacity < 2^31;
+ *   rank_rows in {0, 1}; with 1, num_tokens * num_ranks < 2^31.
  * Receive rows ("rows" below): T*k for the compacted layout (rank_capacity
- * 0), num_ranks * rank_capacity for the RANK_MAJOR layout. */
+ * 0), num_ranks * rank_capacity for the RANK_MAJOR layout.  The (token,
+ * rank) layout (rank_rows 1, the ep_*_ranks calls) has T * min(k, R) rows. */
 typedef struct ep_shape {
     int64_t num_tokens;   /* T: tokens of this source */
     int32_t hidden;       /* H: elements per token row */
@@ -100,6 +102,8 @@ typedef struct ep_shape {
                              rank r owns receive rows [r*M, (r+1)*M) ([PR860] RANK_MAJOR
                              commit: a fixed [num_ranks, max_tokens_per_rank, hidden]
                              slot instead of the compacted prefix offset) */
+    int32_t rank_rows;    /* 1: ep_dispatch_layout also plans the (token, rank) receive
+                             rows the ep_*_ranks calls use; 0: it does not */
 } ep_shape;
 
 /* Version of this ABI (EP_ABI_VERSION). */
@@ -218,6 +222,73 @@ int ep_dispatch_from_layout(const ep_shape *shape, const void *x, const float *x
 int ep_combine(const ep_shape *shape, const void *expert_out, const uint8_t *expert_out_scales,
                const int32_t *token_slot, const float *topk_w, void *y, void *stream);
 
+/* ---- the (token, rank) receive layout ----------------------------------- */
+
+/*
+ * Dispatch into (token, rank) rows, the high-throughput layout ([PR860]:
+ * DeepEP's expanded receive layout, one row per (token, source rank) pair;
+ * [MORI] "NVL / XGMI bandwidth": one received row per token and destination
+ * rank, the rows num_tokens_per_rank counts).  A token reaches rank r when
+ * one of its valid experts lives there; it then gets exactly one row in r's
+ * region.  Regions lie back to back in rank order (rank_offset = exclusive
+ * scan of num_tokens_per_rank), tokens ascending inside a region.
+ * Requires shape->rank_rows == 1 and the plan that the preceding
+ * ep_dispatch_layout call with the same shape, workspace and topk_idx left
+ * in the workspace (stream-ordered before this call); without it the rows
+ * are unspecified (the kernel still never writes outside the T*min(k,R)
+ * receive rows).
+ *   x, x_scales, topk_idx, topk_w: as for ep_dispatch
+ *   recv_x         [T*min(k,R), row] bf16 or e4m3 rows, 16-byte aligned; row
+ *                  s < rank_offset[R] is a bitwise copy of x[recv_src_idx[s]]
+ *   recv_x_scales  [T*min(k,R), H/128] fp32 (FP8_S128), else NULL
+ *   recv_src_idx   [T*min(k,R)] source token of each row
+ *   recv_topk_idx  [T*min(k,R), k] the token's top-k list as the row's rank r
+ *                  sees it: e - r*(E/R) for slots whose expert lives on r, -1
+ *                  for every other slot
+ *   recv_topk_w    [T*min(k,R), k] the slot's weight there, 0 elsewhere
+ *   token_rank_slot[T, R] handle: row of (t, r), -1 if t does not reach r
+ *   rank_offset    [R + 1] handle: region starts; rank_offset[R] = rows used
+ */
+int ep_dispatch_ranks(const ep_shape *shape, const void *x, const float *x_scales,
+                      const int64_t *topk_idx, const float *topk_w, void *recv_x,
+                      float *recv_x_scales, int32_t *recv_src_idx, int32_t *recv_topk_idx,
+                      float *recv_topk_w, int32_t *token_rank_slot, int32_t *rank_offset,
+                      void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Expert stage of the (token, rank) layout (outside dispatch and combine: the
+ * destination applies its own experts' weights and returns one partial row
+ * per received row).  For rows s < rank_offset[R], r the row's rank:
+ *     acc = -0.0f; for j = 0..k-1 with l = recv_topk_idx[s,j] >= 0:
+ *         o = bf16_rne(v(s,h) * factor[r*(E/R) + l])   (bf16_rne(v) if factor NULL)
+ *         acc = fmaf(recv_topk_w[s,j], o, acc)
+ *     partial[s,h] = bf16_rne(acc)
+ * v is the received bf16 element, or e4m3(q) times its row's fp32 scale for
+ * FP8_S128 rows.  Requires rank_rows == 1 and y_format BF16.
+ *   recv_x, recv_x_scales, rank_offset, recv_topk_idx, recv_topk_w: from
+ *                  ep_dispatch_ranks;  factor [E] fp32 or NULL
+ *   partial        [T*min(k,R), H] bf16, 16-byte aligned; rows past
+ *                  rank_offset[R] are left untouched
+ */
+int ep_expert_reduce_ranks(const ep_shape *shape, const void *recv_x, const float *recv_x_scales,
+                           const int32_t *rank_offset, const int32_t *recv_topk_idx,
+                           const float *recv_topk_w, const float *factor, uint16_t *partial,
+                           void *stream);
+
+/*
+ * Combine of the (token, rank) layout ([PR860]: combine runs dispatch in
+ * reverse over the receiver-side layout; the partials arrive weighted):
+ *     acc = -0.0f; for r = 0..R-1 with s = token_rank_slot[t,r] >= 0:
+ *         acc = acc + f32(partial[s, h])
+ *     y[t,h] = bf16_rne(acc)   (+0.0 if token t reaches no rank)
+ * fp32 adds in rank order, one rounding to bf16.  Requires rank_rows == 1
+ * and y_format BF16.  A slot outside [0, T*min(k,R)) counts as not reached.
+ *   partial [T*min(k,R), H] bf16; token_rank_slot [T, R]; y [T, H] bf16
+ *   (16-byte aligned rows)
+ */
+int ep_combine_ranks(const ep_shape *shape, const uint16_t *partial,
+                     const int32_t *token_rank_slot, void *y, void *stream);
+
 /* Synchronize `stream`, read and clear the workspace error word; returns
  * EP_EDEVICE if any kernel flagged bad input (e.g. an expert id >= E), and
  * writes the flags to *flags (host) when flags is not NULL. */
@@ -264,7 +335,8 @@ int ep_expert_requant_mxfp8(const ep_shape *shape, const int32_t *expert_offset,
  * bytes = tokens * H * element size (2 for bf16); combine mirrors dispatch;
  * fp8 factor (1 + 4/128)/2.  hbm_* are the minimum HBM bytes of one
  * dispatch and one combine call on this shape (rows moved plus index and
- * weight metadata), given the valid pair count. */
+ * weight metadata), given the valid pair count; hbm_*_ranks the same for
+ * the (token, rank) layout, whose rows are nvl_tokens. */
 typedef struct ep_accounting_t {
     int64_t rdma_algo_tokens;
     double rdma_physical_tokens;
@@ -280,6 +352,8 @@ typedef struct ep_accounting_t {
     double hbm_layout_bytes;
     double hbm_dispatch_bytes;
     double hbm_combine_bytes;
+    double hbm_dispatch_ranks_bytes;
+    double hbm_combine_ranks_bytes;
 } ep_accounting_t;
 
 int ep_accounting(const ep_shape *shape, int32_t own_node, const int32_t *num_tokens_per_rank,

@@ -119,3 +119,76 @@ def compare(gpu: dict, ref: dict, fp8: bool, nvfp4: bool = False):
     d = ulp_distance(gpu["y"], ref["y"])
     assert d.max() <= 1, f"combine off by {d.max()} ulp"
     return int((gpu["y"] != ref["y"]).sum())
+
+
+def run_ranks(inp: dict, dev="cuda", check=True) -> dict:
+    """The (token, rank) path: layout (planning the rank rows), dispatch_ranks,
+    the expert stage returning per-row partials, combine_ranks."""
+    T, H, E, R, N, k = (inp[n] for n in ("T", "H", "E", "R", "N", "k"))
+    fp8 = inp.get("x_fmt", "bf16") == "fp8"
+    shape = ep.make_shape(T, H, E, R, N, k, ep.EP_FMT_FP8_S128 if fp8 else ep.EP_FMT_BF16, ep.EP_FMT_BF16,
+                          0, rank_rows=1)
+    ws = ep.Workspace(shape, dev)
+    x = to_dev_bf16(inp["x"], dev)
+    idx = torch.from_numpy(np.ascontiguousarray(inp["topk_idx"])).to(dev)
+    w = torch.from_numpy(np.ascontiguousarray(inp["topk_w"])).to(dev)
+    out = {}
+    lay = ep.dispatch_layout(idx, shape, ws)
+    if fp8:
+        q, s = ep.quant_fp8_s128(x)
+        d = ep.dispatch_ranks(q, idx, w, shape, ws, x_scales=s)
+        out.update(x_q=q.cpu().numpy(), x_scales=s.cpu().numpy(), recv_x=d["recv_x"].cpu().numpy(),
+                   recv_x_scales=d["recv_x_scales"].cpu().numpy())
+    else:
+        d = ep.dispatch_ranks(x, idx, w, shape, ws)
+        out.update(recv_x=bf16_bits(d["recv_x"]))
+    factor = inp.get("expert_factor") if inp.get("expert") == "scale" else None
+    f = None if factor is None else torch.from_numpy(factor).to(dev)
+    part = ep.expert_reduce_ranks(d, f)
+    y = ep.combine_ranks(part, d["handle"])
+    if check:
+        ws.check()
+    torch.cuda.synchronize()
+    h = d["handle"]
+    out["layout"] = {key: v.cpu().numpy() for key, v in lay.items()}
+    out["layout"]["rdma_algo_token_count"] = int(out["layout"]["rdma_algo_token_count"][0])
+    out["slots"] = dict(token_rank_slot=h.token_rank_slot.cpu().numpy(), rank_offset=h.rank_offset.cpu().numpy(),
+                        recv_src_idx=d["recv_src_idx"].cpu().numpy(),
+                        recv_topk_idx=d["recv_topk_idx"].cpu().numpy(),
+                        recv_topk_w=d["recv_topk_w"].cpu().numpy())
+    out["expert_out"] = bf16_bits(part)
+    out["y"] = bf16_bits(y)
+    out["ws"] = ws
+    return out
+
+
+def compare_ranks(gpu: dict, ref: dict, fp8: bool):
+    """Parity of the (token, rank) path: counts, handle, index maps, received
+    rows and scales bit-exact on the rows a token landed in; partials and y
+    within 1 bf16 ulp.  Returns the number of y elements that differ (0
+    expected: both sides round the same fp32 values the same way)."""
+    gl, rl = gpu["layout"], ref["layout"]
+    for key in ("num_tokens_per_rank", "num_tokens_per_expert", "is_token_in_rank", "num_tokens_per_node"):
+        np.testing.assert_array_equal(gl[key], rl[key], err_msg=key)
+    assert gl["rdma_algo_token_count"] == rl["rdma_algo_token_count"]
+    gs, rs = gpu["slots"], ref["slots"]
+    np.testing.assert_array_equal(gs["token_rank_slot"], rs["token_rank_slot"], err_msg="token_rank_slot")
+    np.testing.assert_array_equal(gs["rank_offset"], rs["rank_offset"], err_msg="rank_offset")
+    used = np.sort(rs["token_rank_slot"][rs["token_rank_slot"] >= 0])
+    assert len(used) == rs["rank_offset"][-1]
+    np.testing.assert_array_equal(gs["recv_src_idx"][used], rs["recv_src_idx"][used], err_msg="recv_src_idx")
+    np.testing.assert_array_equal(gs["recv_topk_idx"][used], rs["recv_topk_idx"][used], err_msg="recv_topk_idx")
+    np.testing.assert_array_equal(gs["recv_topk_w"][used].view(np.uint32), rs["recv_topk_w"][used].view(np.uint32),
+                                  err_msg="recv_topk_w")
+    np.testing.assert_array_equal(gpu["recv_x"][used], ref["recv_x"][used], err_msg="recv_x")
+    if fp8:
+        np.testing.assert_array_equal(gpu["x_q"], ref["x_q"], err_msg="x_q")
+        np.testing.assert_array_equal(gpu["x_scales"].view(np.uint32), ref["x_scales"].view(np.uint32),
+                                      err_msg="x_scales")
+        np.testing.assert_array_equal(gpu["recv_x_scales"][used].view(np.uint32),
+                                      ref["recv_x_scales"][used].view(np.uint32), err_msg="recv_x_scales")
+    dp = ulp_distance(gpu["expert_out"][used], ref["expert_out"][used])
+    assert dp.size == 0 or dp.max() <= 1, f"partials off by {dp.max()} ulp"
+    d = ulp_distance(gpu["y"], ref["y"])
+    assert d.size == 0 or d.max() <= 1, f"combine off by {d.max()} ulp"
+    return int((gpu["y"] != ref["y"]).sum()) + int((gpu["expert_out"][used] != ref["expert_out"][used]).sum())
