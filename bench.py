@@ -10,7 +10,10 @@ ways: replayed from HIP graphs of 10 captured steps (the reported
 ms_per_step), eager back to back (eager_ms_per_step), and eager with events
 between the calls (the per-call durations in phase_us: median over steps).  The workloads'
 expert stage (identity, per-expert scaling, or fp8 -> mxfp8 re-encoding)
-runs during warmup and is not part of the timed step.
+runs during warmup and is not part of the timed step.  With --layout ranks
+the step is the (token, rank) path: ep_dispatch_layout (planning one row per
+token per rank it reaches) -> ep_dispatch_ranks -> ep_combine_ranks, with
+ep_expert_reduce_ranks (the weighted per-rank partials) as the expert stage.
 
 Prints one JSON line:
   value         algorithmic HBM bytes of the step / step time (GB/s)
@@ -18,7 +21,7 @@ Prints one JSON line:
   roofline      the longest-running call against the 8 TB/s HBM peak, with
                 hardware byte counts when they were measured for this kernel
   cpu_baseline  the CPU oracle (single thread) on the same workload
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--layout pairs|ranks]
 """
 from __future__ import annotations
 
@@ -128,6 +131,9 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="prefill2n")
+    ap.add_argument("--layout", choices=("pairs", "ranks"), default="pairs",
+                    help="receive layout: one row per (token, expert) pair (default), or one row per "
+                         "(token, rank) with per-rank partials (ep_dispatch_ranks / ep_combine_ranks)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-graph", action="store_true",
@@ -170,23 +176,28 @@ def main():
     if args.sweep:
         series = []
         for T in [2 ** i for i in range(14)]:
-            o = measure(args.workload, args.steps, args.warmup, not args.no_graph, T=T)
+            o = measure(args.workload, args.steps, args.warmup, not args.no_graph, args.layout, T=T)
             o.pop("_inp")
             series.append({"tokens": T, "us_per_step": round(o["ms_per_step"] * 1000, 2),
                            "tokens_per_s": o["tokens_per_s"], "gbs": o["value"], "phase_us": o["phase_us"]})
-        print(json.dumps({"metric": "step time vs tokens per source (" + args.workload + " shape)",
+        print(json.dumps({"metric": "step time vs tokens per source (" + args.workload + " shape, "
+                                    + args.layout + " layout)",
                           "unit": "us", "series": series}), flush=True)
         return
-    out = measure(args.workload, args.steps, args.warmup, not args.no_graph)
+    out = measure(args.workload, args.steps, args.warmup, not args.no_graph, args.layout)
     inp = out.pop("_inp")
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds, out["step_algorithmic_bytes"])
+        out["cpu_baseline"] = cpu_baseline(dict(inp, rank_rows=args.layout == "ranks"), args.cpu_seconds,
+                                           out["step_algorithmic_bytes"])
     print(json.dumps(out), flush=True)
 
 
-def measure(workload: str, steps: int, warmup: int, graph: bool = False, **overrides) -> dict:
+def measure(workload: str, steps: int, warmup: int, graph: bool = False, layout_kind: str = "pairs",
+            **overrides) -> dict:
     """Time `steps` steps of the path on `workload` (inputs resident in HBM);
-    keyword overrides change the workload's shape (e.g. T=...)."""
+    keyword overrides change the workload's shape (e.g. T=...).  layout_kind
+    "ranks" times the (token, rank) path: layout, ep_dispatch_ranks,
+    ep_combine_ranks (bf16 partials; the expert stage returns them)."""
     import numpy as np
     import torch
 
@@ -198,8 +209,12 @@ def measure(workload: str, steps: int, warmup: int, graph: bool = False, **overr
     T, H, E, R, N, k = (inp[n] for n in ("T", "H", "E", "R", "N", "k"))
     fp8 = inp["x_fmt"] == "fp8"
     nv = inp.get("y_fmt") == "nvfp4"
-    yf = ep.EP_FMT_NVFP4 if nv else (ep.EP_FMT_MXFP8 if fp8 else ep.EP_FMT_BF16)
-    shape = ep.make_shape(T, H, E, R, N, k, ep.EP_FMT_FP8_S128 if fp8 else ep.EP_FMT_BF16, yf)
+    ranks = layout_kind == "ranks"
+    if ranks and nv:
+        raise ValueError("the (token, rank) path returns bf16 partials; use a bf16-payload workload")
+    yf = ep.EP_FMT_NVFP4 if nv else (ep.EP_FMT_MXFP8 if (fp8 and not ranks) else ep.EP_FMT_BF16)
+    shape = ep.make_shape(T, H, E, R, N, k, ep.EP_FMT_FP8_S128 if fp8 else ep.EP_FMT_BF16, yf,
+                          rank_rows=1 if ranks else 0)
     ws = ep.Workspace(shape, dev)
 
     # inputs resident in HBM before timing
@@ -216,42 +231,63 @@ def measure(workload: str, steps: int, warmup: int, graph: bool = False, **overr
     lay = dict(r=torch.empty(R, dtype=torch.int32, device=dev), e=torch.empty(E, dtype=torch.int32, device=dev),
                m=torch.empty((T, R), dtype=torch.uint8, device=dev), n=torch.empty(N, dtype=torch.int32, device=dev),
                a=torch.empty(1, dtype=torch.int64, device=dev))
-    recv_x = torch.empty((T * k, H), dtype=xin.dtype, device=dev)
-    recv_s = torch.empty((T * k, H // 128), dtype=torch.float32, device=dev) if fp8 else None
-    src = torch.empty(T * k, dtype=torch.int32, device=dev)
-    rw = torch.empty(T * k, dtype=torch.float32, device=dev)
-    slot = torch.empty((T, k), dtype=torch.int32, device=dev)
-    off = torch.empty(E + 1, dtype=torch.int32, device=dev)
-    if fp8:
-        eo = torch.empty((T * k, H), dtype=torch.uint8, device=dev)
-        eos = torch.empty((T * k, H // 32), dtype=torch.uint8, device=dev)
-    elif nv:
-        eo = torch.empty((T * k, H // 2), dtype=torch.uint8, device=dev)
-        eos = torch.empty((T * k, H // 16), dtype=torch.int16, device=dev)
-    elif inp["expert"] == "scale":
-        eo, eos = torch.empty_like(recv_x), None
-    else:
-        eo, eos = recv_x, None   # identity expert: combine reads the receive buffer itself
     y = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
 
     def layout():
         ep.ep_dispatch_layout(shape, idx, lay["r"], lay["e"], lay["m"], lay["n"], lay["a"], ws)
 
-    def dispatch():   # reuses the plan the layout call of this step left in the workspace
-        ep.ep_dispatch(shape, xin, xs, idx, w, recv_x, recv_s, src, rw, slot, off, ws, from_layout=True)
+    if ranks:
+        cap = shape.rank_rows_cap
+        recv_x = torch.empty((cap, H), dtype=xin.dtype, device=dev)
+        recv_s = torch.empty((cap, H // 128), dtype=torch.float32, device=dev) if fp8 else None
+        src = torch.empty(cap, dtype=torch.int32, device=dev)
+        r_idx = torch.empty((cap, k), dtype=torch.int32, device=dev)
+        r_w = torch.empty((cap, k), dtype=torch.float32, device=dev)
+        trs = torch.empty((T, R), dtype=torch.int32, device=dev)
+        roff = torch.empty(R + 1, dtype=torch.int32, device=dev)
+        part = torch.empty((cap, H), dtype=torch.bfloat16, device=dev)
 
-    def expert():
+        def dispatch():   # reuses the plan the layout call of this step left in the workspace
+            ep.ep_dispatch_ranks(shape, xin, xs, idx, w, recv_x, recv_s, src, r_idx, r_w, trs, roff, ws)
+
+        def expert():
+            ep.ep_expert_reduce_ranks(shape, recv_x, recv_s, roff, r_idx, r_w,
+                                      factor if inp["expert"] == "scale" else None, part)
+
+        def combine():
+            ep.ep_combine_ranks(shape, part, trs, y)
+    else:
+        recv_x = torch.empty((T * k, H), dtype=xin.dtype, device=dev)
+        recv_s = torch.empty((T * k, H // 128), dtype=torch.float32, device=dev) if fp8 else None
+        src = torch.empty(T * k, dtype=torch.int32, device=dev)
+        rw = torch.empty(T * k, dtype=torch.float32, device=dev)
+        slot = torch.empty((T, k), dtype=torch.int32, device=dev)
+        off = torch.empty(E + 1, dtype=torch.int32, device=dev)
         if fp8:
-            ep.ep_expert_requant_mxfp8(shape, off, factor, recv_x, recv_s, eo, eos)
+            eo = torch.empty((T * k, H), dtype=torch.uint8, device=dev)
+            eos = torch.empty((T * k, H // 32), dtype=torch.uint8, device=dev)
         elif nv:
-            ep.ep_expert_requant_nvfp4(shape, off, factor, recv_x, eo, eos)
+            eo = torch.empty((T * k, H // 2), dtype=torch.uint8, device=dev)
+            eos = torch.empty((T * k, H // 16), dtype=torch.int16, device=dev)
         elif inp["expert"] == "scale":
-            ep.ep_expert_scale_bf16(shape, off, factor, recv_x, eo)
+            eo, eos = torch.empty_like(recv_x), None
+        else:
+            eo, eos = recv_x, None   # identity expert: combine reads the receive buffer itself
 
-    def combine():
-        ep.ep_combine(shape, eo, eos, slot, w, y)
+        def dispatch():   # reuses the plan the layout call of this step left in the workspace
+            ep.ep_dispatch(shape, xin, xs, idx, w, recv_x, recv_s, src, rw, slot, off, ws, from_layout=True)
 
-    has_expert = fp8 or nv or inp["expert"] == "scale"
+        def expert():
+            if fp8:
+                ep.ep_expert_requant_mxfp8(shape, off, factor, recv_x, recv_s, eo, eos)
+            elif nv:
+                ep.ep_expert_requant_nvfp4(shape, off, factor, recv_x, eo, eos)
+            elif inp["expert"] == "scale":
+                ep.ep_expert_scale_bf16(shape, off, factor, recv_x, eo)
+
+        def combine():
+            ep.ep_combine(shape, eo, eos, slot, w, y)
+
     # the expert stage stands in for the expert computation between dispatch
     # and combine: it runs in warmup (its output does not change from step to
     # step, the inputs being the same) and stays out of the timed step
@@ -268,7 +304,7 @@ def measure(workload: str, steps: int, warmup: int, graph: bool = False, **overr
         combine()
     ws.check()
     torch.cuda.synchronize()
-    V = int(off[-1].item())
+    V = int((inp["topk_idx"] >= 0).sum() - (inp["topk_idx"] >= E).sum())   # valid pairs
     y_ref = y.clone()   # every step recomputes the same y from the same inputs
     hev = HipEvents()
 
@@ -337,15 +373,20 @@ def measure(workload: str, steps: int, warmup: int, graph: bool = False, **overr
 
     # algorithmic bytes (library accounting on host copies of the layout)
     acc = ep.ep_accounting(shape, 0, lay["r"].cpu().numpy(), lay["n"].cpu().numpy(), int(lay["a"].item()), V)
-    algo_bytes = {"layout": acc["hbm_layout_bytes"], "dispatch": acc["hbm_dispatch_bytes"],
-                  "combine": acc["hbm_combine_bytes"]}
+    if ranks:
+        algo_bytes = {"layout": acc["hbm_layout_bytes"], "dispatch": acc["hbm_dispatch_ranks_bytes"],
+                      "combine": acc["hbm_combine_ranks_bytes"]}
+        kernels = {"dispatch": "ep_dispatch_ranks_kernel", "combine": "ep_combine_ranks_kernel"}
+    else:
+        algo_bytes = {"layout": acc["hbm_layout_bytes"], "dispatch": acc["hbm_dispatch_bytes"],
+                      "combine": acc["hbm_combine_bytes"]}
+        kernels = {"dispatch": "ep_dispatch_copy_kernel", "combine": "ep_combine_" +
+                   ("mxfp8" if fp8 else ("nvfp4" if nv else "bf16")) + "_kernel"}
     step_bytes = sum(algo_bytes.values())
     step_s = ms_step / 1000.0
     dom = max(("dispatch", "combine"), key=lambda p: phase_us[p])
-    kernels = {"dispatch": "ep_dispatch_copy_kernel", "combine": "ep_combine_" +
-               ("mxfp8" if fp8 else ("nvfp4" if nv else "bf16")) + "_kernel"}
     achieved = algo_bytes[dom] / (phase_us[dom] * 1e-6) / 1e9
-    traffic = measured_traffic(workload, kernels[dom])
+    traffic = measured_traffic(workload + ("_ranks" if ranks else ""), kernels[dom])
 
     out = {
         "metric": METRIC,
@@ -358,11 +399,13 @@ def measure(workload: str, steps: int, warmup: int, graph: bool = False, **overr
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp8/mxfp8" if fp8 else ("bf16/nvfp4" if nv else "bf16"),
+        "dtype": ("fp8/bf16" if ranks else "fp8/mxfp8") if fp8 else ("bf16/nvfp4" if nv else "bf16"),
         "data": "synthetic",
         "config": {"workload": workload, "tokens": T, "hidden": H, "experts": E, "virtual_ranks": R,
                    "virtual_nodes": N, "topk": k, "routing": inp["routing"], "expert": inp["expert"],
-                   "x_format": inp["x_fmt"], "valid_pairs": V},
+                   "x_format": inp["x_fmt"], "valid_pairs": V,
+                   "receive_layout": "(token, rank) rows" if ranks else "(token, expert) rows",
+                   "receive_rows": int(acc["nvl_tokens"]) if ranks else V},
         "tokens_per_s": round(T / step_s, 1),
         "phase_us": {p: round(v, 2) for p, v in phase_us.items()},
         "step_algorithmic_bytes": int(step_bytes),

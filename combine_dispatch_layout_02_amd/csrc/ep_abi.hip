@@ -67,7 +67,7 @@ WsLayout ws_layout(const Shape &s) {
     L.tile_tokens = (wmax * 64) / s.k;
     if (L.tile_tokens < 1) L.tile_tokens = 1;
     L.tile_waves = (L.tile_tokens * s.k + 63) / 64;
-    L.count_threads = L.tile_waves * 64;
+    L.count_threads = L.tile_waves * 64;   // >= tile_tokens: one token per thread in the count kernel
     L.tiles = (int)((s.T + L.tile_tokens - 1) / L.tile_tokens);
     if (L.tiles < 1) L.tiles = 1;
     const int64_t TK = s.T * s.k;

@@ -74,6 +74,19 @@ __device__ void block_exclusive_scan(const int32_t *in, int32_t *out, int n, int
     __syncthreads();
 }
 
+// Exclusive scan of n <= 64 values held one per lane by the first wave
+// (lanes >= n hold 0): out[i] for i < n, and out[n] = total.
+__device__ void wave_exclusive_scan(int32_t v, int n, int32_t *out) {
+    const int lane = threadIdx.x & (kWave - 1);
+    int32_t incl = v;
+    for (int off = 1; off < kWave; off <<= 1) {
+        const int32_t u = __shfl_up(incl, off);
+        if (lane >= off) incl += u;
+    }
+    if (lane < n) out[lane] = incl - v;
+    if (lane == kWave - 1) out[n] = incl;
+}
+
 struct CountArgs {
     const int64_t *topk_idx;
     int64_t T;
@@ -99,10 +112,10 @@ __global__ __launch_bounds__(1024) void ep_plan_count_kernel(CountArgs a) {
     uint64_t *masks = lds;                                            // [W][E]
     int32_t *ids = reinterpret_cast<int32_t *>(masks + (size_t)a.W * a.E);   // [TT * k]
     int32_t *rn = ids + a.TT * a.k;                                   // [R + N]
-    // rank ballots per token wave ((token, rank) rows only), after the
-    // single-tile counts and scan scratch
-    uint64_t *hb = reinterpret_cast<uint64_t *>(
-        (reinterpret_cast<uintptr_t>(rn + a.R + a.N + a.E + 1 + 1024 / kWave + 1) + 7) & ~uintptr_t(7));
+    // per token wave and rank: tokens of the wave reaching the rank, then the
+    // exclusive prefix over the tile's waves ((token, rank) rows only); after
+    // the single-tile counts and scan scratch
+    int32_t *wc = rn + a.R + a.N + a.E + 1 + 1024 / kWave + 1;        // [W][R]
     const int tid = threadIdx.x, nt = blockDim.x;
     const int lane = tid & (kWave - 1), w = tid / kWave;
     const int E = a.E, k = a.k;
@@ -148,54 +161,55 @@ __global__ __launch_bounds__(1024) void ep_plan_count_kernel(CountArgs a) {
         }
     }
 
-    // ---- tokens: rank / node sets in registers
-    for (int tb = 0; tb < a.TT; tb += nt) {   // one pass unless TT > blockDim
-        const int tl = tb + tid;
-        uint64_t rmask = 0, nmask = 0;
-        if (tl < ntok) {
-            for (int j = 0; j < k; ++j) {
-                const int ej = ids[tl * k + j];
-                if (ej < 0) continue;
-                const int r = a.epr_shift >= 0 ? ej >> a.epr_shift : ej / a.epr;
-                const int n = a.epn_shift >= 0 ? ej >> a.epn_shift : ej / a.epn;
-                rmask |= 1ull << r;
-                nmask |= 1ull << n;
-            }
-            if (a.in_rank) {
-                uint8_t *out = a.in_rank + (t0 + tl) * a.R;
-                if ((a.R & 15) == 0) {
-                    for (int r0 = 0; r0 < a.R; r0 += 16) {
-                        vec16 v;
-                        for (int q = 0; q < 4; ++q) {
-                            uint32_t wd = 0;
-                            for (int b = 0; b < 4; ++b)
-                                wd |= (uint32_t)((rmask >> (r0 + 4 * q + b)) & 1u) << (8 * b);
-                            v[q] = wd;
-                        }
-                        st16(out + r0, v);
-                    }
-                } else if ((a.R & 3) == 0) {
-                    for (int r0 = 0; r0 < a.R; r0 += 4) {
+    // ---- tokens: rank / node sets in registers, one token per thread (the
+    // host sizes a tile to at most blockDim tokens)
+    const bool has_tok = tid < ntok;
+    uint64_t rmask = 0, nmask = 0;
+    if (has_tok) {
+        for (int j = 0; j < k; ++j) {
+            const int ej = ids[tid * k + j];
+            if (ej < 0) continue;
+            const int r = a.epr_shift >= 0 ? ej >> a.epr_shift : ej / a.epr;
+            const int n = a.epn_shift >= 0 ? ej >> a.epn_shift : ej / a.epn;
+            rmask |= 1ull << r;
+            nmask |= 1ull << n;
+        }
+        if (a.in_rank) {
+            uint8_t *out = a.in_rank + (t0 + tid) * a.R;
+            if ((a.R & 15) == 0) {
+                for (int r0 = 0; r0 < a.R; r0 += 16) {
+                    vec16 v;
+                    for (int q = 0; q < 4; ++q) {
                         uint32_t wd = 0;
-                        for (int b = 0; b < 4; ++b) wd |= (uint32_t)((rmask >> (r0 + b)) & 1u) << (8 * b);
-                        *reinterpret_cast<uint32_t *>(out + r0) = wd;
+                        for (int b = 0; b < 4; ++b)
+                            wd |= (uint32_t)((rmask >> (r0 + 4 * q + b)) & 1u) << (8 * b);
+                        v[q] = wd;
                     }
-                } else {
-                    for (int r = 0; r < a.R; ++r) out[r] = (uint8_t)((rmask >> r) & 1u);
+                    st16(out + r0, v);
                 }
+            } else if ((a.R & 3) == 0) {
+                for (int r0 = 0; r0 < a.R; r0 += 4) {
+                    uint32_t wd = 0;
+                    for (int b = 0; b < 4; ++b) wd |= (uint32_t)((rmask >> (r0 + b)) & 1u) << (8 * b);
+                    *reinterpret_cast<uint32_t *>(out + r0) = wd;
+                }
+            } else {
+                for (int r = 0; r < a.R; ++r) out[r] = (uint8_t)((rmask >> r) & 1u);
             }
         }
-        // waves holding no token of this pass skip the ballots (wave-uniform)
-        if (tb + w * kWave < ntok) {
-            for (int r = 0; r < a.R; ++r) {
-                const uint64_t b = __ballot((rmask >> r) & 1u);
-                if (lane == 0 && b) atomicAdd(&rn[r], (int)__popcll(b));
-                if (a.tr_local && lane == 0) hb[w * a.R + r] = b;
+    }
+    const bool tok_wave = w * kWave < ntok;   // the wave holds a token (wave-uniform)
+    if (tok_wave) {
+        for (int r = 0; r < a.R; ++r) {
+            const uint64_t b = __ballot((rmask >> r) & 1u);
+            if (lane == 0) {
+                if (b) atomicAdd(&rn[r], (int)__popcll(b));
+                if (a.tr_local) wc[w * a.R + r] = (int32_t)__popcll(b);
             }
-            for (int n = 0; n < a.N; ++n) {
-                const uint64_t b = __ballot((nmask >> n) & 1u);
-                if (lane == 0 && b) atomicAdd(&rn[a.R + n], (int)__popcll(b));
-            }
+        }
+        for (int n = 0; n < a.N; ++n) {
+            const uint64_t b = __ballot((nmask >> n) & 1u);
+            if (lane == 0 && b) atomicAdd(&rn[a.R + n], (int)__popcll(b));
         }
     }
     if (__ballot(bad) && lane == 0) atomicOr(&a.ctrl[0], kErrBadExpert);
@@ -203,34 +217,49 @@ __global__ __launch_bounds__(1024) void ep_plan_count_kernel(CountArgs a) {
     // single tile: the rank columns hold the prefix over earlier tiles (0)
     // when (token, rank) rows are planned, else the counts
     for (int i = tid; i < a.R + a.N; i += nt) tc[E + i] = (single && a.tr_local && i < a.R) ? 0 : rn[i];
-    if (a.tr_local && tid < ntok) {   // token tid's place among the tile's tokens of each rank
-        uint64_t rm = 0;
-        for (int j = 0; j < k; ++j) {
-            const int ej = ids[tid * k + j];
-            if (ej >= 0) rm |= 1ull << (a.epr_shift >= 0 ? ej >> a.epr_shift : ej / a.epr);
-        }
-        int32_t *out = a.tr_local + (t0 + tid) * a.R;
-        for (int r = 0; r < a.R; ++r) {
-            int32_t v = -1;
-            if ((rm >> r) & 1u) {
-                v = (int32_t)__popcll(hb[w * a.R + r] & lanemask_lt());
-                for (int w2 = 0; w2 < w; ++w2) v += (int32_t)__popcll(hb[w2 * a.R + r]);
+    if (a.tr_local) {   // block-uniform
+        // exclusive prefix of the per-wave counts over the tile's waves, per rank
+        const int twaves = (ntok + kWave - 1) / kWave;
+        for (int r = tid; r < a.R; r += nt) {
+            int32_t run = 0;
+            for (int w2 = 0; w2 < twaves; ++w2) {
+                const int32_t c = wc[w2 * a.R + r];
+                wc[w2 * a.R + r] = run;
+                run += c;
             }
-            out[r] = v;
+        }
+        __syncthreads();
+        // token's place among the tile's tokens of each rank: its place in
+        // its wave (ballot again) plus the earlier waves' tokens of the rank
+        if (tok_wave) {
+            int32_t *out = a.tr_local + (t0 + w * kWave + lane) * a.R;
+            for (int r0 = 0; r0 < a.R; r0 += 4) {
+                int32_t v[4];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int r = r0 + q;
+                    const bool in = r < a.R && ((rmask >> r) & 1u);
+                    const uint64_t b = __ballot(in);
+                    v[q] = -1;
+                    if (in) v[q] = (int32_t)__popcll(b & lanemask_lt()) + wc[w * a.R + r];
+                }
+                if (has_tok) {
+                    if ((a.R & 3) == 0) {
+                        vec16 o;
+                        for (int q = 0; q < 4; ++q) o[q] = (uint32_t)v[q];
+                        st16(out + r0, o);
+                    } else {
+                        for (int q = 0; q < 4 && r0 + q < a.R; ++q) out[r0 + q] = v[q];
+                    }
+                }
+            }
         }
     }
     if (!single) return;   // block-uniform
 
     // ---- single-tile batch: segment starts and layout outputs right here
     block_exclusive_scan(cnt, a.plan_offset, E, reinterpret_cast<int32_t *>(cnt + E));
-    if (a.tr_local && tid == 0) {   // (token, rank) region starts
-        int32_t run = 0;
-        for (int r = 0; r < a.R; ++r) {
-            a.plan_rank_offset[r] = run;
-            run += rn[r];
-        }
-        a.plan_rank_offset[a.R] = run;
-    }
+    if (a.tr_local && tid < kWave) wave_exclusive_scan(tid < a.R ? rn[tid] : 0, a.R, a.plan_rank_offset);
     if (a.per_rank) {
         for (int i = tid; i < a.R + a.N; i += nt) {
             if (i < a.R) a.per_rank[i] = rn[i]; else a.per_node[i - a.R] = rn[i];
@@ -336,14 +365,7 @@ __global__ __launch_bounds__(1024) void ep_plan_scan_kernel(ScanArgs a) {
         for (int n = 0; n < a.N; ++n) al += part[E + a.R + n];
         *a.algo = al;
     }
-    if (a.plan_rank_offset && tid == 0) {
-        int32_t run = 0;
-        for (int r = 0; r < a.R; ++r) {
-            a.plan_rank_offset[r] = run;
-            run += part[E + r];
-        }
-        a.plan_rank_offset[a.R] = run;
-    }
+    if (a.plan_rank_offset && tid < kWave) wave_exclusive_scan(tid < a.R ? part[E + tid] : 0, a.R, a.plan_rank_offset);
     block_exclusive_scan(part, a.plan_offset, E, tmp);
 }
 
@@ -381,7 +403,7 @@ hipError_t launch_plan(const Shape &s, const WsLayout &L, const int64_t *topk_id
         const size_t lds = sizeof(uint64_t) * (size_t)L.tile_waves * s.E +
                            sizeof(int32_t) * ((size_t)L.tile_tokens * s.k + s.R + s.N + s.E + 1 +
                                               1024 / kWave + 1) +
-                           8 + sizeof(uint64_t) * (size_t)L.tile_waves * s.R;   // rank ballots
+                           sizeof(int32_t) * (size_t)L.tile_waves * s.R;   // per-wave rank counts
         hipLaunchKernelGGL(ep_plan_count_kernel, dim3(L.tiles), dim3(L.count_threads), lds, stream, c);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess || L.tiles == 1) return e;   // one tile: the plan is complete

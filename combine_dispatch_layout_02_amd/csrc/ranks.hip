@@ -37,6 +37,12 @@ namespace {
 #ifndef EP_RANKS_COMBINE_WAVES
 #define EP_RANKS_COMBINE_WAVES 16384
 #endif
+#ifndef EP_RANKS_NT_STORE
+#define EP_RANKS_NT_STORE 1          // non-temporal stores for the received rows
+#endif
+#ifndef EP_RANKS_COMBINE_VECS
+#define EP_RANKS_COMBINE_VECS 4      // 16-byte vectors per lane per pass in combine
+#endif
 
 struct RankCopyArgs {
     const char *x;                  // [T][row_bytes]
@@ -143,7 +149,10 @@ __global__ __launch_bounds__(256) void ep_dispatch_ranks_kernel(RankCopyArgs a) 
 #pragma unroll
             for (int i = 0; i < VPL; ++i) {
                 const int v = v0 + i * stride;
-                if (v < a.nvec) st16(dst + (int64_t)v * 16, buf[i]);
+                if (v < a.nvec) {
+                    if (EP_RANKS_NT_STORE) st16_nt(dst + (int64_t)v * 16, buf[i]);
+                    else st16(dst + (int64_t)v * 16, buf[i]);
+                }
             }
         }
     }
@@ -415,7 +424,7 @@ hipError_t launch_combine_ranks(const Shape &s, const uint16_t *partial,
     a.nvec = s.H / 8;
     a.S = waves_per_token(s.T, a.nvec, EP_RANKS_COMBINE_WAVES);
     const int64_t waves = s.T * a.S;
-    hipLaunchKernelGGL(ep_combine_ranks_kernel<4>, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0,
+    hipLaunchKernelGGL(ep_combine_ranks_kernel<EP_RANKS_COMBINE_VECS>, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0,
                        stream, a);
     return hipGetLastError();
 }
