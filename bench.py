@@ -10,7 +10,10 @@ ways: replayed from HIP graphs of 10 captured steps (the reported
 ms_per_step), eager back to back (eager_ms_per_step), and eager with events
 between the calls (the per-call durations in phase_us: median over steps).  The workloads'
 expert stage (identity, per-expert scaling, or fp8 -> mxfp8 re-encoding)
-runs during warmup and is not part of the timed step.  With --layout ranks
+runs during warmup and is not part of the timed step.  A batch of at most
+1024 (token, slot) pairs is laid out and dispatched by one
+ep_dispatch_with_layout call, which the library runs as a single launch
+(phases "layout+dispatch", "combine").  With --layout ranks
 the step is the (token, rank) path: ep_dispatch_layout (planning one row per
 token per rank it reaches) -> ep_dispatch_ranks -> ep_combine_ranks, with
 ep_expert_reduce_ranks (the weighted per-rank partials) as the expert stage.
@@ -39,6 +42,7 @@ METRIC = "dispatch+combine HBM GB/s and tokens/s at T=4096,H=7168,E=256,top-8"
 HBM_PEAK_GBS = 8000.0   # MI355X HBM3E, published peak
 
 GRAPH_STEPS = 10   # steps captured per HIP graph
+SINGLE_LAUNCH_PAIRS = 1024   # batches the library lays out and dispatches in one launch
 PROFILES = os.path.join(ROOT, "profiles")
 
 
@@ -277,6 +281,10 @@ def measure(workload: str, steps: int, warmup: int, graph: bool = False, layout_
         def dispatch():   # reuses the plan the layout call of this step left in the workspace
             ep.ep_dispatch(shape, xin, xs, idx, w, recv_x, recv_s, src, rw, slot, off, ws, from_layout=True)
 
+        def layout_dispatch():   # one call; a single launch for batches of <= 1024 pairs
+            ep.ep_dispatch_with_layout(shape, xin, xs, idx, w, lay["r"], lay["e"], lay["m"], lay["n"], lay["a"],
+                                       recv_x, recv_s, src, rw, slot, off, ws)
+
         def expert():
             if fp8:
                 ep.ep_expert_requant_mxfp8(shape, off, factor, recv_x, recv_s, eo, eos)
@@ -292,16 +300,19 @@ def measure(workload: str, steps: int, warmup: int, graph: bool = False, layout_
     # and combine: it runs in warmup (its output does not change from step to
     # step, the inputs being the same) and stays out of the timed step
     phases = [("layout", layout), ("dispatch", dispatch), ("combine", combine)]
+    single_launch = not ranks and T * k <= SINGLE_LAUNCH_PAIRS
+    if single_launch:   # the library runs layout + dispatch of such a batch as one kernel
+        phases = [("layout+dispatch", layout_dispatch), ("combine", combine)]
 
     def step():
         for _, fn in phases:
             fn()
 
     for _ in range(max(1, warmup)):
-        layout()
-        dispatch()
-        expert()
-        combine()
+        for name, fn in phases:
+            fn()
+            if name != "combine" and name != "layout":
+                expert()
     ws.check()
     torch.cuda.synchronize()
     V = int((inp["topk_idx"] >= 0).sum() - (inp["topk_idx"] >= E).sum())   # valid pairs
@@ -384,7 +395,11 @@ def measure(workload: str, steps: int, warmup: int, graph: bool = False, layout_
                    ("mxfp8" if fp8 else ("nvfp4" if nv else "bf16")) + "_kernel"}
     step_bytes = sum(algo_bytes.values())
     step_s = ms_step / 1000.0
-    dom = max(("dispatch", "combine"), key=lambda p: phase_us[p])
+    if single_launch:
+        algo_bytes = {"layout+dispatch": algo_bytes["layout"] + algo_bytes["dispatch"],
+                      "combine": algo_bytes["combine"]}
+        kernels["layout+dispatch"] = "ep_dispatch_copy_kernel"
+    dom = max((p for p in algo_bytes if p != "layout"), key=lambda p: phase_us[p])
     achieved = algo_bytes[dom] / (phase_us[dom] * 1e-6) / 1e9
     traffic = measured_traffic(workload + ("_ranks" if ranks else ""), kernels[dom])
 

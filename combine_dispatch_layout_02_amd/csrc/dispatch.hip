@@ -15,6 +15,13 @@
 // rows is then still in the memory-side cache when the combine reads them,
 // which measured faster for the dispatch -> combine sequence than
 // non-temporal stores.
+//
+// Batches of at most kFusedPairs pairs (compacted layout) can run as ONE
+// launch that also does the layout: block 0 computes the counts, the
+// token-in-rank map and the segment starts (the handle) while every other
+// wave finds its token's slots by counting, over all pairs of the batch,
+// the pairs that sort before each of them -- the stable counting sort's
+// position written out -- so no wave waits for a plan.
 #include "ep_device.h"
 #include "ep_internal.h"
 
@@ -53,18 +60,143 @@ struct CopyArgs {
     int nvec;                 // row_bytes / 16
     int G;                    // fp32 scales per row (0 for bf16 rows)
     int S;                    // waves per token
+    // single-launch form only: layout outputs (null when not wanted)
+    int R, N, epn, epn_shift;
+    int32_t *per_rank, *per_expert, *per_node;
+    uint8_t *in_rank;
+    int64_t *algo;
 };
 
-// VPL: 16-byte vectors each lane holds per pass.
-template <int VPL>
-__global__ __launch_bounds__(256) void ep_dispatch_copy_kernel(CopyArgs a) {
+constexpr int kFusedPairs = 1024;               // pairs a single-launch batch may hold
+constexpr int kFusedKeys = kFusedPairs / kWave; // pair ids each lane keeps in registers
+
+// Layout of a single-launch batch, by one block of 256 threads: staged ids,
+// per-expert counts (LDS integer adds, order-independent), their exclusive
+// scan into the expert_offset handle, and (when requested) the per-token
+// rank / node sets with their counts.  LDS: ids[T*k], hist[E], rn[R + N],
+// scan scratch.
+__device__ void fused_layout_block(const CopyArgs &a) {
+    extern __shared__ int32_t sm[];
+    const int TK = (int)(a.T * a.k);
+    int32_t *ids = sm;                    // [TK]
+    int32_t *hist = ids + TK;             // [E]
+    int32_t *rn = hist + a.E;             // [R + N]
+    int32_t *tmp = rn + a.R + a.N;        // [blockDim / 64 + 1]
+    const int tid = threadIdx.x, nt = blockDim.x, lane = tid & (kWave - 1), w = tid / kWave;
+    for (int i = tid; i < a.E; i += nt) hist[i] = 0;
+    for (int i = tid; i < a.R + a.N; i += nt) rn[i] = 0;
+    __syncthreads();
+    bool bad = false;
+    for (int q = tid; q < TK; q += nt) {
+        const int64_t v = a.topk_idx[q];
+        bad |= (v >= a.E);
+        const int32_t id = (v >= 0 && v < a.E) ? (int32_t)v : -1;
+        ids[q] = id;
+        if (id >= 0) atomicAdd(&hist[id], 1);
+    }
+    if (__ballot(bad) && lane == 0) atomicOr(&a.ctrl[0], kErrBadExpert);
+    __syncthreads();
+    if (a.per_expert)
+        for (int e = tid; e < a.E; e += nt) a.per_expert[e] = hist[e];
+    block_exclusive_scan(hist, a.expert_offset, a.E, tmp);
+    if (!a.per_rank) return;   // block-uniform
+    for (int tb = 0; tb < a.T; tb += nt) {
+        const int64_t t = tb + tid;
+        uint64_t rmask = 0, nmask = 0;
+        if (t < a.T) {
+            for (int j = 0; j < a.k; ++j) {
+                const int e = ids[t * a.k + j];
+                if (e < 0) continue;
+                rmask |= 1ull << (a.epr_shift >= 0 ? e >> a.epr_shift : e / a.epr);
+                nmask |= 1ull << (a.epn_shift >= 0 ? e >> a.epn_shift : e / a.epn);
+            }
+            for (int r = 0; r < a.R; ++r) a.in_rank[t * a.R + r] = (uint8_t)((rmask >> r) & 1u);
+        }
+        if (tb + w * kWave < a.T) {   // wave-uniform
+            for (int r = 0; r < a.R; ++r) {
+                const uint64_t b = __ballot((rmask >> r) & 1u);
+                if (lane == 0 && b) atomicAdd(&rn[r], (int)__popcll(b));
+            }
+            for (int n = 0; n < a.N; ++n) {
+                const uint64_t b = __ballot((nmask >> n) & 1u);
+                if (lane == 0 && b) atomicAdd(&rn[a.R + n], (int)__popcll(b));
+            }
+        }
+    }
+    __syncthreads();
+    for (int i = tid; i < a.R + a.N; i += nt) {
+        if (i < a.R) a.per_rank[i] = rn[i]; else a.per_node[i - a.R] = rn[i];
+    }
+    if (tid == 0) {
+        int64_t al = 0;
+        for (int n = 0; n < a.N; ++n) al += rn[a.R + n];
+        *a.algo = al;
+    }
+}
+
+// Slot of pair (t, j) held by lane j < k, by counting: the valid pairs whose
+// expert sorts before e_j, plus the pairs of e_j earlier in row-major (t, j)
+// order.  Each lane keeps kFusedKeys pair ids in registers; the counts are
+// ballots.  The token's S waves share the work (wave `sub` counts slots j =
+// sub, sub + S, ...) and exchange the results through LDS: one token per
+// block, every thread of the block calls this.
+__device__ __forceinline__ int32_t counted_slot(const CopyArgs &a, int64_t t, int lane, int sub) {
+    __shared__ int32_t slot_sm[32];
+    const int TK = (int)(a.T * a.k);
+    // every load unconditional (clamped index) so all of them are in flight
+    // together; lanes past the batch then drop their value
+    const int64_t own = a.topk_idx[t * a.k + min(lane, a.k - 1)];   // lane j < k: slot j's id
+    int64_t raw[kFusedKeys];
+#pragma unroll
+    for (int i = 0; i < kFusedKeys; ++i) raw[i] = a.topk_idx[min(lane + kWave * i, TK - 1)];
+    int32_t key[kFusedKeys];   // masked / invalid ids sort after every expert
+#pragma unroll
+    for (int i = 0; i < kFusedKeys; ++i) {
+        const bool ok = lane + kWave * i < TK && raw[i] >= 0 && raw[i] < a.E;
+        key[i] = ok ? (int32_t)raw[i] : 0x7FFFFFFF;
+    }
+    const int32_t mine = (lane < a.k && own >= 0 && own < a.E) ? (int32_t)own : 0x7FFFFFFF;
+    for (int j = sub; j < a.k; j += a.S) {
+        const int32_t e = readlane(mine, j);
+        int32_t c = -1;                  // masked slot
+        if (e != 0x7FFFFFFF) {           // uniform
+            const int p = (int)(t * a.k + j);
+            c = 0;
+#pragma unroll
+            for (int i = 0; i < kFusedKeys; ++i) {
+                const int q = lane + kWave * i;
+                c += (int32_t)__popcll(__ballot(key[i] < e || (key[i] == e && q < p)));
+            }
+        }
+        if (lane == 0) slot_sm[j] = c;
+    }
+    __syncthreads();
+    return lane < a.k ? slot_sm[lane] : -1;
+}
+
+// VPL: 16-byte vectors each lane holds per pass.  FUSED: the single-launch
+// form (block 0 does the layout, the other blocks count their slots).
+// The single-launch form runs one token per block (S waves of 64).
+template <int VPL, bool FUSED>
+__global__ __launch_bounds__(FUSED ? 1024 : 256) void ep_dispatch_copy_kernel(CopyArgs a) {
+    if (FUSED && blockIdx.x == 0) {
+        fused_layout_block(a);
+        return;
+    }
     const int lane = threadIdx.x & (kWave - 1);
-    const int64_t gw = (int64_t)blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
-    const int64_t t = gw / a.S;
-    const int sub = (int)(gw - t * a.S);
-    const int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (g <= a.E) a.expert_offset[g] = a.plan_offset[g];   // handle copy of the segment starts
-    if (t >= a.T) return;   // wave-uniform
+    int64_t t;
+    int sub;
+    if (FUSED) {
+        t = (int64_t)blockIdx.x - 1;   // < T: the grid has 1 + T blocks
+        sub = threadIdx.x / kWave;
+    } else {
+        const int64_t gw = (int64_t)blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
+        t = gw / a.S;
+        sub = (int)(gw - t * a.S);
+        const int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+        if (g <= a.E) a.expert_offset[g] = a.plan_offset[g];   // handle copy of the segment starts
+    }
+    if (t >= a.T) return;   // wave-uniform (never taken in the single-launch form)
 
     // the first pass of row t does not depend on the slots: issue its loads
     // before the slot lookups so the two latencies overlap
@@ -85,10 +217,10 @@ __global__ __launch_bounds__(256) void ep_dispatch_copy_kernel(CopyArgs a) {
     if (g_first < a.G) sc0 = a.x_scales[t * a.G + g_first];
 
     // lanes 0..k-1: the token's slots
-    int32_t slot = -1;
+    int32_t slot = FUSED ? counted_slot(a, t, lane, sub) : -1;
     if (lane < a.k) {
         const int64_t p = t * a.k + lane;
-        const int32_t lr = a.local_rank[p];
+        const int32_t lr = FUSED ? -1 : a.local_rank[p];
         if (lr >= 0) {
             const int e = (int)a.topk_idx[p];
             slot = a.plan_offset[e] + a.tile_prefix[(t / a.TT) * a.cols + e] + lr;
@@ -102,10 +234,10 @@ __global__ __launch_bounds__(256) void ep_dispatch_copy_kernel(CopyArgs a) {
                     slot = -1;
                 }
             }
-            if (slot >= 0 && (uint64_t)slot >= (uint64_t)a.rows) {   // cannot happen; never write outside
-                atomicOr(&a.ctrl[0], kErrBadSlot);
-                slot = -1;
-            }
+        }
+        if (slot >= 0 && (uint64_t)slot >= (uint64_t)a.rows) {   // cannot happen; never write outside
+            atomicOr(&a.ctrl[0], kErrBadSlot);
+            slot = -1;
         }
         if (sub == 0) {
             a.token_slot[p] = slot;
@@ -161,12 +293,12 @@ int waves_per_token(int64_t T, int64_t row_vectors, int64_t target) {
     return S;
 }
 
-hipError_t launch_dispatch_copy(const Shape &s, const WsLayout &L, const void *x,
-                                const float *x_scales, const int64_t *topk_idx,
-                                const float *topk_w, void *recv_x, float *recv_x_scales,
-                                int32_t *recv_src_idx, float *recv_topk_w, int32_t *token_slot,
-                                int32_t *expert_offset, char *ws, hipStream_t stream) {
-    CopyArgs a;
+namespace {
+
+CopyArgs copy_args(const Shape &s, const void *x, const float *x_scales, const int64_t *topk_idx,
+                   const float *topk_w, void *recv_x, float *recv_x_scales, int32_t *recv_src_idx,
+                   float *recv_topk_w, int32_t *token_slot, int32_t *expert_offset) {
+    CopyArgs a{};
     a.x = static_cast<const char *>(x);
     a.x_scales = x_scales;
     a.topk_idx = topk_idx;
@@ -176,39 +308,97 @@ hipError_t launch_dispatch_copy(const Shape &s, const WsLayout &L, const void *x
     a.recv_src_idx = recv_src_idx;
     a.recv_topk_w = recv_topk_w;
     a.token_slot = token_slot;
-    a.plan_offset = reinterpret_cast<const int32_t *>(ws + L.plan_offset);
     a.expert_offset = expert_offset;
-    a.tile_prefix = reinterpret_cast<const int32_t *>(ws + L.tile_count);
-    a.local_rank = reinterpret_cast<const int32_t *>(ws + L.local_rank);
-    a.ctrl = reinterpret_cast<uint32_t *>(ws + L.ctrl);
     a.T = s.T;
     a.k = s.k;
     a.E = s.E;
-    a.TT = L.tile_tokens;
+    a.R = s.R;
+    a.N = s.N;
     a.cols = s.E + s.R + s.N;
     a.M = s.M;
     a.epr = s.E / s.R;
     a.epr_shift = (a.epr & (a.epr - 1)) == 0 ? __builtin_ctz((unsigned)a.epr) : -1;
+    a.epn = s.E / s.N;
+    a.epn_shift = (a.epn & (a.epn - 1)) == 0 ? __builtin_ctz((unsigned)a.epn) : -1;
     a.rows = s.rows();
     const bool fp8 = (s.x_fmt == 1);
     a.row_bytes = fp8 ? (int64_t)s.H : 2 * (int64_t)s.H;
     a.nvec = (int)(a.row_bytes / 16);
     a.G = fp8 ? s.H / 128 : 0;
     a.S = waves_per_token(s.T, a.nvec, EP_DISPATCH_WAVES);
+    return a;
+}
+
+template <bool FUSED>
+void launch_copy(const CopyArgs &a, int64_t blocks, int threads, size_t lds, hipStream_t stream) {
     const int per_lane = (a.nvec + kWave * a.S - 1) / (kWave * a.S);
-    const int64_t waves = s.T * a.S;
-    int64_t blocks = (waves + 3) / 4;
-    if (blocks * 256 < s.E + 1) blocks = (s.E + 1 + 255) / 256;   // threads to copy expert_offset
-    const dim3 grid((unsigned)blocks), block(256);
+    const dim3 grid((unsigned)blocks), block(threads);
     if (per_lane <= 2) {
-        hipLaunchKernelGGL(ep_dispatch_copy_kernel<2>, grid, block, 0, stream, a);
+        hipLaunchKernelGGL((ep_dispatch_copy_kernel<2, FUSED>), grid, block, lds, stream, a);
     } else if (per_lane <= 4) {
-        hipLaunchKernelGGL(ep_dispatch_copy_kernel<4>, grid, block, 0, stream, a);
+        hipLaunchKernelGGL((ep_dispatch_copy_kernel<4, FUSED>), grid, block, lds, stream, a);
     } else if (per_lane <= 8) {
-        hipLaunchKernelGGL(ep_dispatch_copy_kernel<8>, grid, block, 0, stream, a);
+        hipLaunchKernelGGL((ep_dispatch_copy_kernel<8, FUSED>), grid, block, lds, stream, a);
     } else {
-        hipLaunchKernelGGL(ep_dispatch_copy_kernel<16>, grid, block, 0, stream, a);
+        hipLaunchKernelGGL((ep_dispatch_copy_kernel<16, FUSED>), grid, block, lds, stream, a);
     }
+}
+
+}  // namespace
+
+hipError_t launch_dispatch_copy(const Shape &s, const WsLayout &L, const void *x,
+                                const float *x_scales, const int64_t *topk_idx,
+                                const float *topk_w, void *recv_x, float *recv_x_scales,
+                                int32_t *recv_src_idx, float *recv_topk_w, int32_t *token_slot,
+                                int32_t *expert_offset, char *ws, hipStream_t stream) {
+    CopyArgs a = copy_args(s, x, x_scales, topk_idx, topk_w, recv_x, recv_x_scales, recv_src_idx,
+                           recv_topk_w, token_slot, expert_offset);
+    a.plan_offset = reinterpret_cast<const int32_t *>(ws + L.plan_offset);
+    a.tile_prefix = reinterpret_cast<const int32_t *>(ws + L.tile_count);
+    a.local_rank = reinterpret_cast<const int32_t *>(ws + L.local_rank);
+    a.ctrl = reinterpret_cast<uint32_t *>(ws + L.ctrl);
+    a.TT = L.tile_tokens;
+    int64_t blocks = (s.T * a.S + 3) / 4;
+    if (blocks * 256 < s.E + 1) blocks = (s.E + 1 + 255) / 256;   // threads to copy expert_offset
+    launch_copy<false>(a, blocks, 256, 0, stream);
+    return hipGetLastError();
+}
+
+// Waves per token of the single-launch form: enough for the row copy, and at
+// least one per slot (up to 16) so each wave counts few slots.
+int fused_waves(const Shape &s, int nvec) {
+    int S = waves_per_token(s.T, nvec, EP_DISPATCH_WAVES);
+    const int want = s.k < 16 ? s.k : 16;
+    while (S < want) S *= 2;
+    return S > 16 ? 16 : S;
+}
+
+bool fused_dispatch_fits(const Shape &s) {
+    if (!(s.T > 0 && s.T * s.k <= kFusedPairs && s.M == 0 && !s.rank_rows)) return false;
+    const int nvec = (int)((s.x_fmt == 1 ? (int64_t)s.H : 2 * (int64_t)s.H) / 16);
+    const int S = fused_waves(s, nvec);
+    return (nvec + kWave * S - 1) / (kWave * S) <= 8;   // registers for 1024-thread blocks
+}
+
+hipError_t launch_dispatch_fused(const Shape &s, const void *x, const float *x_scales,
+                                 const int64_t *topk_idx, const float *topk_w, void *recv_x,
+                                 float *recv_x_scales, int32_t *recv_src_idx, float *recv_topk_w,
+                                 int32_t *token_slot, int32_t *expert_offset, int32_t *per_rank,
+                                 int32_t *per_expert, uint8_t *in_rank, int32_t *per_node,
+                                 int64_t *algo, uint32_t *ctrl, hipStream_t stream) {
+    CopyArgs a = copy_args(s, x, x_scales, topk_idx, topk_w, recv_x, recv_x_scales, recv_src_idx,
+                           recv_topk_w, token_slot, expert_offset);
+    a.ctrl = ctrl;
+    a.per_rank = per_rank;
+    a.per_expert = per_expert;
+    a.in_rank = in_rank;
+    a.per_node = per_node;
+    a.algo = algo;
+    // block 0: the layout; then one block of S waves per token
+    a.S = fused_waves(s, a.nvec);
+    const int threads = kWave * a.S;
+    const size_t lds = sizeof(int32_t) * ((size_t)s.T * s.k + s.E + s.R + s.N + threads / kWave + 1);
+    launch_copy<true>(a, 1 + s.T, threads, lds, stream);
     return hipGetLastError();
 }
 

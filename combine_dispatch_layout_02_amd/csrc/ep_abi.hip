@@ -185,7 +185,45 @@ int ep_dispatch(const ep_shape *shape, const void *x, const float *x_scales,
     if (rc != EP_OK) return rc;
     hipStream_t st = static_cast<hipStream_t>(stream);
     char *w = static_cast<char *>(ws);
+    if (ep::fused_dispatch_fits(s))   // small batch: one launch, no plan in the workspace
+        return hip_status(ep::launch_dispatch_fused(s, x, x_scales, topk_idx, topk_w, recv_x, recv_x_scales,
+                                                    recv_src_idx, recv_topk_w, token_slot, expert_offset,
+                                                    nullptr, nullptr, nullptr, nullptr, nullptr,
+                                                    reinterpret_cast<uint32_t *>(w + L.ctrl), st));
     hipError_t e = ep::launch_plan(s, L, topk_idx, nullptr, nullptr, nullptr, nullptr, nullptr, w, st);
+    if (e != hipSuccess) return EP_EHIP;
+    e = ep::launch_dispatch_copy(s, L, x, x_scales, topk_idx, topk_w, recv_x, recv_x_scales,
+                                 recv_src_idx, recv_topk_w, token_slot, expert_offset, w, st);
+    return hip_status(e);
+}
+
+int ep_dispatch_with_layout(const ep_shape *shape, const void *x, const float *x_scales,
+                            const int64_t *topk_idx, const float *topk_w, int32_t *num_tokens_per_rank,
+                            int32_t *num_tokens_per_expert, uint8_t *is_token_in_rank,
+                            int32_t *num_tokens_per_node, int64_t *rdma_algo_token_count, void *recv_x,
+                            float *recv_x_scales, int32_t *recv_src_idx, float *recv_topk_w,
+                            int32_t *token_slot, int32_t *expert_offset, void *ws, size_t ws_bytes,
+                            void *stream) {
+    Shape s;
+    WsLayout L;
+    int rc = check_dispatch_args(shape, &s, x, x_scales, topk_idx, topk_w, recv_x, recv_x_scales,
+                                 recv_src_idx, recv_topk_w, token_slot, expert_offset, ws, ws_bytes, &L);
+    if (rc != EP_OK) return rc;
+    if (!num_tokens_per_rank || !num_tokens_per_expert || !num_tokens_per_node || !rdma_algo_token_count)
+        return EP_EINVAL;
+    if (s.T > 0 && !is_token_in_rank) return EP_EINVAL;
+    if (!aligned16(is_token_in_rank) && (s.R % 4 == 0)) return EP_EALIGN;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    char *w = static_cast<char *>(ws);
+    if (ep::fused_dispatch_fits(s))
+        return hip_status(ep::launch_dispatch_fused(s, x, x_scales, topk_idx, topk_w, recv_x, recv_x_scales,
+                                                    recv_src_idx, recv_topk_w, token_slot, expert_offset,
+                                                    num_tokens_per_rank, num_tokens_per_expert,
+                                                    is_token_in_rank, num_tokens_per_node,
+                                                    rdma_algo_token_count,
+                                                    reinterpret_cast<uint32_t *>(w + L.ctrl), st));
+    hipError_t e = ep::launch_plan(s, L, topk_idx, num_tokens_per_rank, num_tokens_per_expert,
+                                   is_token_in_rank, num_tokens_per_node, rdma_algo_token_count, w, st);
     if (e != hipSuccess) return EP_EHIP;
     e = ep::launch_dispatch_copy(s, L, x, x_scales, topk_idx, topk_w, recv_x, recv_x_scales,
                                  recv_src_idx, recv_topk_w, token_slot, expert_offset, w, st);

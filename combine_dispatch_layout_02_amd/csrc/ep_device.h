@@ -165,4 +165,55 @@ __device__ __forceinline__ void st16_nt(void *p, vec16 v) {
     __builtin_nontemporal_store(v, reinterpret_cast<vec16 *>(p));
 }
 
+// ---------------------------------------------------------------- scans
+
+// Exclusive scan of n ints held in LDS (`in`), written to `out` (n + 1
+// entries, out[n] = total).  Called by every thread of the block.
+__device__ __forceinline__ void block_exclusive_scan(const int32_t *in, int32_t *out, int n, int32_t *tmp) {
+    const int nt = blockDim.x, tid = threadIdx.x;
+    const int lane = tid & (kWave - 1), wid = tid / kWave, nw = (nt + kWave - 1) / kWave;
+    const int chunk = (n + nt - 1) / nt;
+    const int b = min(tid * chunk, n), e = min(b + chunk, n);
+    int32_t s = 0;
+    for (int i = b; i < e; ++i) s += in[i];
+    int32_t v = s;
+    for (int off = 1; off < kWave; off <<= 1) {
+        const int32_t u = __shfl_up(v, off);
+        if (lane >= off) v += u;
+    }
+    if (lane == kWave - 1) tmp[wid] = v;
+    __syncthreads();
+    if (tid == 0) {
+        int32_t run = 0;
+        for (int i = 0; i < nw; ++i) {
+            const int32_t x = tmp[i];
+            tmp[i] = run;
+            run += x;
+        }
+        tmp[nw] = run;
+    }
+    __syncthreads();
+    int32_t excl = tmp[wid] + v - s;
+    for (int i = b; i < e; ++i) {
+        const int32_t x = in[i];
+        out[i] = excl;
+        excl += x;
+    }
+    if (tid == 0) out[n] = tmp[nw];
+    __syncthreads();
+}
+
+// Exclusive scan of n <= 64 values held one per lane by the first wave
+// (lanes >= n hold 0): out[i] for i < n, and out[n] = total.
+__device__ __forceinline__ void wave_exclusive_scan(int32_t v, int n, int32_t *out) {
+    const int lane = threadIdx.x & (kWave - 1);
+    int32_t incl = v;
+    for (int off = 1; off < kWave; off <<= 1) {
+        const int32_t u = __shfl_up(incl, off);
+        if (lane >= off) incl += u;
+    }
+    if (lane < n) out[lane] = incl - v;
+    if (lane == kWave - 1) out[n] = incl;
+}
+
 }  // namespace ep

@@ -61,6 +61,17 @@ hipError_t launch_dispatch_copy(const Shape &s, const WsLayout &L, const void *x
                                 int32_t *recv_src_idx, float *recv_topk_w, int32_t *token_slot,
                                 int32_t *expert_offset, char *ws, hipStream_t stream);
 
+// Single-launch layout + dispatch (compacted layout, T * k <= 1024 pairs):
+// fused_dispatch_fits tells whether a shape qualifies.  Layout outputs may be
+// null (all together); the workspace plan is neither read nor written.
+bool fused_dispatch_fits(const Shape &s);
+hipError_t launch_dispatch_fused(const Shape &s, const void *x, const float *x_scales,
+                                 const int64_t *topk_idx, const float *topk_w, void *recv_x,
+                                 float *recv_x_scales, int32_t *recv_src_idx, float *recv_topk_w,
+                                 int32_t *token_slot, int32_t *expert_offset, int32_t *per_rank,
+                                 int32_t *per_expert, uint8_t *in_rank, int32_t *per_node,
+                                 int64_t *algo, uint32_t *ctrl, hipStream_t stream);
+
 hipError_t launch_combine(const Shape &s, const void *expert_out, const uint8_t *expert_scales,
                           const int32_t *token_slot, const float *topk_w, void *y,
                           hipStream_t stream);

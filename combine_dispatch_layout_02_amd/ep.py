@@ -27,7 +27,8 @@ EP_OK, EP_EINVAL, EP_EALIGN, EP_EWORKSPACE, EP_EHIP, EP_EDEVICE = 0, -1, -2, -3,
 # every symbol include/ep.h declares
 EXPORTED = (
     "ep_abi_version", "ep_strerror", "ep_validate_shape", "ep_workspace_bytes", "ep_workspace_init",
-    "ep_dispatch_layout", "ep_dispatch", "ep_dispatch_from_layout", "ep_combine", "ep_check",
+    "ep_dispatch_layout", "ep_dispatch", "ep_dispatch_from_layout", "ep_dispatch_with_layout", "ep_combine",
+    "ep_check",
     "ep_dispatch_ranks", "ep_expert_reduce_ranks", "ep_combine_ranks", "ep_quant_fp8_s128",
     "ep_expert_scale_bf16", "ep_expert_requant_mxfp8", "ep_expert_requant_nvfp4", "ep_accounting",
     "ep_calib_copy",
@@ -108,6 +109,7 @@ def load():
         "ep_dispatch_layout": (ctypes.c_int, [SP, P, P, P, P, P, P, P, sz, P]),
         "ep_dispatch": (ctypes.c_int, [SP, P, P, P, P, P, P, P, P, P, P, P, sz, P]),
         "ep_dispatch_from_layout": (ctypes.c_int, [SP, P, P, P, P, P, P, P, P, P, P, P, sz, P]),
+        "ep_dispatch_with_layout": (ctypes.c_int, [SP] + [P] * 15 + [P, sz, P]),
         "ep_combine": (ctypes.c_int, [SP, P, P, P, P, P, P]),
         "ep_dispatch_ranks": (ctypes.c_int, [SP, P, P, P, P, P, P, P, P, P, P, P, P, sz, P]),
         "ep_expert_reduce_ranks": (ctypes.c_int, [SP, P, P, P, P, P, P, P, P]),
@@ -124,7 +126,7 @@ def load():
         fn = getattr(lib, name)
         fn.restype = res
         fn.argtypes = args
-    if lib.ep_abi_version() != 2:
+    if lib.ep_abi_version() != 3:
         raise RuntimeError("libep_hip ABI version mismatch")
     _lib = lib
     return lib
@@ -250,6 +252,40 @@ def ep_dispatch(shape, x, x_scales, topk_idx, topk_w, recv_x, recv_x_scales, rec
            _ptr(recv_x), _ptr(recv_x_scales), _ptr(recv_src_idx), _ptr(recv_topk_w),
            _ptr(token_slot), _ptr(expert_offset), ws.ptr, ws.nbytes, _stream(stream)),
         "ep_dispatch_from_layout" if from_layout else "ep_dispatch")
+
+
+def ep_dispatch_with_layout(shape, x, x_scales, topk_idx, topk_w, num_tokens_per_rank, num_tokens_per_expert,
+                            is_token_in_rank, num_tokens_per_node, rdma_algo_token_count, recv_x, recv_x_scales,
+                            recv_src_idx, recv_topk_w, token_slot, expert_offset, ws: Workspace, stream=None):
+    """Layout and dispatch in one call (one launch for batches of <= 1024 pairs)."""
+    T, k, H, E, R, N = (shape.num_tokens, shape.num_topk, shape.hidden, shape.num_experts, shape.num_ranks,
+                        shape.num_nodes)
+    fp8 = shape.x_format == EP_FMT_FP8_S128
+    rows = shape.rows
+    _need(x, torch.uint8 if fp8 else torch.bfloat16, (T, H), "x")
+    _need(topk_idx, torch.int64, (T, k), "topk_idx")
+    _need(topk_w, torch.float32, (T, k), "topk_w")
+    _need(num_tokens_per_rank, torch.int32, (R,), "num_tokens_per_rank")
+    _need(num_tokens_per_expert, torch.int32, (E,), "num_tokens_per_expert")
+    _need(is_token_in_rank, torch.uint8, (T, R), "is_token_in_rank")
+    _need(num_tokens_per_node, torch.int32, (N,), "num_tokens_per_node")
+    _need(rdma_algo_token_count, torch.int64, (1,), "rdma_algo_token_count")
+    _need(recv_x, x.dtype, (rows, H), "recv_x")
+    if fp8:
+        _need(x_scales, torch.float32, (T, H // 128), "x_scales")
+        _need(recv_x_scales, torch.float32, (rows, H // 128), "recv_x_scales")
+    _need(recv_src_idx, torch.int32, (rows,), "recv_src_idx")
+    _need(recv_topk_w, torch.float32, (rows,), "recv_topk_w")
+    _need(token_slot, torch.int32, (T, k), "token_slot")
+    _need(expert_offset, torch.int32, (E + 1,), "expert_offset")
+    ws.planned_for = None   # no reusable plan is left in the workspace
+    _ok(load().ep_dispatch_with_layout(ctypes.byref(shape), _ptr(x), _ptr(x_scales), _ptr(topk_idx), _ptr(topk_w),
+                                       _ptr(num_tokens_per_rank), _ptr(num_tokens_per_expert),
+                                       _ptr(is_token_in_rank), _ptr(num_tokens_per_node),
+                                       _ptr(rdma_algo_token_count), _ptr(recv_x), _ptr(recv_x_scales),
+                                       _ptr(recv_src_idx), _ptr(recv_topk_w), _ptr(token_slot),
+                                       _ptr(expert_offset), ws.ptr, ws.nbytes, _stream(stream)),
+        "ep_dispatch_with_layout")
 
 
 def ep_combine(shape, expert_out, expert_out_scales, token_slot, topk_w, y, stream=None):
@@ -413,6 +449,33 @@ def dispatch(x, topk_idx, topk_w, shape, ws: Workspace, x_scales=None, stream=No
     ep_dispatch(shape, x, x_scales, topk_idx, topk_w, recv_x, recv_x_scales, recv_src_idx, recv_topk_w,
                 token_slot, expert_offset, ws, stream, from_layout)
     return recv_x, recv_x_scales, recv_src_idx, recv_topk_w, Handle(shape, token_slot, expert_offset, topk_w)
+
+
+def dispatch_with_layout(x, topk_idx, topk_w, shape, ws: Workspace, x_scales=None, stream=None):
+    """Returns the layout dict and recv_x, recv_x_scales, recv_src_idx, recv_topk_w, handle."""
+    dev = x.device
+    T, k, H, E, R, N = (shape.num_tokens, shape.num_topk, shape.hidden, shape.num_experts, shape.num_ranks,
+                        shape.num_nodes)
+    rows = shape.rows
+    fp8 = shape.x_format == EP_FMT_FP8_S128
+    lay = dict(
+        num_tokens_per_rank=torch.empty(R, dtype=torch.int32, device=dev),
+        num_tokens_per_expert=torch.empty(E, dtype=torch.int32, device=dev),
+        is_token_in_rank=torch.empty((T, R), dtype=torch.uint8, device=dev),
+        num_tokens_per_node=torch.empty(N, dtype=torch.int32, device=dev),
+        rdma_algo_token_count=torch.empty(1, dtype=torch.int64, device=dev),
+    )
+    recv_x = torch.empty((rows, H), dtype=x.dtype, device=dev)
+    recv_x_scales = torch.empty((rows, H // 128), dtype=torch.float32, device=dev) if fp8 else None
+    recv_src_idx = torch.empty(rows, dtype=torch.int32, device=dev)
+    recv_topk_w = torch.empty(rows, dtype=torch.float32, device=dev)
+    token_slot = torch.empty((T, k), dtype=torch.int32, device=dev)
+    expert_offset = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    ep_dispatch_with_layout(shape, x, x_scales, topk_idx, topk_w, lay["num_tokens_per_rank"],
+                            lay["num_tokens_per_expert"], lay["is_token_in_rank"], lay["num_tokens_per_node"],
+                            lay["rdma_algo_token_count"], recv_x, recv_x_scales, recv_src_idx, recv_topk_w,
+                            token_slot, expert_offset, ws, stream)
+    return lay, recv_x, recv_x_scales, recv_src_idx, recv_topk_w, Handle(shape, token_slot, expert_offset, topk_w)
 
 
 def combine(expert_out, handle: Handle, expert_out_scales=None, stream=None):

@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define EP_ABI_VERSION 2
+#define EP_ABI_VERSION 3
 
 /* Status codes. */
 enum ep_status {
@@ -176,13 +176,35 @@ int ep_dispatch_layout(const ep_shape *shape, const int64_t *topk_idx,
  *   expert_offset [E+1] int32: segment starts, expert_offset[E] = valid
  *                 pairs (handle); rank r's region is
  *                 [expert_offset[r*E/R], expert_offset[(r+1)*E/R]).
- * Deterministic: no order-dependent atomics.
+ * Deterministic: no order-dependent atomics.  ep_dispatch plans by itself
+ * (a small batch, as in ep_dispatch_with_layout, in one launch); the plan it
+ * may leave in the workspace is not one ep_dispatch_from_layout may reuse.
  */
 int ep_dispatch(const ep_shape *shape, const void *x, const float *x_scales,
                 const int64_t *topk_idx, const float *topk_w,
                 void *recv_x, float *recv_x_scales, int32_t *recv_src_idx, float *recv_topk_w,
                 int32_t *token_slot, int32_t *expert_offset,
                 void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Layout and dispatch in one call: the outputs of ep_dispatch_layout and of
+ * ep_dispatch together ([PR860] Scope: get_dispatch_layout followed by
+ * dispatch).  A small batch -- T * k <= 1024 pairs, compacted layout
+ * (rank_capacity 0), rank_rows 0 -- runs as ONE kernel launch: one block
+ * computes the layout counts and the segment starts while every other wave
+ * finds its token's slots by counting the pairs that sort before them (the
+ * stable counting sort's position); results are identical to the two calls.
+ * Larger batches run the layout launches then the copy.  Afterwards the
+ * workspace holds no plan that ep_dispatch_from_layout may reuse.
+ * Arguments: as ep_dispatch_layout and ep_dispatch.
+ */
+int ep_dispatch_with_layout(const ep_shape *shape, const void *x, const float *x_scales,
+                            const int64_t *topk_idx, const float *topk_w, int32_t *num_tokens_per_rank,
+                            int32_t *num_tokens_per_expert, uint8_t *is_token_in_rank,
+                            int32_t *num_tokens_per_node, int64_t *rdma_algo_token_count, void *recv_x,
+                            float *recv_x_scales, int32_t *recv_src_idx, float *recv_topk_w,
+                            int32_t *token_slot, int32_t *expert_offset, void *ws, size_t ws_bytes,
+                            void *stream);
 
 /*
  * Dispatch that reuses the plan the preceding ep_dispatch_layout call on the

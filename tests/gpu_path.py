@@ -19,9 +19,10 @@ def bf16_bits(t: torch.Tensor) -> np.ndarray:
     return t.view(torch.int16).cpu().numpy().view(np.uint16)
 
 
-def run(inp: dict, dev="cuda", check=True, from_layout=True) -> dict:
+def run(inp: dict, dev="cuda", check=True, from_layout=True, with_layout=False) -> dict:
     """from_layout: dispatch reuses the layout call's plan (ep_dispatch_from_layout);
-    otherwise the standalone ep_dispatch plans again."""
+    otherwise the standalone ep_dispatch plans again.  with_layout: one
+    ep_dispatch_with_layout call does both (a single launch for small batches)."""
     T, H, E, R, N, k = (inp[n] for n in ("T", "H", "E", "R", "N", "k"))
     fp8 = inp.get("x_fmt", "bf16") == "fp8"
     nv = inp.get("y_fmt") == "nvfp4"
@@ -33,10 +34,18 @@ def run(inp: dict, dev="cuda", check=True, from_layout=True) -> dict:
     idx = torch.from_numpy(np.ascontiguousarray(inp["topk_idx"])).to(dev)
     w = torch.from_numpy(np.ascontiguousarray(inp["topk_w"])).to(dev)
     out = {}
-    lay = ep.dispatch_layout(idx, shape, ws)
+
+    def dispatch(xin, x_scales=None):
+        nonlocal lay
+        if with_layout:
+            lay, *rest = ep.dispatch_with_layout(xin, idx, w, shape, ws, x_scales=x_scales)
+            return rest
+        return ep.dispatch(xin, idx, w, shape, ws, x_scales=x_scales, from_layout=from_layout)
+
+    lay = None if with_layout else ep.dispatch_layout(idx, shape, ws)
     if fp8:
         q, s = ep.quant_fp8_s128(x)
-        recv_x, recv_s, src, rw, h = ep.dispatch(q, idx, w, shape, ws, x_scales=s, from_layout=from_layout)
+        recv_x, recv_s, src, rw, h = dispatch(q, s)
         factor = inp.get("expert_factor")
         f = None if factor is None else torch.from_numpy(factor).to(dev)
         eq = torch.zeros((shape.rows, H), dtype=torch.uint8, device=dev)
@@ -46,7 +55,7 @@ def run(inp: dict, dev="cuda", check=True, from_layout=True) -> dict:
         out.update(x_q=q.cpu().numpy(), x_scales=s.cpu().numpy(), recv_x=recv_x.cpu().numpy(),
                    recv_x_scales=recv_s.cpu().numpy(), expert_q=eq.cpu().numpy(), expert_e8m0=ee.cpu().numpy())
     elif nv:
-        recv_x, _, src, rw, h = ep.dispatch(x, idx, w, shape, ws, from_layout=from_layout)
+        recv_x, _, src, rw, h = dispatch(x)
         factor = inp.get("expert_factor")
         f = None if factor is None else torch.from_numpy(factor).to(dev)
         eq = torch.zeros((shape.rows, H // 2), dtype=torch.uint8, device=dev)
@@ -56,7 +65,7 @@ def run(inp: dict, dev="cuda", check=True, from_layout=True) -> dict:
         out.update(recv_x=bf16_bits(recv_x), expert_q=eq.cpu().numpy(),
                    expert_scales=es.cpu().numpy().view(np.uint16))
     else:
-        recv_x, _, src, rw, h = ep.dispatch(x, idx, w, shape, ws, from_layout=from_layout)
+        recv_x, _, src, rw, h = dispatch(x)
         if inp.get("expert") == "scale":
             eo = torch.zeros_like(recv_x)
             f = torch.from_numpy(inp["expert_factor"]).to(dev)

@@ -26,11 +26,11 @@ def _gpu():
     ep.load()  # fails loudly if the HIP library is missing
 
 
-def _run_both(inp, from_layout=True):
+def _run_both(inp, from_layout=True, with_layout=False):
     import gpu_path
     print(f"case {inp.get('name')} T={inp['T']} H={inp['H']} E={inp['E']} R={inp['R']} N={inp['N']} "
-          f"k={inp['k']} seed={inp.get('seed')} from_layout={from_layout}", flush=True)
-    g = gpu_path.run(inp, from_layout=from_layout)
+          f"k={inp['k']} seed={inp.get('seed')} from_layout={from_layout} with_layout={with_layout}", flush=True)
+    g = gpu_path.run(inp, from_layout=from_layout, with_layout=with_layout)
     r = oracle.run_path(inp)
     ndiff = gpu_path.compare(g, r, inp.get("x_fmt") == "fp8", inp.get("y_fmt") == "nvfp4")
     return g, r, ndiff
@@ -228,3 +228,43 @@ def test_nvfp4_combine_every_code_and_scale_kind():
     ep.ep_combine(shape, torch.from_numpy(q).cuda(), torch.from_numpy(sc.view(np.int16)).cuda(),
                   torch.from_numpy(slot).cuda(), torch.from_numpy(w).cuda(), y)
     np.testing.assert_array_equal(gpu_path.bf16_bits(y), ref)
+
+
+# single-launch layout + dispatch: batches of at most 1024 (token, slot) pairs
+@pytest.mark.parametrize("kw", [
+    dict(T=1), dict(T=5), dict(T=64), dict(T=127), dict(T=128), dict(T=128, mask_frac=0.3),
+    dict(T=128, mask_frac=0.3, mask_tokens=0.2), dict(T=100, routing="replace"), dict(T=32, k=32, E=4096, R=64, N=64),
+    dict(T=1024, k=1), dict(T=64, k=16, routing="replace", mask_frac=0.2), dict(T=128, H=8),
+    dict(T=129)])   # 1032 pairs: the multi-launch path through the same call
+def test_with_layout_small_batches(kw):
+    kw = dict(kw)
+    base = dict(H=kw.pop("H", 1024))
+    base.update(kw)
+    _, _, ndiff = _run_both(W.make_inputs("decode", **base), with_layout=True)
+    assert ndiff == 0
+
+
+@pytest.mark.parametrize("name", ["tiny", "decode"])
+def test_with_layout_workloads(name):
+    _, _, ndiff = _run_both(W.make_inputs(name), with_layout=True)
+    assert ndiff == 0
+
+
+@pytest.mark.parametrize("kw", [dict(T=128), dict(T=100, mask_frac=0.25)])
+def test_with_layout_quantized(kw):
+    _, _, ndiff = _run_both(W.make_inputs("quant", H=1024, **kw), with_layout=True)
+    assert ndiff == 0
+    _, _, ndiff = _run_both(W.make_inputs("nvfp4", H=1024, **kw), with_layout=True)
+    assert ndiff == 0
+
+
+def test_with_layout_flags_invalid_ids():
+    import gpu_path
+    inp = W.make_inputs("decode", T=100, H=512, mask_frac=0.1)
+    bad = inp["topk_idx"].copy()
+    bad[7, 3] = inp["E"] + 1
+    inp["topk_idx"] = bad
+    g = gpu_path.run(inp, check=False, with_layout=True)
+    with pytest.raises(RuntimeError, match="flags 0x1"):
+        g["ws"].check()
+    assert gpu_path.compare(g, oracle.run_path(inp), False) == 0
