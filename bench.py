@@ -8,7 +8,9 @@ workload, if any) -> ep_combine, all on one stream.  W untimed warmup steps,
 then K timed steps bracketed by stream synchronisation and HIP events, three
 ways: replayed from HIP graphs of 10 captured steps (the reported
 ms_per_step), eager back to back (eager_ms_per_step), and eager with events
-between the calls (the per-call durations in phase_us: median over steps).  The workloads'
+between the calls (the per-call durations in phase_us: median over steps);
+phase_us_flushed repeats the calls each after a 512 MiB copy that evicts the
+memory-side cache (cold-cache durations).  The workloads'
 expert stage (identity, per-expert scaling, or fp8 -> mxfp8 re-encoding)
 runs during warmup and is not part of the timed step.  A batch of at most
 1024 (token, slot) pairs is laid out and dispatched by one
@@ -43,6 +45,7 @@ HBM_PEAK_GBS = 8000.0   # MI355X HBM3E, published peak
 
 GRAPH_STEPS = 10   # steps captured per HIP graph
 SINGLE_LAUNCH_PAIRS = 1024   # batches the library lays out and dispatches in one launch
+FLUSH_BYTES = 512 << 20      # copy that evicts the 256 MB memory-side cache
 PROFILES = os.path.join(ROOT, "profiles")
 
 
@@ -139,6 +142,9 @@ def parse():
                     help="receive layout: one row per (token, expert) pair (default), or one row per "
                          "(token, rank) with per-rank partials (ep_dispatch_ranks / ep_combine_ranks)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--flush-steps", type=int, default=10,
+                    help="also time each call after a 512 MiB cache-evicting copy, over this many steps "
+                         "(phase_us_flushed; 0 to skip)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-graph", action="store_true",
                     help="time the eager loop only (default: K steps replayed from HIP graphs of %d steps)" % GRAPH_STEPS)
@@ -188,7 +194,7 @@ def main():
                                     + args.layout + " layout)",
                           "unit": "us", "series": series}), flush=True)
         return
-    out = measure(args.workload, args.steps, args.warmup, not args.no_graph, args.layout)
+    out = measure(args.workload, args.steps, args.warmup, not args.no_graph, args.layout, args.flush_steps)
     inp = out.pop("_inp")
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(dict(inp, rank_rows=args.layout == "ranks"), args.cpu_seconds,
@@ -197,7 +203,7 @@ def main():
 
 
 def measure(workload: str, steps: int, warmup: int, graph: bool = False, layout_kind: str = "pairs",
-            **overrides) -> dict:
+            flush_steps: int = 0, **overrides) -> dict:
     """Time `steps` steps of the path on `workload` (inputs resident in HBM);
     keyword overrides change the workload's shape (e.g. T=...).  layout_kind
     "ranks" times the (token, rank) path: layout, ep_dispatch_ranks,
@@ -355,6 +361,29 @@ def measure(workload: str, steps: int, warmup: int, graph: bool = False, layout_
     for e in ev:
         hev.destroy(e)
 
+    # (2b) the same calls, each after a flush of the memory-side cache (a
+    # 512 MiB copy, more than the 256 MB cache holds, outside the events): the
+    # cold-cache duration of each call
+    phase_us_flushed = None
+    if flush_steps:
+        fl_src = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
+        fl_dst = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
+        evf = [hev.create(2 * len(phases)) for _ in range(flush_steps)]
+        torch.cuda.synchronize()
+        for s_ in range(flush_steps):
+            for i, (_, fn) in enumerate(phases):
+                ep.ep_calib_copy(fl_src, fl_dst, FLUSH_BYTES)
+                hev.record(evf[s_][2 * i], stream)
+                fn()
+                hev.record(evf[s_][2 * i + 1], stream)
+        torch.cuda.synchronize()
+        phase_us_flushed = {name: 1000.0 * statistics.median(hev.ms(evf[s_][2 * i], evf[s_][2 * i + 1])
+                                                             for s_ in range(flush_steps))
+                            for i, (name, _) in enumerate(phases)}
+        for e in evf:
+            hev.destroy(e)
+        del fl_src, fl_dst
+
     # (3) HIP graph: G steps captured once, replayed K/G times (launch gaps
     # between steps vanish inside a graph, as in a captured serving loop)
     graph_ms, G = None, 0
@@ -423,6 +452,8 @@ def measure(workload: str, steps: int, warmup: int, graph: bool = False, layout_
                    "receive_rows": int(acc["nvl_tokens"]) if ranks else V},
         "tokens_per_s": round(T / step_s, 1),
         "phase_us": {p: round(v, 2) for p, v in phase_us.items()},
+        "phase_us_flushed": None if phase_us_flushed is None else
+        {p: round(v, 2) for p, v in phase_us_flushed.items()},
         "step_algorithmic_bytes": int(step_bytes),
         "eager_ms_per_step": round(eager_ms, 4),
         "timing": ("steps replayed from a HIP graph of %d steps" % G) if graph_ms is not None else "eager",

@@ -179,3 +179,20 @@ def test_rank_rows_accounting(lib, name):
     assert got["hbm_dispatch_ranks_bytes"] == (T * row + rows * row + T * k * 12 + T * R * 4
                                                + rows * (4 + 8 * k) + 4 * (R + 1))
     assert got["hbm_combine_ranks_bytes"] == rows * 2 * H + T * 2 * H + T * R * 4
+
+
+def test_dispatch_with_layout_rejects_before_device_work(lib):
+    P = ctypes.c_void_p
+    fake, odd = P(0x1000), P(0x1008)
+    sh = ep.make_shape(64, 256, 16, 4, 1, 2)
+    f = [fake] * 5   # layout outputs
+
+    def call(x=fake, xs=None, lay=f, recv=fake, rs=None, ws=fake, nbytes=1 << 20):
+        return lib.ep_dispatch_with_layout(ctypes.byref(sh), x, xs, fake, fake, *lay, recv, rs, fake, fake, fake,
+                                           fake, ws, nbytes, None)
+    assert call(x=odd) == ep.EP_EALIGN
+    assert call(xs=fake) == ep.EP_EINVAL                          # scales for bf16 rows
+    assert call(lay=[None] + f[1:]) == ep.EP_EINVAL               # a layout output missing
+    assert call(lay=f[:2] + [odd] + f[3:]) == ep.EP_EALIGN        # token-in-rank map misaligned (R % 4 == 0)
+    assert call(ws=None) == ep.EP_EWORKSPACE
+    assert call(nbytes=16) == ep.EP_EWORKSPACE
