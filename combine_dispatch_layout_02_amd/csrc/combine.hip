@@ -50,6 +50,9 @@ constexpr int kSlotBatch = 8;
 #ifndef EP_COMBINE_Y_NT
 #define EP_COMBINE_Y_NT 0      // non-temporal stores for y
 #endif
+#ifndef EP_COMBINE_CONTIG
+#define EP_COMBINE_CONTIG 0    // 1: each wave of a token owns one contiguous part of the row
+#endif
 
 __device__ __forceinline__ void store_y(char *p, vec16 v) {
     if (EP_COMBINE_Y_NT) st16_nt(p, v); else st16(p, v);
@@ -85,7 +88,13 @@ __global__ __launch_bounds__(256) void ep_combine_bf16_kernel(CombineArgs a) {
     char *yrow = a.y + t * (int64_t)a.H * 2;
     const int stride = kWave * a.S;
 
-    for (int v0 = lane + kWave * sub; v0 < a.nvec; v0 += stride * C) {
+    // vectors of this wave: interleaved with the token's other waves, or one
+    // contiguous part of the row per wave
+    const int per = (a.nvec + a.S - 1) / a.S;
+    const int vbeg = EP_COMBINE_CONTIG ? sub * per + lane : lane + kWave * sub;
+    const int vend = EP_COMBINE_CONTIG ? min(a.nvec, (sub + 1) * per) : a.nvec;
+    const int vstep = EP_COMBINE_CONTIG ? kWave : stride;
+    for (int v0 = vbeg; v0 < vend; v0 += vstep * C) {
         float acc[C][8];
 #pragma unroll
         for (int i = 0; i < C; ++i)
@@ -99,8 +108,8 @@ __global__ __launch_bounds__(256) void ep_combine_bf16_kernel(CombineArgs a) {
                 const char *row = a.eo + row_of(readlane(slot, jb + jj)) * a.row_bytes;
 #pragma unroll
                 for (int i = 0; i < C; ++i) {
-                    const int v = v0 + i * stride;
-                    if (v < a.nvec) buf[jj][i] = ld16_nt(row + (int64_t)v * 16);
+                    const int v = v0 + i * vstep;
+                    if (v < vend) buf[jj][i] = ld16_nt(row + (int64_t)v * 16);
                 }
             }
 #pragma unroll
@@ -118,8 +127,8 @@ __global__ __launch_bounds__(256) void ep_combine_bf16_kernel(CombineArgs a) {
         }
 #pragma unroll
         for (int i = 0; i < C; ++i) {
-            const int v = v0 + i * stride;
-            if (v >= a.nvec) continue;
+            const int v = v0 + i * vstep;
+            if (v >= vend) continue;
             vec16 o;
 #pragma unroll
             for (int q = 0; q < 4; ++q)

@@ -11,10 +11,11 @@
 // How: one wave per (token, row part).  Lanes 0..k-1 form the token's k slots
 // and readlane broadcasts them to scalar registers, so the k destinations are
 // wave-uniform.  Every lane loads its 16-byte vectors of row t once and
-// stores them k times.  Stores are plain (write-back): part of the receive
-// rows is then still in the memory-side cache when the combine reads them,
-// which measured faster for the dispatch -> combine sequence than
-// non-temporal stores.
+// stores them k times.  Stores are plain (write-back) when the combine may
+// read the receive rows as they are (bf16 rows, bf16 combine payload): part
+// of them is then still in the memory-side cache when the combine reads
+// them, which measured faster for the dispatch -> combine sequence than
+// non-temporal stores.  Other format pairs store non-temporal.
 //
 // Batches of at most kFusedPairs pairs (compacted layout) can run as ONE
 // launch that also does the layout: block 0 computes the counts, the
@@ -29,7 +30,7 @@ namespace ep {
 namespace {
 
 #ifndef EP_DISPATCH_NT_STORE
-#define EP_DISPATCH_NT_STORE 0   // non-temporal stores for the receive rows
+#define EP_DISPATCH_NT_STORE 0   // 1: non-temporal stores for every receive row
 #endif
 #ifndef EP_DISPATCH_WAVES
 #define EP_DISPATCH_WAVES 4096   // waves the copy aims for (4 per CU)
@@ -60,6 +61,7 @@ struct CopyArgs {
     int nvec;                 // row_bytes / 16
     int G;                    // fp32 scales per row (0 for bf16 rows)
     int S;                    // waves per token
+    int nt_store;             // non-temporal row stores (see copy_args)
     // single-launch form only: layout outputs (null when not wanted)
     int R, N, epn, epn_shift;
     int32_t *per_rank, *per_expert, *per_node;
@@ -176,8 +178,10 @@ __device__ __forceinline__ int32_t counted_slot(const CopyArgs &a, int64_t t, in
 
 // VPL: 16-byte vectors each lane holds per pass.  FUSED: the single-launch
 // form (block 0 does the layout, the other blocks count their slots).
-// The single-launch form runs one token per block (S waves of 64).
-template <int VPL, bool FUSED>
+// The single-launch form runs one token per block (S waves of 64).  NT:
+// non-temporal row stores (a compile-time choice: a run-time test between
+// the two store kinds is merged by the compiler into plain stores).
+template <int VPL, bool FUSED, bool NT>
 __global__ __launch_bounds__(FUSED ? 1024 : 256) void ep_dispatch_copy_kernel(CopyArgs a) {
     if (FUSED && blockIdx.x == 0) {
         fused_layout_block(a);
@@ -276,7 +280,7 @@ __global__ __launch_bounds__(FUSED ? 1024 : 256) void ep_dispatch_copy_kernel(Co
             for (int i = 0; i < VPL; ++i) {
                 const int v = v0 + i * stride;
                 if (v < a.nvec) {
-                    if (EP_DISPATCH_NT_STORE) st16_nt(dst + (int64_t)v * 16, buf[i]);
+                    if (EP_DISPATCH_NT_STORE || NT) st16_nt(dst + (int64_t)v * 16, buf[i]);
                     else st16(dst + (int64_t)v * 16, buf[i]);
                 }
             }
@@ -326,22 +330,36 @@ CopyArgs copy_args(const Shape &s, const void *x, const float *x_scales, const i
     a.nvec = (int)(a.row_bytes / 16);
     a.G = fp8 ? s.H / 128 : 0;
     a.S = waves_per_token(s.T, a.nvec, EP_DISPATCH_WAVES);
+    // When the combine payload has another format than the dispatched rows
+    // (fp8 rows -> mxfp8, bf16 rows -> nvfp4), the combine never reads the
+    // receive rows: the expert stage re-encodes them.  Their stores then
+    // bypass the memory-side cache instead of filling it with lines the
+    // combine will not read (quant: 128 -> 118 us per step, nvfp4: 165 ->
+    // 158 us).  When the formats match, the combine may read them as they
+    // are, and plain stores leave part of them in that cache.
+    a.nt_store = !(s.x_fmt == 0 && s.y_fmt == 0);
     return a;
+}
+
+template <bool FUSED, bool NT>
+void launch_copy_nt(const CopyArgs &a, const dim3 &grid, const dim3 &block, size_t lds, hipStream_t stream) {
+    const int per_lane = (a.nvec + kWave * a.S - 1) / (kWave * a.S);
+    if (per_lane <= 2) {
+        hipLaunchKernelGGL((ep_dispatch_copy_kernel<2, FUSED, NT>), grid, block, lds, stream, a);
+    } else if (per_lane <= 4) {
+        hipLaunchKernelGGL((ep_dispatch_copy_kernel<4, FUSED, NT>), grid, block, lds, stream, a);
+    } else if (per_lane <= 8 || FUSED) {   // the single-launch form has at most 8 (fused_dispatch_fits)
+        hipLaunchKernelGGL((ep_dispatch_copy_kernel<8, FUSED, NT>), grid, block, lds, stream, a);
+    } else {
+        hipLaunchKernelGGL((ep_dispatch_copy_kernel<16, FUSED, NT>), grid, block, lds, stream, a);
+    }
 }
 
 template <bool FUSED>
 void launch_copy(const CopyArgs &a, int64_t blocks, int threads, size_t lds, hipStream_t stream) {
-    const int per_lane = (a.nvec + kWave * a.S - 1) / (kWave * a.S);
     const dim3 grid((unsigned)blocks), block(threads);
-    if (per_lane <= 2) {
-        hipLaunchKernelGGL((ep_dispatch_copy_kernel<2, FUSED>), grid, block, lds, stream, a);
-    } else if (per_lane <= 4) {
-        hipLaunchKernelGGL((ep_dispatch_copy_kernel<4, FUSED>), grid, block, lds, stream, a);
-    } else if (per_lane <= 8) {
-        hipLaunchKernelGGL((ep_dispatch_copy_kernel<8, FUSED>), grid, block, lds, stream, a);
-    } else {
-        hipLaunchKernelGGL((ep_dispatch_copy_kernel<16, FUSED>), grid, block, lds, stream, a);
-    }
+    if (a.nt_store) launch_copy_nt<FUSED, true>(a, grid, block, lds, stream);
+    else launch_copy_nt<FUSED, false>(a, grid, block, lds, stream);
 }
 
 }  // namespace
