@@ -138,9 +138,11 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="prefill2n")
-    ap.add_argument("--layout", choices=("pairs", "ranks"), default="pairs",
-                    help="receive layout: one row per (token, expert) pair (default), or one row per "
-                         "(token, rank) with per-rank partials (ep_dispatch_ranks / ep_combine_ranks)")
+    ap.add_argument("--layout", choices=("pairs", "rank_major", "ranks"), default="pairs",
+                    help="receive layout: one row per (token, expert) pair at compacted offsets (default); "
+                         "the same rows at fixed per-rank blocks (RANK_MAJOR, capacity = the largest rank's "
+                         "pair count); or one row per (token, rank) with per-rank partials "
+                         "(ep_dispatch_ranks / ep_combine_ranks)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--flush-steps", type=int, default=10,
                     help="also time each call after a 512 MiB cache-evicting copy, over this many steps "
@@ -197,8 +199,8 @@ def main():
     out = measure(args.workload, args.steps, args.warmup, not args.no_graph, args.layout, args.flush_steps)
     inp = out.pop("_inp")
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(dict(inp, rank_rows=args.layout == "ranks"), args.cpu_seconds,
-                                           out["step_algorithmic_bytes"])
+        cfg = dict(inp, rank_rows=args.layout == "ranks", rank_capacity=out["config"]["rank_capacity"])
+        out["cpu_baseline"] = cpu_baseline(cfg, args.cpu_seconds, out["step_algorithmic_bytes"])
     print(json.dumps(out), flush=True)
 
 
@@ -222,9 +224,18 @@ def measure(workload: str, steps: int, warmup: int, graph: bool = False, layout_
     ranks = layout_kind == "ranks"
     if ranks and nv:
         raise ValueError("the (token, rank) path returns bf16 partials; use a bf16-payload workload")
+    M = 0
+    if layout_kind == "rank_major" and (fp8 or nv or inp["expert"] == "scale"):
+        raise ValueError("the workloads' expert stages use the compacted layout; RANK_MAJOR runs bf16 "
+                         "identity workloads (prefill2n, skewed, tiny)")
+    if layout_kind == "rank_major":   # capacity per rank: the largest rank's pair count (nothing dropped)
+        ids = inp["topk_idx"]
+        ok = (ids >= 0) & (ids < E)
+        M = int(np.bincount(ids[ok] // (E // R), minlength=R).max())
     yf = ep.EP_FMT_NVFP4 if nv else (ep.EP_FMT_MXFP8 if (fp8 and not ranks) else ep.EP_FMT_BF16)
     shape = ep.make_shape(T, H, E, R, N, k, ep.EP_FMT_FP8_S128 if fp8 else ep.EP_FMT_BF16, yf,
-                          rank_rows=1 if ranks else 0)
+                          rank_capacity=M, rank_rows=1 if ranks else 0)
+    rows = shape.rows
     ws = ep.Workspace(shape, dev)
 
     # inputs resident in HBM before timing
@@ -267,18 +278,18 @@ def measure(workload: str, steps: int, warmup: int, graph: bool = False, layout_
         def combine():
             ep.ep_combine_ranks(shape, part, trs, y)
     else:
-        recv_x = torch.empty((T * k, H), dtype=xin.dtype, device=dev)
-        recv_s = torch.empty((T * k, H // 128), dtype=torch.float32, device=dev) if fp8 else None
-        src = torch.empty(T * k, dtype=torch.int32, device=dev)
-        rw = torch.empty(T * k, dtype=torch.float32, device=dev)
+        recv_x = torch.empty((rows, H), dtype=xin.dtype, device=dev)
+        recv_s = torch.empty((rows, H // 128), dtype=torch.float32, device=dev) if fp8 else None
+        src = torch.empty(rows, dtype=torch.int32, device=dev)
+        rw = torch.empty(rows, dtype=torch.float32, device=dev)
         slot = torch.empty((T, k), dtype=torch.int32, device=dev)
         off = torch.empty(E + 1, dtype=torch.int32, device=dev)
         if fp8:
-            eo = torch.empty((T * k, H), dtype=torch.uint8, device=dev)
-            eos = torch.empty((T * k, H // 32), dtype=torch.uint8, device=dev)
+            eo = torch.empty((rows, H), dtype=torch.uint8, device=dev)
+            eos = torch.empty((rows, H // 32), dtype=torch.uint8, device=dev)
         elif nv:
-            eo = torch.empty((T * k, H // 2), dtype=torch.uint8, device=dev)
-            eos = torch.empty((T * k, H // 16), dtype=torch.int16, device=dev)
+            eo = torch.empty((rows, H // 2), dtype=torch.uint8, device=dev)
+            eos = torch.empty((rows, H // 16), dtype=torch.int16, device=dev)
         elif inp["expert"] == "scale":
             eo, eos = torch.empty_like(recv_x), None
         else:
@@ -306,7 +317,7 @@ def measure(workload: str, steps: int, warmup: int, graph: bool = False, layout_
     # and combine: it runs in warmup (its output does not change from step to
     # step, the inputs being the same) and stays out of the timed step
     phases = [("layout", layout), ("dispatch", dispatch), ("combine", combine)]
-    single_launch = not ranks and T * k <= SINGLE_LAUNCH_PAIRS
+    single_launch = not ranks and M == 0 and T * k <= SINGLE_LAUNCH_PAIRS
     if single_launch:   # the library runs layout + dispatch of such a batch as one kernel
         phases = [("layout+dispatch", layout_dispatch), ("combine", combine)]
 
@@ -448,8 +459,9 @@ def measure(workload: str, steps: int, warmup: int, graph: bool = False, layout_
         "config": {"workload": workload, "tokens": T, "hidden": H, "experts": E, "virtual_ranks": R,
                    "virtual_nodes": N, "topk": k, "routing": inp["routing"], "expert": inp["expert"],
                    "x_format": inp["x_fmt"], "valid_pairs": V,
-                   "receive_layout": "(token, rank) rows" if ranks else "(token, expert) rows",
-                   "receive_rows": int(acc["nvl_tokens"]) if ranks else V},
+                   "receive_layout": "(token, rank) rows" if ranks else
+                   ("(token, expert) rows, RANK_MAJOR" if M else "(token, expert) rows"),
+                   "rank_capacity": M, "receive_rows": int(acc["nvl_tokens"]) if ranks else V},
         "tokens_per_s": round(T / step_s, 1),
         "phase_us": {p: round(v, 2) for p, v in phase_us.items()},
         "phase_us_flushed": None if phase_us_flushed is None else
