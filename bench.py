@@ -13,7 +13,7 @@ phase_us_flushed repeats the calls each after a 512 MiB copy that evicts the
 memory-side cache (cold-cache durations).  The workloads'
 expert stage (identity, per-expert scaling, or fp8 -> mxfp8 re-encoding)
 runs during warmup and is not part of the timed step.  A batch of at most
-1024 (token, slot) pairs is laid out and dispatched by one
+2048 (token, slot) pairs is laid out and dispatched by one
 ep_dispatch_with_layout call, which the library runs as a single launch
 (phases "layout+dispatch", "combine").  With --layout ranks
 the step is the (token, rank) path: ep_dispatch_layout (planning one row per
@@ -44,7 +44,7 @@ METRIC = "dispatch+combine HBM GB/s and tokens/s at T=4096,H=7168,E=256,top-8"
 HBM_PEAK_GBS = 8000.0   # MI355X HBM3E, published peak
 
 GRAPH_STEPS = 10   # steps captured per HIP graph
-SINGLE_LAUNCH_PAIRS = 1024   # batches the library lays out and dispatches in one launch
+SINGLE_LAUNCH_PAIRS = 2048   # batches the library lays out and dispatches in one launch
 FLUSH_BYTES = 512 << 20      # copy that evicts the 256 MB memory-side cache
 PROFILES = os.path.join(ROOT, "profiles")
 
@@ -298,7 +298,7 @@ def measure(workload: str, steps: int, warmup: int, graph: bool = False, layout_
         def dispatch():   # reuses the plan the layout call of this step left in the workspace
             ep.ep_dispatch(shape, xin, xs, idx, w, recv_x, recv_s, src, rw, slot, off, ws, from_layout=True)
 
-        def layout_dispatch():   # one call; a single launch for batches of <= 1024 pairs
+        def layout_dispatch():   # one call; a single launch for batches of <= 2048 pairs
             ep.ep_dispatch_with_layout(shape, xin, xs, idx, w, lay["r"], lay["e"], lay["m"], lay["n"], lay["a"],
                                        recv_x, recv_s, src, rw, slot, off, ws)
 

@@ -17,7 +17,7 @@
 // them, which measured faster for the dispatch -> combine sequence than
 // non-temporal stores.  Other format pairs store non-temporal.
 //
-// Batches of at most kFusedPairs pairs (compacted layout) can run as ONE
+// Batches of at most kFusedPairs (2048) pairs (compacted layout) can run as ONE
 // launch that also does the layout: block 0 computes the counts, the
 // token-in-rank map and the segment starts (the handle) while every other
 // wave finds its token's slots by counting, over all pairs of the batch,
@@ -69,8 +69,7 @@ struct CopyArgs {
     int64_t *algo;
 };
 
-constexpr int kFusedPairs = 1024;               // pairs a single-launch batch may hold
-constexpr int kFusedKeys = kFusedPairs / kWave; // pair ids each lane keeps in registers
+constexpr int kFusedPairs = 2048;   // pairs a single-launch batch may hold (32 ids per lane)
 
 // Layout of a single-launch batch, by one block of 256 threads: staged ids,
 // per-expert counts (LDS integer adds, order-independent), their exclusive
@@ -138,22 +137,23 @@ __device__ void fused_layout_block(const CopyArgs &a) {
 
 // Slot of pair (t, j) held by lane j < k, by counting: the valid pairs whose
 // expert sorts before e_j, plus the pairs of e_j earlier in row-major (t, j)
-// order.  Each lane keeps kFusedKeys pair ids in registers; the counts are
+// order.  Each lane keeps KEYS pair ids in registers (KEYS * 64 >= T * k); the counts are
 // ballots.  The token's S waves share the work (wave `sub` counts slots j =
 // sub, sub + S, ...) and exchange the results through LDS: one token per
 // block, every thread of the block calls this.
+template <int KEYS>
 __device__ __forceinline__ int32_t counted_slot(const CopyArgs &a, int64_t t, int lane, int sub) {
     __shared__ int32_t slot_sm[32];
     const int TK = (int)(a.T * a.k);
     // every load unconditional (clamped index) so all of them are in flight
     // together; lanes past the batch then drop their value
     const int64_t own = a.topk_idx[t * a.k + min(lane, a.k - 1)];   // lane j < k: slot j's id
-    int64_t raw[kFusedKeys];
+    int64_t raw[KEYS];
 #pragma unroll
-    for (int i = 0; i < kFusedKeys; ++i) raw[i] = a.topk_idx[min(lane + kWave * i, TK - 1)];
-    int32_t key[kFusedKeys];   // masked / invalid ids sort after every expert
+    for (int i = 0; i < KEYS; ++i) raw[i] = a.topk_idx[min(lane + kWave * i, TK - 1)];
+    int32_t key[KEYS];   // masked / invalid ids sort after every expert
 #pragma unroll
-    for (int i = 0; i < kFusedKeys; ++i) {
+    for (int i = 0; i < KEYS; ++i) {
         const bool ok = lane + kWave * i < TK && raw[i] >= 0 && raw[i] < a.E;
         key[i] = ok ? (int32_t)raw[i] : 0x7FFFFFFF;
     }
@@ -165,7 +165,7 @@ __device__ __forceinline__ int32_t counted_slot(const CopyArgs &a, int64_t t, in
             const int p = (int)(t * a.k + j);
             c = 0;
 #pragma unroll
-            for (int i = 0; i < kFusedKeys; ++i) {
+            for (int i = 0; i < KEYS; ++i) {
                 const int q = lane + kWave * i;
                 c += (int32_t)__popcll(__ballot(key[i] < e || (key[i] == e && q < p)));
             }
@@ -176,13 +176,15 @@ __device__ __forceinline__ int32_t counted_slot(const CopyArgs &a, int64_t t, in
     return lane < a.k ? slot_sm[lane] : -1;
 }
 
-// VPL: 16-byte vectors each lane holds per pass.  FUSED: the single-launch
-// form (block 0 does the layout, the other blocks count their slots).
+// VPL: 16-byte vectors each lane holds per pass.  KEYS > 0: the single-launch
+// form (block 0 does the layout, the other blocks count their slots over
+// KEYS pair ids per lane); KEYS == 0: slots from the plan.
 // The single-launch form runs one token per block (S waves of 64).  NT:
 // non-temporal row stores (a compile-time choice: a run-time test between
 // the two store kinds is merged by the compiler into plain stores).
-template <int VPL, bool FUSED, bool NT>
-__global__ __launch_bounds__(FUSED ? 1024 : 256) void ep_dispatch_copy_kernel(CopyArgs a) {
+template <int VPL, int KEYS, bool NT>
+__global__ __launch_bounds__(KEYS ? 1024 : 256) void ep_dispatch_copy_kernel(CopyArgs a) {
+    constexpr bool FUSED = KEYS > 0;
     if (FUSED && blockIdx.x == 0) {
         fused_layout_block(a);
         return;
@@ -221,7 +223,7 @@ __global__ __launch_bounds__(FUSED ? 1024 : 256) void ep_dispatch_copy_kernel(Co
     if (g_first < a.G) sc0 = a.x_scales[t * a.G + g_first];
 
     // lanes 0..k-1: the token's slots
-    int32_t slot = FUSED ? counted_slot(a, t, lane, sub) : -1;
+    int32_t slot = FUSED ? counted_slot<(KEYS > 0 ? KEYS : 1)>(a, t, lane, sub) : -1;
     if (lane < a.k) {
         const int64_t p = t * a.k + lane;
         const int32_t lr = FUSED ? -1 : a.local_rank[p];
@@ -341,25 +343,25 @@ CopyArgs copy_args(const Shape &s, const void *x, const float *x_scales, const i
     return a;
 }
 
-template <bool FUSED, bool NT>
+template <int KEYS, bool NT>
 void launch_copy_nt(const CopyArgs &a, const dim3 &grid, const dim3 &block, size_t lds, hipStream_t stream) {
     const int per_lane = (a.nvec + kWave * a.S - 1) / (kWave * a.S);
     if (per_lane <= 2) {
-        hipLaunchKernelGGL((ep_dispatch_copy_kernel<2, FUSED, NT>), grid, block, lds, stream, a);
+        hipLaunchKernelGGL((ep_dispatch_copy_kernel<2, KEYS, NT>), grid, block, lds, stream, a);
     } else if (per_lane <= 4) {
-        hipLaunchKernelGGL((ep_dispatch_copy_kernel<4, FUSED, NT>), grid, block, lds, stream, a);
-    } else if (per_lane <= 8 || FUSED) {   // the single-launch form has at most 8 (fused_dispatch_fits)
-        hipLaunchKernelGGL((ep_dispatch_copy_kernel<8, FUSED, NT>), grid, block, lds, stream, a);
+        hipLaunchKernelGGL((ep_dispatch_copy_kernel<4, KEYS, NT>), grid, block, lds, stream, a);
+    } else if (per_lane <= 8 || KEYS) {   // the single-launch form has at most 8 (fused_dispatch_fits)
+        hipLaunchKernelGGL((ep_dispatch_copy_kernel<8, KEYS, NT>), grid, block, lds, stream, a);
     } else {
-        hipLaunchKernelGGL((ep_dispatch_copy_kernel<16, FUSED, NT>), grid, block, lds, stream, a);
+        hipLaunchKernelGGL((ep_dispatch_copy_kernel<16, KEYS, NT>), grid, block, lds, stream, a);
     }
 }
 
-template <bool FUSED>
+template <int KEYS>
 void launch_copy(const CopyArgs &a, int64_t blocks, int threads, size_t lds, hipStream_t stream) {
     const dim3 grid((unsigned)blocks), block(threads);
-    if (a.nt_store) launch_copy_nt<FUSED, true>(a, grid, block, lds, stream);
-    else launch_copy_nt<FUSED, false>(a, grid, block, lds, stream);
+    if (a.nt_store) launch_copy_nt<KEYS, true>(a, grid, block, lds, stream);
+    else launch_copy_nt<KEYS, false>(a, grid, block, lds, stream);
 }
 
 }  // namespace
@@ -378,7 +380,7 @@ hipError_t launch_dispatch_copy(const Shape &s, const WsLayout &L, const void *x
     a.TT = L.tile_tokens;
     int64_t blocks = (s.T * a.S + 3) / 4;
     if (blocks * 256 < s.E + 1) blocks = (s.E + 1 + 255) / 256;   // threads to copy expert_offset
-    launch_copy<false>(a, blocks, 256, 0, stream);
+    launch_copy<0>(a, blocks, 256, 0, stream);
     return hipGetLastError();
 }
 
@@ -416,7 +418,8 @@ hipError_t launch_dispatch_fused(const Shape &s, const void *x, const float *x_s
     a.S = fused_waves(s, a.nvec);
     const int threads = kWave * a.S;
     const size_t lds = sizeof(int32_t) * ((size_t)s.T * s.k + s.E + s.R + s.N + threads / kWave + 1);
-    launch_copy<true>(a, 1 + s.T, threads, lds, stream);
+    if (s.T * s.k <= 16 * kWave) launch_copy<16>(a, 1 + s.T, threads, lds, stream);
+    else launch_copy<32>(a, 1 + s.T, threads, lds, stream);
     return hipGetLastError();
 }
 

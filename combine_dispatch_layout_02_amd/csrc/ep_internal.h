@@ -61,7 +61,7 @@ hipError_t launch_dispatch_copy(const Shape &s, const WsLayout &L, const void *x
                                 int32_t *recv_src_idx, float *recv_topk_w, int32_t *token_slot,
                                 int32_t *expert_offset, char *ws, hipStream_t stream);
 
-// Single-launch layout + dispatch (compacted layout, T * k <= 1024 pairs):
+// Single-launch layout + dispatch (compacted layout, T * k <= 2048 pairs):
 // fused_dispatch_fits tells whether a shape qualifies.  Layout outputs may be
 // null (all together); the workspace plan is neither read nor written.
 bool fused_dispatch_fits(const Shape &s);

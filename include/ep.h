@@ -189,7 +189,7 @@ int ep_dispatch(const ep_shape *shape, const void *x, const float *x_scales,
 /*
  * Layout and dispatch in one call: the outputs of ep_dispatch_layout and of
  * ep_dispatch together ([PR860] Scope: get_dispatch_layout followed by
- * dispatch).  A small batch -- T * k <= 1024 pairs, compacted layout
+ * dispatch).  A small batch -- T * k <= 2048 pairs, compacted layout
  * (rank_capacity 0), rank_rows 0 -- runs as ONE kernel launch: one block
  * computes the layout counts and the segment starts while every other wave
  * finds its token's slots by counting the pairs that sort before them (the

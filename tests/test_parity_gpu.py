@@ -230,12 +230,15 @@ def test_nvfp4_combine_every_code_and_scale_kind():
     np.testing.assert_array_equal(gpu_path.bf16_bits(y), ref)
 
 
-# single-launch layout + dispatch: batches of at most 1024 (token, slot) pairs
+# single-launch layout + dispatch: batches of at most 2048 (token, slot) pairs
+# (16 pair ids per lane up to 1024 pairs, 32 beyond)
 @pytest.mark.parametrize("kw", [
     dict(T=1), dict(T=5), dict(T=64), dict(T=127), dict(T=128), dict(T=128, mask_frac=0.3),
     dict(T=128, mask_frac=0.3, mask_tokens=0.2), dict(T=100, routing="replace"), dict(T=32, k=32, E=4096, R=64, N=64),
     dict(T=1024, k=1), dict(T=64, k=16, routing="replace", mask_frac=0.2), dict(T=128, H=8),
-    dict(T=129)])   # 1032 pairs: the multi-launch path through the same call
+    dict(T=129), dict(T=200, mask_frac=0.2), dict(T=256), dict(T=2048, k=1), dict(T=64, k=32, E=4096, R=64, N=64),
+    dict(T=256, routing="replace", H=8),
+    dict(T=257)])   # 2056 pairs: the multi-launch path through the same call
 def test_with_layout_small_batches(kw):
     kw = dict(kw)
     base = dict(H=kw.pop("H", 1024))
