@@ -162,8 +162,9 @@ def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(json.dumps({"error": "this build measures one GPU's share of the exchange; "
-                                   "runs on more than one GPU are not part of it (use --gpus 1)"}))
+        print(json.dumps({"error": "bench.py measures one GPU's share of the exchange (destinations are "
+                                   "regions of one GPU's memory); runs on more than one GPU are not "
+                                   "supported (use --gpus 1)"}))
         sys.exit(2)
 
     import torch
@@ -367,8 +368,11 @@ def measure(workload: str, steps: int, warmup: int, graph: bool = False, layout_
     # median over the steps: a host-side submission stall (e.g. a pause of the
     # interpreter) leaves the GPU idle between two events and inflates one
     # sample; the median keeps the kernel's own duration
-    phase_us = {name: 1000.0 * statistics.median(hev.ms(ev[s][i], ev[s][i + 1]) for s in range(steps))
-                for i, (name, _) in enumerate(phases)}
+    samples = {name: sorted(1000.0 * hev.ms(ev[s][i], ev[s][i + 1]) for s in range(steps))
+               for i, (name, _) in enumerate(phases)}
+    phase_us = {name: statistics.median(v) for name, v in samples.items()}
+    phase_stats = {name: {"min": round(v[0], 2), "p90": round(v[min(len(v) - 1, int(0.9 * len(v)))], 2)}
+                   for name, v in samples.items()}
     for e in ev:
         hev.destroy(e)
 
@@ -464,6 +468,7 @@ def measure(workload: str, steps: int, warmup: int, graph: bool = False, layout_
                    "rank_capacity": M, "receive_rows": int(acc["nvl_tokens"]) if ranks else V},
         "tokens_per_s": round(T / step_s, 1),
         "phase_us": {p: round(v, 2) for p, v in phase_us.items()},
+        "phase_us_min_p90": phase_stats,
         "phase_us_flushed": None if phase_us_flushed is None else
         {p: round(v, 2) for p, v in phase_us_flushed.items()},
         "step_algorithmic_bytes": int(step_bytes),
@@ -485,7 +490,8 @@ def measure(workload: str, steps: int, warmup: int, graph: bool = False, layout_
 def cpu_baseline(inp, seconds, step_bytes):
     """The CPU oracle as it stands (plain C, one thread) on the same workload:
     whole passes (layout, slots, dispatch rows, expert stage, combine) repeated
-    until `seconds` of CPU work, at least one pass."""
+    until `seconds` of CPU work, at least one pass; then one more pass timed
+    part by part (layout, slots + dispatch rows, combine)."""
     import oracle
 
     reps, t_start = 0, time.perf_counter()
@@ -495,8 +501,20 @@ def cpu_baseline(inp, seconds, step_bytes):
         if time.perf_counter() - t_start >= seconds:
             break
     dt = (time.perf_counter() - t_start) / reps
+    parts = {}
+    if not inp.get("rank_rows") and inp.get("x_fmt", "bf16") == "bf16" and inp.get("y_fmt", "bf16") == "bf16":
+        idx, w = inp["topk_idx"], inp["topk_w"]
+        t0 = time.perf_counter()
+        oracle.layout(idx, inp["E"], inp["R"], inp["N"])
+        t1 = time.perf_counter()
+        sl = oracle.slots(idx, w, inp["E"])
+        recv = oracle.dispatch_rows(inp["x"], sl["token_slot"])
+        t2 = time.perf_counter()
+        oracle.combine_bf16(recv, sl["token_slot"], w)
+        t3 = time.perf_counter()
+        parts = {"layout_s": round(t1 - t0, 4), "slots_dispatch_s": round(t2 - t1, 4), "combine_s": round(t3 - t2, 4)}
     return {"value": round(inp["T"] / dt, 1), "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "gbs": round(step_bytes / dt / 1e9, 3),
+            "gbs": round(step_bytes / dt / 1e9, 3), "parts": parts,
             "sample": f"{reps} full passes of workload {inp['name']} (T={inp['T']}), {dt:.3f} s per pass"}
 
 
