@@ -23,6 +23,9 @@ ep_expert_reduce_ranks (the weighted per-rank partials) as the expert stage.
 Prints one JSON line:
   value         algorithmic HBM bytes of the step / step time (GB/s)
   tokens_per_s  tokens of the batch / step time
+  dispatch_combine_gbs  the dispatch and combine calls' algorithmic bytes / their
+                summed per-call durations (the layout pass left out)
+  rel_l2_vs_fp32  relative L2 distance of y from the unquantized fp32 result
   roofline      the longest-running call against the 8 TB/s HBM peak, with
                 hardware byte counts when they were measured for this kernel
   cpu_baseline  the CPU oracle (single thread) on the same workload
@@ -426,6 +429,22 @@ def measure(workload: str, steps: int, warmup: int, graph: bool = False, layout_
             raise RuntimeError("graph replays differ from the eager step")
     ms_step = graph_ms if graph_ms is not None else eager_ms
 
+    # accuracy of the step's y against the unquantized fp32 result, computed
+    # in float64 from the inputs: sum over valid slots of w * s_e * x (s_e = 1
+    # for the identity expert)
+    xf = x.double()
+    y32 = torch.zeros_like(xf)
+    fac = factor.double() if (factor is not None and inp["expert"] == "scale") else None
+    for j in range(k):
+        e = idx[:, j]
+        ok = (e >= 0) & (e < E)
+        wj = torch.where(ok, w[:, j].double(), torch.zeros_like(w[:, j], dtype=torch.float64))
+        if fac is not None:
+            wj = wj * fac[torch.where(ok, e, torch.zeros_like(e))]
+        y32 += wj[:, None] * xf
+    rel_l2 = float(torch.linalg.vector_norm(y.double() - y32) / torch.linalg.vector_norm(y32).clamp_min(1e-300))
+    del xf, y32
+
     # algorithmic bytes (library accounting on host copies of the layout)
     acc = ep.ep_accounting(shape, 0, lay["r"].cpu().numpy(), lay["n"].cpu().numpy(), int(lay["a"].item()), V)
     if ranks:
@@ -467,6 +486,9 @@ def measure(workload: str, steps: int, warmup: int, graph: bool = False, layout_
                    ("(token, expert) rows, RANK_MAJOR" if M else "(token, expert) rows"),
                    "rank_capacity": M, "receive_rows": int(acc["nvl_tokens"]) if ranks else V},
         "tokens_per_s": round(T / step_s, 1),
+        "dispatch_combine_gbs": round(sum(algo_bytes[p] for p in algo_bytes if p != "layout")
+                                      / (sum(phase_us[p] for p in phase_us if p != "layout") * 1e-6) / 1e9, 1),
+        "rel_l2_vs_fp32": round(rel_l2, 6),
         "phase_us": {p: round(v, 2) for p, v in phase_us.items()},
         "phase_us_min_p90": phase_stats,
         "phase_us_flushed": None if phase_us_flushed is None else
