@@ -27,7 +27,8 @@ Prints one JSON line:
                 summed per-call durations (the layout pass left out)
   rel_l2_vs_fp32  relative L2 distance of y from the unquantized fp32 result
   roofline      the longest-running call against the 8 TB/s HBM peak, with
-                hardware byte counts when they were measured for this kernel
+                hardware byte counts when they were measured for this kernel,
+                and against a plain 1 GiB device copy timed in the same run
   cpu_baseline  the CPU oracle (single thread) on the same workload
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--layout pairs|ranks]
 """
@@ -49,6 +50,7 @@ HBM_PEAK_GBS = 8000.0   # MI355X HBM3E, published peak
 GRAPH_STEPS = 10   # steps captured per HIP graph
 SINGLE_LAUNCH_PAIRS = 2048   # batches the library lays out and dispatches in one launch
 FLUSH_BYTES = 512 << 20      # copy that evicts the 256 MB memory-side cache
+COPY_REF_BYTES = 1 << 30     # plain copy timed as the box's streaming reference
 PROFILES = os.path.join(ROOT, "profiles")
 
 
@@ -429,6 +431,22 @@ def measure(workload: str, steps: int, warmup: int, graph: bool = False, layout_
             raise RuntimeError("graph replays differ from the eager step")
     ms_step = graph_ms if graph_ms is not None else eager_ms
 
+    # the same box's plain device copy (1 GiB read + 1 GiB written), as a
+    # measured streaming reference next to the published peak
+    cp_src = torch.empty(COPY_REF_BYTES, dtype=torch.uint8, device=dev)
+    cp_dst = torch.empty(COPY_REF_BYTES, dtype=torch.uint8, device=dev)
+    ep.ep_calib_copy(cp_src, cp_dst, COPY_REF_BYTES)
+    c0, c1 = hev.create(2)
+    torch.cuda.synchronize()
+    hev.record(c0, stream)
+    for _ in range(5):
+        ep.ep_calib_copy(cp_src, cp_dst, COPY_REF_BYTES)
+    hev.record(c1, stream)
+    torch.cuda.synchronize()
+    copy_gbs = 2 * COPY_REF_BYTES * 5 / (hev.ms(c0, c1) * 1e-3) / 1e9
+    hev.destroy([c0, c1])
+    del cp_src, cp_dst
+
     # accuracy of the step's y against the unquantized fp32 result, computed
     # in float64 from the inputs: sum over valid slots of w * s_e * x (s_e = 1
     # for the identity expert)
@@ -498,7 +516,8 @@ def measure(workload: str, steps: int, warmup: int, graph: bool = False, layout_
         "timing": ("steps replayed from a HIP graph of %d steps" % G) if graph_ms is not None else "eager",
         "roofline": {"bound": "hbm", "kernel": kernels[dom], "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": traffic, "algorithmic_bytes_per_launch": int(algo_bytes[dom])},
+                     "traffic": traffic, "algorithmic_bytes_per_launch": int(algo_bytes[dom]),
+                     "measured_copy_gbs": round(copy_gbs, 1), "frac_of_copy": round(achieved / copy_gbs, 4)},
         "pages_accounting": {"rdma_algo_tokens": acc["rdma_algo_tokens"],
                              "rdma_physical_tokens": acc["rdma_physical_tokens"],
                              "nvl_tokens": acc["nvl_tokens"],
