@@ -55,16 +55,20 @@ PROFILES = os.path.join(ROOT, "profiles")
 
 
 def kernel_source_hash() -> str:
-    """sha256 over the HIP sources and headers of the library."""
-    import glob
+    """sha256 over the code of the step's kernels (layout, dispatch, combine,
+    both receive layouts) and their device headers, with comments and
+    whitespace removed: an edit that changes no code keeps the hash."""
     import hashlib
+    import re
 
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "combine_dispatch_layout_02_amd", "csrc")
-    for path in sorted(glob.glob(os.path.join(csrc, "*.hip")) + glob.glob(os.path.join(csrc, "*.h"))
-                       + [os.path.join(ROOT, "include", "ep.h")]):
-        h.update(os.path.basename(path).encode())
-        h.update(open(path, "rb").read())
+    for name in ("plan.hip", "dispatch.hip", "combine.hip", "ranks.hip", "ep_device.h", "ep_internal.h"):
+        text = open(os.path.join(csrc, name)).read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(name.encode())
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()
 
 

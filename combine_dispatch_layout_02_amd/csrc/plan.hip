@@ -26,10 +26,15 @@
 //        64-bit masks in registers (a repeated rank / node is a no-op), the
 //        token-in-rank row is written from the rank mask, and per-rank /
 //        per-node counts are wavefront ballots of one mask bit plus popcount.
-//  ep_plan_scan_kernel   one block: per expert the exclusive prefix of the
-//      tile counts over tiles (in place) and the total; the exclusive scan of
-//      the totals over experts (segment starts); per rank / node the sum over
-//      tiles.  Integer sums only: the plan and the counts are deterministic.
+//      - (token, rank) rows, when planned: the token's place among the
+//        tile's tokens of each rank it reaches = its place in its wave (the
+//        ballot again) plus the earlier waves' counts (an LDS prefix).
+//  ep_plan_scan_kernel   one block: per expert (and per rank, when (token,
+//      rank) rows are planned) the exclusive prefix of the tile counts over
+//      tiles (in place) and the total; the exclusive scan of the expert totals
+//      (segment starts) and of the rank totals (region starts); per rank /
+//      node the sum over tiles.  Integer sums only: the plan and the counts
+//      are deterministic.
 //  A batch that fits one tile (T * k <= 1024 pairs at E <= 384) is planned by
 //  the count kernel alone: its block holds every count and scans them in LDS.
 #include "ep_device.h"

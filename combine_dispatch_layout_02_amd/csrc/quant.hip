@@ -181,6 +181,11 @@ __global__ __launch_bounds__(256) void ep_fill_zero_kernel(uint32_t *p, size_t w
         p[i] = 0u;
 }
 
+#ifndef EP_CALIB_BLOCKS
+#define EP_CALIB_BLOCKS 1024
+#endif
+
+// Plain streaming copy: consecutive 16-byte vectors across the grid.
 __global__ __launch_bounds__(256) void ep_calib_copy_kernel(const vec16 *src, vec16 *dst, size_t n) {
     for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
          i += (size_t)gridDim.x * blockDim.x)
@@ -246,7 +251,7 @@ hipError_t launch_calib_copy(const void *src, void *dst, size_t bytes, hipStream
     const size_t n = bytes / 16;
     if (n == 0) return hipSuccess;
     size_t blocks = (n + 255) / 256;
-    if (blocks > 8192) blocks = 8192;
+    if (blocks > EP_CALIB_BLOCKS) blocks = EP_CALIB_BLOCKS;   // 4 blocks per CU measured fastest
     hipLaunchKernelGGL(ep_calib_copy_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
                        static_cast<const vec16 *>(src), static_cast<vec16 *>(dst), n);
     return hipGetLastError();
