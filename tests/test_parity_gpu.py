@@ -271,3 +271,18 @@ def test_with_layout_flags_invalid_ids():
     with pytest.raises(RuntimeError, match="flags 0x1"):
         g["ws"].check()
     assert gpu_path.compare(g, oracle.run_path(inp), False) == 0
+
+
+@pytest.mark.parametrize("kw", [dict(T=20000, H=64, E=256, R=16, N=2, k=8),      # 157 plan tiles
+                                dict(T=40000, H=8, E=64, R=8, N=2, k=4, mask_frac=0.1),
+                                dict(T=3000, H=64, E=4096, R=64, N=8, k=32)])   # tiles of 2 tokens
+def test_many_plan_tiles(kw):
+    """Batches with more plan tiles than the scan keeps in registers (its
+    loop form), and tiny tiles at E = 4096."""
+    inp = W.make_inputs("tiny", **kw)
+    for from_layout in (True, False):
+        _, _, ndiff = _run_both(inp, from_layout)
+        assert ndiff == 0
+    import gpu_path
+    g = gpu_path.run_ranks(inp)
+    assert gpu_path.compare_ranks(g, oracle.run_path(dict(inp, rank_rows=True)), False) == 0
