@@ -287,7 +287,7 @@ hipError_t launch_combine(const Shape &s, const void *expert_out, const uint8_t 
                           const int32_t *token_slot, const float *topk_w, void *y,
                           hipStream_t stream) {
     if (s.T == 0) return hipSuccess;
-    CombineArgs a;
+    CombineArgs a{};
     a.eo = static_cast<const char *>(expert_out);
     a.eo_scales = expert_scales;
     a.token_slot = token_slot;

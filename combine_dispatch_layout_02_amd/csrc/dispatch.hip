@@ -17,6 +17,10 @@
 // them, which measured faster for the dispatch -> combine sequence than
 // non-temporal stores.  Other format pairs store non-temporal.
 //
+// The cached form (ep_dispatch_cached) takes the slots from a previous
+// dispatch's handle instead of a plan: the same rows, for another tensor of
+// the same tokens, with no layout work and no metadata writes.
+//
 // Batches of at most kFusedPairs (2048) pairs (compacted layout) can run as ONE
 // launch that also does the layout: block 0 computes the counts, the
 // token-in-rank map and the segment starts (the handle) while every other
@@ -50,6 +54,7 @@ struct CopyArgs {
     int32_t *expert_offset;       // [E + 1] handle copy of plan_offset
     const int32_t *tile_prefix;   // [ntiles][E + R + N] (expert columns first)
     const int32_t *local_rank;    // [T*k]
+    const int32_t *slots_in;      // [T*k] a previous dispatch's token_slot (cached form), else null
     uint32_t *ctrl;               // error word
     int64_t T;
     int k, E, TT;             // TT: tokens per plan tile
@@ -200,7 +205,7 @@ __global__ __launch_bounds__(KEYS ? 1024 : 256) void ep_dispatch_copy_kernel(Cop
         t = gw / a.S;
         sub = (int)(gw - t * a.S);
         const int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-        if (g <= a.E) a.expert_offset[g] = a.plan_offset[g];   // handle copy of the segment starts
+        if (!a.slots_in && g <= a.E) a.expert_offset[g] = a.plan_offset[g];   // handle copy of the segment starts
     }
     if (t >= a.T) return;   // wave-uniform (never taken in the single-launch form)
 
@@ -226,7 +231,11 @@ __global__ __launch_bounds__(KEYS ? 1024 : 256) void ep_dispatch_copy_kernel(Cop
     int32_t slot = FUSED ? counted_slot<(KEYS > 0 ? KEYS : 1)>(a, t, lane, sub) : -1;
     if (lane < a.k) {
         const int64_t p = t * a.k + lane;
-        const int32_t lr = FUSED ? -1 : a.local_rank[p];
+        if (!FUSED && a.slots_in) {   // cached: the slots of a previous dispatch's handle
+            slot = a.slots_in[p];
+            if ((uint64_t)slot >= (uint64_t)a.rows) slot = -1;   // masked, or not a receive row
+        }
+        const int32_t lr = (FUSED || a.slots_in) ? -1 : a.local_rank[p];
         if (lr >= 0) {
             const int e = (int)a.topk_idx[p];
             slot = a.plan_offset[e] + a.tile_prefix[(t / a.TT) * a.cols + e] + lr;
@@ -245,7 +254,7 @@ __global__ __launch_bounds__(KEYS ? 1024 : 256) void ep_dispatch_copy_kernel(Cop
             atomicOr(&a.ctrl[0], kErrBadSlot);
             slot = -1;
         }
-        if (sub == 0) {
+        if (sub == 0 && !a.slots_in) {
             a.token_slot[p] = slot;
             if (slot >= 0) {
                 a.recv_src_idx[slot] = (int32_t)t;
@@ -391,6 +400,17 @@ int fused_waves(const Shape &s, int nvec) {
     const int want = s.k < 16 ? s.k : 16;
     while (S < want) S *= 2;
     return S > 16 ? 16 : S;
+}
+
+hipError_t launch_dispatch_cached(const Shape &s, const void *x, const float *x_scales,
+                                  const int32_t *token_slot, void *recv_x, float *recv_x_scales,
+                                  hipStream_t stream) {
+    CopyArgs a = copy_args(s, x, x_scales, nullptr, nullptr, recv_x, recv_x_scales, nullptr, nullptr,
+                           nullptr, nullptr);
+    a.slots_in = token_slot;
+    const int64_t blocks = (s.T * a.S + 3) / 4;
+    if (blocks > 0) launch_copy<0>(a, blocks, 256, 0, stream);
+    return hipGetLastError();
 }
 
 bool fused_dispatch_fits(const Shape &s) {

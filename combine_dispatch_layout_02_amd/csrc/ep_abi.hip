@@ -320,6 +320,36 @@ int ep_combine_ranks(const ep_shape *shape, const uint16_t *partial,
                                                static_cast<hipStream_t>(stream)));
 }
 
+int ep_dispatch_cached(const ep_shape *shape, const void *x, const float *x_scales,
+                       const int32_t *token_slot, void *recv_x, float *recv_x_scales, void *stream) {
+    Shape s;
+    int rc = check_shape(shape, &s);
+    if (rc != EP_OK) return rc;
+    if (s.T == 0) return EP_OK;
+    if (!x || !token_slot || !recv_x) return EP_EINVAL;
+    const bool fp8 = s.x_fmt == EP_FMT_FP8_S128;
+    if (fp8 != (x_scales != nullptr) || fp8 != (recv_x_scales != nullptr)) return EP_EINVAL;
+    if (!aligned16(x) || !aligned16(recv_x)) return EP_EALIGN;
+    return hip_status(ep::launch_dispatch_cached(s, x, x_scales, token_slot, recv_x, recv_x_scales,
+                                                 static_cast<hipStream_t>(stream)));
+}
+
+int ep_dispatch_ranks_cached(const ep_shape *shape, const void *x, const float *x_scales,
+                             const int32_t *token_rank_slot, void *recv_x, float *recv_x_scales,
+                             void *stream) {
+    Shape s;
+    int rc = check_shape(shape, &s);
+    if (rc != EP_OK) return rc;
+    if (!s.rank_rows) return EP_EINVAL;
+    if (s.T == 0) return EP_OK;
+    if (!x || !token_rank_slot || !recv_x) return EP_EINVAL;
+    const bool fp8 = s.x_fmt == EP_FMT_FP8_S128;
+    if (fp8 != (x_scales != nullptr) || fp8 != (recv_x_scales != nullptr)) return EP_EINVAL;
+    if (!aligned16(x) || !aligned16(recv_x)) return EP_EALIGN;
+    return hip_status(ep::launch_dispatch_ranks_cached(s, x, x_scales, token_rank_slot, recv_x, recv_x_scales,
+                                                       static_cast<hipStream_t>(stream)));
+}
+
 int ep_check(void *ws, size_t ws_bytes, void *stream, uint32_t *flags) {
     if (!ws || ws_bytes < 256) return EP_EINVAL;
     hipStream_t st = static_cast<hipStream_t>(stream);

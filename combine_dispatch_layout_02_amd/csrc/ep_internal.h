@@ -61,6 +61,15 @@ hipError_t launch_dispatch_copy(const Shape &s, const WsLayout &L, const void *x
                                 int32_t *recv_src_idx, float *recv_topk_w, int32_t *token_slot,
                                 int32_t *expert_offset, char *ws, hipStream_t stream);
 
+// Cached dispatch: rows placed by a previous dispatch's handle (token_slot
+// [T][k], or token_rank_slot [T][R] for (token, rank) rows).
+hipError_t launch_dispatch_cached(const Shape &s, const void *x, const float *x_scales,
+                                  const int32_t *token_slot, void *recv_x, float *recv_x_scales,
+                                  hipStream_t stream);
+hipError_t launch_dispatch_ranks_cached(const Shape &s, const void *x, const float *x_scales,
+                                        const int32_t *token_rank_slot, void *recv_x,
+                                        float *recv_x_scales, hipStream_t stream);
+
 // Single-launch layout + dispatch (compacted layout, T * k <= 2048 pairs):
 // fused_dispatch_fits tells whether a shape qualifies.  Layout outputs may be
 // null (all together); the workspace plan is neither read nor written.

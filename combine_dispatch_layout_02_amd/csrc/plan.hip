@@ -330,7 +330,7 @@ __global__ __launch_bounds__(1024) void ep_plan_scan_kernel(ScanArgs a) {
 hipError_t launch_plan(const Shape &s, const WsLayout &L, const int64_t *topk_idx,
                        int32_t *per_rank, int32_t *per_expert, uint8_t *in_rank,
                        int32_t *per_node, int64_t *algo, char *ws, hipStream_t stream) {
-    CountArgs c;
+    CountArgs c{};
     c.topk_idx = topk_idx;
     c.T = s.T;
     c.k = s.k;
@@ -364,7 +364,7 @@ hipError_t launch_plan(const Shape &s, const WsLayout &L, const int64_t *topk_id
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess || L.tiles == 1) return e;   // one tile: the plan is complete
     }
-    ScanArgs a;
+    ScanArgs a{};
     a.E = s.E;
     a.R = s.R;
     a.N = s.N;

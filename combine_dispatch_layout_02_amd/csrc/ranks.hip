@@ -21,6 +21,10 @@
 //       ranks, ascending, of its partials), from -0.0; +0.0 when it reaches
 //       no rank.
 //
+// The cached form (ep_dispatch_ranks_cached) takes the rows from a previous
+// dispatch's token_rank_slot: the same rows for another tensor of the same
+// tokens, no plan and no metadata writes.
+//
 // How: one wave per (token or row, row part), as in the token-major kernels.
 // Lanes 0..R-1 of a token's wave hold its row on each rank; a ballot gives
 // the uniform mask of ranks reached, walked in ascending order with readlane,
@@ -59,6 +63,7 @@ struct RankCopyArgs {
     const int32_t *plan_rank_offset;   // [R + 1] (workspace)
     const int32_t *tile_prefix;     // [ntiles][E + R + N]; rank columns: prefix over tiles
     const int32_t *tr_local;        // [T][R]
+    const int32_t *slots_in;        // [T][R] a previous dispatch's token_rank_slot (cached form), else null
     uint32_t *ctrl;
     int64_t T;
     int k, E, R, TT, cols;
@@ -75,7 +80,7 @@ __global__ __launch_bounds__(256) void ep_dispatch_ranks_kernel(RankCopyArgs a) 
     const int64_t t = gw / a.S;
     const int sub = (int)(gw - t * a.S);
     const int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (g <= a.R) a.rank_offset[g] = a.plan_rank_offset[g];   // handle copy of the region starts
+    if (!a.slots_in && g <= a.R) a.rank_offset[g] = a.plan_rank_offset[g];   // handle copy of the region starts
     if (t >= a.T) return;   // wave-uniform
 
     const char *src = a.x + t * a.row_bytes;
@@ -90,7 +95,10 @@ __global__ __launch_bounds__(256) void ep_dispatch_ranks_kernel(RankCopyArgs a) 
 
     // lanes 0..R-1: the token's row on each rank (-1: not reached)
     int32_t slot = -1;
-    if (lane < a.R) {
+    if (lane < a.R && a.slots_in) {   // cached: the rows of a previous dispatch's handle
+        slot = a.slots_in[t * a.R + lane];
+        if ((uint64_t)slot >= (uint64_t)a.cap) slot = -1;
+    } else if (lane < a.R) {
         const int32_t lr = a.tr_local[t * a.R + lane];
         if (lr >= 0) {
             slot = a.plan_rank_offset[lane] + a.tile_prefix[(t / a.TT) * a.cols + a.E + lane] + lr;
@@ -104,7 +112,7 @@ __global__ __launch_bounds__(256) void ep_dispatch_ranks_kernel(RankCopyArgs a) 
     const uint64_t live = __ballot(slot >= 0);
     if (live == 0) return;
 
-    if (sub == 0) {   // source index and the token's top-k list as each rank sees it
+    if (sub == 0 && !a.slots_in) {   // source index and the token's top-k list as each rank sees it
         int e = -1;
         float w = 0.0f;
         if (lane < a.k) {
@@ -340,7 +348,7 @@ hipError_t launch_dispatch_ranks(const Shape &s, const WsLayout &L, const void *
                                  int32_t *recv_src_idx, int32_t *recv_topk_idx, float *recv_topk_w,
                                  int32_t *token_rank_slot, int32_t *rank_offset, const char *ws,
                                  hipStream_t stream) {
-    RankCopyArgs a;
+    RankCopyArgs a{};
     a.x = static_cast<const char *>(x);
     a.x_scales = x_scales;
     a.topk_idx = topk_idx;
@@ -386,11 +394,46 @@ hipError_t launch_dispatch_ranks(const Shape &s, const WsLayout &L, const void *
     return hipGetLastError();
 }
 
+hipError_t launch_dispatch_ranks_cached(const Shape &s, const void *x, const float *x_scales,
+                                        const int32_t *token_rank_slot, void *recv_x,
+                                        float *recv_x_scales, hipStream_t stream) {
+    RankCopyArgs a{};
+    a.x = static_cast<const char *>(x);
+    a.x_scales = x_scales;
+    a.recv_x = static_cast<char *>(recv_x);
+    a.recv_scales = recv_x_scales;
+    a.slots_in = token_rank_slot;
+    a.T = s.T;
+    a.k = s.k;
+    a.E = s.E;
+    a.R = s.R;
+    a.cap = s.rank_rows_cap();
+    const bool fp8 = (s.x_fmt == 1);
+    a.row_bytes = fp8 ? (int64_t)s.H : 2 * (int64_t)s.H;
+    a.nvec = (int)(a.row_bytes / 16);
+    a.G = fp8 ? s.H / 128 : 0;
+    a.S = waves_per_token(s.T, a.nvec, EP_RANKS_WAVES);
+    const int per_lane = (a.nvec + kWave * a.S - 1) / (kWave * a.S);
+    const int64_t blocks = (s.T * a.S + 3) / 4;
+    if (blocks == 0) return hipSuccess;
+    const dim3 grid((unsigned)blocks), block(256);
+    if (per_lane <= 2) {
+        hipLaunchKernelGGL(ep_dispatch_ranks_kernel<2>, grid, block, 0, stream, a);
+    } else if (per_lane <= 4) {
+        hipLaunchKernelGGL(ep_dispatch_ranks_kernel<4>, grid, block, 0, stream, a);
+    } else if (per_lane <= 8) {
+        hipLaunchKernelGGL(ep_dispatch_ranks_kernel<8>, grid, block, 0, stream, a);
+    } else {
+        hipLaunchKernelGGL(ep_dispatch_ranks_kernel<16>, grid, block, 0, stream, a);
+    }
+    return hipGetLastError();
+}
+
 hipError_t launch_expert_reduce_ranks(const Shape &s, const void *recv_x, const float *recv_scales,
                                       const int32_t *rank_offset, const int32_t *recv_topk_idx,
                                       const float *recv_topk_w, const float *factor,
                                       uint16_t *partial, hipStream_t stream) {
-    ReduceArgs a;
+    ReduceArgs a{};
     a.recv = static_cast<const char *>(recv_x);
     a.recv_scales = recv_scales;
     a.rank_offset = rank_offset;
@@ -414,7 +457,7 @@ hipError_t launch_expert_reduce_ranks(const Shape &s, const void *recv_x, const 
 
 hipError_t launch_combine_ranks(const Shape &s, const uint16_t *partial,
                                 const int32_t *token_rank_slot, void *y, hipStream_t stream) {
-    RankCombineArgs a;
+    RankCombineArgs a{};
     a.partial = reinterpret_cast<const char *>(partial);
     a.token_rank_slot = token_rank_slot;
     a.y = static_cast<char *>(y);

@@ -27,8 +27,8 @@ EP_OK, EP_EINVAL, EP_EALIGN, EP_EWORKSPACE, EP_EHIP, EP_EDEVICE = 0, -1, -2, -3,
 # every symbol include/ep.h declares
 EXPORTED = (
     "ep_abi_version", "ep_strerror", "ep_validate_shape", "ep_workspace_bytes", "ep_workspace_init",
-    "ep_dispatch_layout", "ep_dispatch", "ep_dispatch_from_layout", "ep_dispatch_with_layout", "ep_combine",
-    "ep_check",
+    "ep_dispatch_layout", "ep_dispatch", "ep_dispatch_from_layout", "ep_dispatch_with_layout", "ep_dispatch_cached",
+    "ep_dispatch_ranks_cached", "ep_combine", "ep_check",
     "ep_dispatch_ranks", "ep_expert_reduce_ranks", "ep_combine_ranks", "ep_quant_fp8_s128",
     "ep_expert_scale_bf16", "ep_expert_requant_mxfp8", "ep_expert_requant_nvfp4", "ep_accounting",
     "ep_calib_copy",
@@ -110,6 +110,8 @@ def load():
         "ep_dispatch": (ctypes.c_int, [SP, P, P, P, P, P, P, P, P, P, P, P, sz, P]),
         "ep_dispatch_from_layout": (ctypes.c_int, [SP, P, P, P, P, P, P, P, P, P, P, P, sz, P]),
         "ep_dispatch_with_layout": (ctypes.c_int, [SP] + [P] * 15 + [P, sz, P]),
+        "ep_dispatch_cached": (ctypes.c_int, [SP, P, P, P, P, P, P]),
+        "ep_dispatch_ranks_cached": (ctypes.c_int, [SP, P, P, P, P, P, P]),
         "ep_combine": (ctypes.c_int, [SP, P, P, P, P, P, P]),
         "ep_dispatch_ranks": (ctypes.c_int, [SP, P, P, P, P, P, P, P, P, P, P, P, P, sz, P]),
         "ep_expert_reduce_ranks": (ctypes.c_int, [SP, P, P, P, P, P, P, P, P]),
@@ -126,7 +128,7 @@ def load():
         fn = getattr(lib, name)
         fn.restype = res
         fn.argtypes = args
-    if lib.ep_abi_version() != 3:
+    if lib.ep_abi_version() != 4:
         raise RuntimeError("libep_hip ABI version mismatch")
     _lib = lib
     return lib
@@ -286,6 +288,36 @@ def ep_dispatch_with_layout(shape, x, x_scales, topk_idx, topk_w, num_tokens_per
                                        _ptr(recv_src_idx), _ptr(recv_topk_w), _ptr(token_slot),
                                        _ptr(expert_offset), ws.ptr, ws.nbytes, _stream(stream)),
         "ep_dispatch_with_layout")
+
+
+def ep_dispatch_cached(shape, x, x_scales, token_slot, recv_x, recv_x_scales=None, stream=None):
+    """Rows of a previous dispatch's handle (token_slot [T, k]) for another tensor x."""
+    T, k, H = shape.num_tokens, shape.num_topk, shape.hidden
+    fp8 = shape.x_format == EP_FMT_FP8_S128
+    _need(x, torch.uint8 if fp8 else torch.bfloat16, (T, H), "x")
+    _need(token_slot, torch.int32, (T, k), "token_slot")
+    _need(recv_x, x.dtype, (shape.rows, H), "recv_x")
+    if fp8:
+        _need(x_scales, torch.float32, (T, H // 128), "x_scales")
+        _need(recv_x_scales, torch.float32, (shape.rows, H // 128), "recv_x_scales")
+    _ok(load().ep_dispatch_cached(ctypes.byref(shape), _ptr(x), _ptr(x_scales), _ptr(token_slot), _ptr(recv_x),
+                                  _ptr(recv_x_scales), _stream(stream)), "ep_dispatch_cached")
+
+
+def ep_dispatch_ranks_cached(shape, x, x_scales, token_rank_slot, recv_x, recv_x_scales=None, stream=None):
+    """Rows of a previous (token, rank) dispatch's handle (token_rank_slot [T, R]) for another tensor x."""
+    T, H, R = shape.num_tokens, shape.hidden, shape.num_ranks
+    fp8 = shape.x_format == EP_FMT_FP8_S128
+    cap = shape.rank_rows_cap
+    _need(x, torch.uint8 if fp8 else torch.bfloat16, (T, H), "x")
+    _need(token_rank_slot, torch.int32, (T, R), "token_rank_slot")
+    _need(recv_x, x.dtype, (cap, H), "recv_x")
+    if fp8:
+        _need(x_scales, torch.float32, (T, H // 128), "x_scales")
+        _need(recv_x_scales, torch.float32, (cap, H // 128), "recv_x_scales")
+    _ok(load().ep_dispatch_ranks_cached(ctypes.byref(shape), _ptr(x), _ptr(x_scales), _ptr(token_rank_slot),
+                                        _ptr(recv_x), _ptr(recv_x_scales), _stream(stream)),
+        "ep_dispatch_ranks_cached")
 
 
 def ep_combine(shape, expert_out, expert_out_scales, token_slot, topk_w, y, stream=None):

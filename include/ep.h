@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define EP_ABI_VERSION 3
+#define EP_ABI_VERSION 4
 
 /* Status codes. */
 enum ep_status {
@@ -222,6 +222,19 @@ int ep_dispatch_from_layout(const ep_shape *shape, const void *x, const float *x
                             void *ws, size_t ws_bytes, void *stream);
 
 /*
+ * Cached dispatch ([PR860] Scope: cached_notify; the dispatch that takes a
+ * previous_handle): the rows of a previous dispatch's handle, for another
+ * tensor of the same tokens -- recv_x[token_slot[t,j]] = x[t] (and the scale
+ * rows for FP8_S128) -- with no layout work, no workspace and no metadata
+ * writes.  token_slot is the [T, k] handle of ep_dispatch /
+ * ep_dispatch_from_layout / ep_dispatch_with_layout for the same shape
+ * (compacted or RANK_MAJOR); a slot outside [0, rows) is skipped.  x,
+ * x_scales, recv_x, recv_x_scales: as for ep_dispatch.
+ */
+int ep_dispatch_cached(const ep_shape *shape, const void *x, const float *x_scales,
+                       const int32_t *token_slot, void *recv_x, float *recv_x_scales, void *stream);
+
+/*
  * Combine: the top-k weighted gather-reduce back into token order ([MORI]
  * "Combine": reverse of dispatch; [PR860] one copy per dispatched token per
  * expert, combine consumes the receiver-side layout from dispatch):
@@ -276,6 +289,16 @@ int ep_dispatch_ranks(const ep_shape *shape, const void *x, const float *x_scale
                       float *recv_x_scales, int32_t *recv_src_idx, int32_t *recv_topk_idx,
                       float *recv_topk_w, int32_t *token_rank_slot, int32_t *rank_offset,
                       void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Cached (token, rank) dispatch: recv_x[token_rank_slot[t,r]] = x[t] for the
+ * [T, R] handle of a previous ep_dispatch_ranks of the same shape (rank_rows
+ * 1), with the scale rows for FP8_S128; no workspace, no metadata writes; a
+ * row outside [0, T*min(k,R)) is skipped.
+ */
+int ep_dispatch_ranks_cached(const ep_shape *shape, const void *x, const float *x_scales,
+                             const int32_t *token_rank_slot, void *recv_x, float *recv_x_scales,
+                             void *stream);
 
 /*
  * Expert stage of the (token, rank) layout (outside dispatch and combine: the

@@ -35,7 +35,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_strerror(lib):
-    assert lib.ep_abi_version() == 3
+    assert lib.ep_abi_version() == 4
     for rc in (0, -1, -2, -3, -4, -5):
         assert ep.strerror(rc)
     assert "unknown" in ep.strerror(-99)
@@ -196,3 +196,19 @@ def test_dispatch_with_layout_rejects_before_device_work(lib):
     assert call(lay=f[:2] + [odd] + f[3:]) == ep.EP_EALIGN        # token-in-rank map misaligned (R % 4 == 0)
     assert call(ws=None) == ep.EP_EWORKSPACE
     assert call(nbytes=16) == ep.EP_EWORKSPACE
+
+
+def test_cached_dispatch_rejects_before_device_work(lib):
+    P = ctypes.c_void_p
+    fake, odd = P(0x1000), P(0x1008)
+    sh = ep.make_shape(64, 256, 16, 4, 1, 2)
+    shr = ep.make_shape(64, 256, 16, 4, 1, 2, rank_rows=1)
+    shq = ep.make_shape(64, 256, 16, 4, 1, 2, ep.EP_FMT_FP8_S128)
+    assert lib.ep_dispatch_cached(ctypes.byref(sh), odd, None, fake, fake, None, None) == ep.EP_EALIGN
+    assert lib.ep_dispatch_cached(ctypes.byref(sh), fake, fake, fake, fake, None, None) == ep.EP_EINVAL
+    assert lib.ep_dispatch_cached(ctypes.byref(shq), fake, fake, fake, fake, None, None) == ep.EP_EINVAL
+    assert lib.ep_dispatch_cached(ctypes.byref(sh), fake, None, None, fake, None, None) == ep.EP_EINVAL
+    assert lib.ep_dispatch_ranks_cached(ctypes.byref(sh), fake, None, fake, fake, None, None) == ep.EP_EINVAL
+    assert lib.ep_dispatch_ranks_cached(ctypes.byref(shr), fake, None, fake, odd, None, None) == ep.EP_EALIGN
+    empty = ep.make_shape(0, 256, 16, 4, 1, 2)
+    assert lib.ep_dispatch_cached(ctypes.byref(empty), None, None, None, None, None, None) == ep.EP_OK

@@ -286,3 +286,89 @@ def test_many_plan_tiles(kw):
     import gpu_path
     g = gpu_path.run_ranks(inp)
     assert gpu_path.compare_ranks(g, oracle.run_path(dict(inp, rank_rows=True)), False) == 0
+
+
+@pytest.mark.parametrize("kw", [dict(), dict(mask_frac=0.2, T=333), dict(x_fmt="fp8", T=300, H=1024),
+                                dict(rank_capacity="fit"), dict(T=100)])
+def test_cached_dispatch_reuses_a_handle(kw):
+    """ep_dispatch_cached with the handle of a first dispatch moves a second
+    tensor of the same tokens to the same rows (PR 860: cached dispatch with a
+    previous handle): the rows equal the oracle's dispatch of that tensor
+    under the handle's slots."""
+    from combine_dispatch_layout_02_amd import ep
+    import gpu_path
+    kw = dict(kw)
+    fp8 = kw.pop("x_fmt", "bf16") == "fp8"
+    cap = kw.pop("rank_capacity", 0)
+    base = dict(T=kw.pop("T", 500), H=kw.pop("H", 512))
+    base.update(kw)
+    inp = W.make_inputs("prefill2n", **base)
+    T, H, E, R, N, k = (inp[n] for n in ("T", "H", "E", "R", "N", "k"))
+    if cap == "fit":
+        ok = (inp["topk_idx"] >= 0) & (inp["topk_idx"] < E)
+        cap = int(np.bincount(inp["topk_idx"][ok] // (E // R), minlength=R).max())
+    shape = ep.make_shape(T, H, E, R, N, k, ep.EP_FMT_FP8_S128 if fp8 else ep.EP_FMT_BF16, rank_capacity=cap)
+    ws = ep.Workspace(shape)
+    idx = torch.from_numpy(inp["topk_idx"]).cuda()
+    w = torch.from_numpy(inp["topk_w"]).cuda()
+    x1 = gpu_path.to_dev_bf16(inp["x"])
+    x2_bits = W.f32_to_bf16_bits(np.random.default_rng(77).standard_normal((T, H), dtype=np.float32))
+    x2 = gpu_path.to_dev_bf16(x2_bits)
+    if fp8:
+        x1, s1 = ep.quant_fp8_s128(x1)
+        x2, s2 = ep.quant_fp8_s128(x2)
+    else:
+        s1 = s2 = None
+    _, _, _, _, h = ep.dispatch(x1, idx, w, shape, ws, x_scales=s1)
+    recv2 = torch.zeros((shape.rows, H), dtype=x2.dtype, device="cuda")
+    rs2 = torch.zeros((shape.rows, H // 128), dtype=torch.float32, device="cuda") if fp8 else None
+    ep.ep_dispatch_cached(shape, x2, s2, h.token_slot, recv2, rs2)
+    ws.check()
+    ts = h.token_slot.cpu().numpy()
+    used = np.sort(ts[ts >= 0])
+    src = x2.cpu().numpy() if fp8 else x2_bits
+    ref = oracle.dispatch_rows(src, ts, rows=shape.rows)
+    got = recv2.cpu().numpy() if fp8 else gpu_path.bf16_bits(recv2)
+    np.testing.assert_array_equal(got[used], ref[used])
+    if fp8:
+        refs = oracle.dispatch_rows(s2.cpu().numpy(), ts, rows=shape.rows)
+        np.testing.assert_array_equal(rs2.cpu().numpy()[used].view(np.uint32), refs[used].view(np.uint32))
+
+
+@pytest.mark.parametrize("kw", [dict(), dict(x_fmt="fp8", H=1024)])
+def test_cached_rank_dispatch_reuses_a_handle(kw):
+    from combine_dispatch_layout_02_amd import ep
+    import gpu_path
+    kw = dict(kw)
+    fp8 = kw.pop("x_fmt", "bf16") == "fp8"
+    inp = W.make_inputs("prefill2n", T=400, H=kw.pop("H", 512), mask_frac=0.1)
+    T, H, E, R, N, k = (inp[n] for n in ("T", "H", "E", "R", "N", "k"))
+    shape = ep.make_shape(T, H, E, R, N, k, ep.EP_FMT_FP8_S128 if fp8 else ep.EP_FMT_BF16, rank_rows=1)
+    ws = ep.Workspace(shape)
+    idx = torch.from_numpy(inp["topk_idx"]).cuda()
+    w = torch.from_numpy(inp["topk_w"]).cuda()
+    x1 = gpu_path.to_dev_bf16(inp["x"])
+    x2_bits = W.f32_to_bf16_bits(np.random.default_rng(78).standard_normal((T, H), dtype=np.float32))
+    x2 = gpu_path.to_dev_bf16(x2_bits)
+    if fp8:
+        x1, s1 = ep.quant_fp8_s128(x1)
+        x2, s2 = ep.quant_fp8_s128(x2)
+    else:
+        s1 = s2 = None
+    ep.dispatch_layout(idx, shape, ws)
+    d = ep.dispatch_ranks(x1, idx, w, shape, ws, x_scales=s1)
+    cap = shape.rank_rows_cap
+    recv2 = torch.zeros((cap, H), dtype=x2.dtype, device="cuda")
+    rs2 = torch.zeros((cap, H // 128), dtype=torch.float32, device="cuda") if fp8 else None
+    ep.ep_dispatch_ranks_cached(shape, x2, s2, d["handle"].token_rank_slot, recv2, rs2)
+    ws.check()
+    trs = d["handle"].token_rank_slot.cpu().numpy()
+    np.testing.assert_array_equal(trs, oracle.slots_ranks(inp["topk_idx"], inp["topk_w"], E, R)["token_rank_slot"])
+    used = np.sort(trs[trs >= 0])
+    src = x2.cpu().numpy() if fp8 else x2_bits
+    ref = oracle.dispatch_rows(src, trs, rows=cap)
+    got = recv2.cpu().numpy() if fp8 else gpu_path.bf16_bits(recv2)
+    np.testing.assert_array_equal(got[used], ref[used])
+    if fp8:
+        refs = oracle.dispatch_rows(s2.cpu().numpy(), trs, rows=cap)
+        np.testing.assert_array_equal(rs2.cpu().numpy()[used].view(np.uint32), refs[used].view(np.uint32))
