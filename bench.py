@@ -14,8 +14,8 @@ memory-side cache (cold-cache durations).  The workloads'
 expert stage (identity, per-expert scaling, or fp8 -> mxfp8 re-encoding)
 runs during warmup and is not part of the timed step.  A batch of at most
 2048 (token, slot) pairs is laid out and dispatched by one
-ep_dispatch_with_layout call, which the library runs as a single launch
-(phases "layout+dispatch", "combine").  With --layout ranks
+ep_dispatch_with_layout (ep_dispatch_ranks_with_layout) call, which the
+library runs as a single launch (phases "layout+dispatch", "combine").  With --layout ranks
 the step is the (token, rank) path: ep_dispatch_layout (planning one row per
 token per rank it reaches) -> ep_dispatch_ranks -> ep_combine_ranks, with
 ep_expert_reduce_ranks (the weighted per-rank partials) as the expert stage.
@@ -63,7 +63,8 @@ def kernel_source_hash() -> str:
 
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "combine_dispatch_layout_02_amd", "csrc")
-    for name in ("plan.hip", "dispatch.hip", "combine.hip", "ranks.hip", "ep_device.h", "ep_internal.h"):
+    for name in ("plan.hip", "dispatch.hip", "combine.hip", "ranks.hip", "ep_device.h", "ep_internal.h",
+                 "small_layout.h"):
         text = open(os.path.join(csrc, name)).read()
         text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
         text = re.sub(r"//[^\n]*", " ", text)
@@ -281,6 +282,10 @@ def measure(workload: str, steps: int, warmup: int, graph: bool = False, layout_
         def dispatch():   # reuses the plan the layout call of this step left in the workspace
             ep.ep_dispatch_ranks(shape, xin, xs, idx, w, recv_x, recv_s, src, r_idx, r_w, trs, roff, ws)
 
+        def layout_dispatch():   # one call; a single launch for batches of <= 2048 pairs
+            ep.ep_dispatch_ranks_with_layout(shape, xin, xs, idx, w, lay["r"], lay["e"], lay["m"], lay["n"],
+                                             lay["a"], recv_x, recv_s, src, r_idx, r_w, trs, roff, ws)
+
         def expert():
             ep.ep_expert_reduce_ranks(shape, recv_x, recv_s, roff, r_idx, r_w,
                                       factor if inp["expert"] == "scale" else None, part)
@@ -327,7 +332,7 @@ def measure(workload: str, steps: int, warmup: int, graph: bool = False, layout_
     # and combine: it runs in warmup (its output does not change from step to
     # step, the inputs being the same) and stays out of the timed step
     phases = [("layout", layout), ("dispatch", dispatch), ("combine", combine)]
-    single_launch = not ranks and M == 0 and T * k <= SINGLE_LAUNCH_PAIRS
+    single_launch = M == 0 and T * k <= SINGLE_LAUNCH_PAIRS
     if single_launch:   # the library runs layout + dispatch of such a batch as one kernel
         phases = [("layout+dispatch", layout_dispatch), ("combine", combine)]
 
@@ -483,7 +488,7 @@ def measure(workload: str, steps: int, warmup: int, graph: bool = False, layout_
     if single_launch:
         algo_bytes = {"layout+dispatch": algo_bytes["layout"] + algo_bytes["dispatch"],
                       "combine": algo_bytes["combine"]}
-        kernels["layout+dispatch"] = "ep_dispatch_copy_kernel"
+        kernels["layout+dispatch"] = kernels["dispatch"]
     dom = max((p for p in algo_bytes if p != "layout"), key=lambda p: phase_us[p])
     achieved = algo_bytes[dom] / (phase_us[dom] * 1e-6) / 1e9
     traffic = measured_traffic(workload + ("_ranks" if ranks else ""), kernels[dom])

@@ -29,6 +29,7 @@
 // position written out -- so no wave waits for a plan.
 #include "ep_device.h"
 #include "ep_internal.h"
+#include "small_layout.h"
 
 namespace ep {
 namespace {
@@ -75,70 +76,6 @@ struct CopyArgs {
 };
 
 constexpr int kFusedPairs = 2048;   // pairs a single-launch batch may hold (32 ids per lane)
-
-// Layout of a single-launch batch, by one block of 256 threads: staged ids,
-// per-expert counts (LDS integer adds, order-independent), their exclusive
-// scan into the expert_offset handle, and (when requested) the per-token
-// rank / node sets with their counts.  LDS: ids[T*k], hist[E], rn[R + N],
-// scan scratch.
-__device__ void fused_layout_block(const CopyArgs &a) {
-    extern __shared__ int32_t sm[];
-    const int TK = (int)(a.T * a.k);
-    int32_t *ids = sm;                    // [TK]
-    int32_t *hist = ids + TK;             // [E]
-    int32_t *rn = hist + a.E;             // [R + N]
-    int32_t *tmp = rn + a.R + a.N;        // [blockDim / 64 + 1]
-    const int tid = threadIdx.x, nt = blockDim.x, lane = tid & (kWave - 1), w = tid / kWave;
-    for (int i = tid; i < a.E; i += nt) hist[i] = 0;
-    for (int i = tid; i < a.R + a.N; i += nt) rn[i] = 0;
-    __syncthreads();
-    bool bad = false;
-    for (int q = tid; q < TK; q += nt) {
-        const int64_t v = a.topk_idx[q];
-        bad |= (v >= a.E);
-        const int32_t id = (v >= 0 && v < a.E) ? (int32_t)v : -1;
-        ids[q] = id;
-        if (id >= 0) atomicAdd(&hist[id], 1);
-    }
-    if (__ballot(bad) && lane == 0) atomicOr(&a.ctrl[0], kErrBadExpert);
-    __syncthreads();
-    if (a.per_expert)
-        for (int e = tid; e < a.E; e += nt) a.per_expert[e] = hist[e];
-    block_exclusive_scan(hist, a.expert_offset, a.E, tmp);
-    if (!a.per_rank) return;   // block-uniform
-    for (int tb = 0; tb < a.T; tb += nt) {
-        const int64_t t = tb + tid;
-        uint64_t rmask = 0, nmask = 0;
-        if (t < a.T) {
-            for (int j = 0; j < a.k; ++j) {
-                const int e = ids[t * a.k + j];
-                if (e < 0) continue;
-                rmask |= 1ull << (a.epr_shift >= 0 ? e >> a.epr_shift : e / a.epr);
-                nmask |= 1ull << (a.epn_shift >= 0 ? e >> a.epn_shift : e / a.epn);
-            }
-            for (int r = 0; r < a.R; ++r) a.in_rank[t * a.R + r] = (uint8_t)((rmask >> r) & 1u);
-        }
-        if (tb + w * kWave < a.T) {   // wave-uniform
-            for (int r = 0; r < a.R; ++r) {
-                const uint64_t b = __ballot((rmask >> r) & 1u);
-                if (lane == 0 && b) atomicAdd(&rn[r], (int)__popcll(b));
-            }
-            for (int n = 0; n < a.N; ++n) {
-                const uint64_t b = __ballot((nmask >> n) & 1u);
-                if (lane == 0 && b) atomicAdd(&rn[a.R + n], (int)__popcll(b));
-            }
-        }
-    }
-    __syncthreads();
-    for (int i = tid; i < a.R + a.N; i += nt) {
-        if (i < a.R) a.per_rank[i] = rn[i]; else a.per_node[i - a.R] = rn[i];
-    }
-    if (tid == 0) {
-        int64_t al = 0;
-        for (int n = 0; n < a.N; ++n) al += rn[a.R + n];
-        *a.algo = al;
-    }
-}
 
 // Slot of pair (t, j) held by lane j < k, by counting: the valid pairs whose
 // expert sorts before e_j, plus the pairs of e_j earlier in row-major (t, j)
@@ -191,7 +128,25 @@ template <int VPL, int KEYS, bool NT>
 __global__ __launch_bounds__(KEYS ? 1024 : 256) void ep_dispatch_copy_kernel(CopyArgs a) {
     constexpr bool FUSED = KEYS > 0;
     if (FUSED && blockIdx.x == 0) {
-        fused_layout_block(a);
+        SmallLayout L{};
+        L.topk_idx = a.topk_idx;
+        L.T = a.T;
+        L.k = a.k;
+        L.E = a.E;
+        L.R = a.R;
+        L.N = a.N;
+        L.epr = a.epr;
+        L.epr_shift = a.epr_shift;
+        L.epn = a.epn;
+        L.epn_shift = a.epn_shift;
+        L.ctrl = a.ctrl;
+        L.per_expert = a.per_expert;
+        L.expert_offset = a.expert_offset;
+        L.per_rank = a.per_rank;
+        L.per_node = a.per_node;
+        L.in_rank = a.in_rank;
+        L.algo = a.algo;
+        small_layout_block(L);
         return;
     }
     const int lane = threadIdx.x & (kWave - 1);

@@ -289,6 +289,45 @@ int ep_dispatch_ranks(const ep_shape *shape, const void *x, const float *x_scale
                                                 static_cast<hipStream_t>(stream)));
 }
 
+int ep_dispatch_ranks_with_layout(const ep_shape *shape, const void *x, const float *x_scales,
+                                  const int64_t *topk_idx, const float *topk_w, int32_t *num_tokens_per_rank,
+                                  int32_t *num_tokens_per_expert, uint8_t *is_token_in_rank,
+                                  int32_t *num_tokens_per_node, int64_t *rdma_algo_token_count, void *recv_x,
+                                  float *recv_x_scales, int32_t *recv_src_idx, int32_t *recv_topk_idx,
+                                  float *recv_topk_w, int32_t *token_rank_slot, int32_t *rank_offset,
+                                  void *ws, size_t ws_bytes, void *stream) {
+    Shape s;
+    int rc = check_shape(shape, &s);
+    if (rc != EP_OK) return rc;
+    if (!s.rank_rows || !rank_offset) return EP_EINVAL;
+    if (!num_tokens_per_rank || !num_tokens_per_expert || !num_tokens_per_node || !rdma_algo_token_count)
+        return EP_EINVAL;
+    if (s.T > 0 && (!x || !topk_idx || !topk_w || !recv_x || !recv_src_idx || !recv_topk_idx ||
+                    !recv_topk_w || !token_rank_slot || !is_token_in_rank))
+        return EP_EINVAL;
+    const bool fp8 = s.x_fmt == EP_FMT_FP8_S128;
+    if (fp8 && s.T > 0 && (!x_scales || !recv_x_scales)) return EP_EINVAL;
+    if (!fp8 && (x_scales || recv_x_scales)) return EP_EINVAL;
+    if (s.T > 0 && (!aligned16(x) || !aligned16(recv_x))) return EP_EALIGN;
+    if (!aligned16(is_token_in_rank) && (s.R % 4 == 0)) return EP_EALIGN;
+    const WsLayout L = ep::ws_layout(s);
+    if (!ws || ws_bytes < L.total) return EP_EWORKSPACE;
+    if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0) return EP_EALIGN;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    char *w = static_cast<char *>(ws);
+    if (ep::fused_ranks_fits(s))   // small batch: one launch, no plan in the workspace
+        return hip_status(ep::launch_dispatch_ranks_fused(
+            s, x, x_scales, topk_idx, topk_w, num_tokens_per_rank, num_tokens_per_expert, is_token_in_rank,
+            num_tokens_per_node, rdma_algo_token_count, recv_x, recv_x_scales, recv_src_idx, recv_topk_idx,
+            recv_topk_w, token_rank_slot, rank_offset, reinterpret_cast<uint32_t *>(w + L.ctrl), st));
+    hipError_t e = ep::launch_plan(s, L, topk_idx, num_tokens_per_rank, num_tokens_per_expert,
+                                   is_token_in_rank, num_tokens_per_node, rdma_algo_token_count, w, st);
+    if (e != hipSuccess) return EP_EHIP;
+    return hip_status(ep::launch_dispatch_ranks(s, L, x, x_scales, topk_idx, topk_w, recv_x, recv_x_scales,
+                                                recv_src_idx, recv_topk_idx, recv_topk_w, token_rank_slot,
+                                                rank_offset, w, st));
+}
+
 int ep_expert_reduce_ranks(const ep_shape *shape, const void *recv_x, const float *recv_x_scales,
                            const int32_t *rank_offset, const int32_t *recv_topk_idx,
                            const float *recv_topk_w, const float *factor, uint16_t *partial,

@@ -93,6 +93,17 @@ hipError_t launch_dispatch_ranks(const Shape &s, const WsLayout &L, const void *
                                  int32_t *token_rank_slot, int32_t *rank_offset, const char *ws,
                                  hipStream_t stream);
 
+// Single-launch layout + (token, rank) dispatch (T * k <= 2048 pairs, rank
+// rows); the workspace plan is neither read nor written.
+bool fused_ranks_fits(const Shape &s);
+hipError_t launch_dispatch_ranks_fused(const Shape &s, const void *x, const float *x_scales,
+                                       const int64_t *topk_idx, const float *topk_w, int32_t *per_rank,
+                                       int32_t *per_expert, uint8_t *in_rank, int32_t *per_node,
+                                       int64_t *algo, void *recv_x, float *recv_x_scales,
+                                       int32_t *recv_src_idx, int32_t *recv_topk_idx, float *recv_topk_w,
+                                       int32_t *token_rank_slot, int32_t *rank_offset, uint32_t *ctrl,
+                                       hipStream_t stream);
+
 hipError_t launch_expert_reduce_ranks(const Shape &s, const void *recv_x, const float *recv_scales,
                                       const int32_t *rank_offset, const int32_t *recv_topk_idx,
                                       const float *recv_topk_w, const float *factor,

@@ -31,6 +31,7 @@
 // so every store and every add happens in a fixed order.
 #include "ep_device.h"
 #include "ep_internal.h"
+#include "small_layout.h"
 
 namespace ep {
 namespace {
@@ -73,15 +74,84 @@ struct RankCopyArgs {
     int nvec, G, S;
 };
 
-template <int VPL>
-__global__ __launch_bounds__(256) void ep_dispatch_ranks_kernel(RankCopyArgs a) {
+constexpr int kRankFusedPairs = 2048;   // pairs a single-launch batch may hold
+
+// Row of (t, r) for every rank r the token reaches, by counting (single-launch
+// form, one token per block, every thread of the block calls this): the
+// block ORs each pair's rank bit into an LDS mask per token (order-
+// independent), then, for each rank r of token t (spread over the S waves),
+//   row = #{(t', r') : t' reaches r', r' < r}      (the region start of r)
+//       + #{t' < t : t' reaches r}                 (t's place in the region)
+// over the masks of all tokens (TOK per lane): the first term a wave sum of
+// popcounts, the second ballots.  Returns lane r's row (-1 when t does not
+// reach r).
+template <int TOK>
+__device__ __forceinline__ int32_t counted_rank_slot(const RankCopyArgs &a, int64_t t, int lane, int sub) {
+    extern __shared__ uint64_t tok_mask[];   // [T]
+    __shared__ int32_t row_sm[64];
+    const int TK = (int)(a.T * a.k);
+    const int nt = blockDim.x;
+    for (int i = threadIdx.x; i < a.T; i += nt) tok_mask[i] = 0ull;
+    __syncthreads();
+    for (int q0 = threadIdx.x; q0 < TK; q0 += 4 * nt) {   // four loads in flight per thread
+        int64_t e[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) e[u] = a.topk_idx[min(q0 + u * nt, TK - 1)];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int q = q0 + u * nt;
+            if (q < TK && e[u] >= 0 && e[u] < a.E) {
+                const int r = a.epr_shift >= 0 ? (int)e[u] >> a.epr_shift : (int)e[u] / a.epr;
+                atomicOr((unsigned long long *)&tok_mask[q / a.k], 1ull << r);
+            }
+        }
+    }
+    __syncthreads();
+    const uint64_t mine = tok_mask[t];
+    int idx = 0;
+    for (uint64_t m = mine; m; m &= m - 1, ++idx) {
+        if (idx % a.S != sub) continue;   // this rank belongs to another wave (uniform)
+        const int r = __builtin_ctzll(m);
+        const uint64_t below = (1ull << r) - 1;
+        int32_t before = 0, lower = 0;
+#pragma unroll
+        for (int i = 0; i < TOK; ++i) {
+            const int tt = lane + kWave * i;
+            const uint64_t mk = tt < a.T ? tok_mask[tt] : 0ull;
+            before += (int32_t)__popcll(__ballot(tt < t && ((mk >> r) & 1u)));
+            lower += (int32_t)__popcll(mk & below);
+        }
+        for (int off = kWave / 2; off > 0; off >>= 1) lower += __shfl_xor(lower, off);
+        if (lane == 0) row_sm[r] = lower + before;
+    }
+    __syncthreads();
+    return (lane < a.R && ((mine >> lane) & 1u)) ? row_sm[lane] : -1;
+}
+
+// TOK > 0: the single-launch form (block 0 does the layout, every other block
+// holds one token in S waves and counts its rows); TOK == 0: rows from the
+// plan, or from a previous handle (cached form).
+template <int VPL, int TOK>
+__global__ __launch_bounds__(TOK ? 1024 : 256) void ep_dispatch_ranks_kernel(RankCopyArgs a, SmallLayout L) {
+    constexpr bool FUSED = TOK > 0;
+    if (FUSED && blockIdx.x == 0) {
+        small_layout_block(L);
+        return;
+    }
     const int lane = threadIdx.x & (kWave - 1);
-    const int64_t gw = (int64_t)blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
-    const int64_t t = gw / a.S;
-    const int sub = (int)(gw - t * a.S);
-    const int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (!a.slots_in && g <= a.R) a.rank_offset[g] = a.plan_rank_offset[g];   // handle copy of the region starts
-    if (t >= a.T) return;   // wave-uniform
+    int64_t t;
+    int sub;
+    if (FUSED) {
+        t = (int64_t)blockIdx.x - 1;   // < T: the grid has 1 + T blocks
+        sub = threadIdx.x / kWave;
+    } else {
+        const int64_t gw = (int64_t)blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
+        t = gw / a.S;
+        sub = (int)(gw - t * a.S);
+        const int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+        if (!a.slots_in && g <= a.R) a.rank_offset[g] = a.plan_rank_offset[g];   // handle copy of the region starts
+    }
+    if (t >= a.T) return;   // wave-uniform (never taken in the single-launch form)
 
     const char *src = a.x + t * a.row_bytes;
     const int stride = kWave * a.S;
@@ -95,7 +165,16 @@ __global__ __launch_bounds__(256) void ep_dispatch_ranks_kernel(RankCopyArgs a) 
 
     // lanes 0..R-1: the token's row on each rank (-1: not reached)
     int32_t slot = -1;
-    if (lane < a.R && a.slots_in) {   // cached: the rows of a previous dispatch's handle
+    if (FUSED) {
+        slot = counted_rank_slot<(TOK > 0 ? TOK : 1)>(a, t, lane, sub);
+        if (lane < a.R) {
+            if ((uint64_t)slot >= (uint64_t)a.cap && slot != -1) {   // cannot happen; never write outside
+                atomicOr(&a.ctrl[0], kErrBadSlot);
+                slot = -1;
+            }
+            if (sub == 0) a.token_rank_slot[t * a.R + lane] = slot;
+        }
+    } else if (lane < a.R && a.slots_in) {   // cached: the rows of a previous dispatch's handle
         slot = a.slots_in[t * a.R + lane];
         if ((uint64_t)slot >= (uint64_t)a.cap) slot = -1;
     } else if (lane < a.R) {
@@ -340,7 +419,98 @@ __global__ __launch_bounds__(256) void ep_combine_ranks_kernel(RankCombineArgs a
     }
 }
 
+template <int TOK>
+void launch_ranks_copy(const RankCopyArgs &a, const SmallLayout &L, const dim3 &grid, const dim3 &block,
+                       size_t lds, hipStream_t stream) {
+    const int per_lane = (a.nvec + kWave * a.S - 1) / (kWave * a.S);
+    if (per_lane <= 2) {
+        hipLaunchKernelGGL((ep_dispatch_ranks_kernel<2, TOK>), grid, block, lds, stream, a, L);
+    } else if (per_lane <= 4) {
+        hipLaunchKernelGGL((ep_dispatch_ranks_kernel<4, TOK>), grid, block, lds, stream, a, L);
+    } else if (per_lane <= 8 || TOK) {   // the single-launch form has at most 8 (fused_ranks_fits)
+        hipLaunchKernelGGL((ep_dispatch_ranks_kernel<8, TOK>), grid, block, lds, stream, a, L);
+    } else {
+        hipLaunchKernelGGL((ep_dispatch_ranks_kernel<16, TOK>), grid, block, lds, stream, a, L);
+    }
+}
+
+// Waves per token of the single-launch form: enough for the row copy and at
+// least one per rank the token can reach (up to 16).
+int fused_rank_waves(const Shape &s, int nvec) {
+    int S = waves_per_token(s.T, nvec, EP_RANKS_WAVES);
+    const int kr = s.k < s.R ? s.k : s.R;
+    const int want = kr < 16 ? kr : 16;
+    while (S < want) S *= 2;
+    return S > 16 ? 16 : S;
+}
+
 }  // namespace
+
+bool fused_ranks_fits(const Shape &s) {
+    if (!(s.T > 0 && s.T * s.k <= kRankFusedPairs && s.rank_rows && s.M == 0)) return false;
+    const int nvec = (int)((s.x_fmt == 1 ? (int64_t)s.H : 2 * (int64_t)s.H) / 16);
+    const int S = fused_rank_waves(s, nvec);
+    return (nvec + kWave * S - 1) / (kWave * S) <= 8;   // registers for 1024-thread blocks
+}
+
+hipError_t launch_dispatch_ranks_fused(const Shape &s, const void *x, const float *x_scales,
+                                       const int64_t *topk_idx, const float *topk_w, int32_t *per_rank,
+                                       int32_t *per_expert, uint8_t *in_rank, int32_t *per_node,
+                                       int64_t *algo, void *recv_x, float *recv_x_scales,
+                                       int32_t *recv_src_idx, int32_t *recv_topk_idx, float *recv_topk_w,
+                                       int32_t *token_rank_slot, int32_t *rank_offset, uint32_t *ctrl,
+                                       hipStream_t stream) {
+    RankCopyArgs a{};
+    a.x = static_cast<const char *>(x);
+    a.x_scales = x_scales;
+    a.topk_idx = topk_idx;
+    a.topk_w = topk_w;
+    a.recv_x = static_cast<char *>(recv_x);
+    a.recv_scales = recv_x_scales;
+    a.recv_src_idx = recv_src_idx;
+    a.recv_topk_idx = recv_topk_idx;
+    a.recv_topk_w = recv_topk_w;
+    a.token_rank_slot = token_rank_slot;
+    a.ctrl = ctrl;
+    a.T = s.T;
+    a.k = s.k;
+    a.E = s.E;
+    a.R = s.R;
+    a.epr = s.E / s.R;
+    a.epr_shift = (a.epr & (a.epr - 1)) == 0 ? __builtin_ctz((unsigned)a.epr) : -1;
+    a.cap = s.rank_rows_cap();
+    const bool fp8 = (s.x_fmt == 1);
+    a.row_bytes = fp8 ? (int64_t)s.H : 2 * (int64_t)s.H;
+    a.nvec = (int)(a.row_bytes / 16);
+    a.G = fp8 ? s.H / 128 : 0;
+    a.S = fused_rank_waves(s, a.nvec);
+    SmallLayout L{};
+    L.topk_idx = topk_idx;
+    L.T = s.T;
+    L.k = s.k;
+    L.E = s.E;
+    L.R = s.R;
+    L.N = s.N;
+    L.epr = a.epr;
+    L.epr_shift = a.epr_shift;
+    L.epn = s.E / s.N;
+    L.epn_shift = (L.epn & (L.epn - 1)) == 0 ? __builtin_ctz((unsigned)L.epn) : -1;
+    L.ctrl = ctrl;
+    L.per_expert = per_expert;
+    L.per_rank = per_rank;
+    L.per_node = per_node;
+    L.in_rank = in_rank;
+    L.algo = algo;
+    L.rank_offset = rank_offset;
+    const int threads = kWave * a.S;
+    const size_t lds_layout = sizeof(int32_t) * ((size_t)s.T * s.k + s.E + s.R + s.N + threads / kWave + 1);
+    const size_t lds_masks = sizeof(uint64_t) * (size_t)s.T;
+    const size_t lds = lds_layout > lds_masks ? lds_layout : lds_masks;
+    const dim3 grid((unsigned)(1 + s.T)), block(threads);
+    if (s.T <= 8 * kWave) launch_ranks_copy<8>(a, L, grid, block, lds, stream);
+    else launch_ranks_copy<32>(a, L, grid, block, lds, stream);
+    return hipGetLastError();
+}
 
 hipError_t launch_dispatch_ranks(const Shape &s, const WsLayout &L, const void *x,
                                  const float *x_scales, const int64_t *topk_idx,
@@ -382,15 +552,7 @@ hipError_t launch_dispatch_ranks(const Shape &s, const WsLayout &L, const void *
     int64_t blocks = (s.T * a.S + 3) / 4;
     if (blocks * 256 < s.R + 1) blocks = 1;   // threads to copy rank_offset (R <= 64)
     const dim3 grid((unsigned)blocks), block(256);
-    if (per_lane <= 2) {
-        hipLaunchKernelGGL(ep_dispatch_ranks_kernel<2>, grid, block, 0, stream, a);
-    } else if (per_lane <= 4) {
-        hipLaunchKernelGGL(ep_dispatch_ranks_kernel<4>, grid, block, 0, stream, a);
-    } else if (per_lane <= 8) {
-        hipLaunchKernelGGL(ep_dispatch_ranks_kernel<8>, grid, block, 0, stream, a);
-    } else {
-        hipLaunchKernelGGL(ep_dispatch_ranks_kernel<16>, grid, block, 0, stream, a);
-    }
+    launch_ranks_copy<0>(a, SmallLayout{}, grid, block, 0, stream);
     return hipGetLastError();
 }
 
@@ -417,15 +579,7 @@ hipError_t launch_dispatch_ranks_cached(const Shape &s, const void *x, const flo
     const int64_t blocks = (s.T * a.S + 3) / 4;
     if (blocks == 0) return hipSuccess;
     const dim3 grid((unsigned)blocks), block(256);
-    if (per_lane <= 2) {
-        hipLaunchKernelGGL(ep_dispatch_ranks_kernel<2>, grid, block, 0, stream, a);
-    } else if (per_lane <= 4) {
-        hipLaunchKernelGGL(ep_dispatch_ranks_kernel<4>, grid, block, 0, stream, a);
-    } else if (per_lane <= 8) {
-        hipLaunchKernelGGL(ep_dispatch_ranks_kernel<8>, grid, block, 0, stream, a);
-    } else {
-        hipLaunchKernelGGL(ep_dispatch_ranks_kernel<16>, grid, block, 0, stream, a);
-    }
+    launch_ranks_copy<0>(a, SmallLayout{}, grid, block, 0, stream);
     return hipGetLastError();
 }
 

@@ -28,7 +28,7 @@ EP_OK, EP_EINVAL, EP_EALIGN, EP_EWORKSPACE, EP_EHIP, EP_EDEVICE = 0, -1, -2, -3,
 EXPORTED = (
     "ep_abi_version", "ep_strerror", "ep_validate_shape", "ep_workspace_bytes", "ep_workspace_init",
     "ep_dispatch_layout", "ep_dispatch", "ep_dispatch_from_layout", "ep_dispatch_with_layout", "ep_dispatch_cached",
-    "ep_dispatch_ranks_cached", "ep_combine", "ep_check",
+    "ep_dispatch_ranks_cached", "ep_dispatch_ranks_with_layout", "ep_combine", "ep_check",
     "ep_dispatch_ranks", "ep_expert_reduce_ranks", "ep_combine_ranks", "ep_quant_fp8_s128",
     "ep_expert_scale_bf16", "ep_expert_requant_mxfp8", "ep_expert_requant_nvfp4", "ep_accounting",
     "ep_calib_copy",
@@ -112,6 +112,7 @@ def load():
         "ep_dispatch_with_layout": (ctypes.c_int, [SP] + [P] * 15 + [P, sz, P]),
         "ep_dispatch_cached": (ctypes.c_int, [SP, P, P, P, P, P, P]),
         "ep_dispatch_ranks_cached": (ctypes.c_int, [SP, P, P, P, P, P, P]),
+        "ep_dispatch_ranks_with_layout": (ctypes.c_int, [SP] + [P] * 16 + [P, sz, P]),
         "ep_combine": (ctypes.c_int, [SP, P, P, P, P, P, P]),
         "ep_dispatch_ranks": (ctypes.c_int, [SP, P, P, P, P, P, P, P, P, P, P, P, P, sz, P]),
         "ep_expert_reduce_ranks": (ctypes.c_int, [SP, P, P, P, P, P, P, P, P]),
@@ -128,7 +129,7 @@ def load():
         fn = getattr(lib, name)
         fn.restype = res
         fn.argtypes = args
-    if lib.ep_abi_version() != 4:
+    if lib.ep_abi_version() != 5:
         raise RuntimeError("libep_hip ABI version mismatch")
     _lib = lib
     return lib
@@ -368,6 +369,40 @@ def ep_dispatch_ranks(shape, x, x_scales, topk_idx, topk_w, recv_x, recv_x_scale
                                  ws.nbytes, _stream(stream)), "ep_dispatch_ranks")
 
 
+def ep_dispatch_ranks_with_layout(shape, x, x_scales, topk_idx, topk_w, num_tokens_per_rank,
+                                  num_tokens_per_expert, is_token_in_rank, num_tokens_per_node,
+                                  rdma_algo_token_count, recv_x, recv_x_scales, recv_src_idx, recv_topk_idx,
+                                  recv_topk_w, token_rank_slot, rank_offset, ws: Workspace, stream=None):
+    """Layout and (token, rank) dispatch in one call (one launch for batches of <= 2048 pairs)."""
+    T, k, H, E, R, N = (shape.num_tokens, shape.num_topk, shape.hidden, shape.num_experts, shape.num_ranks,
+                        shape.num_nodes)
+    fp8 = shape.x_format == EP_FMT_FP8_S128
+    cap = shape.rank_rows_cap
+    _need(x, torch.uint8 if fp8 else torch.bfloat16, (T, H), "x")
+    _need(topk_idx, torch.int64, (T, k), "topk_idx")
+    _need(topk_w, torch.float32, (T, k), "topk_w")
+    _need(num_tokens_per_rank, torch.int32, (R,), "num_tokens_per_rank")
+    _need(num_tokens_per_expert, torch.int32, (E,), "num_tokens_per_expert")
+    _need(is_token_in_rank, torch.uint8, (T, R), "is_token_in_rank")
+    _need(num_tokens_per_node, torch.int32, (N,), "num_tokens_per_node")
+    _need(rdma_algo_token_count, torch.int64, (1,), "rdma_algo_token_count")
+    _need(recv_x, x.dtype, (cap, H), "recv_x")
+    if fp8:
+        _need(x_scales, torch.float32, (T, H // 128), "x_scales")
+        _need(recv_x_scales, torch.float32, (cap, H // 128), "recv_x_scales")
+    _need(recv_src_idx, torch.int32, (cap,), "recv_src_idx")
+    _need(recv_topk_idx, torch.int32, (cap, k), "recv_topk_idx")
+    _need(recv_topk_w, torch.float32, (cap, k), "recv_topk_w")
+    _need(token_rank_slot, torch.int32, (T, R), "token_rank_slot")
+    _need(rank_offset, torch.int32, (R + 1,), "rank_offset")
+    ws.planned_for = None   # no reusable plan is left in the workspace
+    _ok(load().ep_dispatch_ranks_with_layout(
+        ctypes.byref(shape), _ptr(x), _ptr(x_scales), _ptr(topk_idx), _ptr(topk_w), _ptr(num_tokens_per_rank),
+        _ptr(num_tokens_per_expert), _ptr(is_token_in_rank), _ptr(num_tokens_per_node), _ptr(rdma_algo_token_count),
+        _ptr(recv_x), _ptr(recv_x_scales), _ptr(recv_src_idx), _ptr(recv_topk_idx), _ptr(recv_topk_w),
+        _ptr(token_rank_slot), _ptr(rank_offset), ws.ptr, ws.nbytes, _stream(stream)), "ep_dispatch_ranks_with_layout")
+
+
 def ep_expert_reduce_ranks(shape, recv_x, recv_x_scales, rank_offset, recv_topk_idx, recv_topk_w, factor,
                            partial, stream=None):
     cap, H, k, R = shape.rank_rows_cap, shape.hidden, shape.num_topk, shape.num_ranks
@@ -555,6 +590,38 @@ def dispatch_ranks(x, topk_idx, topk_w, shape, ws: Workspace, x_scales=None, str
                       h.rank_offset, ws, stream)
     out["handle"] = h
     return out
+
+
+def dispatch_ranks_with_layout(x, topk_idx, topk_w, shape, ws: Workspace, x_scales=None, stream=None):
+    """Layout and (token, rank) dispatch in one call; returns (layout dict, dispatch_ranks-style dict)."""
+    dev = x.device
+    T, k, H, E, R, N = (shape.num_tokens, shape.num_topk, shape.hidden, shape.num_experts, shape.num_ranks,
+                        shape.num_nodes)
+    cap = shape.rank_rows_cap
+    fp8 = shape.x_format == EP_FMT_FP8_S128
+    lay = dict(
+        num_tokens_per_rank=torch.empty(R, dtype=torch.int32, device=dev),
+        num_tokens_per_expert=torch.empty(E, dtype=torch.int32, device=dev),
+        is_token_in_rank=torch.empty((T, R), dtype=torch.uint8, device=dev),
+        num_tokens_per_node=torch.empty(N, dtype=torch.int32, device=dev),
+        rdma_algo_token_count=torch.empty(1, dtype=torch.int64, device=dev),
+    )
+    out = dict(
+        recv_x=torch.empty((cap, H), dtype=x.dtype, device=dev),
+        recv_x_scales=torch.empty((cap, H // 128), dtype=torch.float32, device=dev) if fp8 else None,
+        recv_src_idx=torch.empty(cap, dtype=torch.int32, device=dev),
+        recv_topk_idx=torch.empty((cap, k), dtype=torch.int32, device=dev),
+        recv_topk_w=torch.empty((cap, k), dtype=torch.float32, device=dev),
+    )
+    h = RankHandle(shape, torch.empty((T, R), dtype=torch.int32, device=dev),
+                   torch.empty(R + 1, dtype=torch.int32, device=dev))
+    ep_dispatch_ranks_with_layout(shape, x, x_scales, topk_idx, topk_w, lay["num_tokens_per_rank"],
+                                  lay["num_tokens_per_expert"], lay["is_token_in_rank"], lay["num_tokens_per_node"],
+                                  lay["rdma_algo_token_count"], out["recv_x"], out["recv_x_scales"],
+                                  out["recv_src_idx"], out["recv_topk_idx"], out["recv_topk_w"], h.token_rank_slot,
+                                  h.rank_offset, ws, stream)
+    out["handle"] = h
+    return lay, out
 
 
 def expert_reduce_ranks(d: dict, factor=None, stream=None):

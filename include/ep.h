@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define EP_ABI_VERSION 4
+#define EP_ABI_VERSION 5
 
 /* Status codes. */
 enum ep_status {
@@ -289,6 +289,25 @@ int ep_dispatch_ranks(const ep_shape *shape, const void *x, const float *x_scale
                       float *recv_x_scales, int32_t *recv_src_idx, int32_t *recv_topk_idx,
                       float *recv_topk_w, int32_t *token_rank_slot, int32_t *rank_offset,
                       void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Layout and (token, rank) dispatch in one call: the outputs of
+ * ep_dispatch_layout and of ep_dispatch_ranks together (rank_rows 1).  A
+ * small batch -- T * k <= 2048 pairs -- runs as ONE kernel launch: one block
+ * computes the layout counts and the region starts while every other block
+ * (one token) finds the token's rows by counting the tokens and ranks that
+ * come before them; results are identical to the two calls.  Larger batches
+ * run the layout launches, then the copy.  Afterwards the workspace holds no
+ * plan that ep_dispatch_ranks may reuse.  Arguments: as ep_dispatch_layout
+ * and ep_dispatch_ranks.
+ */
+int ep_dispatch_ranks_with_layout(const ep_shape *shape, const void *x, const float *x_scales,
+                                  const int64_t *topk_idx, const float *topk_w, int32_t *num_tokens_per_rank,
+                                  int32_t *num_tokens_per_expert, uint8_t *is_token_in_rank,
+                                  int32_t *num_tokens_per_node, int64_t *rdma_algo_token_count, void *recv_x,
+                                  float *recv_x_scales, int32_t *recv_src_idx, int32_t *recv_topk_idx,
+                                  float *recv_topk_w, int32_t *token_rank_slot, int32_t *rank_offset,
+                                  void *ws, size_t ws_bytes, void *stream);
 
 /*
  * Cached (token, rank) dispatch: recv_x[token_rank_slot[t,r]] = x[t] for the

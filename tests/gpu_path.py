@@ -130,9 +130,11 @@ def compare(gpu: dict, ref: dict, fp8: bool, nvfp4: bool = False):
     return int((gpu["y"] != ref["y"]).sum())
 
 
-def run_ranks(inp: dict, dev="cuda", check=True) -> dict:
+def run_ranks(inp: dict, dev="cuda", check=True, with_layout=False) -> dict:
     """The (token, rank) path: layout (planning the rank rows), dispatch_ranks,
-    the expert stage returning per-row partials, combine_ranks."""
+    the expert stage returning per-row partials, combine_ranks.  with_layout:
+    one ep_dispatch_ranks_with_layout call for layout + dispatch (a single
+    launch for small batches)."""
     T, H, E, R, N, k = (inp[n] for n in ("T", "H", "E", "R", "N", "k"))
     fp8 = inp.get("x_fmt", "bf16") == "fp8"
     shape = ep.make_shape(T, H, E, R, N, k, ep.EP_FMT_FP8_S128 if fp8 else ep.EP_FMT_BF16, ep.EP_FMT_BF16,
@@ -142,14 +144,19 @@ def run_ranks(inp: dict, dev="cuda", check=True) -> dict:
     idx = torch.from_numpy(np.ascontiguousarray(inp["topk_idx"])).to(dev)
     w = torch.from_numpy(np.ascontiguousarray(inp["topk_w"])).to(dev)
     out = {}
-    lay = ep.dispatch_layout(idx, shape, ws)
+
+    def dispatch(xin, x_scales=None):
+        if with_layout:
+            return ep.dispatch_ranks_with_layout(xin, idx, w, shape, ws, x_scales=x_scales)
+        return ep.dispatch_layout(idx, shape, ws), ep.dispatch_ranks(xin, idx, w, shape, ws, x_scales=x_scales)
+
     if fp8:
         q, s = ep.quant_fp8_s128(x)
-        d = ep.dispatch_ranks(q, idx, w, shape, ws, x_scales=s)
+        lay, d = dispatch(q, s)
         out.update(x_q=q.cpu().numpy(), x_scales=s.cpu().numpy(), recv_x=d["recv_x"].cpu().numpy(),
                    recv_x_scales=d["recv_x_scales"].cpu().numpy())
     else:
-        d = ep.dispatch_ranks(x, idx, w, shape, ws)
+        lay, d = dispatch(x)
         out.update(recv_x=bf16_bits(d["recv_x"]))
     factor = inp.get("expert_factor") if inp.get("expert") == "scale" else None
     f = None if factor is None else torch.from_numpy(factor).to(dev)

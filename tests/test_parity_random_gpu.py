@@ -73,7 +73,8 @@ def test_random_shapes_all_paths(seed):
             assert flags == 0
         assert gpu_path.compare(g, r, False) == 0, f"rank_major M={M}"
 
-    # (token, rank) rows
-    g = gpu_path.run_ranks(inp)
+    # (token, rank) rows, from the layout call's plan and in one call
     r = oracle.run_path(dict(inp, rank_rows=True))
-    assert gpu_path.compare_ranks(g, r, False) == 0
+    for with_layout in (False, True):
+        g = gpu_path.run_ranks(inp, with_layout=with_layout)
+        assert gpu_path.compare_ranks(g, r, False) == 0, f"ranks with_layout={with_layout}"

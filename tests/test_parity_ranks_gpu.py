@@ -28,11 +28,11 @@ def _gpu():
     ep.load()  # fails loudly if the HIP library is missing
 
 
-def _run_both(inp):
+def _run_both(inp, with_layout=False):
     import gpu_path
     print(f"ranks case {inp.get('name')} T={inp['T']} H={inp['H']} E={inp['E']} R={inp['R']} N={inp['N']} "
-          f"k={inp['k']} seed={inp.get('seed')} x_fmt={inp.get('x_fmt')}", flush=True)
-    g = gpu_path.run_ranks(inp)
+          f"k={inp['k']} seed={inp.get('seed')} x_fmt={inp.get('x_fmt')} with_layout={with_layout}", flush=True)
+    g = gpu_path.run_ranks(inp, with_layout=with_layout)
     r = oracle.run_path(dict(inp, rank_rows=True))
     return g, r, gpu_path.compare_ranks(g, r, inp.get("x_fmt") == "fp8")
 
@@ -137,3 +137,28 @@ def test_same_plan_serves_both_layouts():
     np.testing.assert_array_equal(h.token_slot.cpu().numpy(), tm["slots"]["token_slot"])
     np.testing.assert_array_equal(gpu_path.bf16_bits(y), tm["y"])
     np.testing.assert_array_equal(gpu_path.bf16_bits(yr), ht["y"])
+
+
+# single-launch layout + (token, rank) dispatch: batches of at most 2048 pairs
+@pytest.mark.parametrize("kw", [
+    dict(T=1), dict(T=5), dict(T=64), dict(T=128), dict(T=256), dict(T=200, mask_frac=0.3, mask_tokens=0.1),
+    dict(T=100, routing="replace"), dict(T=64, k=32, E=4096, R=64, N=64), dict(T=2048, k=1),
+    dict(T=300, E=24, R=3, N=1, k=5), dict(T=256, R=1, N=1), dict(T=128, H=8), dict(T=600, E=36, R=6, N=3, k=3),
+    dict(T=257)])   # 2056 pairs: the multi-launch path through the same call
+def test_with_layout_small_batches(kw):
+    kw = dict(kw)
+    base = dict(H=kw.pop("H", 1024))
+    base.update(kw)
+    _, _, ndiff = _run_both(W.make_inputs("decode", **base), with_layout=True)
+    assert ndiff == 0
+
+
+@pytest.mark.parametrize("name", ["tiny", "decode"])
+def test_with_layout_workloads(name):
+    _, _, ndiff = _run_both(W.make_inputs(name), with_layout=True)
+    assert ndiff == 0
+
+
+def test_with_layout_fp8_rows():
+    _, _, ndiff = _run_both(W.make_inputs("quant", T=128, H=1024, mask_frac=0.2), with_layout=True)
+    assert ndiff == 0
