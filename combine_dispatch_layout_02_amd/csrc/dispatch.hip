@@ -79,27 +79,29 @@ constexpr int kFusedPairs = 2048;   // pairs a single-launch batch may hold (32 
 
 // Slot of pair (t, j) held by lane j < k, by counting: the valid pairs whose
 // expert sorts before e_j, plus the pairs of e_j earlier in row-major (t, j)
-// order.  Each lane keeps KEYS pair ids in registers (KEYS * 64 >= T * k); the counts are
+// order.  The block stages the batch's pair ids in LDS once (masked and
+// invalid ids as INT_MAX, which sorts after every expert); each lane then
+// holds KEYS of them in registers (KEYS * 64 >= T * k) and the counts are
 // ballots.  The token's S waves share the work (wave `sub` counts slots j =
 // sub, sub + S, ...) and exchange the results through LDS: one token per
 // block, every thread of the block calls this.
 template <int KEYS>
 __device__ __forceinline__ int32_t counted_slot(const CopyArgs &a, int64_t t, int lane, int sub) {
+    extern __shared__ int32_t ids_sm[];   // [T * k]
     __shared__ int32_t slot_sm[32];
     const int TK = (int)(a.T * a.k);
-    // every load unconditional (clamped index) so all of them are in flight
-    // together; lanes past the batch then drop their value
-    const int64_t own = a.topk_idx[t * a.k + min(lane, a.k - 1)];   // lane j < k: slot j's id
-    int64_t raw[KEYS];
-#pragma unroll
-    for (int i = 0; i < KEYS; ++i) raw[i] = a.topk_idx[min(lane + kWave * i, TK - 1)];
-    int32_t key[KEYS];   // masked / invalid ids sort after every expert
+    for (int q = threadIdx.x; q < TK; q += blockDim.x) {
+        const int64_t id = a.topk_idx[q];
+        ids_sm[q] = (id >= 0 && id < a.E) ? (int32_t)id : 0x7FFFFFFF;
+    }
+    __syncthreads();
+    int32_t key[KEYS];
 #pragma unroll
     for (int i = 0; i < KEYS; ++i) {
-        const bool ok = lane + kWave * i < TK && raw[i] >= 0 && raw[i] < a.E;
-        key[i] = ok ? (int32_t)raw[i] : 0x7FFFFFFF;
+        const int q = lane + kWave * i;
+        key[i] = q < TK ? ids_sm[q] : 0x7FFFFFFF;
     }
-    const int32_t mine = (lane < a.k && own >= 0 && own < a.E) ? (int32_t)own : 0x7FFFFFFF;
+    const int32_t mine = lane < a.k ? ids_sm[t * a.k + lane] : 0x7FFFFFFF;   // lane j < k: slot j's id
     for (int j = sub; j < a.k; j += a.S) {
         const int32_t e = readlane(mine, j);
         int32_t c = -1;                  // masked slot
@@ -389,7 +391,8 @@ hipError_t launch_dispatch_fused(const Shape &s, const void *x, const float *x_s
     a.in_rank = in_rank;
     a.per_node = per_node;
     a.algo = algo;
-    // block 0: the layout; then one block of S waves per token
+    // block 0: the layout; then one block of S waves per token (LDS: the
+    // layout's staging, which is larger than the other blocks' pair ids)
     a.S = fused_waves(s, a.nvec);
     const int threads = kWave * a.S;
     const size_t lds = sizeof(int32_t) * ((size_t)s.T * s.k + s.E + s.R + s.N + threads / kWave + 1);
