@@ -548,7 +548,6 @@ hipError_t launch_dispatch_ranks(const Shape &s, const WsLayout &L, const void *
     a.nvec = (int)(a.row_bytes / 16);
     a.G = fp8 ? s.H / 128 : 0;
     a.S = waves_per_token(s.T, a.nvec, EP_RANKS_WAVES);
-    const int per_lane = (a.nvec + kWave * a.S - 1) / (kWave * a.S);
     int64_t blocks = (s.T * a.S + 3) / 4;
     if (blocks * 256 < s.R + 1) blocks = 1;   // threads to copy rank_offset (R <= 64)
     const dim3 grid((unsigned)blocks), block(256);
@@ -575,7 +574,6 @@ hipError_t launch_dispatch_ranks_cached(const Shape &s, const void *x, const flo
     a.nvec = (int)(a.row_bytes / 16);
     a.G = fp8 ? s.H / 128 : 0;
     a.S = waves_per_token(s.T, a.nvec, EP_RANKS_WAVES);
-    const int per_lane = (a.nvec + kWave * a.S - 1) / (kWave * a.S);
     const int64_t blocks = (s.T * a.S + 3) / 4;
     if (blocks == 0) return hipSuccess;
     const dim3 grid((unsigned)blocks), block(256);
