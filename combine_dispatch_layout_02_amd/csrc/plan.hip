@@ -280,12 +280,21 @@ __global__ __launch_bounds__(1024) void ep_plan_scan_kernel(ScanArgs a) {
             }
         }
     } else {
+        // the same sums in batches of kScanRegs tiles; every load of a batch
+        // is unconditional (clamped index, value dropped past the range) so
+        // the batch is in flight together
         for (int idx = tid; idx < cols * Q; idx += nt) {
             const int c = idx % cols, q = idx / cols;
             const int ta = min(q * chunk, a.ntiles), tb = min(ta + chunk, a.ntiles);
             const int32_t *col = a.tile_count + c;
             int32_t s = 0;
-            for (int t = ta; t < tb; ++t) s += col[(size_t)t * cols];
+            for (int t0 = ta; t0 < tb; t0 += kScanRegs) {
+                int32_t v[kScanRegs];
+#pragma unroll
+                for (int u = 0; u < kScanRegs; ++u) v[u] = col[(size_t)min(t0 + u, tb - 1) * cols];
+#pragma unroll
+                for (int u = 0; u < kScanRegs; ++u) s += (t0 + u < tb) ? v[u] : 0;
+            }
             part[idx] = s;
         }
         __syncthreads();
@@ -296,10 +305,17 @@ __global__ __launch_bounds__(1024) void ep_plan_scan_kernel(ScanArgs a) {
             int32_t *col = a.tile_count + c;
             int32_t run = 0;
             for (int q2 = 0; q2 < q; ++q2) run += part[q2 * cols + c];
-            for (int t = ta; t < tb; ++t) {
-                const int32_t x = col[(size_t)t * cols];
-                col[(size_t)t * cols] = run;
-                run += x;
+            for (int t0 = ta; t0 < tb; t0 += kScanRegs) {
+                int32_t v[kScanRegs];
+#pragma unroll
+                for (int u = 0; u < kScanRegs; ++u) v[u] = col[(size_t)min(t0 + u, tb - 1) * cols];
+#pragma unroll
+                for (int u = 0; u < kScanRegs; ++u) {
+                    if (t0 + u < tb) {
+                        col[(size_t)(t0 + u) * cols] = run;
+                        run += v[u];
+                    }
+                }
             }
         }
     }
