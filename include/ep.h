@@ -22,7 +22,10 @@
  *           fix commit); TOKEN_MAJOR compacted prefix offsets (RANK_MAJOR
  *           commit); one copy per dispatched token per expert (LL combine
  *           byte commit); capacity-sized buffers instead of a CPU wait for
- *           exact receive counts (DeepEP V2 graph-capture comment).
+ *           exact receive counts (DeepEP V2 graph-capture comment); DeepEP's
+ *           expanded receive layout, one row per (token, source rank) (the
+ *           high-throughput path; BW accounting commit); cached_notify and
+ *           the previous handle (cached dispatch).
  *
  * Conventions for every call:
  *   - Data pointers are DEVICE pointers owned by the caller, except where a
@@ -39,6 +42,8 @@
  *   - bf16 values are raw 16-bit patterns; e4m3 (OCP "fn") and e8m0 are bytes.
  *   - Calls that share one workspace must be ordered (same stream, or
  *     explicit events); two concurrent calls on one workspace race.
+ *   - Plain C: the header needs only <stddef.h> and <stdint.h>; streams are
+ *     passed as void *.
  */
 #ifndef EP_HIP_H
 #define EP_HIP_H
