@@ -352,9 +352,14 @@ hipError_t launch_dispatch_copy(const Shape &s, const WsLayout &L, const void *x
 
 // Waves per token of the single-launch form: enough for the row copy, and at
 // least one per slot (up to 16) so each wave counts few slots.
+#ifndef EP_FUSED_MIN_WAVES
+#define EP_FUSED_MIN_WAVES 1     // waves per token of the single-launch form, at least
+#endif
+
 int fused_waves(const Shape &s, int nvec) {
     int S = waves_per_token(s.T, nvec, EP_DISPATCH_WAVES);
-    const int want = s.k < 16 ? s.k : 16;
+    int want = s.k < 16 ? s.k : 16;
+    if (want < EP_FUSED_MIN_WAVES) want = EP_FUSED_MIN_WAVES;
     while (S < want) S *= 2;
     return S > 16 ? 16 : S;
 }
