@@ -19,6 +19,11 @@
 // slot order.  Nothing is reduced across lanes, so the result does not depend on
 // the launch shape.  The gathered rows are read once: the loads carry the
 // non-temporal hint so they do not evict what the caches still hold.
+// bf16 rows: the tokens are taken last to first and y is stored
+// non-temporal.  The dispatch leaves the first tokens' receive rows in the
+// memory-side cache and streams the later ones to HBM; this order reads the
+// HBM rows first and the cached rows last, and y does not evict them
+// (T = 4096, hidden 7168, top-8: 101 -> 85 us).
 #include "ep_device.h"
 #include "ep_internal.h"
 
@@ -48,14 +53,22 @@ constexpr int kSlotBatch = 8;
 #define EP_COMBINE_WAVES 16384   // waves the combine aims for (16 per CU)
 #endif
 #ifndef EP_COMBINE_Y_NT
-#define EP_COMBINE_Y_NT 0      // non-temporal stores for y
+#define EP_COMBINE_Y_NT 1      // bf16 rows: non-temporal stores for y
 #endif
 #ifndef EP_COMBINE_CONTIG
 #define EP_COMBINE_CONTIG 0    // 1: each wave of a token owns one contiguous part of the row
 #endif
+#ifndef EP_COMBINE_REVERSE
+#define EP_COMBINE_REVERSE 1   // bf16 rows: tokens from last to first
+#endif
 
+// NT: non-temporal.  Only where each store instruction of a wave covers
+// whole cache lines (the bf16 kernel's 64 lanes x 16 contiguous bytes); the
+// mxfp8 / nvfp4 kernels' lanes write 32 / 64-byte pieces, and non-temporal
+// partial lines there made the nvfp4 combine twice as slow.
+template <bool NT>
 __device__ __forceinline__ void store_y(char *p, vec16 v) {
-    if (EP_COMBINE_Y_NT) st16_nt(p, v); else st16(p, v);
+    if (NT) st16_nt(p, v); else st16(p, v);
 }
 
 // Slot j of the token in a scalar register; lanes >= k hold -1, so any j < 64
@@ -72,9 +85,10 @@ __global__ __launch_bounds__(256) void ep_combine_bf16_kernel(CombineArgs a) {
     constexpr int KB = KC > 0 ? KC : kSlotBatch;
     const int lane = threadIdx.x & (kWave - 1);
     const int64_t gw = (int64_t)blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
-    const int64_t t = gw / a.S;
-    const int sub = (int)(gw - t * a.S);
-    if (t >= a.T) return;
+    const int64_t tw = gw / a.S;
+    const int sub = (int)(gw - tw * a.S);
+    if (tw >= a.T) return;
+    const int64_t t = EP_COMBINE_REVERSE ? a.T - 1 - tw : tw;
     const int k = KC > 0 ? KC : a.k;
 
     int32_t slot = -1;
@@ -133,7 +147,7 @@ __global__ __launch_bounds__(256) void ep_combine_bf16_kernel(CombineArgs a) {
 #pragma unroll
             for (int q = 0; q < 4; ++q)
                 o[q] = any_valid ? pack_bf16x2(acc[i][2 * q], acc[i][2 * q + 1]) : 0u;
-            store_y(yrow + (int64_t)v * 16, o);
+            store_y<EP_COMBINE_Y_NT>(yrow + (int64_t)v * 16, o);
         }
     }
 }
@@ -203,8 +217,8 @@ __global__ __launch_bounds__(256) void ep_combine_mxfp8_kernel(CombineArgs a) {
             o0[q] = any_valid ? pack_bf16x2(acc[2 * q], acc[2 * q + 1]) : 0u;
             o1[q] = any_valid ? pack_bf16x2(acc[8 + 2 * q], acc[8 + 2 * q + 1]) : 0u;
         }
-        store_y(yrow + (int64_t)v * 32, o0);
-        store_y(yrow + (int64_t)v * 32 + 16, o1);
+        store_y<false>(yrow + (int64_t)v * 32, o0);
+        store_y<false>(yrow + (int64_t)v * 32 + 16, o1);
     }
 }
 
@@ -276,7 +290,7 @@ __global__ __launch_bounds__(256) void ep_combine_nvfp4_kernel(CombineArgs a) {
 #pragma unroll
             for (int q = 0; q < 4; ++q)
                 out[q] = any_valid ? pack_bf16x2(acc[8 * o + 2 * q], acc[8 * o + 2 * q + 1]) : 0u;
-            store_y(yrow + (int64_t)v * 64 + 16 * o, out);
+            store_y<false>(yrow + (int64_t)v * 64 + 16 * o, out);
         }
     }
 }

@@ -11,11 +11,13 @@
 // How: one wave per (token, row part).  Lanes 0..k-1 form the token's k slots
 // and readlane broadcasts them to scalar registers, so the k destinations are
 // wave-uniform.  Every lane loads its 16-byte vectors of row t once and
-// stores them k times.  Stores are plain (write-back) when the combine may
-// read the receive rows as they are (bf16 rows, bf16 combine payload): part
-// of them is then still in the memory-side cache when the combine reads
-// them, which measured faster for the dispatch -> combine sequence than
-// non-temporal stores.  Other format pairs store non-temporal.
+// stores them k times.  When the combine may read the receive rows as they
+// are (bf16 rows, bf16 combine payload), the rows of the first tokens, up to
+// EP_DISPATCH_PLAIN_MIB, are stored plain (write-back) and stay in the 256 MB
+// memory-side cache until the combine reads them; the later tokens' rows are
+// stored non-temporal so they do not evict the first ones.  The combine
+// reads the tokens last to first (the rows that come from HBM first) and
+// stores y non-temporal.  Other format pairs store every row non-temporal.
 //
 // The cached form (ep_dispatch_cached) takes the slots from a previous
 // dispatch's handle instead of a plan: the same rows, for another tensor of
@@ -39,6 +41,9 @@ namespace {
 #endif
 #ifndef EP_DISPATCH_WAVES
 #define EP_DISPATCH_WAVES 4096   // waves the copy aims for (4 per CU)
+#endif
+#ifndef EP_DISPATCH_PLAIN_MIB
+#define EP_DISPATCH_PLAIN_MIB 192   // receive bytes (MiB) stored plain when the combine reads them
 #endif
 
 struct CopyArgs {
@@ -67,7 +72,8 @@ struct CopyArgs {
     int nvec;                 // row_bytes / 16
     int G;                    // fp32 scales per row (0 for bf16 rows)
     int S;                    // waves per token
-    int nt_store;             // non-temporal row stores (see copy_args)
+    int nt_store;             // non-temporal row stores for every token (see copy_args)
+    int64_t plain_tokens;     // otherwise: tokens t < plain_tokens store plain, the rest non-temporal
     // single-launch form only: layout outputs (null when not wanted)
     int R, N, epn, epn_shift;
     int32_t *per_rank, *per_expert, *per_node;
@@ -118,6 +124,35 @@ __device__ __forceinline__ int32_t counted_slot(const CopyArgs &a, int64_t t, in
     }
     __syncthreads();
     return lane < a.k ? slot_sm[lane] : -1;
+}
+
+// Row t's vectors of this wave into the token's valid slots, VPL vectors per
+// lane per pass (the first pass is already in buf); NT: non-temporal stores.
+template <int VPL, bool NT>
+__device__ __forceinline__ void store_rows(const CopyArgs &a, const char *src, int32_t slot, vec16 (&buf)[VPL],
+                                           int v_first, int stride) {
+    for (int v0 = v_first; v0 < a.nvec; v0 += stride * VPL) {
+        if (v0 != v_first) {
+#pragma unroll
+            for (int i = 0; i < VPL; ++i) {
+                const int v = v0 + i * stride;
+                if (v < a.nvec) buf[i] = ld16(src + (int64_t)v * 16);
+            }
+        }
+        for (int j = 0; j < a.k; ++j) {
+            const int32_t s = readlane(slot, j);
+            if (s < 0) continue;
+            char *dst = a.recv_x + (int64_t)s * a.row_bytes;
+#pragma unroll
+            for (int i = 0; i < VPL; ++i) {
+                const int v = v0 + i * stride;
+                if (v < a.nvec) {
+                    if (NT) st16_nt(dst + (int64_t)v * 16, buf[i]);
+                    else st16(dst + (int64_t)v * 16, buf[i]);
+                }
+            }
+        }
+    }
 }
 
 // VPL: 16-byte vectors each lane holds per pass.  KEYS > 0: the single-launch
@@ -232,28 +267,12 @@ __global__ __launch_bounds__(KEYS ? 1024 : 256) void ep_dispatch_copy_kernel(Cop
         }
     }
 
-    for (int v0 = v_first; v0 < a.nvec; v0 += stride * VPL) {
-        if (v0 != v_first) {
-#pragma unroll
-            for (int i = 0; i < VPL; ++i) {
-                const int v = v0 + i * stride;
-                if (v < a.nvec) buf[i] = ld16(src + (int64_t)v * 16);
-            }
-        }
-        for (int j = 0; j < a.k; ++j) {
-            const int32_t s = readlane(slot, j);
-            if (s < 0) continue;
-            char *dst = a.recv_x + (int64_t)s * a.row_bytes;
-#pragma unroll
-            for (int i = 0; i < VPL; ++i) {
-                const int v = v0 + i * stride;
-                if (v < a.nvec) {
-                    if (EP_DISPATCH_NT_STORE || NT) st16_nt(dst + (int64_t)v * 16, buf[i]);
-                    else st16(dst + (int64_t)v * 16, buf[i]);
-                }
-            }
-        }
-    }
+    // wave-uniform choice between two copies of the store loop (one store
+    // kind each, so the compiler keeps both)
+    if (EP_DISPATCH_NT_STORE || NT || t >= a.plain_tokens)
+        store_rows<VPL, true>(a, src, slot, buf, v_first, stride);
+    else
+        store_rows<VPL, false>(a, src, slot, buf, v_first, stride);
 }
 
 }  // namespace
@@ -266,6 +285,20 @@ int waves_per_token(int64_t T, int64_t row_vectors, int64_t target) {
 }
 
 namespace {
+
+// Tokens whose receive rows are stored plain when the combine reads the
+// receive rows as they are: the first ones, up to EP_DISPATCH_PLAIN_MIB of
+// rows (under the 256 MB memory-side cache, leaving room for x); the later
+// tokens' rows are stored non-temporal, so they do not evict the first ones.
+// Measured per dispatch -> combine step against plain stores for every row:
+// T = 2048, 4096 and 8192 (skewed) at hidden 7168, top-8: 105 -> 94,
+// 193 -> 181 and 413 -> 376 us.
+int64_t plain_tokens(int64_t T, int64_t bytes_per_token) {
+    const int64_t budget = (int64_t)EP_DISPATCH_PLAIN_MIB << 20;
+    if (bytes_per_token <= 0) return T;
+    const int64_t n = budget / bytes_per_token;
+    return n < T ? n : T;
+}
 
 CopyArgs copy_args(const Shape &s, const void *x, const float *x_scales, const int64_t *topk_idx,
                    const float *topk_w, void *recv_x, float *recv_x_scales, int32_t *recv_src_idx,
@@ -304,8 +337,9 @@ CopyArgs copy_args(const Shape &s, const void *x, const float *x_scales, const i
     // bypass the memory-side cache instead of filling it with lines the
     // combine will not read (quant: 128 -> 118 us per step, nvfp4: 165 ->
     // 158 us).  When the formats match, the combine may read them as they
-    // are, and plain stores leave part of them in that cache.
+    // are, and the first plain_tokens tokens' rows stay in that cache.
     a.nt_store = !(s.x_fmt == 0 && s.y_fmt == 0);
+    a.plain_tokens = a.nt_store ? 0 : plain_tokens(s.T, (int64_t)s.k * a.row_bytes);
     return a;
 }
 

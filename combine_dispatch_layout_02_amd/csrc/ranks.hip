@@ -45,6 +45,9 @@ namespace {
 #ifndef EP_RANKS_NT_STORE
 #define EP_RANKS_NT_STORE 1          // non-temporal stores for the received rows
 #endif
+#ifndef EP_RANKS_Y_NT
+#define EP_RANKS_Y_NT 1              // non-temporal stores for y (whole lines per instruction)
+#endif
 #ifndef EP_RANKS_COMBINE_VECS
 #define EP_RANKS_COMBINE_VECS 4      // 16-byte vectors per lane per pass in combine
 #endif
@@ -414,7 +417,8 @@ __global__ __launch_bounds__(256) void ep_combine_ranks_kernel(RankCombineArgs a
             vec16 o;
 #pragma unroll
             for (int q = 0; q < 4; ++q) o[q] = live ? pack_bf16x2(acc[i][2 * q], acc[i][2 * q + 1]) : 0u;
-            st16(yrow + (int64_t)v * 16, o);
+            if (EP_RANKS_Y_NT) st16_nt(yrow + (int64_t)v * 16, o);
+            else st16(yrow + (int64_t)v * 16, o);
         }
     }
 }
