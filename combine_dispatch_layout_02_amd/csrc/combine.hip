@@ -58,6 +58,9 @@ constexpr int kSlotBatch = 8;
 #ifndef EP_COMBINE_CONTIG
 #define EP_COMBINE_CONTIG 0    // 1: each wave of a token owns one contiguous part of the row
 #endif
+#ifndef EP_COMBINE_SMALL_WAVES
+#define EP_COMBINE_SMALL_WAVES 4096   // bf16 rows: fewer waves than this -> one vector per lane
+#endif
 #ifndef EP_COMBINE_REVERSE
 #define EP_COMBINE_REVERSE 1   // bf16 rows: tokens from last to first
 #endif
@@ -323,6 +326,13 @@ hipError_t launch_combine(const Shape &s, const void *expert_out, const uint8_t 
     } else if (mx) {
         if (s.k == 8) hipLaunchKernelGGL(ep_combine_mxfp8_kernel<8>, grid, block, 0, stream, a);
         else hipLaunchKernelGGL(ep_combine_mxfp8_kernel<0>, grid, block, 0, stream, a);
+    } else if (waves < EP_COMBINE_SMALL_WAVES) {
+        // a small batch does not fill the chip at 64 row vectors per wave:
+        // one wave per 64 vectors of a row, one vector per lane
+        a.S = (a.nvec + kWave - 1) / kWave;
+        const dim3 g2((unsigned)((s.T * a.S + 3) / 4));
+        if (s.k == 8) hipLaunchKernelGGL((ep_combine_bf16_kernel<1, 8>), g2, block, 0, stream, a);
+        else hipLaunchKernelGGL((ep_combine_bf16_kernel<1, 0>), g2, block, 0, stream, a);
     } else {
         if (s.k == 8) hipLaunchKernelGGL((ep_combine_bf16_kernel<EP_COMBINE_VECS, 8>), grid, block, 0, stream, a);
         else hipLaunchKernelGGL((ep_combine_bf16_kernel<EP_COMBINE_VECS, 0>), grid, block, 0, stream, a);

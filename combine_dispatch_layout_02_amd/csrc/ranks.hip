@@ -48,6 +48,9 @@ namespace {
 #ifndef EP_RANKS_Y_NT
 #define EP_RANKS_Y_NT 1              // non-temporal stores for y (whole lines per instruction)
 #endif
+#ifndef EP_RANKS_COMBINE_SMALL_WAVES
+#define EP_RANKS_COMBINE_SMALL_WAVES 4096   // fewer combine waves than this -> one vector per lane
+#endif
 #ifndef EP_RANKS_COMBINE_VECS
 #define EP_RANKS_COMBINE_VECS 4      // 16-byte vectors per lane per pass in combine
 #endif
@@ -623,8 +626,14 @@ hipError_t launch_combine_ranks(const Shape &s, const uint16_t *partial,
     a.nvec = s.H / 8;
     a.S = waves_per_token(s.T, a.nvec, EP_RANKS_COMBINE_WAVES);
     const int64_t waves = s.T * a.S;
-    hipLaunchKernelGGL(ep_combine_ranks_kernel<EP_RANKS_COMBINE_VECS>, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0,
-                       stream, a);
+    if (waves < EP_RANKS_COMBINE_SMALL_WAVES) {
+        // a small batch: one wave per 64 vectors of a row, one vector per lane
+        a.S = (a.nvec + kWave - 1) / kWave;
+        hipLaunchKernelGGL(ep_combine_ranks_kernel<1>, dim3((unsigned)((s.T * a.S + 3) / 4)), dim3(256), 0, stream, a);
+    } else {
+        hipLaunchKernelGGL(ep_combine_ranks_kernel<EP_RANKS_COMBINE_VECS>, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0,
+                           stream, a);
+    }
     return hipGetLastError();
 }
 
