@@ -183,14 +183,15 @@ __device__ __forceinline__ void block_exclusive_scan(const int32_t *in, int32_t 
     }
     if (lane == kWave - 1) tmp[wid] = v;
     __syncthreads();
-    if (tid == 0) {
-        int32_t run = 0;
-        for (int i = 0; i < nw; ++i) {
-            const int32_t x = tmp[i];
-            tmp[i] = run;
-            run += x;
+    if (wid == 0) {   // the wave totals (nw <= 16), scanned by the first wave
+        const int32_t x = lane < nw ? tmp[lane] : 0;
+        int32_t incl = x;
+        for (int off = 1; off < kWave; off <<= 1) {
+            const int32_t u = __shfl_up(incl, off);
+            if (lane >= off) incl += u;
         }
-        tmp[nw] = run;
+        if (lane < nw) tmp[lane] = incl - x;
+        if (lane == kWave - 1) tmp[nw] = incl;
     }
     __syncthreads();
     int32_t excl = tmp[wid] + v - s;

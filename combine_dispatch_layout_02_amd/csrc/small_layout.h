@@ -10,9 +10,9 @@
 // Ids >= E count as masked and raise the bad-expert flag.
 //
 // How: the batch's ids staged in LDS once; per-expert counts are LDS integer
-// adds (order-independent); per-rank / per-node counts are ballots of one bit
-// of each token's rank / node mask plus popcount; scans are the block and
-// wave scans of ep_device.h.  LDS: 4 * (T*k + E + R + N + blockDim/64 + 1)
+// adds (order-independent), and so are the per-rank / per-node counts (one
+// add per rank / node a token reaches, from its rank / node mask); scans are
+// the block and wave scans of ep_device.h.  LDS: 4 * (T*k + E + R + N + blockDim/64 + 1)
 // bytes (dynamic).
 #pragma once
 
@@ -43,7 +43,7 @@ __device__ inline void small_layout_block(const SmallLayout &a) {
     int32_t *hist = ids + TK;             // [E]
     int32_t *rn = hist + a.E;             // [R + N]
     int32_t *tmp = rn + a.R + a.N;        // [blockDim / 64 + 1]
-    const int tid = threadIdx.x, nt = blockDim.x, lane = tid & (kWave - 1), w = tid / kWave;
+    const int tid = threadIdx.x, nt = blockDim.x, lane = tid & (kWave - 1);
     for (int i = tid; i < a.E; i += nt) hist[i] = 0;
     for (int i = tid; i < a.R + a.N; i += nt) rn[i] = 0;
     __syncthreads();
@@ -72,19 +72,21 @@ __device__ inline void small_layout_block(const SmallLayout &a) {
                 rmask |= 1ull << (a.epr_shift >= 0 ? e >> a.epr_shift : e / a.epr);
                 nmask |= 1ull << (a.epn_shift >= 0 ? e >> a.epn_shift : e / a.epn);
             }
-            if (a.in_rank)
-                for (int r = 0; r < a.R; ++r) a.in_rank[t * a.R + r] = (uint8_t)((rmask >> r) & 1u);
-        }
-        if (tb + w * kWave < a.T) {   // wave-uniform
-            for (int r = 0; r < a.R; ++r) {
-                const uint64_t b = __ballot((rmask >> r) & 1u);
-                if (lane == 0 && b) atomicAdd(&rn[r], (int)__popcll(b));
+            if (a.in_rank) {
+                uint8_t *out = a.in_rank + t * a.R;
+                if ((a.R & 3) == 0) {   // 4 flags per 32-bit store (rows of R bytes, R % 4 == 0)
+                    for (int r0 = 0; r0 < a.R; r0 += 4) {
+                        uint32_t wd = 0;
+                        for (int b = 0; b < 4; ++b) wd |= (uint32_t)((rmask >> (r0 + b)) & 1u) << (8 * b);
+                        *reinterpret_cast<uint32_t *>(out + r0) = wd;
+                    }
+                } else {
+                    for (int r = 0; r < a.R; ++r) out[r] = (uint8_t)((rmask >> r) & 1u);
+                }
             }
-            for (int n = 0; n < a.N; ++n) {
-                const uint64_t b = __ballot((nmask >> n) & 1u);
-                if (lane == 0 && b) atomicAdd(&rn[a.R + n], (int)__popcll(b));
-            }
         }
+        for (uint64_t m = rmask; m; m &= m - 1) atomicAdd(&rn[__builtin_ctzll(m)], 1);
+        for (uint64_t m = nmask; m; m &= m - 1) atomicAdd(&rn[a.R + __builtin_ctzll(m)], 1);
     }
     __syncthreads();
     if (a.per_rank) {
