@@ -260,7 +260,7 @@ def ep_dispatch(shape, x, x_scales, topk_idx, topk_w, recv_x, recv_x_scales, rec
 def ep_dispatch_with_layout(shape, x, x_scales, topk_idx, topk_w, num_tokens_per_rank, num_tokens_per_expert,
                             is_token_in_rank, num_tokens_per_node, rdma_algo_token_count, recv_x, recv_x_scales,
                             recv_src_idx, recv_topk_w, token_slot, expert_offset, ws: Workspace, stream=None):
-    """Layout and dispatch in one call (one launch for batches of <= 1024 pairs)."""
+    """Layout and dispatch in one call (one launch for batches of <= 2048 pairs)."""
     T, k, H, E, R, N = (shape.num_tokens, shape.num_topk, shape.hidden, shape.num_experts, shape.num_ranks,
                         shape.num_nodes)
     fp8 = shape.x_format == EP_FMT_FP8_S128
