@@ -57,7 +57,8 @@ def test_ragged_token_counts(T):
     dict(mask_frac=0.3), dict(mask_frac=0.3, mask_tokens=0.1), dict(routing="replace"),
     dict(routing="replace", mask_frac=0.2, k=16), dict(k=1), dict(E=16, R=16, N=16, k=4),
     dict(E=64, R=64, N=8, k=8), dict(E=4096, R=64, N=64, k=32, T=300), dict(H=8, T=100),
-    dict(H=7176, T=130)])
+    dict(H=7176, T=130),
+    dict(T=5000, H=2048, k=6, mask_frac=0.1)])   # enough waves for the multi-vector combine, k not 8
 def test_edge_cases_bf16(kw):
     kw = dict(kw)
     base = dict(T=kw.pop("T", 700), H=kw.pop("H", 512))
@@ -67,7 +68,8 @@ def test_edge_cases_bf16(kw):
         assert ndiff == 0
 
 
-@pytest.mark.parametrize("kw", [dict(mask_frac=0.25), dict(routing="replace", T=333), dict(E=32, R=8, N=2)])
+@pytest.mark.parametrize("kw", [dict(mask_frac=0.25), dict(routing="replace", T=333), dict(E=32, R=8, N=2),
+                                dict(k=6, T=300, mask_frac=0.1)])
 def test_edge_cases_quantized(kw):
     kw = dict(kw)
     base = dict(T=kw.pop("T", 500), H=1024)
@@ -200,7 +202,8 @@ def test_rank_major_overflow_is_flagged_and_dropped():
     gpu_path.compare(g, r, False)
 
 
-@pytest.mark.parametrize("kw", [dict(), dict(mask_frac=0.25, T=777), dict(routing="replace", T=300)])
+@pytest.mark.parametrize("kw", [dict(), dict(mask_frac=0.25, T=777), dict(routing="replace", T=300),
+                                dict(k=5, T=300)])
 def test_nvfp4_payload(kw):
     kw = dict(kw)
     base = dict(T=kw.pop("T", 500), H=1024)
