@@ -58,7 +58,8 @@ def test_ragged_token_counts(T):
     dict(routing="replace", mask_frac=0.2, k=16), dict(k=1), dict(E=16, R=16, N=16, k=4),
     dict(E=64, R=64, N=8, k=8), dict(E=4096, R=64, N=64, k=32, T=300), dict(H=8, T=100),
     dict(H=7176, T=130),
-    dict(T=5000, H=2048, k=6, mask_frac=0.1)])   # enough waves for the multi-vector combine, k not 8
+    dict(T=5000, H=2048, k=6, mask_frac=0.1),    # enough waves for the multi-vector combine, k not 8
+    dict(T=13000, H=1024, k=8, mask_frac=0.1)])  # receive rows past the plain-store budget, short rows
 def test_edge_cases_bf16(kw):
     kw = dict(kw)
     base = dict(T=kw.pop("T", 700), H=kw.pop("H", 512))
