@@ -23,7 +23,9 @@
 // non-temporal.  The dispatch leaves the first tokens' receive rows in the
 // memory-side cache and streams the later ones to HBM; this order reads the
 // HBM rows first and the cached rows last, and y does not evict them
-// (T = 4096, hidden 7168, top-8: 101 -> 85 us).
+// (T = 4096, hidden 7168, top-8: 101 -> 85 us).  Taking the cached tokens
+// interleaved with the others, as the dispatch does, made the combine slower
+// (85 -> 92 us); first to last is on par with last to first.
 #include "ep_device.h"
 #include "ep_internal.h"
 
@@ -42,6 +44,7 @@ struct CombineArgs {
     int64_t rows;               // receive rows (T*k, or R*M for RANK_MAJOR)
     int nvec;                   // 16-byte vectors per payload row
     int S;                      // waves per token
+    int64_t cached;             // tokens [0, cached) have their rows in the memory-side cache
 };
 
 constexpr int kSlotBatch = 8;
@@ -61,8 +64,9 @@ constexpr int kSlotBatch = 8;
 #ifndef EP_COMBINE_SMALL_WAVES
 #define EP_COMBINE_SMALL_WAVES 4096   // bf16 rows: fewer waves than this -> one vector per lane
 #endif
-#ifndef EP_COMBINE_REVERSE
-#define EP_COMBINE_REVERSE 1   // bf16 rows: tokens from last to first
+#ifndef EP_COMBINE_ORDER
+#define EP_COMBINE_ORDER 1     // bf16 rows: 0 tokens first to last, 1 last to first,
+                               // 2 cached tokens interleaved with the others
 #endif
 
 // NT: non-temporal.  Only where each store instruction of a wave covers
@@ -91,7 +95,8 @@ __global__ __launch_bounds__(256) void ep_combine_bf16_kernel(CombineArgs a) {
     const int64_t tw = gw / a.S;
     const int sub = (int)(gw - tw * a.S);
     if (tw >= a.T) return;
-    const int64_t t = EP_COMBINE_REVERSE ? a.T - 1 - tw : tw;
+    const int64_t t = EP_COMBINE_ORDER == 1 ? a.T - 1 - tw
+                      : EP_COMBINE_ORDER == 2 ? interleaved_token(tw, a.T, a.cached) : tw;
     const int k = KC > 0 ? KC : a.k;
 
     int32_t slot = -1;
@@ -314,6 +319,7 @@ hipError_t launch_combine(const Shape &s, const void *expert_out, const uint8_t 
     a.k = s.k;
     a.H = s.H;
     a.rows = s.rows();
+    a.cached = cached_tokens(s);
     const bool mx = (s.y_fmt == 2), nv = (s.y_fmt == 3);
     a.row_bytes = nv ? (int64_t)s.H / 2 : (mx ? (int64_t)s.H : 2 * (int64_t)s.H);
     a.nvec = (int)(a.row_bytes / 16);

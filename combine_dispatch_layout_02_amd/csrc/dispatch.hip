@@ -15,9 +15,14 @@
 // are (bf16 rows, bf16 combine payload), the rows of the first tokens, up to
 // EP_DISPATCH_PLAIN_MIB, are stored plain (write-back) and stay in the 256 MB
 // memory-side cache until the combine reads them; the later tokens' rows are
-// stored non-temporal so they do not evict the first ones.  The combine
-// reads the tokens last to first (the rows that come from HBM first) and
-// stores y non-temporal.  Other format pairs store every row non-temporal.
+// stored non-temporal so they do not evict the first ones.  The waves take
+// the two kinds of token interleaved (position g of P cached tokens among T
+// goes to a cached token when floor((g+1)P/T) > floor(gP/T)), so writes into
+// the cache and writes to HBM run side by side instead of one phase after
+// the other (T = 4096, hidden 7168, top-8: 83 -> 78 us; T = 8192 skewed:
+// 174 -> 158 us).  The combine reads the tokens last to first (the rows that
+// come from HBM first) and stores y non-temporal.  Other format pairs store
+// every row non-temporal.
 //
 // The cached form (ep_dispatch_cached) takes the slots from a previous
 // dispatch's handle instead of a plan: the same rows, for another tensor of
@@ -41,6 +46,9 @@ namespace {
 #endif
 #ifndef EP_DISPATCH_WAVES
 #define EP_DISPATCH_WAVES 4096   // waves the copy aims for (4 per CU)
+#endif
+#ifndef EP_DISPATCH_ORDER
+#define EP_DISPATCH_ORDER 1      // 1: tokens stored plain interleaved with the non-temporal ones
 #endif
 #ifndef EP_DISPATCH_PLAIN_MIB
 #define EP_DISPATCH_PLAIN_MIB 192   // receive bytes (MiB) stored plain when the combine reads them
@@ -194,8 +202,9 @@ __global__ __launch_bounds__(KEYS ? 1024 : 256) void ep_dispatch_copy_kernel(Cop
         sub = threadIdx.x / kWave;
     } else {
         const int64_t gw = (int64_t)blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
-        t = gw / a.S;
-        sub = (int)(gw - t * a.S);
+        const int64_t pos = gw / a.S;
+        sub = (int)(gw - pos * a.S);
+        t = (EP_DISPATCH_ORDER && pos < a.T) ? interleaved_token(pos, a.T, a.plain_tokens) : pos;
         const int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
         if (!a.slots_in && g <= a.E) a.expert_offset[g] = a.plan_offset[g];   // handle copy of the segment starts
     }
@@ -277,6 +286,21 @@ __global__ __launch_bounds__(KEYS ? 1024 : 256) void ep_dispatch_copy_kernel(Cop
 
 }  // namespace
 
+// Tokens whose receive rows are stored plain when the combine reads the
+// receive rows as they are: the first ones, up to EP_DISPATCH_PLAIN_MIB of
+// rows (under the 256 MB memory-side cache, leaving room for x); the later
+// tokens' rows are stored non-temporal, so they do not evict the first ones.
+// Measured per dispatch -> combine step against plain stores for every row:
+// T = 2048, 4096 and 8192 (skewed) at hidden 7168, top-8: 105 -> 94,
+// 193 -> 181 and 413 -> 376 us.  The combine derives the same count from the
+// shape.
+int64_t cached_tokens(const Shape &s) {
+    if (!(s.x_fmt == 0 && s.y_fmt == 0)) return 0;   // the combine reads re-encoded rows
+    const int64_t bytes_per_token = (int64_t)s.k * 2 * s.H;
+    const int64_t n = ((int64_t)EP_DISPATCH_PLAIN_MIB << 20) / bytes_per_token;
+    return n < s.T ? n : s.T;
+}
+
 int waves_per_token(int64_t T, int64_t row_vectors, int64_t target) {
     // aim for `target` waves, keep >= 64 row vectors per wave
     int S = 1;
@@ -285,20 +309,6 @@ int waves_per_token(int64_t T, int64_t row_vectors, int64_t target) {
 }
 
 namespace {
-
-// Tokens whose receive rows are stored plain when the combine reads the
-// receive rows as they are: the first ones, up to EP_DISPATCH_PLAIN_MIB of
-// rows (under the 256 MB memory-side cache, leaving room for x); the later
-// tokens' rows are stored non-temporal, so they do not evict the first ones.
-// Measured per dispatch -> combine step against plain stores for every row:
-// T = 2048, 4096 and 8192 (skewed) at hidden 7168, top-8: 105 -> 94,
-// 193 -> 181 and 413 -> 376 us.
-int64_t plain_tokens(int64_t T, int64_t bytes_per_token) {
-    const int64_t budget = (int64_t)EP_DISPATCH_PLAIN_MIB << 20;
-    if (bytes_per_token <= 0) return T;
-    const int64_t n = budget / bytes_per_token;
-    return n < T ? n : T;
-}
 
 CopyArgs copy_args(const Shape &s, const void *x, const float *x_scales, const int64_t *topk_idx,
                    const float *topk_w, void *recv_x, float *recv_x_scales, int32_t *recv_src_idx,
@@ -339,7 +349,7 @@ CopyArgs copy_args(const Shape &s, const void *x, const float *x_scales, const i
     // 158 us).  When the formats match, the combine may read them as they
     // are, and the first plain_tokens tokens' rows stay in that cache.
     a.nt_store = !(s.x_fmt == 0 && s.y_fmt == 0);
-    a.plain_tokens = a.nt_store ? 0 : plain_tokens(s.T, (int64_t)s.k * a.row_bytes);
+    a.plain_tokens = cached_tokens(s);
     return a;
 }
 

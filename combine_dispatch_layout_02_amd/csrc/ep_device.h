@@ -165,6 +165,18 @@ __device__ __forceinline__ void st16_nt(void *p, vec16 v) {
     __builtin_nontemporal_store(v, reinterpret_cast<vec16 *>(p));
 }
 
+// ---------------------------------------------------------------- token orders
+
+// Execution position g in [0, T) -> token, spreading the tokens [0, P) evenly
+// among the tokens [P, T): position g takes the next token of [0, P) when
+// floor((g + 1) P / T) > floor(g P / T), else the next token of [P, T).  A
+// bijection of [0, T) (the first kind occurs exactly P times).
+__device__ __forceinline__ int64_t interleaved_token(int64_t g, int64_t T, int64_t P) {
+    if (P <= 0 || P >= T) return g;
+    const int64_t c0 = (g * P) / T, c1 = ((g + 1) * P) / T;
+    return c1 > c0 ? c0 : P + (g - c0);
+}
+
 // ---------------------------------------------------------------- scans
 
 // Exclusive scan of n ints held in LDS (`in`), written to `out` (n + 1

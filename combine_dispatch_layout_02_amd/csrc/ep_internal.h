@@ -81,6 +81,10 @@ hipError_t launch_dispatch_fused(const Shape &s, const void *x, const float *x_s
                                  int32_t *per_expert, uint8_t *in_rank, int32_t *per_node,
                                  int64_t *algo, uint32_t *ctrl, hipStream_t stream);
 
+// Tokens [0, n) whose receive rows the dispatch stores plain (they stay in
+// the memory-side cache for the combine); the others are stored non-temporal.
+int64_t cached_tokens(const Shape &s);
+
 hipError_t launch_combine(const Shape &s, const void *expert_out, const uint8_t *expert_scales,
                           const int32_t *token_slot, const float *topk_w, void *y,
                           hipStream_t stream);
