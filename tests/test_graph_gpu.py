@@ -86,10 +86,14 @@ def _ranks_step(inp):
     return step, ws, lambda: (gpu_path.bf16_bits(y), trs.cpu().numpy(), lay["r"].cpu().numpy())
 
 
-@pytest.mark.parametrize("case", ["pairs", "pairs_one_call_small", "pairs_one_call_large", "ranks"])
+@pytest.mark.parametrize("case", ["pairs", "pairs_full_size", "pairs_one_call_small", "pairs_one_call_large", "ranks"])
 def test_graph_replays_match_eager(case):
     if case == "pairs":
         inp = W.make_inputs("prefill2n", T=1000, H=1024, mask_frac=0.05)
+        step, ws, read = _pairs_step(inp, one_call=False)
+        ref = oracle.run_path(inp)
+    elif case == "pairs_full_size":   # receive rows beyond the cache budget: interleaved dispatch order
+        inp = W.make_inputs("prefill2n")
         step, ws, read = _pairs_step(inp, one_call=False)
         ref = oracle.run_path(inp)
     elif case == "pairs_one_call_small":   # a single launch for layout + dispatch
