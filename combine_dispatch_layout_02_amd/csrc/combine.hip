@@ -69,13 +69,43 @@ constexpr int kSlotBatch = 8;
                                // 2 cached tokens interleaved with the others
 #endif
 
+#ifndef EP_COMBINE_Q_YT
+#define EP_COMBINE_Q_YT 1      // mxfp8 / nvfp4: y through a per-wave LDS transpose, non-temporal
+                               // (0: plain stores of each lane's pieces)
+#endif
+
 // NT: non-temporal.  Only where each store instruction of a wave covers
-// whole cache lines (the bf16 kernel's 64 lanes x 16 contiguous bytes); the
-// mxfp8 / nvfp4 kernels' lanes write 32 / 64-byte pieces, and non-temporal
-// partial lines there made the nvfp4 combine twice as slow.
+// whole cache lines (64 lanes x 16 contiguous bytes): the lanes of the mxfp8
+// / nvfp4 kernels hold 32 / 64 contiguous bytes of y each, and non-temporal
+// stores of those pieces straight from the lanes (partial lines per
+// instruction) made the nvfp4 combine twice as slow; they go through an LDS
+// transpose first (store_y_transposed).
 template <bool NT>
 __device__ __forceinline__ void store_y(char *p, vec16 v) {
     if (NT) st16_nt(p, v); else st16(p, v);
+}
+
+// y of one pass of a quantized-payload combine: lane l holds O 16-byte
+// vectors, bytes [(v0 + l) * 16 * O, (v0 + l + 1) * 16 * O) of the y row, so
+// the wave's O * 64 vectors are one contiguous stretch.  They go through LDS
+// (each wave its own O * 64 slots; the wave barriers keep the LDS accesses of
+// consecutive passes in order) and each store instruction then writes 1 KB
+// of contiguous y -- whole lines, stored non-temporal (nvfp4, T = 4096,
+// hidden 7168, top-8: 43.1 -> 38.9 us against plain stores of the pieces;
+// mxfp8 on par).  Vectors of lanes past the row end are not stored.
+template <int O>
+__device__ __forceinline__ void store_y_transposed(vec16 *wbuf, const vec16 (&out)[O], char *yrow, int v0,
+                                                   int nvec, int lane) {
+#pragma unroll
+    for (int o = 0; o < O; ++o) wbuf[lane * O + o] = out[o];
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int o = 0; o < O; ++o) {
+        const int idx = o * kWave + lane;   // 16-byte vector of the stretch
+        const vec16 val = wbuf[idx];
+        if (v0 + idx / O < nvec) store_y<true>(yrow + ((int64_t)v0 * O + idx) * 16, val);
+    }
+    __builtin_amdgcn_wave_barrier();
 }
 
 // Slot j of the token in a scalar register; lanes >= k hold -1, so any j < 64
@@ -189,7 +219,11 @@ __global__ __launch_bounds__(256) void ep_combine_mxfp8_kernel(CombineArgs a) {
     const int stride = kWave * a.S;
     const int G32 = a.H / 32;
 
-    for (int v = lane + kWave * sub; v < a.nvec; v += stride) {
+    __shared__ vec16 ybuf[4][2 * kWave];   // per wave of the block (EP_COMBINE_Q_YT)
+    for (int v0 = kWave * sub; v0 < a.nvec; v0 += stride) {   // uniform passes
+        // lanes past the row re-read its last vector and store nothing
+        const bool in_row = v0 + lane < a.nvec;
+        const int v = in_row ? v0 + lane : a.nvec - 1;
         float acc[16];
 #pragma unroll
         for (int q = 0; q < 16; ++q) acc[q] = -0.0f;
@@ -219,14 +253,18 @@ __global__ __launch_bounds__(256) void ep_combine_mxfp8_kernel(CombineArgs a) {
                 }
             }
         }
-        vec16 o0, o1;
+        vec16 out[2];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-            o0[q] = any_valid ? pack_bf16x2(acc[2 * q], acc[2 * q + 1]) : 0u;
-            o1[q] = any_valid ? pack_bf16x2(acc[8 + 2 * q], acc[8 + 2 * q + 1]) : 0u;
+            out[0][q] = any_valid ? pack_bf16x2(acc[2 * q], acc[2 * q + 1]) : 0u;
+            out[1][q] = any_valid ? pack_bf16x2(acc[8 + 2 * q], acc[8 + 2 * q + 1]) : 0u;
         }
-        store_y<false>(yrow + (int64_t)v * 32, o0);
-        store_y<false>(yrow + (int64_t)v * 32 + 16, o1);
+        if (EP_COMBINE_Q_YT) {
+            store_y_transposed<2>(ybuf[threadIdx.x / kWave], out, yrow, v0, a.nvec, lane);
+        } else if (in_row) {
+            store_y<false>(yrow + (int64_t)v * 32, out[0]);
+            store_y<false>(yrow + (int64_t)v * 32 + 16, out[1]);
+        }
     }
 }
 
@@ -260,7 +298,11 @@ __global__ __launch_bounds__(256) void ep_combine_nvfp4_kernel(CombineArgs a) {
     const int G16 = a.H / 16;
     const uint16_t *scales = reinterpret_cast<const uint16_t *>(a.eo_scales);
 
-    for (int v = lane + kWave * sub; v < a.nvec; v += stride) {
+    __shared__ vec16 ybuf[4][4 * kWave];   // per wave of the block (EP_COMBINE_Q_YT)
+    for (int v0 = kWave * sub; v0 < a.nvec; v0 += stride) {   // uniform passes
+        // lanes past the row re-read its last vector and store nothing
+        const bool in_row = v0 + lane < a.nvec;
+        const int v = in_row ? v0 + lane : a.nvec - 1;
         float acc[32];
 #pragma unroll
         for (int q = 0; q < 32; ++q) acc[q] = -0.0f;
@@ -292,13 +334,17 @@ __global__ __launch_bounds__(256) void ep_combine_nvfp4_kernel(CombineArgs a) {
                 }
             }
         }
+        vec16 out[4];
 #pragma unroll
-        for (int o = 0; o < 4; ++o) {
-            vec16 out;
+        for (int o = 0; o < 4; ++o)
 #pragma unroll
             for (int q = 0; q < 4; ++q)
-                out[q] = any_valid ? pack_bf16x2(acc[8 * o + 2 * q], acc[8 * o + 2 * q + 1]) : 0u;
-            store_y<false>(yrow + (int64_t)v * 64 + 16 * o, out);
+                out[o][q] = any_valid ? pack_bf16x2(acc[8 * o + 2 * q], acc[8 * o + 2 * q + 1]) : 0u;
+        if (EP_COMBINE_Q_YT) {
+            store_y_transposed<4>(ybuf[threadIdx.x / kWave], out, yrow, v0, a.nvec, lane);
+        } else if (in_row) {
+#pragma unroll
+            for (int o = 0; o < 4; ++o) store_y<false>(yrow + (int64_t)v * 64 + 16 * o, out[o]);
         }
     }
 }
