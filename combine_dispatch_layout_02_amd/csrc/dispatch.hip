@@ -210,35 +210,55 @@ __global__ __launch_bounds__(KEYS ? 1024 : 256) void ep_dispatch_copy_kernel(Cop
     }
     if (t >= a.T) return;   // wave-uniform (never taken in the single-launch form)
 
-    // the first pass of row t does not depend on the slots: issue its loads
-    // before the slot lookups so the two latencies overlap
-    const char *src = a.x + t * a.row_bytes;
-    const int stride = kWave * a.S;            // vectors between a lane's consecutive vectors
-    const int v_first = lane + kWave * sub;
-    vec16 buf[VPL];
-#pragma unroll
-    for (int i = 0; i < VPL; ++i) {
-        const int v = v_first + i * stride;
-        if (v < a.nvec) buf[i] = ld16(src + (int64_t)v * 16);
+    // A wave's vector loads return in issue order.  The inputs of the
+    // token's slots are loaded first (lanes 0..k-1), then the first pass of
+    // row t, which does not depend on them; the plan lookups that need the
+    // inputs are issued as soon as those arrive, while the row is still in
+    // flight, instead of queueing behind the whole row.
+    int32_t lr = -1, slot_in = -1;
+    int64_t eid = -1;
+    float wv = 0.0f;
+    if (lane < a.k) {
+        const int64_t p = t * a.k + lane;
+        if (!FUSED && a.slots_in) {
+            slot_in = a.slots_in[p];
+        } else {
+            wv = a.topk_w[p];
+            if (!FUSED) {
+                lr = a.local_rank[p];
+                eid = a.topk_idx[p];
+            }
+        }
     }
-    // fp32 scales of an fp8 row (one per 128 elements): this wave's share,
-    // loaded with the row (G <= 64 * S, one value per lane, in every shape the
-    // ABI accepts with hidden <= 8192 * S; larger rows loop below)
+    // fp32 scales of an fp8 row (one per 128 elements): this wave's share
+    // (G <= 64 * S, one value per lane, in every shape the ABI accepts with
+    // hidden <= 8192 * S; larger rows loop below)
     const int g_first = lane + kWave * sub;
     float sc0 = 0.0f;
     if (g_first < a.G) sc0 = a.x_scales[t * a.G + g_first];
+    const char *src = a.x + t * a.row_bytes;
+    const int stride = kWave * a.S;            // vectors between a lane's consecutive vectors
+    const int v_first = lane + kWave * sub;
+    // Unconditional loads (a vector past the row re-reads its last vector and
+    // is not stored), so the compiler knows how many row loads are younger
+    // than the slot inputs and waits for those inputs alone.
+    vec16 buf[VPL];
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) {
+        const int v = min(v_first + i * stride, a.nvec - 1);
+        buf[i] = ld16(src + (int64_t)v * 16);
+    }
 
     // lanes 0..k-1: the token's slots
     int32_t slot = FUSED ? counted_slot<(KEYS > 0 ? KEYS : 1)>(a, t, lane, sub) : -1;
     if (lane < a.k) {
         const int64_t p = t * a.k + lane;
         if (!FUSED && a.slots_in) {   // cached: the slots of a previous dispatch's handle
-            slot = a.slots_in[p];
+            slot = slot_in;
             if ((uint64_t)slot >= (uint64_t)a.rows) slot = -1;   // masked, or not a receive row
         }
-        const int32_t lr = (FUSED || a.slots_in) ? -1 : a.local_rank[p];
-        if (lr >= 0) {
-            const int e = (int)a.topk_idx[p];
+        if (lr >= 0) {   // a valid pair (the plan's local rank is -1 for masked ones)
+            const int e = (int)eid;
             slot = a.plan_offset[e] + a.tile_prefix[(t / a.TT) * a.cols + e] + lr;
             if (a.M > 0) {   // RANK_MAJOR: the same place inside the rank, at the rank's fixed block
                 const int r = a.epr_shift >= 0 ? e >> a.epr_shift : e / a.epr;
@@ -259,7 +279,7 @@ __global__ __launch_bounds__(KEYS ? 1024 : 256) void ep_dispatch_copy_kernel(Cop
             a.token_slot[p] = slot;
             if (slot >= 0) {
                 a.recv_src_idx[slot] = (int32_t)t;
-                a.recv_topk_w[slot] = a.topk_w[p];
+                a.recv_topk_w[slot] = wv;
             }
         }
     }
@@ -356,6 +376,18 @@ CopyArgs copy_args(const Shape &s, const void *x, const float *x_scales, const i
 template <int KEYS, bool NT>
 void launch_copy_nt(const CopyArgs &a, const dim3 &grid, const dim3 &block, size_t lds, hipStream_t stream) {
     const int per_lane = (a.nvec + kWave * a.S - 1) / (kWave * a.S);
+    if constexpr (KEYS == 0) {
+        // hidden 7168 at one wave per token: exactly 14 (bf16) or 7 (e4m3)
+        // vectors per lane, so no lane loads a vector past the row
+        if (a.nvec == 14 * kWave * a.S) {
+            hipLaunchKernelGGL((ep_dispatch_copy_kernel<14, KEYS, NT>), grid, block, lds, stream, a);
+            return;
+        }
+        if (a.nvec == 7 * kWave * a.S) {
+            hipLaunchKernelGGL((ep_dispatch_copy_kernel<7, KEYS, NT>), grid, block, lds, stream, a);
+            return;
+        }
+    }
     if (per_lane <= 2) {
         hipLaunchKernelGGL((ep_dispatch_copy_kernel<2, KEYS, NT>), grid, block, lds, stream, a);
     } else if (per_lane <= 4) {
