@@ -78,3 +78,37 @@ def test_random_shapes_all_paths(seed):
     for with_layout in (False, True):
         g = gpu_path.run_ranks(inp, with_layout=with_layout)
         assert gpu_path.compare_ranks(g, r, False) == 0, f"ranks with_layout={with_layout}"
+
+
+def _draw_quantized(seed):
+    """fp8 rows with an mxfp8 payload, or bf16 rows with an nvfp4 payload, at
+    hidden sizes whose payload rows end part-way through a wave's pass."""
+    rng = np.random.default_rng(5000 + seed)
+    name = "quant" if seed % 2 == 0 else "nvfp4"
+    N = int(rng.choice([1, 2]))
+    R = N * int(rng.choice([1, 2, 4, 8]))
+    E = R * int(rng.choice([1, 3, 4, 16]))
+    k = int(rng.integers(1, min(E, 9) + 1))
+    T = int(rng.choice([1, 7, 64, 130, 257, 600]))
+    H = int(rng.choice([128, 384, 1152, 2176]))
+    kw = dict(T=T, H=H, E=E, R=R, N=N, k=k, routing="replace" if rng.random() < 0.3 else "uniform")
+    if rng.random() < 0.5:
+        kw["mask_frac"] = float(rng.choice([0.1, 0.4]))
+    if rng.random() < 0.3:
+        kw["mask_tokens"] = 0.1
+    if rng.random() < 0.4:
+        kw["expert"] = "scale"
+    return W.make_inputs(name, seed=seed, **kw)
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_random_shapes_quantized(seed):
+    import gpu_path
+    inp = _draw_quantized(seed)
+    fp8, nv = inp.get("x_fmt") == "fp8", inp.get("y_fmt") == "nvfp4"
+    print(f"random quantized case seed={seed} {inp['name']} T={inp['T']} H={inp['H']} E={inp['E']} "
+          f"R={inp['R']} N={inp['N']} k={inp['k']} routing={inp['routing']}", flush=True)
+    ref = oracle.run_path(inp)
+    for mode in ("from_layout", "with_layout"):
+        g = gpu_path.run(inp, from_layout=(mode == "from_layout"), with_layout=(mode == "with_layout"))
+        assert gpu_path.compare(g, ref, fp8, nv) == 0, mode
