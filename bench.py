@@ -25,6 +25,7 @@ Prints one JSON line:
   tokens_per_s  tokens of the batch / step time
   dispatch_combine_gbs  the dispatch and combine calls' algorithmic bytes / their
                 summed per-call durations (the layout pass left out)
+  phase_gbs     each call's algorithmic bytes / its per-call duration
   rel_l2_vs_fp32  relative L2 distance of y from the unquantized fp32 result
   roofline      the longest-running call against the 8 TB/s HBM peak, with
                 hardware byte counts when they were measured for this kernel,
@@ -517,6 +518,7 @@ def measure(workload: str, steps: int, warmup: int, graph: bool = False, layout_
                                       / (sum(phase_us[p] for p in phase_us if p != "layout") * 1e-6) / 1e9, 1),
         "rel_l2_vs_fp32": round(rel_l2, 6),
         "phase_us": {p: round(v, 2) for p, v in phase_us.items()},
+        "phase_gbs": {p: round(algo_bytes[p] / (phase_us[p] * 1e-6) / 1e9, 1) for p in algo_bytes},
         "phase_us_min_p90": phase_stats,
         "phase_us_flushed": None if phase_us_flushed is None else
         {p: round(v, 2) for p, v in phase_us_flushed.items()},
