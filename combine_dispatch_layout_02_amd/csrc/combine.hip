@@ -64,6 +64,12 @@ constexpr int kSlotBatch = 8;
 #ifndef EP_COMBINE_SMALL_WAVES
 #define EP_COMBINE_SMALL_WAVES 4096   // bf16 rows: fewer waves than this -> one vector per lane
 #endif
+#ifndef EP_COMBINE_ONE_PASS
+#define EP_COMBINE_ONE_PASS 1  // bf16 rows: waves per token so that one pass covers a wave's part of the row
+#endif
+#ifndef EP_COMBINE_Q_ONE_PASS
+#define EP_COMBINE_Q_ONE_PASS 1  // mxfp8 / nvfp4: waves per token so that one pass covers a wave's part
+#endif
 #ifndef EP_COMBINE_ORDER
 #define EP_COMBINE_ORDER 1     // bf16 rows: 0 tokens first to last, 1 last to first,
                                // 2 cached tokens interleaved with the others
@@ -370,24 +376,38 @@ hipError_t launch_combine(const Shape &s, const void *expert_out, const uint8_t 
     a.row_bytes = nv ? (int64_t)s.H / 2 : (mx ? (int64_t)s.H : 2 * (int64_t)s.H);
     a.nvec = (int)(a.row_bytes / 16);
     a.S = waves_per_token(s.T, a.nvec, EP_COMBINE_WAVES);
-    const int64_t waves = s.T * a.S;
-    const dim3 grid((unsigned)((waves + 3) / 4)), block(256);
-    if (nv) {
-        if (s.k == 8) hipLaunchKernelGGL(ep_combine_nvfp4_kernel<8>, grid, block, 0, stream, a);
-        else hipLaunchKernelGGL(ep_combine_nvfp4_kernel<0>, grid, block, 0, stream, a);
-    } else if (mx) {
-        if (s.k == 8) hipLaunchKernelGGL(ep_combine_mxfp8_kernel<8>, grid, block, 0, stream, a);
-        else hipLaunchKernelGGL(ep_combine_mxfp8_kernel<0>, grid, block, 0, stream, a);
-    } else if (waves < EP_COMBINE_SMALL_WAVES) {
-        // a small batch does not fill the chip at 64 row vectors per wave:
-        // one wave per 64 vectors of a row, one vector per lane
-        a.S = (a.nvec + kWave - 1) / kWave;
-        const dim3 g2((unsigned)((s.T * a.S + 3) / 4));
-        if (s.k == 8) hipLaunchKernelGGL((ep_combine_bf16_kernel<1, 8>), g2, block, 0, stream, a);
-        else hipLaunchKernelGGL((ep_combine_bf16_kernel<1, 0>), g2, block, 0, stream, a);
+    const dim3 block(256);
+    if (nv || mx) {
+        // one vector per lane per pass; with EP_COMBINE_Q_ONE_PASS exactly one
+        // pass per wave (ceil(row vectors / 64) waves per token)
+        if (EP_COMBINE_Q_ONE_PASS) a.S = (a.nvec + kWave - 1) / kWave;
+        const dim3 gq((unsigned)((s.T * a.S + 3) / 4));
+        if (nv) {
+            if (s.k == 8) hipLaunchKernelGGL(ep_combine_nvfp4_kernel<8>, gq, block, 0, stream, a);
+            else hipLaunchKernelGGL(ep_combine_nvfp4_kernel<0>, gq, block, 0, stream, a);
+        } else {
+            if (s.k == 8) hipLaunchKernelGGL(ep_combine_mxfp8_kernel<8>, gq, block, 0, stream, a);
+            else hipLaunchKernelGGL(ep_combine_mxfp8_kernel<0>, gq, block, 0, stream, a);
+        }
     } else {
-        if (s.k == 8) hipLaunchKernelGGL((ep_combine_bf16_kernel<EP_COMBINE_VECS, 8>), grid, block, 0, stream, a);
-        else hipLaunchKernelGGL((ep_combine_bf16_kernel<EP_COMBINE_VECS, 0>), grid, block, 0, stream, a);
+        int S = a.S;
+        if (EP_COMBINE_ONE_PASS) {   // the smallest power of two with one pass per wave
+            S = 1;
+            while ((int64_t)kWave * EP_COMBINE_VECS * S < a.nvec && S < 64) S *= 2;
+        }
+        if (s.T * S < EP_COMBINE_SMALL_WAVES) {
+            // a small batch does not fill the chip at 64 row vectors per wave:
+            // one wave per 64 vectors of a row, one vector per lane
+            a.S = (a.nvec + kWave - 1) / kWave;
+            const dim3 g2((unsigned)((s.T * a.S + 3) / 4));
+            if (s.k == 8) hipLaunchKernelGGL((ep_combine_bf16_kernel<1, 8>), g2, block, 0, stream, a);
+            else hipLaunchKernelGGL((ep_combine_bf16_kernel<1, 0>), g2, block, 0, stream, a);
+        } else {
+            a.S = S;
+            const dim3 g3((unsigned)((s.T * a.S + 3) / 4));
+            if (s.k == 8) hipLaunchKernelGGL((ep_combine_bf16_kernel<EP_COMBINE_VECS, 8>), g3, block, 0, stream, a);
+            else hipLaunchKernelGGL((ep_combine_bf16_kernel<EP_COMBINE_VECS, 0>), g3, block, 0, stream, a);
+        }
     }
     return hipGetLastError();
 }

@@ -51,6 +51,9 @@ namespace {
 #ifndef EP_RANKS_COMBINE_SMALL_WAVES
 #define EP_RANKS_COMBINE_SMALL_WAVES 4096   // fewer combine waves than this -> one vector per lane
 #endif
+#ifndef EP_RANKS_COMBINE_ONE_PASS
+#define EP_RANKS_COMBINE_ONE_PASS 1   // waves per token so that one pass covers a wave's part of the row
+#endif
 #ifndef EP_RANKS_COMBINE_VECS
 #define EP_RANKS_COMBINE_VECS 4      // 16-byte vectors per lane per pass in combine
 #endif
@@ -625,6 +628,10 @@ hipError_t launch_combine_ranks(const Shape &s, const uint16_t *partial,
     a.R = s.R;
     a.nvec = s.H / 8;
     a.S = waves_per_token(s.T, a.nvec, EP_RANKS_COMBINE_WAVES);
+    if (EP_RANKS_COMBINE_ONE_PASS) {   // the smallest power of two with one pass per wave
+        a.S = 1;
+        while ((int64_t)kWave * EP_RANKS_COMBINE_VECS * a.S < a.nvec && a.S < 64) a.S *= 2;
+    }
     const int64_t waves = s.T * a.S;
     if (waves < EP_RANKS_COMBINE_SMALL_WAVES) {
         // a small batch: one wave per 64 vectors of a row, one vector per lane
