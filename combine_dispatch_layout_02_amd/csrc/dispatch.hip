@@ -426,6 +426,10 @@ hipError_t launch_dispatch_copy(const Shape &s, const WsLayout &L, const void *x
     return hipGetLastError();
 }
 
+#ifndef EP_FUSED_NT_MIB
+#define EP_FUSED_NT_MIB 4        // single-launch form: receive bytes (MiB) from which every row is stored non-temporal
+#endif
+
 // Waves per token of the single-launch form: enough for the row copy, and at
 // least one per slot (up to 16) so each wave counts few slots.
 #ifndef EP_FUSED_MIN_WAVES
@@ -475,6 +479,17 @@ hipError_t launch_dispatch_fused(const Shape &s, const void *x, const float *x_s
     // block 0: the layout; then one block of S waves per token (LDS: the
     // layout's staging, which is larger than the other blocks' pair ids)
     a.S = fused_waves(s, a.nvec);
+    // A single-launch batch is over in a few microseconds; from a few MiB of
+    // receive rows on, non-temporal stores make the whole dispatch -> combine
+    // step faster (T = 128 at hidden 7168, top-8, 14.7 MB: 11.3 -> 10.7 us;
+    // T = 256: 24.4 -> 22.6 us), below it plain ones (T = 1 .. 32: 0.3 -
+    // 0.5 us faster).  A likely reason: plain-stored rows are still dirty in
+    // the L2s when so short a kernel ends, and the kernel boundary writes
+    // them back.
+    if ((int64_t)s.T * s.k * a.row_bytes >= ((int64_t)EP_FUSED_NT_MIB << 20)) {
+        a.nt_store = 1;
+        a.plain_tokens = 0;
+    }
     const int threads = kWave * a.S;
     const size_t lds = sizeof(int32_t) * ((size_t)s.T * s.k + s.E + s.R + s.N + threads / kWave + 1);
     if (s.T * s.k <= 16 * kWave) launch_copy<16>(a, 1 + s.T, threads, lds, stream);
