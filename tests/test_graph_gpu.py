@@ -1,4 +1,6 @@
-"""HIP graph capture of whole steps (layout -> dispatch -> combine).
+"""HIP graph capture of whole steps (layout -> dispatch -> [expert stage] -> combine),
+for bf16 rows, the single launch, the (token, rank) rows and both quantized
+payloads (fp8 rows -> mxfp8, bf16 rows -> nvfp4).
 
 The library never allocates, synchronises or records a memset inside a call,
 so a step can be captured once and replayed.  Each case captures two steps,
@@ -86,7 +88,48 @@ def _ranks_step(inp):
     return step, ws, lambda: (gpu_path.bf16_bits(y), trs.cpu().numpy(), lay["r"].cpu().numpy())
 
 
-@pytest.mark.parametrize("case", ["pairs", "pairs_full_size", "pairs_one_call_small", "pairs_one_call_large", "ranks"])
+def _quantized_step(inp):
+    """fp8 rows -> mxfp8 payload, or bf16 rows -> nvfp4 payload: layout,
+    dispatch, the expert stage's re-encoding and the combine."""
+    import gpu_path
+    from combine_dispatch_layout_02_amd import ep
+    T, H, E, R, N, k = (inp[n] for n in ("T", "H", "E", "R", "N", "k"))
+    nv = inp.get("y_fmt") == "nvfp4"
+    shape = ep.make_shape(T, H, E, R, N, k, ep.EP_FMT_BF16 if nv else ep.EP_FMT_FP8_S128,
+                          ep.EP_FMT_NVFP4 if nv else ep.EP_FMT_MXFP8)
+    ws = ep.Workspace(shape)
+    x = gpu_path.to_dev_bf16(inp["x"])
+    xq, xs = (x, None) if nv else ep.quant_fp8_s128(x)
+    idx = torch.from_numpy(inp["topk_idx"]).cuda()
+    w = torch.from_numpy(inp["topk_w"]).cuda()
+    rows = shape.rows
+    lay = dict(r=torch.empty(R, dtype=torch.int32, device="cuda"), e=torch.empty(E, dtype=torch.int32, device="cuda"),
+               m=torch.empty((T, R), dtype=torch.uint8, device="cuda"),
+               n=torch.empty(N, dtype=torch.int32, device="cuda"), a=torch.empty(1, dtype=torch.int64, device="cuda"))
+    recv = torch.empty((rows, H), dtype=torch.bfloat16 if nv else torch.uint8, device="cuda")
+    recv_s = None if nv else torch.empty((rows, H // 128), dtype=torch.float32, device="cuda")
+    src = torch.empty(rows, dtype=torch.int32, device="cuda")
+    rw = torch.empty(rows, dtype=torch.float32, device="cuda")
+    slot = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    off = torch.empty(E + 1, dtype=torch.int32, device="cuda")
+    eq = torch.zeros((rows, H // 2 if nv else H), dtype=torch.uint8, device="cuda")
+    es = torch.zeros((rows, H // 16), dtype=torch.int16, device="cuda") if nv else \
+        torch.zeros((rows, H // 32), dtype=torch.uint8, device="cuda")
+    y = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
+
+    def step():
+        ep.ep_dispatch_layout(shape, idx, lay["r"], lay["e"], lay["m"], lay["n"], lay["a"], ws)
+        ep.ep_dispatch(shape, xq, xs, idx, w, recv, recv_s, src, rw, slot, off, ws, from_layout=True)
+        if nv:
+            ep.ep_expert_requant_nvfp4(shape, off, None, recv, eq, es)
+        else:
+            ep.ep_expert_requant_mxfp8(shape, off, None, recv, recv_s, eq, es)
+        ep.ep_combine(shape, eq, es, slot, w, y)
+
+    return step, ws, lambda: (gpu_path.bf16_bits(y), slot.cpu().numpy(), lay["r"].cpu().numpy())
+
+
+@pytest.mark.parametrize("case", ["pairs", "pairs_full_size", "pairs_one_call_small", "pairs_one_call_large", "ranks", "quant_mxfp8", "nvfp4"])
 def test_graph_replays_match_eager(case):
     if case == "pairs":
         inp = W.make_inputs("prefill2n", T=1000, H=1024, mask_frac=0.05)
@@ -103,6 +146,10 @@ def test_graph_replays_match_eager(case):
     elif case == "pairs_one_call_large":
         inp = W.make_inputs("prefill2n", T=700, H=1024)
         step, ws, read = _pairs_step(inp, one_call=True)
+        ref = oracle.run_path(inp)
+    elif case in ("quant_mxfp8", "nvfp4"):
+        inp = W.make_inputs("quant" if case == "quant_mxfp8" else "nvfp4", T=1000, H=1024, mask_frac=0.05)
+        step, ws, read = _quantized_step(inp)
         ref = oracle.run_path(inp)
     else:
         inp = W.make_inputs("prefill2n", T=1000, H=1024, mask_frac=0.05)
