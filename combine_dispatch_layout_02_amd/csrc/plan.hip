@@ -284,9 +284,27 @@ __global__ __launch_bounds__(1024) void ep_plan_scan_kernel(ScanArgs a) {
         int32_t *col = a.tile_count + c;
         int32_t v[kScanRegs];
         int32_t s = 0;
+        // batches of 8 loads, each load unconditional (the tile index is
+        // clamped to the thread's last tile, or tile 0 for an empty range;
+        // the value is dropped outside the range), so a batch is in flight
+        // together
+        // Here tiles * cols <= kScanRegs * blockDim.x, so 32-bit byte offsets
+        // from the kernel argument address the tile counts.
+        const int lastt = max(tb - 1, 0);
+        const char *base = reinterpret_cast<const char *>(a.tile_count);
+#pragma unroll
+        for (int u0 = 0; u0 < kScanRegs; u0 += 8) {
+            if (ta + u0 < tb) {
+#pragma unroll
+                for (int u = u0; u < u0 + 8; ++u) {
+                    const uint32_t off = ((uint32_t)min(ta + u, lastt) * (uint32_t)cols + (uint32_t)c) * 4u;
+                    v[u] = *reinterpret_cast<const int32_t *>(base + off);
+                }
+            }
+        }
 #pragma unroll
         for (int u = 0; u < kScanRegs; ++u) {
-            v[u] = (live && ta + u < tb) ? col[(size_t)(ta + u) * cols] : 0;
+            v[u] = (live && ta + u < tb) ? v[u] : 0;
             s += v[u];
         }
         if (live) part[tid] = s;   // tid = q * cols + c
