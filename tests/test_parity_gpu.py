@@ -292,6 +292,21 @@ def test_many_plan_tiles(kw):
     assert gpu_path.compare_ranks(g, oracle.run_path(dict(inp, rank_rows=True)), False) == 0
 
 
+# At E = 256, R = 16, N = 2, top-8 a plan tile holds 128 tokens and the scan
+# block's 1024 threads split each of the 274 count columns into 3 ranges of
+# ceil(tiles / 3) tiles, read in batches of 8 while a range fits 32 tiles.
+# The tile counts put the ranges just below and just above each batch edge
+# (8, 16, 24 tiles), at the 32-tile limit and one tile past it (the loop form).
+@pytest.mark.parametrize("tiles", [3, 24, 25, 48, 49, 72, 73, 96, 97])
+def test_scan_batch_edges(tiles):
+    inp = W.make_inputs("tiny", T=tiles * 128 - 5, H=64, E=256, R=16, N=2, k=8, mask_frac=0.05)
+    _, _, ndiff = _run_both(inp)
+    assert ndiff == 0
+    import gpu_path
+    g = gpu_path.run_ranks(inp)
+    assert gpu_path.compare_ranks(g, oracle.run_path(dict(inp, rank_rows=True)), False) == 0
+
+
 @pytest.mark.parametrize("kw", [dict(), dict(mask_frac=0.2, T=333), dict(x_fmt="fp8", T=300, H=1024),
                                 dict(rank_capacity="fit"), dict(T=100)])
 def test_cached_dispatch_reuses_a_handle(kw):
