@@ -1,6 +1,7 @@
 """HIP graph capture of whole steps (layout -> dispatch -> [expert stage] -> combine),
-for bf16 rows, the single launch, the (token, rank) rows and both quantized
-payloads (fp8 rows -> mxfp8, bf16 rows -> nvfp4).
+for bf16 rows, the single launch, the cached dispatch through a previous
+handle, the (token, rank) rows and both quantized payloads (fp8 rows -> mxfp8,
+bf16 rows -> nvfp4).
 
 The library never allocates, synchronises or records a memset inside a call,
 so a step can be captured once and replayed.  Each case captures two steps,
@@ -52,6 +53,37 @@ def _pairs_step(inp, one_call):
         else:
             ep.ep_dispatch_layout(shape, idx, lay["r"], lay["e"], lay["m"], lay["n"], lay["a"], ws)
             ep.ep_dispatch(shape, x, None, idx, w, recv, None, src, rw, slot, off, ws, from_layout=True)
+        ep.ep_combine(shape, recv, None, slot, w, y)
+
+    return step, ws, lambda: (gpu_path.bf16_bits(y), slot.cpu().numpy(), lay["r"].cpu().numpy())
+
+
+def _cached_step(inp, x2):
+    """The handle comes from one eager layout + dispatch of x; the captured
+    step moves x2 to the same rows (ep_dispatch_cached) and combines them."""
+    import gpu_path
+    from combine_dispatch_layout_02_amd import ep
+    T, H, E, R, N, k = (inp[n] for n in ("T", "H", "E", "R", "N", "k"))
+    shape = ep.make_shape(T, H, E, R, N, k)
+    ws = ep.Workspace(shape)
+    x = gpu_path.to_dev_bf16(inp["x"])
+    xb = gpu_path.to_dev_bf16(x2)
+    idx = torch.from_numpy(inp["topk_idx"]).cuda()
+    w = torch.from_numpy(inp["topk_w"]).cuda()
+    lay = dict(r=torch.empty(R, dtype=torch.int32, device="cuda"), e=torch.empty(E, dtype=torch.int32, device="cuda"),
+               m=torch.empty((T, R), dtype=torch.uint8, device="cuda"),
+               n=torch.empty(N, dtype=torch.int32, device="cuda"), a=torch.empty(1, dtype=torch.int64, device="cuda"))
+    recv = torch.empty((T * k, H), dtype=torch.bfloat16, device="cuda")
+    src = torch.empty(T * k, dtype=torch.int32, device="cuda")
+    rw = torch.empty(T * k, dtype=torch.float32, device="cuda")
+    slot = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    off = torch.empty(E + 1, dtype=torch.int32, device="cuda")
+    y = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
+    ep.ep_dispatch_layout(shape, idx, lay["r"], lay["e"], lay["m"], lay["n"], lay["a"], ws)
+    ep.ep_dispatch(shape, x, None, idx, w, recv, None, src, rw, slot, off, ws, from_layout=True)
+
+    def step():
+        ep.ep_dispatch_cached(shape, xb, None, slot, recv)
         ep.ep_combine(shape, recv, None, slot, w, y)
 
     return step, ws, lambda: (gpu_path.bf16_bits(y), slot.cpu().numpy(), lay["r"].cpu().numpy())
@@ -129,7 +161,8 @@ def _quantized_step(inp):
     return step, ws, lambda: (gpu_path.bf16_bits(y), slot.cpu().numpy(), lay["r"].cpu().numpy())
 
 
-@pytest.mark.parametrize("case", ["pairs", "pairs_full_size", "pairs_one_call_small", "pairs_one_call_large", "ranks", "quant_mxfp8", "nvfp4"])
+@pytest.mark.parametrize("case", ["pairs", "pairs_full_size", "pairs_one_call_small", "pairs_one_call_large", "cached",
+                                  "ranks", "quant_mxfp8", "nvfp4"])
 def test_graph_replays_match_eager(case):
     if case == "pairs":
         inp = W.make_inputs("prefill2n", T=1000, H=1024, mask_frac=0.05)
@@ -147,6 +180,11 @@ def test_graph_replays_match_eager(case):
         inp = W.make_inputs("prefill2n", T=700, H=1024)
         step, ws, read = _pairs_step(inp, one_call=True)
         ref = oracle.run_path(inp)
+    elif case == "cached":   # another tensor of the same tokens through a previous handle
+        inp = W.make_inputs("prefill2n", T=1000, H=1024, mask_frac=0.05)
+        x2 = np.ascontiguousarray(inp["x"][::-1])
+        step, ws, read = _cached_step(inp, x2)
+        ref = oracle.run_path(dict(inp, x=x2))
     elif case in ("quant_mxfp8", "nvfp4"):
         inp = W.make_inputs("quant" if case == "quant_mxfp8" else "nvfp4", T=1000, H=1024, mask_frac=0.05)
         step, ws, read = _quantized_step(inp)
