@@ -80,8 +80,9 @@ WsLayout ws_layout(const Shape &s) {
     off = align256(off + sizeof(int32_t) * (size_t)(TK > 0 ? TK : 1));
     L.plan_offset = off;
     off = align256(off + sizeof(int32_t) * (size_t)(s.E + 1));
-    L.tr_local = off;
-    off = align256(off + (s.rank_rows ? sizeof(int32_t) * (size_t)(s.T > 0 ? s.T : 1) * (size_t)s.R : 0));
+    L.tile_token_waves = (L.tile_tokens + 63) / 64;
+    L.rank_mask = off;
+    off = align256(off + (s.rank_rows ? sizeof(uint64_t) * (size_t)L.tiles * (size_t)s.R * L.tile_token_waves : 0));
     L.plan_rank_offset = off;
     off = align256(off + sizeof(int32_t) * (size_t)(s.R + 1));
     L.total = off;

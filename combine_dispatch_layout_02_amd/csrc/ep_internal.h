@@ -17,17 +17,20 @@ namespace ep {
 //   local_rank  : i32[T * k]         rank of a pair among the same-expert pairs
 //                                    of its tile that precede it (-1: masked)
 //   plan_offset : i32[E + 1]         expert segment starts
-//   tr_local    : i32[T * R]         (token, rank) rows only: rank of token t
-//                                    among its tile's tokens reaching rank r
+//   rank_mask   : u64[tiles][R][TW]  (token, rank) rows only: per tile, rank
+//                                    and 64-token wave of the tile (TW =
+//                                    ceil(tile_tokens / 64) waves), bit i set
+//                                    when the wave's token i reaches the rank
 //   plan_rank_offset : i32[R + 1]    (token, rank) region starts
 // A tile holds tile_tokens whole tokens (tile_tokens * k <= count_threads
 // pairs, one thread per pair).
 struct WsLayout {
-    size_t ctrl, tile_count, local_rank, plan_offset, tr_local, plan_rank_offset, total;
+    size_t ctrl, tile_count, local_rank, plan_offset, rank_mask, plan_rank_offset, total;
     int tiles;           // ceil(T / tile_tokens)
     int tile_tokens;
     int tile_waves;      // ceil(tile_tokens * k / 64): waves that own pair masks
     int count_threads;   // tile_waves * 64
+    int tile_token_waves;   // ceil(tile_tokens / 64): words per (tile, rank) of rank_mask
 };
 
 constexpr int kCtrlWords = 64;

@@ -28,10 +28,10 @@
 //        per-node counts are LDS integer adds, one per rank / node a token
 //        reaches (order-independent; a wavefront ballot per rank cost
 //        2.4 us more at 16 ranks).
-//      - (token, rank) rows, when planned: the token's place among the
-//        tile's tokens of each rank it reaches = its place in its wave (a
-//        ballot per rank) plus the earlier waves' counts (per-wave LDS adds,
-//        then an LDS prefix over the waves).
+//      - (token, rank) rows, when planned: per (rank, 64-token wave) the
+//        ballot of the wave's tokens reaching the rank, written as one 64-bit
+//        word; the dispatch takes a token's place among the tile's tokens of
+//        a rank as the popcount of the bits before it.
 //  ep_plan_scan_kernel   one block: per expert (and per rank, when (token,
 //      rank) rows are planned) the exclusive prefix of the tile counts over
 //      tiles (in place) and the total; the exclusive scan of the expert totals
@@ -57,8 +57,9 @@ struct CountArgs {
     int32_t *tile_count;      // [ntiles][E + R + N]: experts, ranks, nodes
     int32_t *local_rank;      // [T * k]
     uint32_t *ctrl;
-    int32_t *tr_local;        // [T][R] rank of token t among the tile's tokens reaching rank r
-                              // (-1: t does not reach r); null unless (token, rank) rows are planned
+    uint64_t *rank_mask;      // [ntiles][R][TW]: bit i of word w = token w * 64 + i of the tile
+                              // reaches rank r; null unless (token, rank) rows are planned
+    int TW;                   // 64-token waves per tile: ceil(TT / 64)
     // single-tile batches (one block) finish the plan in the same launch:
     int32_t *plan_offset;     // [E + 1]
     int32_t *plan_rank_offset;   // [R + 1] (token, rank) region starts
@@ -71,10 +72,6 @@ __global__ __launch_bounds__(1024) void ep_plan_count_kernel(CountArgs a) {
     uint64_t *masks = lds;                                            // [W][E]
     int32_t *ids = reinterpret_cast<int32_t *>(masks + (size_t)a.W * a.E);   // [TT * k]
     int32_t *rn = ids + a.TT * a.k;                                   // [R + N]
-    // per token wave and rank: tokens of the wave reaching the rank, then the
-    // exclusive prefix over the tile's waves ((token, rank) rows only); after
-    // the single-tile counts and scan scratch
-    int32_t *wc = rn + a.R + a.N + a.E + 1 + 1024 / kWave + 1;        // [W][R]
     const int tid = threadIdx.x, nt = blockDim.x;
     const int lane = tid & (kWave - 1), w = tid / kWave;
     const int E = a.E, k = a.k;
@@ -84,8 +81,6 @@ __global__ __launch_bounds__(1024) void ep_plan_count_kernel(CountArgs a) {
 
     for (int i = tid; i < a.W * E; i += nt) masks[i] = 0ull;
     for (int i = tid; i < a.R + a.N; i += nt) rn[i] = 0;
-    if (a.tr_local)
-        for (int i = tid; i < a.W * a.R; i += nt) wc[i] = 0;
     bool bad = false;
     for (int q = tid; q < npairs; q += nt) {   // stage ids; invalid ids become masked
         const int64_t v = a.topk_idx[t0 * k + q];
@@ -180,63 +175,30 @@ __global__ __launch_bounds__(1024) void ep_plan_count_kernel(CountArgs a) {
         }
     }
     const bool tok_wave = w * kWave < ntok;   // the wave holds a token (wave-uniform)
-    // one LDS add per rank / node the token reaches (integer adds: the counts
-    // do not depend on their order); with (token, rank) rows also per (wave,
-    // rank)
-    for (uint64_t m = rmask; m; m &= m - 1) {
-        const int r = __builtin_ctzll(m);
-        atomicAdd(&rn[r], 1);
-        if (a.tr_local) atomicAdd(&wc[w * a.R + r], 1);
+    if (a.rank_mask && tok_wave) {
+        // (token, rank) rows: per rank, the wave's tokens reaching it as one
+        // ballot; lane r keeps rank r's and writes it (R <= 64)
+        uint64_t mine = 0;
+        for (int r = 0; r < a.R; ++r) {
+            const uint64_t b = __ballot((rmask >> r) & 1u);
+            if (lane == r) mine = b;
+        }
+        if (lane < a.R) a.rank_mask[((size_t)blockIdx.x * a.R + lane) * a.TW + w] = mine;
     }
+    // one LDS add per rank / node the token reaches (integer adds: the counts
+    // do not depend on their order)
+    for (uint64_t m = rmask; m; m &= m - 1) atomicAdd(&rn[__builtin_ctzll(m)], 1);
     for (uint64_t m = nmask; m; m &= m - 1) atomicAdd(&rn[a.R + __builtin_ctzll(m)], 1);
     if (__ballot(bad) && lane == 0) atomicOr(&a.ctrl[0], kErrBadExpert);
     __syncthreads();
     // single tile: the rank columns hold the prefix over earlier tiles (0)
     // when (token, rank) rows are planned, else the counts
-    for (int i = tid; i < a.R + a.N; i += nt) tc[E + i] = (single && a.tr_local && i < a.R) ? 0 : rn[i];
-    if (a.tr_local) {   // block-uniform
-        // exclusive prefix of the per-wave counts over the tile's waves, per rank
-        const int twaves = (ntok + kWave - 1) / kWave;
-        for (int r = tid; r < a.R; r += nt) {
-            int32_t run = 0;
-            for (int w2 = 0; w2 < twaves; ++w2) {
-                const int32_t c = wc[w2 * a.R + r];
-                wc[w2 * a.R + r] = run;
-                run += c;
-            }
-        }
-        __syncthreads();
-        // token's place among the tile's tokens of each rank: its place in
-        // its wave (ballot again) plus the earlier waves' tokens of the rank
-        if (tok_wave) {
-            int32_t *out = a.tr_local + (t0 + w * kWave + lane) * a.R;
-            for (int r0 = 0; r0 < a.R; r0 += 4) {
-                int32_t v[4];
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const int r = r0 + q;
-                    const bool in = r < a.R && ((rmask >> r) & 1u);
-                    const uint64_t b = __ballot(in);
-                    v[q] = -1;
-                    if (in) v[q] = (int32_t)__popcll(b & lanemask_lt()) + wc[w * a.R + r];
-                }
-                if (has_tok) {
-                    if ((a.R & 3) == 0) {
-                        vec16 o;
-                        for (int q = 0; q < 4; ++q) o[q] = (uint32_t)v[q];
-                        st16(out + r0, o);
-                    } else {
-                        for (int q = 0; q < 4 && r0 + q < a.R; ++q) out[r0 + q] = v[q];
-                    }
-                }
-            }
-        }
-    }
+    for (int i = tid; i < a.R + a.N; i += nt) tc[E + i] = (single && a.rank_mask && i < a.R) ? 0 : rn[i];
     if (!single) return;   // block-uniform
 
     // ---- single-tile batch: segment starts and layout outputs right here
     block_exclusive_scan(cnt, a.plan_offset, E, reinterpret_cast<int32_t *>(cnt + E));
-    if (a.tr_local && tid < kWave) wave_exclusive_scan(tid < a.R ? rn[tid] : 0, a.R, a.plan_rank_offset);
+    if (a.rank_mask && tid < kWave) wave_exclusive_scan(tid < a.R ? rn[tid] : 0, a.R, a.plan_rank_offset);
     if (a.per_rank) {
         for (int i = tid; i < a.R + a.N; i += nt) {
             if (i < a.R) a.per_rank[i] = rn[i]; else a.per_node[i - a.R] = rn[i];
@@ -403,7 +365,8 @@ hipError_t launch_plan(const Shape &s, const WsLayout &L, const int64_t *topk_id
     c.local_rank = reinterpret_cast<int32_t *>(ws + L.local_rank);
     c.ctrl = reinterpret_cast<uint32_t *>(ws + L.ctrl);
     c.plan_offset = reinterpret_cast<int32_t *>(ws + L.plan_offset);
-    c.tr_local = s.rank_rows ? reinterpret_cast<int32_t *>(ws + L.tr_local) : nullptr;
+    c.rank_mask = s.rank_rows ? reinterpret_cast<uint64_t *>(ws + L.rank_mask) : nullptr;
+    c.TW = L.tile_token_waves;
     c.plan_rank_offset = reinterpret_cast<int32_t *>(ws + L.plan_rank_offset);
     c.per_expert = per_expert;
     c.per_rank = per_rank;
@@ -413,8 +376,7 @@ hipError_t launch_plan(const Shape &s, const WsLayout &L, const int64_t *topk_id
         // masks, staged ids, rank/node counts, and (single tile) expert counts + scan scratch
         const size_t lds = sizeof(uint64_t) * (size_t)L.tile_waves * s.E +
                            sizeof(int32_t) * ((size_t)L.tile_tokens * s.k + s.R + s.N + s.E + 1 +
-                                              1024 / kWave + 1) +
-                           sizeof(int32_t) * (size_t)L.tile_waves * s.R;   // per-wave rank counts
+                                              1024 / kWave + 1);
         hipLaunchKernelGGL(ep_plan_count_kernel, dim3(L.tiles), dim3(L.count_threads), lds, stream, c);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess || L.tiles == 1) return e;   // one tile: the plan is complete

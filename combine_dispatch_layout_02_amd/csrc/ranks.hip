@@ -72,11 +72,11 @@ struct RankCopyArgs {
     int32_t *rank_offset;           // [R + 1] handle copy
     const int32_t *plan_rank_offset;   // [R + 1] (workspace)
     const int32_t *tile_prefix;     // [ntiles][E + R + N]; rank columns: prefix over tiles
-    const int32_t *tr_local;        // [T][R]
+    const uint64_t *rank_mask;      // [ntiles][R][TW] tokens of each 64-token wave of a tile reaching each rank
     const int32_t *slots_in;        // [T][R] a previous dispatch's token_rank_slot (cached form), else null
     uint32_t *ctrl;
     int64_t T;
-    int k, E, R, TT, cols;
+    int k, E, R, TT, TW, cols;
     int epr, epr_shift;
     int64_t cap;                    // receive rows: T * min(k, R)
     int64_t row_bytes;
@@ -187,9 +187,19 @@ __global__ __launch_bounds__(TOK ? 1024 : 256) void ep_dispatch_ranks_kernel(Ran
         slot = a.slots_in[t * a.R + lane];
         if ((uint64_t)slot >= (uint64_t)a.cap) slot = -1;
     } else if (lane < a.R) {
-        const int32_t lr = a.tr_local[t * a.R + lane];
-        if (lr >= 0) {
-            slot = a.plan_rank_offset[lane] + a.tile_prefix[(t / a.TT) * a.cols + a.E + lane] + lr;
+        // t's place among its tile's tokens reaching rank `lane`: the set
+        // bits before t's bit in the tile's mask of that rank
+        const int64_t tile = t / a.TT;
+        const int pos = (int)(t - tile * a.TT);
+        const uint64_t *m = a.rank_mask + ((size_t)tile * a.R + lane) * a.TW;
+        const int wt = pos >> 6, bit = pos & 63;
+        // every lookup is independent of the others: one memory round trip
+        const uint64_t mw = m[wt];
+        const int32_t start = a.plan_rank_offset[lane] + a.tile_prefix[tile * a.cols + a.E + lane];
+        int32_t lr = (int32_t)__popcll(mw & ((1ull << bit) - 1ull));
+        for (int i = 0; i < wt; ++i) lr += (int32_t)__popcll(m[i]);
+        if ((mw >> bit) & 1u) {
+            slot = start + lr;
             if ((uint64_t)slot >= (uint64_t)a.cap) {   // cannot happen; never write outside
                 atomicOr(&a.ctrl[0], kErrBadSlot);
                 slot = -1;
@@ -542,7 +552,8 @@ hipError_t launch_dispatch_ranks(const Shape &s, const WsLayout &L, const void *
     a.rank_offset = rank_offset;
     a.plan_rank_offset = reinterpret_cast<const int32_t *>(ws + L.plan_rank_offset);
     a.tile_prefix = reinterpret_cast<const int32_t *>(ws + L.tile_count);
-    a.tr_local = reinterpret_cast<const int32_t *>(ws + L.tr_local);
+    a.rank_mask = reinterpret_cast<const uint64_t *>(ws + L.rank_mask);
+    a.TW = L.tile_token_waves;
     a.ctrl = reinterpret_cast<uint32_t *>(const_cast<char *>(ws) + L.ctrl);
     a.T = s.T;
     a.k = s.k;

@@ -140,7 +140,9 @@ def test_rank_rows_calls_reject_before_device_work(lib):
     n0, n1 = ctypes.c_size_t(), ctypes.c_size_t()
     assert lib.ep_workspace_bytes(ctypes.byref(sh0), ctypes.byref(n0)) == ep.EP_OK
     assert lib.ep_workspace_bytes(ctypes.byref(sh1), ctypes.byref(n1)) == ep.EP_OK
-    assert n1.value >= n0.value + 4 * 64 * 4                   # the [T, R] local ranks
+    # the rank masks: one tile of 512 tokens (16 waves of 64 pairs at top-2),
+    # 4 ranks, 8 words of 64 tokens each
+    assert n1.value >= n0.value + 1 * 4 * 8 * 8
     assert lib.ep_dispatch_ranks(ctypes.byref(sh0), fake, None, fake, fake, fake, None, *([fake] * 5),
                                  fake, 1 << 20, None) == ep.EP_EINVAL
     assert lib.ep_dispatch_ranks(ctypes.byref(sh1), odd, None, fake, fake, fake, None, *([fake] * 5),
