@@ -246,12 +246,11 @@ __global__ __launch_bounds__(1024) void ep_plan_scan_kernel(ScanArgs a) {
         int32_t *col = a.tile_count + c;
         int32_t v[kScanRegs];
         int32_t s = 0;
-        // batches of 8 loads, each load unconditional (the tile index is
+        // Batches of 8 loads, each load unconditional (the tile index is
         // clamped to the thread's last tile, or tile 0 for an empty range;
         // the value is dropped outside the range), so a batch is in flight
-        // together
-        // Here tiles * cols <= kScanRegs * blockDim.x, so 32-bit byte offsets
-        // from the kernel argument address the tile counts.
+        // together.  In this form tiles * cols <= kScanRegs * blockDim.x, so
+        // 32-bit byte offsets from the kernel argument address the counts.
         const int lastt = max(tb - 1, 0);
         const char *base = reinterpret_cast<const char *>(a.tile_count);
 #pragma unroll
