@@ -56,7 +56,8 @@ def test_ragged_token_counts(T):
     dict(mask_frac=0.3), dict(mask_frac=0.3, mask_tokens=0.1), dict(routing="replace"),
     dict(routing="replace", mask_frac=0.2, k=16), dict(k=1), dict(E=16, R=16, N=16, k=4),
     dict(E=64, R=64, N=8, k=8), dict(E=4096, R=64, N=64, k=32, T=300), dict(H=8, T=100),
-    dict(H=7176, T=130), dict(E=24, R=3, N=1, k=5), dict(R=1, N=1)])
+    dict(H=7176, T=130), dict(E=24, R=3, N=1, k=5), dict(R=1, N=1),
+    dict(k=1, T=3000, mask_frac=0.1)])   # 3 tiles of 1024 tokens: 16 mask words per (tile, rank)
 def test_edge_cases(kw):
     kw = dict(kw)
     base = dict(T=kw.pop("T", 700), H=kw.pop("H", 512))
