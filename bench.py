@@ -8,29 +8,51 @@ workload, if any) -> ep_combine, all on one stream.  W untimed warmup steps,
 then K timed steps bracketed by stream synchronisation and HIP events, three
 ways: replayed from HIP graphs of 10 captured steps (the reported
 ms_per_step), eager back to back (eager_ms_per_step), and eager with events
-between the calls (the per-call durations in phase_us: median over steps);
-phase_us_flushed repeats the calls each after a 512 MiB copy that evicts the
-memory-side cache (cold-cache durations).  The workloads'
-expert stage (identity, per-expert scaling, or fp8 -> mxfp8 re-encoding)
-runs during warmup and is not part of the timed step.  A batch of at most
-2048 (token, slot) pairs is laid out and dispatched by one
+between the calls (the per-call durations in phase_us: median over steps).
+The workloads' expert stage (identity, per-expert scaling, or fp8 -> mxfp8
+re-encoding) runs during warmup and is not part of the timed step.  A batch
+of at most 2048 (token, slot) pairs is laid out and dispatched by one
 ep_dispatch_with_layout (ep_dispatch_ranks_with_layout) call, which the
-library runs as a single launch (phases "layout+dispatch", "combine").  With --layout ranks
-the step is the (token, rank) path: ep_dispatch_layout (planning one row per
-token per rank it reaches) -> ep_dispatch_ranks -> ep_combine_ranks, with
-ep_expert_reduce_ranks (the weighted per-rank partials) as the expert stage.
+library runs as a single launch (phases "layout+dispatch", "combine").  With
+--layout ranks the step is the (token, rank) path: ep_dispatch_layout
+(planning one row per token per rank it reaches) -> ep_dispatch_ranks ->
+ep_combine_ranks, with ep_expert_reduce_ranks (the weighted per-rank
+partials) as the expert stage.
+
+Warm and cold.  The 256 MB memory-side cache (MALL) of MI355X is a
+write-back cache: stores (plain and non-temporal alike) leave dirty lines
+there.  Back to back on the same buffers (the warm `value`), the receive
+rows and x that one step leaves in it are read by the combine from it and
+rewritten by the next step's dispatch before they ever reach HBM, so the
+warm figure counts up to ~256 MB of "HBM" writes per step that HBM never
+sees.  The cold figures charge them: `cold` times HIP graphs of [a 512 MiB
+plain-read flush, step] minus graphs of [flush] alone.  The flush leaves the
+cache clean and evicts everything the step left there, so the write-back of
+the step's dirty lines lands in the flush that follows it and is counted in
+the difference.  cold.phase_us does the same for each call alone; within
+a step the combine reads rows the dispatch just left in the cache, so the
+cold step can take less than its calls alone.
 
 Prints one JSON line:
-  value         algorithmic HBM bytes of the step / step time (GB/s)
-  tokens_per_s  tokens of the batch / step time
+  value         algorithmic HBM bytes of the step / warm step time (GB/s)
+  tokens_per_s  tokens of the batch / warm step time
+  cold          ms_per_step, value, tokens_per_s, phase_us and phase_gbs with
+                the memory-side cache flushed before each step and the
+                step's write-back charged (see above)
   dispatch_combine_gbs  the dispatch and combine calls' algorithmic bytes / their
                 summed per-call durations (the layout pass left out)
-  phase_gbs     each call's algorithmic bytes / its per-call duration
+  phase_gbs     each call's algorithmic bytes / its warm per-call duration
   rel_l2_vs_fp32  relative L2 distance of y from the unquantized fp32 result
-  roofline      the longest-running call against the 8 TB/s HBM peak, with
-                hardware byte counts when they were measured for this kernel,
-                and against a plain 1 GiB device copy timed in the same run
-  cpu_baseline  the CPU oracle (single thread) on the same workload
+  roofline      the longest-running call against the 8 TB/s HBM peak (warm,
+                MALL-assisted: frac; cold: cold_frac), with hardware byte
+                counts when they were measured for this kernel; each row
+                call's cold rate against 8 TB/s and against the ceiling that
+                matches its mix of reads and writes (ceilings, below)
+  ceilings      the box's streaming read, write and copy rates, measured in
+                the same run: back-to-back launches alternating over 1 GiB
+                buffers (so write-backs are charged), best over a few launch
+                shapes
+  cpu_baseline  the CPU oracle on the same workload, one thread and all cores
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--layout pairs|ranks]
 """
 from __future__ import annotations
@@ -50,8 +72,11 @@ HBM_PEAK_GBS = 8000.0   # MI355X HBM3E, published peak
 
 GRAPH_STEPS = 10   # steps captured per HIP graph
 SINGLE_LAUNCH_PAIRS = 2048   # batches the library lays out and dispatches in one launch
-FLUSH_BYTES = 512 << 20      # copy that evicts the 256 MB memory-side cache
-COPY_REF_BYTES = 1 << 30     # plain copy timed as the box's streaming reference
+FLUSH_BYTES = 512 << 20      # plain read that evicts the 256 MB memory-side cache and leaves it clean
+FLUSH_CHUNK, FLUSH_WAVES = 16384, 4096
+CEIL_BYTES = 1 << 30         # streaming ceilings: launches alternate over buffers of this size
+CEIL_LAUNCHES = 8
+CEIL_SHAPES = [(c, w) for c in (4096, 16384, 65536) for w in (4096, 16384, 65536)]
 PROFILES = os.path.join(ROOT, "profiles")
 
 
@@ -155,10 +180,13 @@ def parse():
                          "pair count); or one row per (token, rank) with per-rank partials "
                          "(ep_dispatch_ranks / ep_combine_ranks)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--flush-steps", type=int, default=10,
-                    help="also time each call after a 512 MiB cache-evicting copy, over this many steps "
-                         "(phase_us_flushed; 0 to skip)")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cold", action="store_true",
+                    help="skip the cold-cache step and per-call timings (graphs with a 512 MiB read flush "
+                         "before each step)")
+    ap.add_argument("--no-ceilings", action="store_true",
+                    help="skip the streaming read / write / copy ceilings")
+    ap.add_argument("--cpu-seconds", type=float, default=16.0,
+                    help="CPU work for the oracle baseline, split between its one-thread and all-core timings")
     ap.add_argument("--no-graph", action="store_true",
                     help="time the eager loop only (default: K steps replayed from HIP graphs of %d steps)" % GRAPH_STEPS)
     ap.add_argument("--sweep", action="store_true",
@@ -208,7 +236,8 @@ def main():
                                     + args.layout + " layout)",
                           "unit": "us", "series": series}), flush=True)
         return
-    out = measure(args.workload, args.steps, args.warmup, not args.no_graph, args.layout, args.flush_steps)
+    out = measure(args.workload, args.steps, args.warmup, not args.no_graph, args.layout,
+                  cold=not args.no_cold and not args.no_graph, ceilings=not args.no_ceilings)
     inp = out.pop("_inp")
     if not args.no_cpu_baseline:
         cfg = dict(inp, rank_rows=args.layout == "ranks", rank_capacity=out["config"]["rank_capacity"])
@@ -217,7 +246,7 @@ def main():
 
 
 def measure(workload: str, steps: int, warmup: int, graph: bool = False, layout_kind: str = "pairs",
-            flush_steps: int = 0, **overrides) -> dict:
+            cold: bool = False, ceilings: bool = False, **overrides) -> dict:
     """Time `steps` steps of the path on `workload` (inputs resident in HBM);
     keyword overrides change the workload's shape (e.g. T=...).  layout_kind
     "ranks" times the (token, rank) path: layout, ep_dispatch_ranks,
@@ -391,29 +420,6 @@ def measure(workload: str, steps: int, warmup: int, graph: bool = False, layout_
     for e in ev:
         hev.destroy(e)
 
-    # (2b) the same calls, each after a flush of the memory-side cache (a
-    # 512 MiB copy, more than the 256 MB cache holds, outside the events): the
-    # cold-cache duration of each call
-    phase_us_flushed = None
-    if flush_steps:
-        fl_src = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
-        fl_dst = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
-        evf = [hev.create(2 * len(phases)) for _ in range(flush_steps)]
-        torch.cuda.synchronize()
-        for s_ in range(flush_steps):
-            for i, (_, fn) in enumerate(phases):
-                ep.ep_calib_copy(fl_src, fl_dst, FLUSH_BYTES)
-                hev.record(evf[s_][2 * i], stream)
-                fn()
-                hev.record(evf[s_][2 * i + 1], stream)
-        torch.cuda.synchronize()
-        phase_us_flushed = {name: 1000.0 * statistics.median(hev.ms(evf[s_][2 * i], evf[s_][2 * i + 1])
-                                                             for s_ in range(flush_steps))
-                            for i, (name, _) in enumerate(phases)}
-        for e in evf:
-            hev.destroy(e)
-        del fl_src, fl_dst
-
     # (3) HIP graph: G steps captured once, replayed K/G times (launch gaps
     # between steps vanish inside a graph, as in a captured serving loop)
     graph_ms, G = None, 0
@@ -441,21 +447,18 @@ def measure(workload: str, steps: int, warmup: int, graph: bool = False, layout_
             raise RuntimeError("graph replays differ from the eager step")
     ms_step = graph_ms if graph_ms is not None else eager_ms
 
-    # the same box's plain device copy (1 GiB read + 1 GiB written), as a
-    # measured streaming reference next to the published peak
-    cp_src = torch.empty(COPY_REF_BYTES, dtype=torch.uint8, device=dev)
-    cp_dst = torch.empty(COPY_REF_BYTES, dtype=torch.uint8, device=dev)
-    ep.ep_calib_copy(cp_src, cp_dst, COPY_REF_BYTES)
-    c0, c1 = hev.create(2)
-    torch.cuda.synchronize()
-    hev.record(c0, stream)
-    for _ in range(5):
-        ep.ep_calib_copy(cp_src, cp_dst, COPY_REF_BYTES)
-    hev.record(c1, stream)
-    torch.cuda.synchronize()
-    copy_gbs = 2 * COPY_REF_BYTES * 5 / (hev.ms(c0, c1) * 1e-3) / 1e9
-    hev.destroy([c0, c1])
-    del cp_src, cp_dst
+    # (4) cold: the memory-side cache flushed (512 MiB plain read: evicts
+    # everything, writes back what was dirty, leaves the cache clean) before
+    # every step; graphs of [flush, calls 0..i] minus graphs of [flush, calls
+    # 0..i-1], so the write-back of what the calls leave dirty in the cache
+    # (it happens during the next flush) is charged to them
+    cold_res = None
+    if cold and graph_ms is not None:
+        cold_res = cold_timing(phases, steps, G, hev, stream, dev)
+        if not torch.equal(y.view(torch.int16), y_ref.view(torch.int16)):
+            raise RuntimeError("cold graph replays differ from the eager step")
+
+    ceil = stream_ceilings(hev, stream, dev) if ceilings else None
 
     # accuracy of the step's y against the unquantized fp32 result, computed
     # in float64 from the inputs: sum over valid slots of w * s_e * x (s_e = 1
@@ -476,23 +479,56 @@ def measure(workload: str, steps: int, warmup: int, graph: bool = False, layout_
     # algorithmic bytes (library accounting on host copies of the layout)
     acc = ep.ep_accounting(shape, 0, lay["r"].cpu().numpy(), lay["n"].cpu().numpy(), int(lay["a"].item()), V)
     if ranks:
-        algo_bytes = {"layout": acc["hbm_layout_bytes"], "dispatch": acc["hbm_dispatch_ranks_bytes"],
-                      "combine": acc["hbm_combine_ranks_bytes"]}
+        calls = {"layout": "layout", "dispatch": "dispatch_ranks", "combine": "combine_ranks"}
         kernels = {"dispatch": "ep_dispatch_ranks_kernel", "combine": "ep_combine_ranks_kernel"}
     else:
-        algo_bytes = {"layout": acc["hbm_layout_bytes"], "dispatch": acc["hbm_dispatch_bytes"],
-                      "combine": acc["hbm_combine_bytes"]}
+        calls = {"layout": "layout", "dispatch": "dispatch", "combine": "combine"}
         kernels = {"dispatch": "ep_dispatch_copy_kernel", "combine": "ep_combine_" +
                    ("mxfp8" if fp8 else ("nvfp4" if nv else "bf16")) + "_kernel"}
+    rw = {p: (acc[f"hbm_{c}_read_bytes"], acc[f"hbm_{c}_write_bytes"]) for p, c in calls.items()}
+    if single_launch:
+        rw = {"layout+dispatch": (rw["layout"][0] + rw["dispatch"][0], rw["layout"][1] + rw["dispatch"][1]),
+              "combine": rw["combine"]}
+        kernels["layout+dispatch"] = kernels["dispatch"]
+    algo_bytes = {p: r + w_ for p, (r, w_) in rw.items()}
     step_bytes = sum(algo_bytes.values())
     step_s = ms_step / 1000.0
-    if single_launch:
-        algo_bytes = {"layout+dispatch": algo_bytes["layout"] + algo_bytes["dispatch"],
-                      "combine": algo_bytes["combine"]}
-        kernels["layout+dispatch"] = kernels["dispatch"]
-    dom = max((p for p in algo_bytes if p != "layout"), key=lambda p: phase_us[p])
+    rows_calls = [p for p in algo_bytes if p != "layout"]
+    dom = max(rows_calls, key=lambda p: phase_us[p])
     achieved = algo_bytes[dom] / (phase_us[dom] * 1e-6) / 1e9
     traffic = measured_traffic(workload + ("_ranks" if ranks else ""), kernels[dom])
+    roofline = {"bound": "hbm", "kernel": kernels[dom], "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                "algorithmic_bytes_per_launch": int(algo_bytes[dom]),
+                "mall_assisted": True}   # warm: back-to-back calls on the same buffers
+    cold_out = None
+    if cold_res is not None:
+        cs = cold_res["step_us"] * 1e-6
+        cph = cold_res["phase_us"]
+        cold_out = {"ms_per_step": round(cold_res["step_us"] / 1000.0, 4),
+                    "value": round(step_bytes / cs / 1e9, 2), "tokens_per_s": round(T / cs, 1),
+                    "frac": round(step_bytes / cs / 1e9 / HBM_PEAK_GBS, 4),
+                    "phase_us": {p: round(v, 2) for p, v in cph.items()},
+                    "phase_gbs": {p: round(algo_bytes[p] / (cph[p] * 1e-6) / 1e9, 1) for p in algo_bytes},
+                    "flush_us": round(cold_res["flush_us"], 2),
+                    "method": "HIP graphs of [512 MiB plain-read flush, step] (phase_us: [flush, one call]) "
+                              "minus graphs of [flush]: every step (call) starts with a clean memory-side "
+                              "cache and the write-back of what it leaves dirty there is charged to it"}
+        cdom = max(rows_calls, key=lambda p: cph[p])
+        cach = algo_bytes[cdom] / (cph[cdom] * 1e-6) / 1e9
+        roofline.update({"cold_kernel": kernels[cdom], "cold_achieved": round(cach, 1),
+                         "cold_frac": round(cach / HBM_PEAK_GBS, 4),
+                         "cold_step_frac": round(step_bytes / cs / 1e9 / HBM_PEAK_GBS, 4)})
+        calls_out = {}
+        for p in rows_calls:
+            g = algo_bytes[p] / (cph[p] * 1e-6) / 1e9
+            c = {"kernel": kernels[p], "cold_gbs": round(g, 1), "frac": round(g / HBM_PEAK_GBS, 4),
+                 "read_bytes": int(rw[p][0]), "write_bytes": int(rw[p][1])}
+            if ceil is not None:
+                m = mix_ceiling(rw[p][0], rw[p][1], ceil)
+                c.update({"ceiling_gbs": round(m, 1), "frac_of_ceiling": round(g / m, 4)})
+            calls_out[p] = c
+        roofline["calls"] = calls_out
 
     out = {
         "metric": METRIC,
@@ -514,21 +550,18 @@ def measure(workload: str, steps: int, warmup: int, graph: bool = False, layout_
                    ("(token, expert) rows, RANK_MAJOR" if M else "(token, expert) rows"),
                    "rank_capacity": M, "receive_rows": int(acc["nvl_tokens"]) if ranks else V},
         "tokens_per_s": round(T / step_s, 1),
-        "dispatch_combine_gbs": round(sum(algo_bytes[p] for p in algo_bytes if p != "layout")
-                                      / (sum(phase_us[p] for p in phase_us if p != "layout") * 1e-6) / 1e9, 1),
+        "cold": cold_out,
+        "dispatch_combine_gbs": round(sum(algo_bytes[p] for p in rows_calls)
+                                      / (sum(phase_us[p] for p in rows_calls) * 1e-6) / 1e9, 1),
         "rel_l2_vs_fp32": round(rel_l2, 6),
         "phase_us": {p: round(v, 2) for p, v in phase_us.items()},
         "phase_gbs": {p: round(algo_bytes[p] / (phase_us[p] * 1e-6) / 1e9, 1) for p in algo_bytes},
         "phase_us_min_p90": phase_stats,
-        "phase_us_flushed": None if phase_us_flushed is None else
-        {p: round(v, 2) for p, v in phase_us_flushed.items()},
         "step_algorithmic_bytes": int(step_bytes),
         "eager_ms_per_step": round(eager_ms, 4),
         "timing": ("steps replayed from a HIP graph of %d steps" % G) if graph_ms is not None else "eager",
-        "roofline": {"bound": "hbm", "kernel": kernels[dom], "achieved": round(achieved, 1),
-                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": traffic, "algorithmic_bytes_per_launch": int(algo_bytes[dom]),
-                     "measured_copy_gbs": round(copy_gbs, 1), "frac_of_copy": round(achieved / copy_gbs, 4)},
+        "roofline": roofline,
+        "ceilings": ceil,
         "pages_accounting": {"rdma_algo_tokens": acc["rdma_algo_tokens"],
                              "rdma_physical_tokens": acc["rdma_physical_tokens"],
                              "nvl_tokens": acc["nvl_tokens"],
@@ -539,20 +572,160 @@ def measure(workload: str, steps: int, warmup: int, graph: bool = False, layout_
     return out
 
 
-def cpu_baseline(inp, seconds, step_bytes):
-    """The CPU oracle as it stands (plain C, one thread) on the same workload:
-    whole passes (layout, slots, dispatch rows, expert stage, combine) repeated
-    until `seconds` of CPU work, at least one pass; then one more pass timed
-    part by part (layout, slots + dispatch rows, combine)."""
-    import oracle
+def _graph(body, reps: int):
+    import torch
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(reps):
+            body()
+    return g
 
+
+def cold_timing(phases, steps: int, G: int, hev, stream, dev) -> dict:
+    """Cold-cache step and per-call durations (us), write-back charged.
+
+    Graphs of G copies of [512 MiB plain-read flush, body]: a plain read of
+    more than the memory-side cache holds evicts every line, writing back the
+    dirty ones, and leaves the cache clean; so each copy's body starts cold,
+    and what it leaves dirty in the cache is written back during the next
+    copy's flush, inside the same graph.  Subtracting the graph of G flushes
+    alone leaves the body's duration with its write-back.  Bodies: the whole
+    step (the cold step), and each call alone (its inputs are those of the
+    last step, still in place, so every call starts from HBM; the calls of
+    one step share the cache, so the step can take less than its calls
+    alone).  Each graph is replayed K/G times per timing, three rounds
+    alternating over the graphs, median."""
+    import torch
+
+    from combine_dispatch_layout_02_amd import ep
+
+    flush_buf = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
+    sink = torch.empty(256, dtype=torch.uint8, device=dev)
+
+    def flush():
+        ep.ep_stream(ep.EP_STREAM_READ, flush_buf, sink, FLUSH_BYTES, FLUSH_CHUNK, FLUSH_WAVES)
+
+    def body_of(fns):
+        def body():
+            flush()
+            for fn in fns:
+                fn()
+        return body
+
+    bodies = [[], [fn for _, fn in phases]] + [[fn] for _, fn in phases]
+    graphs = [_graph(body_of(b), G) for b in bodies]
+    reps = max(1, steps // G)
+    for g in graphs:
+        g.replay()
+    torch.cuda.synchronize()
+    samples = [[] for _ in graphs]
+    for _ in range(3):
+        for i, g in enumerate(graphs):
+            a0, a1 = hev.create(2)
+            torch.cuda.synchronize()
+            hev.record(a0, stream)
+            for _ in range(reps):
+                g.replay()
+            hev.record(a1, stream)
+            torch.cuda.synchronize()
+            samples[i].append(1000.0 * hev.ms(a0, a1) / (reps * G))
+            hev.destroy([a0, a1])
+    us = [statistics.median(v) for v in samples]
+    del graphs
+    return {"flush_us": us[0], "step_us": us[1] - us[0],
+            "phase_us": {name: us[2 + i] - us[0] for i, (name, _) in enumerate(phases)}}
+
+
+def stream_ceilings(hev, stream, dev) -> dict:
+    """The box's streaming read, write and copy rates (GB/s): CEIL_LAUNCHES
+    back-to-back launches of ep_stream alternating over two sets of 1 GiB
+    buffers, so the cache holds nothing a launch reuses and the dirty lines
+    each launch leaves are written back during the next one; best over the
+    launch shapes CEIL_SHAPES (chunk bytes x waves) and over plain /
+    non-temporal accesses."""
+    import torch
+
+    from combine_dispatch_layout_02_amd import ep
+
+    bufs = [torch.empty(CEIL_BYTES, dtype=torch.uint8, device=dev) for _ in range(4)]
+    sink = torch.empty(256, dtype=torch.uint8, device=dev)
+    kinds = {"read": (ep.EP_STREAM_READ, ep.EP_STREAM_READ_NT), "write": (ep.EP_STREAM_WRITE, ep.EP_STREAM_WRITE_NT),
+             "copy": (ep.EP_STREAM_COPY, ep.EP_STREAM_COPY_NT)}
+    best = {}
+    for name, ks in kinds.items():
+        for kind in ks:
+            for chunk, waves in CEIL_SHAPES:
+                def launch(i):
+                    a, b = (bufs[0], bufs[1]) if i % 2 == 0 else (bufs[2], bufs[3])
+                    if name == "read":
+                        ep.ep_stream(kind, a, sink, CEIL_BYTES, chunk, waves)
+                    elif name == "write":
+                        ep.ep_stream(kind, None, a, CEIL_BYTES, chunk, waves)
+                    else:
+                        ep.ep_stream(kind, a, b, CEIL_BYTES, chunk, waves)
+                launch(1)
+                a0, a1 = hev.create(2)
+                torch.cuda.synchronize()
+                hev.record(a0, stream)
+                for i in range(CEIL_LAUNCHES):
+                    launch(i)
+                hev.record(a1, stream)
+                torch.cuda.synchronize()
+                moved = CEIL_BYTES * CEIL_LAUNCHES * (2 if name == "copy" else 1)
+                gbs = moved / (hev.ms(a0, a1) * 1e-3) / 1e9
+                hev.destroy([a0, a1])
+                if name not in best or gbs > best[name]["gbs"]:
+                    best[name] = {"gbs": round(gbs, 1), "chunk_bytes": chunk, "waves": waves,
+                                  "non_temporal": kind % 2 == 1}
+    del bufs
+    return best
+
+
+def mix_ceiling(read_bytes: float, write_bytes: float, ceil: dict) -> float:
+    """Ceiling (GB/s) for a call that reads and writes these bytes: the read
+    and write streams' rates, each for its share of the bytes, one after the
+    other -- the rate of a stream with the same mix if reads and writes cannot
+    overlap on the memory bus."""
+    t = read_bytes / ceil["read"]["gbs"] + write_bytes / ceil["write"]["gbs"]
+    return (read_bytes + write_bytes) / t if t > 0 else 0.0
+
+
+def host_cores() -> int:
+    """Cores this process may use: the CPU share the job was given
+    (OMP_NUM_THREADS when set, else the affinity mask)."""
+    n = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1)
+    env = os.environ.get("OMP_NUM_THREADS", "")
+    if env.isdigit() and int(env) > 0:
+        n = min(n, int(env))
+    return max(1, n)
+
+
+def _oracle_rate(oracle, inp, seconds):
     reps, t_start = 0, time.perf_counter()
     while True:
         oracle.run_path(inp)
         reps += 1
         if time.perf_counter() - t_start >= seconds:
             break
-    dt = (time.perf_counter() - t_start) / reps
+    return reps, (time.perf_counter() - t_start) / reps
+
+
+def cpu_baseline(inp, seconds, step_bytes):
+    """The CPU oracle as it stands on the same workload: whole passes (layout,
+    slots, dispatch rows, expert stage, combine) repeated until `seconds` of
+    work, at least one pass; once with one thread, once with the row-level
+    calls (dispatch rows, expert stage, combine) split over every core this
+    process may use (the oracle's threads() mode: the same C code per token
+    block, identical bytes).  The reported value is the all-core one; the
+    one-thread figure sits beside it, each with its core count, and one more
+    single-thread pass is timed part by part (layout, slots + dispatch rows,
+    combine)."""
+    import oracle
+
+    cores = host_cores()
+    reps1, dt1 = _oracle_rate(oracle, inp, seconds / 2)
+    with oracle.threads(cores):
+        repsn, dtn = _oracle_rate(oracle, inp, seconds / 2)
     parts = {}
     if not inp.get("rank_rows") and inp.get("x_fmt", "bf16") == "bf16" and inp.get("y_fmt", "bf16") == "bf16":
         idx, w = inp["topk_idx"], inp["topk_w"]
@@ -565,9 +738,13 @@ def cpu_baseline(inp, seconds, step_bytes):
         oracle.combine_bf16(recv, sl["token_slot"], w)
         t3 = time.perf_counter()
         parts = {"layout_s": round(t1 - t0, 4), "slots_dispatch_s": round(t2 - t1, 4), "combine_s": round(t3 - t2, 4)}
-    return {"value": round(inp["T"] / dt, 1), "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "gbs": round(step_bytes / dt / 1e9, 3), "parts": parts,
-            "sample": f"{reps} full passes of workload {inp['name']} (T={inp['T']}), {dt:.3f} s per pass"}
+    return {"value": round(inp["T"] / dtn, 1), "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "gbs": round(step_bytes / dtn / 1e9, 3),
+            "sample": f"{repsn} full passes of workload {inp['name']} (T={inp['T']}) on {cores} threads, "
+                      f"{dtn:.3f} s per pass",
+            "single_thread": {"value": round(inp["T"] / dt1, 1), "unit": "tokens/s", "cores": 1,
+                              "gbs": round(step_bytes / dt1 / 1e9, 3), "parts": parts,
+                              "sample": f"{reps1} full passes, {dt1:.3f} s per pass"}}
 
 
 if __name__ == "__main__":

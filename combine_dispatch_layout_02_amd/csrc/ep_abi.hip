@@ -55,6 +55,20 @@ int check_shape(const ep_shape *sh, Shape *out) {
 
 int hip_status(hipError_t e) { return e == hipSuccess ? EP_OK : EP_EHIP; }
 
+// Bytes of one token row of `H` elements in a payload format: the elements
+// plus that row's share of scales (fp8: one fp32 per 128, as the MORI-EP
+// Benchmark's fp8 factor counts them; mxfp8: one e8m0 byte per 32; nvfp4:
+// one bf16 per 16).
+double row_bytes(int fmt, int H) {
+    const double h = (double)H;
+    switch (fmt) {
+        case EP_FMT_FP8_S128: return h * 1.0 + (h / 128.0) * sizeof(float);
+        case EP_FMT_MXFP8: return h * 1.0 + (h / 32.0) * 1.0;
+        case EP_FMT_NVFP4: return h * 0.5 + (h / 16.0) * sizeof(uint16_t);
+        default: return h * sizeof(uint16_t);
+    }
+}
+
 }  // namespace
 
 namespace ep {
@@ -149,12 +163,11 @@ int ep_dispatch_layout(const ep_shape *shape, const int64_t *topk_idx, int32_t *
 
 namespace {
 
-int check_dispatch_args(const ep_shape *shape, Shape *s, const void *x, const float *x_scales,
-                        const int64_t *topk_idx, const float *topk_w, const void *recv_x,
-                        const float *recv_x_scales, const int32_t *recv_src_idx,
-                        const float *recv_topk_w, const int32_t *token_slot,
-                        const int32_t *expert_offset, const void *ws, size_t ws_bytes,
-                        WsLayout *L) {
+int check_dispatch_inputs(const ep_shape *shape, Shape *s, const void *x, const float *x_scales,
+                          const int64_t *topk_idx, const float *topk_w, const void *recv_x,
+                          const float *recv_x_scales, const int32_t *recv_src_idx,
+                          const float *recv_topk_w, const int32_t *token_slot,
+                          const int32_t *expert_offset) {
     int rc = check_shape(shape, s);
     if (rc != EP_OK) return rc;
     if (!expert_offset) return EP_EINVAL;
@@ -165,10 +178,53 @@ int check_dispatch_args(const ep_shape *shape, Shape *s, const void *x, const fl
     if (fp8 && s->T > 0 && (!x_scales || !recv_x_scales)) return EP_EINVAL;
     if (!fp8 && (x_scales || recv_x_scales)) return EP_EINVAL;
     if (s->T > 0 && (!aligned16(x) || !aligned16(recv_x))) return EP_EALIGN;
-    *L = ep::ws_layout(*s);
+    return EP_OK;
+}
+
+int check_workspace(const Shape &s, const void *ws, size_t ws_bytes, WsLayout *L) {
+    *L = ep::ws_layout(s);
     if (!ws || ws_bytes < L->total) return EP_EWORKSPACE;
     if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0) return EP_EALIGN;
     return EP_OK;
+}
+
+int check_dispatch_args(const ep_shape *shape, Shape *s, const void *x, const float *x_scales,
+                        const int64_t *topk_idx, const float *topk_w, const void *recv_x,
+                        const float *recv_x_scales, const int32_t *recv_src_idx,
+                        const float *recv_topk_w, const int32_t *token_slot,
+                        const int32_t *expert_offset, const void *ws, size_t ws_bytes,
+                        WsLayout *L) {
+    int rc = check_dispatch_inputs(shape, s, x, x_scales, topk_idx, topk_w, recv_x, recv_x_scales,
+                                   recv_src_idx, recv_topk_w, token_slot, expert_offset);
+    if (rc != EP_OK) return rc;
+    return check_workspace(*s, ws, ws_bytes, L);
+}
+
+int check_layout_outputs(const Shape &s, const int32_t *per_rank, const int32_t *per_expert,
+                         const uint8_t *in_rank, const int32_t *per_node, const int64_t *algo) {
+    if (!per_rank || !per_expert || !per_node || !algo) return EP_EINVAL;
+    if (s.T > 0 && !in_rank) return EP_EINVAL;
+    if (!aligned16(in_rank) && (s.R % 4 == 0)) return EP_EALIGN;
+    return EP_OK;
+}
+
+// Layout + dispatch on a checked shape, with the workspace at w (plan regions
+// as in L): a small batch in one launch, else the plan launches and the copy.
+int dispatch_with_layout_impl(const Shape &s, const WsLayout &L, const void *x, const float *x_scales,
+                              const int64_t *topk_idx, const float *topk_w, int32_t *per_rank,
+                              int32_t *per_expert, uint8_t *in_rank, int32_t *per_node, int64_t *algo,
+                              void *recv_x, float *recv_x_scales, int32_t *recv_src_idx, float *recv_topk_w,
+                              int32_t *token_slot, int32_t *expert_offset, char *w, hipStream_t st) {
+    if (ep::fused_dispatch_fits(s))
+        return hip_status(ep::launch_dispatch_fused(s, x, x_scales, topk_idx, topk_w, recv_x, recv_x_scales,
+                                                    recv_src_idx, recv_topk_w, token_slot, expert_offset,
+                                                    per_rank, per_expert, in_rank, per_node, algo,
+                                                    reinterpret_cast<uint32_t *>(w + L.ctrl), st));
+    hipError_t e = ep::launch_plan(s, L, topk_idx, per_rank, per_expert, in_rank, per_node, algo, w, st);
+    if (e != hipSuccess) return EP_EHIP;
+    e = ep::launch_dispatch_copy(s, L, x, x_scales, topk_idx, topk_w, recv_x, recv_x_scales,
+                                 recv_src_idx, recv_topk_w, token_slot, expert_offset, w, st);
+    return hip_status(e);
 }
 
 }  // namespace
@@ -210,25 +266,14 @@ int ep_dispatch_with_layout(const ep_shape *shape, const void *x, const float *x
     int rc = check_dispatch_args(shape, &s, x, x_scales, topk_idx, topk_w, recv_x, recv_x_scales,
                                  recv_src_idx, recv_topk_w, token_slot, expert_offset, ws, ws_bytes, &L);
     if (rc != EP_OK) return rc;
-    if (!num_tokens_per_rank || !num_tokens_per_expert || !num_tokens_per_node || !rdma_algo_token_count)
-        return EP_EINVAL;
-    if (s.T > 0 && !is_token_in_rank) return EP_EINVAL;
-    if (!aligned16(is_token_in_rank) && (s.R % 4 == 0)) return EP_EALIGN;
-    hipStream_t st = static_cast<hipStream_t>(stream);
-    char *w = static_cast<char *>(ws);
-    if (ep::fused_dispatch_fits(s))
-        return hip_status(ep::launch_dispatch_fused(s, x, x_scales, topk_idx, topk_w, recv_x, recv_x_scales,
-                                                    recv_src_idx, recv_topk_w, token_slot, expert_offset,
-                                                    num_tokens_per_rank, num_tokens_per_expert,
-                                                    is_token_in_rank, num_tokens_per_node,
-                                                    rdma_algo_token_count,
-                                                    reinterpret_cast<uint32_t *>(w + L.ctrl), st));
-    hipError_t e = ep::launch_plan(s, L, topk_idx, num_tokens_per_rank, num_tokens_per_expert,
-                                   is_token_in_rank, num_tokens_per_node, rdma_algo_token_count, w, st);
-    if (e != hipSuccess) return EP_EHIP;
-    e = ep::launch_dispatch_copy(s, L, x, x_scales, topk_idx, topk_w, recv_x, recv_x_scales,
-                                 recv_src_idx, recv_topk_w, token_slot, expert_offset, w, st);
-    return hip_status(e);
+    rc = check_layout_outputs(s, num_tokens_per_rank, num_tokens_per_expert, is_token_in_rank,
+                              num_tokens_per_node, rdma_algo_token_count);
+    if (rc != EP_OK) return rc;
+    return dispatch_with_layout_impl(s, L, x, x_scales, topk_idx, topk_w, num_tokens_per_rank,
+                                     num_tokens_per_expert, is_token_in_rank, num_tokens_per_node,
+                                     rdma_algo_token_count, recv_x, recv_x_scales, recv_src_idx, recv_topk_w,
+                                     token_slot, expert_offset, static_cast<char *>(ws),
+                                     static_cast<hipStream_t>(stream));
 }
 
 int ep_dispatch_from_layout(const ep_shape *shape, const void *x, const float *x_scales,
@@ -464,41 +509,57 @@ int ep_accounting(const ep_shape *shape, int32_t own_node, const int32_t *num_to
     if (!num_tokens_per_rank || !num_tokens_per_node || !out) return EP_EINVAL;
     if (own_node < 0 || own_node >= s.N || valid_pairs < 0 || valid_pairs > s.T * s.k)
         return EP_EINVAL;
+    // The pages' token counts (MORI-EP Benchmark, "Algo BW vs Physical BW",
+    // "NVL / XGMI bandwidth"): every (token, node) pair of the layout crosses
+    // RDMA once, the local node included; a fraction (N-1)/N of them leaves
+    // the node; every (token, rank) pair is one NVL row.
     int64_t nvl = 0;
     for (int r = 0; r < s.R; ++r) nvl += num_tokens_per_rank[r];
-    const double H = (double)s.H;
-    out->rdma_algo_tokens = rdma_algo_token_count;
-    out->rdma_physical_tokens = (double)rdma_algo_token_count * (double)(s.N - 1) / (double)s.N;
-    out->rdma_physical_tokens_exact = rdma_algo_token_count - num_tokens_per_node[own_node];
+    const int64_t algo = rdma_algo_token_count;
+    out->rdma_algo_tokens = algo;
+    out->rdma_physical_tokens = (double)algo * (double)(s.N - 1) / (double)s.N;
+    out->rdma_physical_tokens_exact = algo - num_tokens_per_node[own_node];
     out->nvl_tokens = nvl;
-    out->dispatch_rdma_bytes_bf16 = (double)rdma_algo_token_count * H * 2.0;
-    out->dispatch_nvl_bytes_bf16 = (double)nvl * H * 2.0;
-    out->combine_rdma_bytes_bf16 = out->dispatch_rdma_bytes_bf16;
-    out->combine_nvl_bytes_bf16 = out->dispatch_nvl_bytes_bf16;
-    out->fp8_factor = (1.0 + 4.0 / 128.0) / 2.0;
-    out->dispatch_rdma_bytes_fp8 = out->dispatch_rdma_bytes_bf16 * out->fp8_factor;
-    out->dispatch_nvl_bytes_fp8 = out->dispatch_nvl_bytes_bf16 * out->fp8_factor;
-    // minimum HBM traffic of one call each (payload rows + index/weight metadata)
-    const double T = (double)s.T, TK = (double)s.T * s.k, V = (double)valid_pairs;
-    const double xrow = (s.x_fmt == EP_FMT_FP8_S128) ? H + 4.0 * H / 128.0 : 2.0 * H;
-    const double yrow = (s.y_fmt == EP_FMT_MXFP8) ? H + H / 32.0
-                        : (s.y_fmt == EP_FMT_NVFP4) ? H / 2.0 + 2.0 * H / 16.0 : 2.0 * H;
-    out->hbm_layout_bytes = TK * 8.0 + T * s.R + 4.0 * (s.R + s.N + s.E) + 8.0;
-    out->hbm_dispatch_bytes = T * xrow + V * xrow             // rows: read once, written per pair
-                              + TK * (8.0 + 4.0 + 4.0)        // topk_idx, topk_w read; token_slot written
-                              + V * (4.0 + 4.0)               // recv_src_idx, recv_topk_w written
-                              + 4.0 * (s.E + 1);              // expert_offset
-    out->hbm_combine_bytes = V * yrow + T * 2.0 * H          // rows gathered, y written
-                             + TK * (4.0 + 4.0);             // token_slot, topk_w read
-    // (token, rank) rows: one per (t, r) pair, i.e. nvl_tokens rows
-    const double NR = (double)nvl;
-    out->hbm_dispatch_ranks_bytes = T * xrow + NR * xrow       // rows: read once, written per rank
-                                    + TK * (8.0 + 4.0)         // topk_idx, topk_w read
-                                    + T * s.R * 4.0            // token_rank_slot written
-                                    + NR * (4.0 + 8.0 * s.k)   // recv_src_idx, recv_topk_idx / _w
-                                    + 4.0 * (s.R + 1);         // rank_offset
-    out->hbm_combine_ranks_bytes = NR * 2.0 * H + T * 2.0 * H  // partials gathered, y written
-                                   + T * s.R * 4.0;            // token_rank_slot read
+    // Bytes = rows x bytes of one row in the payload format; the combine
+    // sends the same rows back.
+    const double bf16_row = row_bytes(EP_FMT_BF16, s.H), fp8_row = row_bytes(EP_FMT_FP8_S128, s.H);
+    out->dispatch_rdma_bytes_bf16 = (double)algo * bf16_row;
+    out->dispatch_nvl_bytes_bf16 = (double)nvl * bf16_row;
+    out->combine_rdma_bytes_bf16 = (double)algo * bf16_row;
+    out->combine_nvl_bytes_bf16 = (double)nvl * bf16_row;
+    out->fp8_factor = fp8_row / bf16_row;
+    out->dispatch_rdma_bytes_fp8 = (double)algo * fp8_row;
+    out->dispatch_nvl_bytes_fp8 = (double)nvl * fp8_row;
+
+    // Minimum HBM traffic of one call each on this GPU: every row it moves
+    // and every index / weight element it reads or writes, exactly once.
+    const double T = (double)s.T, TK = (double)s.T * s.k, V = (double)valid_pairs, NR = (double)nvl;
+    const double R = s.R, E = s.E, N = s.N, k = s.k;
+    const double xrow = row_bytes(s.x_fmt, s.H), yrow = row_bytes(s.y_fmt, s.H), out_row = bf16_row;
+    // layout: topk_idx in; token-in-rank map, the three count vectors and the algo count out
+    out->hbm_layout_read_bytes = TK * sizeof(int64_t);
+    out->hbm_layout_write_bytes = T * R * sizeof(uint8_t) + (R + N + E) * sizeof(int32_t) + sizeof(int64_t);
+    // dispatch: x rows, topk_idx, topk_w in; one row per valid pair, token_slot,
+    // recv_src_idx, recv_topk_w and expert_offset out
+    out->hbm_dispatch_read_bytes = T * xrow + TK * (sizeof(int64_t) + sizeof(float));
+    out->hbm_dispatch_write_bytes = V * xrow + TK * sizeof(int32_t) + V * (sizeof(int32_t) + sizeof(float)) +
+                                    (E + 1) * sizeof(int32_t);
+    // combine: one row per valid pair, token_slot, topk_w in; y out
+    out->hbm_combine_read_bytes = V * yrow + TK * (sizeof(int32_t) + sizeof(float));
+    out->hbm_combine_write_bytes = T * out_row;
+    // (token, rank) rows: one per (t, r) pair, i.e. nvl_tokens rows; the
+    // metadata per row is its source index and its k-wide local top-k list
+    out->hbm_dispatch_ranks_read_bytes = T * xrow + TK * (sizeof(int64_t) + sizeof(float));
+    out->hbm_dispatch_ranks_write_bytes = NR * xrow + T * R * sizeof(int32_t) +
+                                          NR * (sizeof(int32_t) + k * (sizeof(int32_t) + sizeof(float))) +
+                                          (R + 1) * sizeof(int32_t);
+    out->hbm_combine_ranks_read_bytes = NR * out_row + T * R * sizeof(int32_t);
+    out->hbm_combine_ranks_write_bytes = T * out_row;
+    out->hbm_layout_bytes = out->hbm_layout_read_bytes + out->hbm_layout_write_bytes;
+    out->hbm_dispatch_bytes = out->hbm_dispatch_read_bytes + out->hbm_dispatch_write_bytes;
+    out->hbm_combine_bytes = out->hbm_combine_read_bytes + out->hbm_combine_write_bytes;
+    out->hbm_dispatch_ranks_bytes = out->hbm_dispatch_ranks_read_bytes + out->hbm_dispatch_ranks_write_bytes;
+    out->hbm_combine_ranks_bytes = out->hbm_combine_ranks_read_bytes + out->hbm_combine_ranks_write_bytes;
     return EP_OK;
 }
 
@@ -506,6 +567,22 @@ int ep_calib_copy(const void *src, void *dst, size_t bytes, void *stream) {
     if (!src || !dst || bytes % 16 != 0) return EP_EINVAL;
     if (!aligned16(src) || !aligned16(dst)) return EP_EALIGN;
     return hip_status(ep::launch_calib_copy(src, dst, bytes, static_cast<hipStream_t>(stream)));
+}
+
+int ep_stream(int32_t kind, const void *src, void *dst, size_t bytes, size_t chunk_bytes, int32_t waves,
+              void *stream) {
+    if (kind < EP_STREAM_READ || kind > EP_STREAM_COPY_NT) return EP_EINVAL;
+    if (chunk_bytes < 1024 || chunk_bytes % 1024 != 0 || chunk_bytes > (size_t(1) << 20)) return EP_EINVAL;
+    if (bytes % chunk_bytes != 0 || waves < 4 || waves % 4 != 0 || waves > (1 << 20)) return EP_EINVAL;
+    const int k = kind / 2;   // 0 read, 1 write, 2 copy
+    if (!dst || (k == 1) != (src == nullptr)) return EP_EINVAL;
+    if (!aligned16(dst) || (src && !aligned16(src))) return EP_EALIGN;
+    if (k == 2) {   // overlapping copies are not supported
+        const uintptr_t s0 = reinterpret_cast<uintptr_t>(src), d0 = reinterpret_cast<uintptr_t>(dst);
+        if (bytes && s0 < d0 + bytes && d0 < s0 + bytes) return EP_EINVAL;
+    }
+    return hip_status(ep::launch_stream(k, (kind & 1) != 0, src, dst, bytes, chunk_bytes, waves,
+                                        static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

@@ -137,6 +137,11 @@ hipError_t launch_expert_requant_nvfp4(const Shape &s, const int32_t *expert_off
 
 hipError_t launch_calib_copy(const void *src, void *dst, size_t bytes, hipStream_t stream);
 
+// Streaming kernels (stream.hip): kind 0 read, 1 write, 2 copy; nt selects
+// non-temporal loads / stores.  Whole chunks of `chunk` bytes, `waves` waves.
+hipError_t launch_stream(int kind, bool nt, const void *src, void *dst, size_t bytes, size_t chunk, int waves,
+                         hipStream_t stream);
+
 // Waves per token for the row kernels: the smallest power of two that gives
 // `target` waves in all, never so many that a wave has fewer than 64 row
 // vectors.

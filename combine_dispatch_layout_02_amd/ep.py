@@ -31,7 +31,7 @@ EXPORTED = (
     "ep_dispatch_ranks_cached", "ep_dispatch_ranks_with_layout", "ep_combine", "ep_check",
     "ep_dispatch_ranks", "ep_expert_reduce_ranks", "ep_combine_ranks", "ep_quant_fp8_s128",
     "ep_expert_scale_bf16", "ep_expert_requant_mxfp8", "ep_expert_requant_nvfp4", "ep_accounting",
-    "ep_calib_copy",
+    "ep_calib_copy", "ep_stream",
 )
 
 
@@ -80,7 +80,8 @@ class ep_accounting_t(ctypes.Structure):
         ("hbm_combine_bytes", ctypes.c_double),
         ("hbm_dispatch_ranks_bytes", ctypes.c_double),
         ("hbm_combine_ranks_bytes", ctypes.c_double),
-    ]
+    ] + [(f"hbm_{call}_{rw}_bytes", ctypes.c_double)
+         for call in ("layout", "dispatch", "combine", "dispatch_ranks", "combine_ranks") for rw in ("read", "write")]
 
     def as_dict(self):
         return {name: getattr(self, name) for name, _ in self._fields_}
@@ -124,12 +125,13 @@ def load():
         "ep_expert_requant_nvfp4": (ctypes.c_int, [SP, P, P, P, P, P, P]),
         "ep_accounting": (ctypes.c_int, [SP, i32, P, P, i64, i64, ctypes.POINTER(ep_accounting_t)]),
         "ep_calib_copy": (ctypes.c_int, [P, P, sz, P]),
+        "ep_stream": (ctypes.c_int, [i32, P, P, sz, sz, i32, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
         fn.restype = res
         fn.argtypes = args
-    if lib.ep_abi_version() != 5:
+    if lib.ep_abi_version() != 6:
         raise RuntimeError("libep_hip ABI version mismatch")
     _lib = lib
     return lib
@@ -257,10 +259,9 @@ def ep_dispatch(shape, x, x_scales, topk_idx, topk_w, recv_x, recv_x_scales, rec
         "ep_dispatch_from_layout" if from_layout else "ep_dispatch")
 
 
-def ep_dispatch_with_layout(shape, x, x_scales, topk_idx, topk_w, num_tokens_per_rank, num_tokens_per_expert,
-                            is_token_in_rank, num_tokens_per_node, rdma_algo_token_count, recv_x, recv_x_scales,
-                            recv_src_idx, recv_topk_w, token_slot, expert_offset, ws: Workspace, stream=None):
-    """Layout and dispatch in one call (one launch for batches of <= 2048 pairs)."""
+def _check_with_layout(shape, x, x_scales, topk_idx, topk_w, num_tokens_per_rank, num_tokens_per_expert,
+                       is_token_in_rank, num_tokens_per_node, rdma_algo_token_count, recv_x, recv_x_scales,
+                       recv_src_idx, recv_topk_w, token_slot, expert_offset):
     T, k, H, E, R, N = (shape.num_tokens, shape.num_topk, shape.hidden, shape.num_experts, shape.num_ranks,
                         shape.num_nodes)
     fp8 = shape.x_format == EP_FMT_FP8_S128
@@ -281,6 +282,15 @@ def ep_dispatch_with_layout(shape, x, x_scales, topk_idx, topk_w, num_tokens_per
     _need(recv_topk_w, torch.float32, (rows,), "recv_topk_w")
     _need(token_slot, torch.int32, (T, k), "token_slot")
     _need(expert_offset, torch.int32, (E + 1,), "expert_offset")
+
+
+def ep_dispatch_with_layout(shape, x, x_scales, topk_idx, topk_w, num_tokens_per_rank, num_tokens_per_expert,
+                            is_token_in_rank, num_tokens_per_node, rdma_algo_token_count, recv_x, recv_x_scales,
+                            recv_src_idx, recv_topk_w, token_slot, expert_offset, ws: Workspace, stream=None):
+    """Layout and dispatch in one call (one launch for batches of <= 2048 pairs)."""
+    _check_with_layout(shape, x, x_scales, topk_idx, topk_w, num_tokens_per_rank, num_tokens_per_expert,
+                       is_token_in_rank, num_tokens_per_node, rdma_algo_token_count, recv_x, recv_x_scales,
+                       recv_src_idx, recv_topk_w, token_slot, expert_offset)
     ws.planned_for = None   # no reusable plan is left in the workspace
     _ok(load().ep_dispatch_with_layout(ctypes.byref(shape), _ptr(x), _ptr(x_scales), _ptr(topk_idx), _ptr(topk_w),
                                        _ptr(num_tokens_per_rank), _ptr(num_tokens_per_expert),
@@ -289,6 +299,7 @@ def ep_dispatch_with_layout(shape, x, x_scales, topk_idx, topk_w, num_tokens_per
                                        _ptr(recv_src_idx), _ptr(recv_topk_w), _ptr(token_slot),
                                        _ptr(expert_offset), ws.ptr, ws.nbytes, _stream(stream)),
         "ep_dispatch_with_layout")
+
 
 
 def ep_dispatch_cached(shape, x, x_scales, token_slot, recv_x, recv_x_scales=None, stream=None):
@@ -472,6 +483,18 @@ def ep_accounting(shape, own_node, num_tokens_per_rank, num_tokens_per_node, rdm
 
 def ep_calib_copy(src, dst, nbytes, stream=None):
     _ok(load().ep_calib_copy(_ptr(src), _ptr(dst), int(nbytes), _stream(stream)), "ep_calib_copy")
+
+
+EP_STREAM_READ, EP_STREAM_READ_NT, EP_STREAM_WRITE, EP_STREAM_WRITE_NT, EP_STREAM_COPY, EP_STREAM_COPY_NT = range(6)
+
+
+def ep_stream(kind, src, dst, nbytes, chunk_bytes, waves, stream=None):
+    """Streaming measurement kernel (read / write / copy, plain or non-temporal)."""
+    for t in (src, dst):
+        if t is not None and t.numel() * t.element_size() < (16 if t is dst and kind < 2 else nbytes):
+            raise ValueError("ep_stream: buffer smaller than the bytes streamed")
+    _ok(load().ep_stream(int(kind), _ptr(src), _ptr(dst), int(nbytes), int(chunk_bytes), int(waves),
+                         _stream(stream)), "ep_stream")
 
 
 # --------------------------------------------------------------------------- allocating forms

@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define EP_ABI_VERSION 5
+#define EP_ABI_VERSION 6
 
 /* Status codes. */
 enum ep_status {
@@ -398,14 +398,17 @@ int ep_expert_requant_mxfp8(const ep_shape *shape, const int32_t *expert_offset,
 
 /* ---- accounting (host arithmetic on host copies of the layout counts) ---- */
 
-/* [MORI] "Bandwidth Computation": RDMA algo tokens include the local node;
- * physical = algo * (N-1)/N; the exact per-source physical count drops pairs
- * whose node is own_node; NVL rows of one source = its (token, rank) pairs;
- * bytes = tokens * H * element size (2 for bf16); combine mirrors dispatch;
- * fp8 factor (1 + 4/128)/2.  hbm_* are the minimum HBM bytes of one
- * dispatch and one combine call on this shape (rows moved plus index and
- * weight metadata), given the valid pair count; hbm_*_ranks the same for
- * the (token, rank) layout, whose rows are nvl_tokens. */
+/* [MORI] "Bandwidth Computation": RDMA algo tokens are the layout's (token,
+ * node) pairs, local node included; physical = algo * (N-1)/N; the exact
+ * per-source physical count drops the pairs whose node is own_node; NVL rows
+ * of one source are its (token, rank) pairs; bytes = rows x bytes of one row
+ * (bf16: 2 per element; fp8: 1 per element + one fp32 scale per 128, whose
+ * ratio to bf16 is the pages' fp8 factor); the combine returns the same rows.
+ * hbm_* are the minimum HBM bytes of one call on this shape -- every row it
+ * moves and every index / weight element it reads or writes, once -- split
+ * into bytes read (_read_) and written (_write_), given the valid pair
+ * count; hbm_*_ranks the same for the (token, rank) layout, whose rows are
+ * nvl_tokens. */
 typedef struct ep_accounting_t {
     int64_t rdma_algo_tokens;
     double rdma_physical_tokens;
@@ -423,6 +426,11 @@ typedef struct ep_accounting_t {
     double hbm_combine_bytes;
     double hbm_dispatch_ranks_bytes;
     double hbm_combine_ranks_bytes;
+    double hbm_layout_read_bytes, hbm_layout_write_bytes;
+    double hbm_dispatch_read_bytes, hbm_dispatch_write_bytes;
+    double hbm_combine_read_bytes, hbm_combine_write_bytes;
+    double hbm_dispatch_ranks_read_bytes, hbm_dispatch_ranks_write_bytes;
+    double hbm_combine_ranks_read_bytes, hbm_combine_ranks_write_bytes;
 } ep_accounting_t;
 
 int ep_accounting(const ep_shape *shape, int32_t own_node, const int32_t *num_tokens_per_rank,
@@ -434,6 +442,28 @@ int ep_accounting(const ep_shape *shape, int32_t own_node, const int32_t *num_to
 /* Plain device copy of `bytes` bytes (16-byte aligned pointers, bytes % 16
  * == 0): a known-size reference for scaling hardware byte counters. */
 int ep_calib_copy(const void *src, void *dst, size_t bytes, void *stream);
+
+/* Streaming kernels for measurement: the box's read, write and copy
+ * ceilings, and a clean flush of the 256 MB memory-side cache (a plain
+ * read of more than it holds evicts every line, writing back the dirty
+ * ones, and leaves it clean).  `bytes` are walked in whole chunks of
+ * `chunk_bytes` (a multiple of 1024, at most 1 MiB, dividing `bytes`);
+ * wave w of `waves` (a multiple of 4, 4 <= waves <= 2^20) takes chunks w,
+ * w + waves, ...; each wave instruction moves 1 KiB of one chunk.
+ *   EP_STREAM_READ*  : reads src; dst is a 16-byte aligned sink of 16 bytes,
+ *                      written only if the XOR of all data read equals a
+ *                      fixed 128-bit value (it keeps the loads alive)
+ *   EP_STREAM_WRITE* : writes a fixed pattern to dst; src must be NULL
+ *   EP_STREAM_COPY*  : dst = src (buffers must not overlap)
+ * The _NT kinds use non-temporal loads / stores.  16-byte aligned pointers.
+ * Returns EP_EINVAL / EP_EALIGN on bad arguments, else the launch status. */
+enum ep_stream_kind {
+    EP_STREAM_READ = 0, EP_STREAM_READ_NT = 1,
+    EP_STREAM_WRITE = 2, EP_STREAM_WRITE_NT = 3,
+    EP_STREAM_COPY = 4, EP_STREAM_COPY_NT = 5
+};
+int ep_stream(int32_t kind, const void *src, void *dst, size_t bytes, size_t chunk_bytes,
+              int32_t waves, void *stream);
 
 #ifdef __cplusplus
 }

@@ -19,12 +19,20 @@ Parity status per function (what pins it, all in ``tests/test_oracle_*.py``):
   formats / quantization    exhaustive e4m3 / e8m0 tables against exact
                             rational arithmetic, torch's bf16 and fp8 casts
   expert stage              same format pins (it is a composition of them)
+
+Timing only: inside ``with oracle.threads(n):`` the row-level wrappers
+(dispatch rows, combines, expert stages, fp8 input quantisation) split their
+rows over n threads -- each thread calls the same C function on a block of
+tokens (or of experts), whose rows no other block touches -- so the bytes are
+those of one thread (a test checks it).  Correctness tests run with one.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 import subprocess
+from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 
@@ -108,6 +116,35 @@ def _load():
         fn.argtypes = args
     _lib = lib
     return lib
+
+
+_THREADS = 1
+_POOL: ThreadPoolExecutor | None = None
+
+
+@contextlib.contextmanager
+def threads(n: int):
+    """Run the row-level wrappers on `n` threads inside the block (timing)."""
+    global _THREADS, _POOL
+    old = _THREADS
+    _THREADS = max(1, int(n))
+    if _THREADS > 1 and (_POOL is None or _POOL._max_workers < _THREADS):
+        _POOL = ThreadPoolExecutor(max_workers=_THREADS)
+    try:
+        yield
+    finally:
+        _THREADS = old
+
+
+def _split(n: int, fn) -> None:
+    """fn(b0, b1) over [0, n) in _THREADS contiguous blocks (one call when
+    single-threaded).  ctypes releases the GIL during each C call."""
+    nb = min(_THREADS, n)
+    if nb <= 1:
+        fn(0, n)
+        return
+    bounds = [n * i // nb for i in range(nb + 1)]
+    list(_POOL.map(lambda i: fn(bounds[i], bounds[i + 1]), range(nb)))
 
 
 def _p(a: np.ndarray | None):
@@ -272,7 +309,7 @@ def combine_ranks(partial: np.ndarray, token_rank_slot: np.ndarray) -> np.ndarra
     T, R = ts.shape
     H = pt.shape[1]
     y = np.empty((T, H), np.uint16)
-    lib.oracle_combine_ranks(T, R, H, _p(pt), _p(ts), _p(y))
+    _split(T, lambda t0, t1: lib.oracle_combine_ranks(t1 - t0, R, H, _p(pt), _p(ts[t0:t1]), _p(y[t0:t1])))
     return y
 
 
@@ -284,7 +321,8 @@ def dispatch_rows(src: np.ndarray, token_slot: np.ndarray, fill=0, rows=None) ->
     T, k = ts.shape
     recv = np.full(((T * k) if rows is None else rows,) + src.shape[1:], fill, dtype=src.dtype)
     row_bytes = src.dtype.itemsize * int(np.prod(src.shape[1:], dtype=np.int64))
-    lib.oracle_dispatch_rows(T, k, row_bytes, _p(src), _p(ts), _p(recv))
+    _split(T, lambda t0, t1: lib.oracle_dispatch_rows(t1 - t0, k, row_bytes, _p(src[t0:t1]), _p(ts[t0:t1]),
+                                                       _p(recv)))
     return recv
 
 
@@ -298,7 +336,8 @@ def combine_bf16(expert_out: np.ndarray, token_slot: np.ndarray, topk_w: np.ndar
     T, k = ts.shape
     H = eo.shape[1]
     y = np.empty((T, H), np.uint16)
-    lib.oracle_combine_bf16(T, k, H, _p(eo), _p(ts), _p(w), _p(y))
+    _split(T, lambda t0, t1: lib.oracle_combine_bf16(t1 - t0, k, H, _p(eo), _p(ts[t0:t1]), _p(w[t0:t1]),
+                                                      _p(y[t0:t1])))
     return y
 
 
@@ -312,7 +351,8 @@ def combine_mxfp8(expert_q: np.ndarray, expert_e8m0: np.ndarray, token_slot: np.
     T, k = ts.shape
     H = q.shape[1]
     y = np.empty((T, H), np.uint16)
-    lib.oracle_combine_mxfp8(T, k, H, _p(q), _p(sc), _p(ts), _p(w), _p(y))
+    _split(T, lambda t0, t1: lib.oracle_combine_mxfp8(t1 - t0, k, H, _p(q), _p(sc), _p(ts[t0:t1]), _p(w[t0:t1]),
+                                                       _p(y[t0:t1])))
     return y
 
 
@@ -366,7 +406,7 @@ def quant_fp8_s128(x_bf16: np.ndarray):
     rows, H = x.shape
     q = np.empty((rows, H), np.uint8)
     s = np.empty((rows, H // 128), np.float32)
-    lib.oracle_quant_fp8_s128(rows, H, _p(x), _p(q), _p(s))
+    _split(rows, lambda r0, r1: lib.oracle_quant_fp8_s128(r1 - r0, H, _p(x[r0:r1]), _p(q[r0:r1]), _p(s[r0:r1])))
     return q, s
 
 
@@ -411,7 +451,8 @@ def combine_nvfp4(expert_q, expert_scales, token_slot, topk_w) -> np.ndarray:
     T, k = ts.shape
     H = q.shape[1] * 2
     y = np.empty((T, H), np.uint16)
-    lib.oracle_combine_nvfp4(T, k, H, _p(q), _p(sc), _p(ts), _p(w), _p(y))
+    _split(T, lambda t0, t1: lib.oracle_combine_nvfp4(t1 - t0, k, H, _p(q), _p(sc), _p(ts[t0:t1]), _p(w[t0:t1]),
+                                                       _p(y[t0:t1])))
     return y
 
 
@@ -424,7 +465,9 @@ def expert_requant_nvfp4(recv: np.ndarray, expert_offset: np.ndarray, factor=Non
     rows, H = r.shape
     out_q = np.zeros((rows, H // 2), np.uint8)
     out_s = np.zeros((rows, H // 16), np.uint16)
-    lib.oracle_expert_requant_nvfp4(E, H, _p(off), _p(f), _p(r), _p(out_q), _p(out_s))
+    _split(E, lambda e0, e1: lib.oracle_expert_requant_nvfp4(e1 - e0, H, _p(off[e0:]),
+                                                              None if f is None else _p(f[e0:]), _p(r),
+                                                              _p(out_q), _p(out_s)))
     return out_q, out_s
 
 
@@ -436,7 +479,7 @@ def expert_scale_bf16(recv: np.ndarray, expert_offset: np.ndarray, factor: np.nd
     E = off.shape[0] - 1
     H = r.shape[1]
     out = r.copy()
-    lib.oracle_expert_scale_bf16(E, H, _p(off), _p(f), _p(r), _p(out))
+    _split(E, lambda e0, e1: lib.oracle_expert_scale_bf16(e1 - e0, H, _p(off[e0:]), _p(f[e0:]), _p(r), _p(out)))
     return out
 
 
@@ -451,7 +494,9 @@ def expert_requant_mxfp8(recv_q: np.ndarray, recv_scales: np.ndarray, expert_off
     rows, H = q.shape
     out_q = np.zeros((rows, H), np.uint8)
     out_e = np.zeros((rows, H // 32), np.uint8)
-    lib.oracle_expert_requant_mxfp8(E, H, _p(off), _p(f), _p(q), _p(sc), _p(out_q), _p(out_e))
+    _split(E, lambda e0, e1: lib.oracle_expert_requant_mxfp8(e1 - e0, H, _p(off[e0:]),
+                                                              None if f is None else _p(f[e0:]), _p(q), _p(sc),
+                                                              _p(out_q), _p(out_e)))
     return out_q, out_e
 
 

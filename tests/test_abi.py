@@ -35,7 +35,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_strerror(lib):
-    assert lib.ep_abi_version() == 5
+    assert lib.ep_abi_version() == 6
     for rc in (0, -1, -2, -3, -4, -5):
         assert ep.strerror(rc)
     assert "unknown" in ep.strerror(-99)
