@@ -7,6 +7,8 @@
 
 #include <hip/hip_runtime.h>
 
+#include <mutex>
+
 #ifndef EP_PLAN_WAVES
 #define EP_PLAN_WAVES 16   // waves (64 pairs each) per plan tile, at most
 #endif
@@ -586,3 +588,64 @@ int ep_stream(int32_t kind, const void *src, void *dst, size_t bytes, size_t chu
 }
 
 }  // extern "C"
+
+// ---- allocation-free layout + dispatch ---------------------------------
+
+namespace {
+
+constexpr size_t kStaticScratchBytes = size_t(16) << 20;   // EP_STATIC_SCRATCH_BYTES in ep.h
+static_assert(kStaticScratchBytes == EP_STATIC_SCRATCH_BYTES, "scratch size and header disagree");
+constexpr int kMaxDevices = 64;
+
+// The workspace of ep_dispatch_with_layout_static: one copy per GPU, held
+// until the process ends.  In host code `scratch` names a host-side stand-in,
+// not the device array: kernels get the address from hipGetSymbolAddress.
+static __device__ __align__(256) uint8_t scratch[kStaticScratchBytes];
+
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current device's scratch; looked up (and its error
+// word cleared by a fill kernel on `st`) at the first call on that device.
+int static_scratch(void **out, hipStream_t st) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return EP_EHIP;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return EP_EHIP;
+        if ((reinterpret_cast<uintptr_t>(p) & 255u) != 0) return EP_EHIP;
+        if (ep::launch_ws_init(static_cast<uint32_t *>(p), ep::kCtrlWords, st) != hipSuccess) return EP_EHIP;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return EP_OK;
+}
+
+}  // namespace
+
+extern "C" int ep_dispatch_with_layout_static(const ep_shape *shape, const void *x, const float *x_scales,
+                                              const int64_t *topk_idx, const float *topk_w,
+                                              int32_t *num_tokens_per_rank, int32_t *num_tokens_per_expert,
+                                              uint8_t *is_token_in_rank, int32_t *num_tokens_per_node,
+                                              int64_t *rdma_algo_token_count, void *recv_x, float *recv_x_scales,
+                                              int32_t *recv_src_idx, float *recv_topk_w, int32_t *token_slot,
+                                              int32_t *expert_offset, void *stream) {
+    Shape s;
+    int rc = check_dispatch_inputs(shape, &s, x, x_scales, topk_idx, topk_w, recv_x, recv_x_scales,
+                                   recv_src_idx, recv_topk_w, token_slot, expert_offset);
+    if (rc != EP_OK) return rc;
+    rc = check_layout_outputs(s, num_tokens_per_rank, num_tokens_per_expert, is_token_in_rank,
+                              num_tokens_per_node, rdma_algo_token_count);
+    if (rc != EP_OK) return rc;
+    const WsLayout L = ep::ws_layout(s);
+    if (L.total > kStaticScratchBytes) return EP_EWORKSPACE;   // before any device work
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    void *w = nullptr;
+    rc = static_scratch(&w, st);
+    if (rc != EP_OK) return rc;
+    return dispatch_with_layout_impl(s, L, x, x_scales, topk_idx, topk_w, num_tokens_per_rank,
+                                     num_tokens_per_expert, is_token_in_rank, num_tokens_per_node,
+                                     rdma_algo_token_count, recv_x, recv_x_scales, recv_src_idx, recv_topk_w,
+                                     token_slot, expert_offset, static_cast<char *>(w), st);
+}

@@ -23,6 +23,7 @@ LIB_PATH = os.path.join(_PKG, "libep_hip.so")
 
 EP_FMT_BF16, EP_FMT_FP8_S128, EP_FMT_MXFP8, EP_FMT_NVFP4 = 0, 1, 2, 3
 EP_OK, EP_EINVAL, EP_EALIGN, EP_EWORKSPACE, EP_EHIP, EP_EDEVICE = 0, -1, -2, -3, -4, -5
+EP_STATIC_SCRATCH_BYTES = 16 << 20   # the static scratch of ep_dispatch_with_layout_static
 
 # every symbol include/ep.h declares
 EXPORTED = (
@@ -31,7 +32,7 @@ EXPORTED = (
     "ep_dispatch_ranks_cached", "ep_dispatch_ranks_with_layout", "ep_combine", "ep_check",
     "ep_dispatch_ranks", "ep_expert_reduce_ranks", "ep_combine_ranks", "ep_quant_fp8_s128",
     "ep_expert_scale_bf16", "ep_expert_requant_mxfp8", "ep_expert_requant_nvfp4", "ep_accounting",
-    "ep_calib_copy", "ep_stream",
+    "ep_calib_copy", "ep_stream", "ep_dispatch_with_layout_static",
 )
 
 
@@ -126,6 +127,7 @@ def load():
         "ep_accounting": (ctypes.c_int, [SP, i32, P, P, i64, i64, ctypes.POINTER(ep_accounting_t)]),
         "ep_calib_copy": (ctypes.c_int, [P, P, sz, P]),
         "ep_stream": (ctypes.c_int, [i32, P, P, sz, sz, i32, P]),
+        "ep_dispatch_with_layout_static": (ctypes.c_int, [SP] + [P] * 15 + [P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -300,6 +302,21 @@ def ep_dispatch_with_layout(shape, x, x_scales, topk_idx, topk_w, num_tokens_per
                                        _ptr(expert_offset), ws.ptr, ws.nbytes, _stream(stream)),
         "ep_dispatch_with_layout")
 
+
+def ep_dispatch_with_layout_static(shape, x, x_scales, topk_idx, topk_w, num_tokens_per_rank,
+                                   num_tokens_per_expert, is_token_in_rank, num_tokens_per_node,
+                                   rdma_algo_token_count, recv_x, recv_x_scales, recv_src_idx, recv_topk_w,
+                                   token_slot, expert_offset, stream=None):
+    """ep_dispatch_with_layout without a workspace: the library's static
+    per-GPU scratch holds the plan (no device allocation anywhere)."""
+    _check_with_layout(shape, x, x_scales, topk_idx, topk_w, num_tokens_per_rank, num_tokens_per_expert,
+                       is_token_in_rank, num_tokens_per_node, rdma_algo_token_count, recv_x, recv_x_scales,
+                       recv_src_idx, recv_topk_w, token_slot, expert_offset)
+    _ok(load().ep_dispatch_with_layout_static(
+        ctypes.byref(shape), _ptr(x), _ptr(x_scales), _ptr(topk_idx), _ptr(topk_w), _ptr(num_tokens_per_rank),
+        _ptr(num_tokens_per_expert), _ptr(is_token_in_rank), _ptr(num_tokens_per_node),
+        _ptr(rdma_algo_token_count), _ptr(recv_x), _ptr(recv_x_scales), _ptr(recv_src_idx), _ptr(recv_topk_w),
+        _ptr(token_slot), _ptr(expert_offset), _stream(stream)), "ep_dispatch_with_layout_static")
 
 
 def ep_dispatch_cached(shape, x, x_scales, token_slot, recv_x, recv_x_scales=None, stream=None):

@@ -212,6 +212,35 @@ int ep_dispatch_with_layout(const ep_shape *shape, const void *x, const float *x
                             void *stream);
 
 /*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * arguments and results as ep_dispatch_with_layout, minus the workspace.
+ * The plan lives in a static device array of EP_STATIC_SCRATCH_BYTES per
+ * GPU, part of the library's code object (each GPU the library runs on holds
+ * its copy until the process ends); nothing is allocated and nothing
+ * allocating is called.
+ *   - Shapes whose workspace (ep_workspace_bytes) exceeds
+ *     EP_STATIC_SCRATCH_BYTES return EP_EWORKSPACE before any device work
+ *     (about 4 M (token, slot) pairs at E = 256).
+ *   - The first call on a device (the current device) looks the array up and
+ *     clears its error word with a fill kernel on `stream`; make that first
+ *     call outside stream capture.
+ *   - Every call on one GPU shares that GPU's array, which keeps the last
+ *     call's plan: calls that overlap on one GPU (other streams, other host
+ *     threads) race and must be ordered by the caller.
+ *   - Invalid expert ids are treated as masked, as everywhere; their error
+ *     flag stays in the array and is not reported (use ep_check with a
+ *     workspace call to see it).
+ */
+#define EP_STATIC_SCRATCH_BYTES ((size_t)16 << 20)
+int ep_dispatch_with_layout_static(const ep_shape *shape, const void *x, const float *x_scales,
+                                   const int64_t *topk_idx, const float *topk_w, int32_t *num_tokens_per_rank,
+                                   int32_t *num_tokens_per_expert, uint8_t *is_token_in_rank,
+                                   int32_t *num_tokens_per_node, int64_t *rdma_algo_token_count, void *recv_x,
+                                   float *recv_x_scales, int32_t *recv_src_idx, float *recv_topk_w,
+                                   int32_t *token_slot, int32_t *expert_offset, void *stream);
+
+/*
  * Dispatch that reuses the plan the preceding ep_dispatch_layout call on the
  * SAME workspace and the SAME topk_idx left there (stream-ordered before
  * this call): same arguments and results as ep_dispatch, minus the planning
