@@ -2,26 +2,27 @@
 """Throughput of the MoE dispatch/combine hot path on one MI355X.
 
 One step = the whole path over one batch of synthetic input already resident
-in HBM: ep_dispatch_layout (layout counts and the dispatch plan) ->
-ep_dispatch_from_layout (the row permutation) -> (expert stage of the
-workload, if any) -> ep_combine, all on one stream.  W untimed warmup steps,
-then K timed steps bracketed by stream synchronisation and HIP events, three
-ways: replayed from HIP graphs of 10 captured steps (the reported
-ms_per_step), eager back to back (eager_ms_per_step), and eager with events
-between the calls (the per-call durations in phase_us: median over steps).
-The workloads' expert stage (identity, per-expert scaling, or fp8 -> mxfp8
-re-encoding) runs during warmup and is not part of the timed step.  A batch
-of at most 2048 (token, slot) pairs is laid out and dispatched by one
-ep_dispatch_with_layout (ep_dispatch_ranks_with_layout) call, which the
-library runs as a single launch (phases "layout+dispatch", "combine").  With
---layout ranks the step is the (token, rank) path: ep_dispatch_layout
-(planning one row per token per rank it reaches) -> ep_dispatch_ranks ->
-ep_combine_ranks, with ep_expert_reduce_ranks (the weighted per-rank
-partials) as the expert stage.
+in HBM, all on one stream: layout -> dispatch -> (the workload's expert
+stage, if any) -> combine.  Token-major rows: one ep_dispatch_with_layout
+call (layout counts, plan and row permutation; a single launch up to 2048
+(token, slot) pairs, else a count launch and the copy that scans the
+counts) -> ep_combine; phases "layout+dispatch" and "combine".
+--split-layout times ep_dispatch_layout -> ep_dispatch_from_layout (the
+layout call's plan reused) -> ep_combine instead.  --layout ranks times the
+(token, rank) path: ep_dispatch_layout (planning one row per token per rank
+it reaches) -> ep_dispatch_ranks -> ep_combine_ranks, with
+ep_expert_reduce_ranks (the weighted per-rank partials) as the expert stage.
+The expert stage (identity, per-expert scaling, fp8 -> mxfp8 or bf16 ->
+nvfp4 re-encoding) runs during warmup and is not part of the timed step.
+W untimed warmup steps, then K timed steps bracketed by stream
+synchronisation and HIP events, three ways: replayed from HIP graphs of 10
+captured steps (the reported ms_per_step), eager back to back
+(eager_ms_per_step), and eager with events between the calls (the per-call
+durations in phase_us: median over steps).
 
 Warm and cold.  The 256 MB memory-side cache (MALL) of MI355X is a
-write-back cache: stores (plain and non-temporal alike) leave dirty lines
-there.  Back to back on the same buffers (the warm `value`), the receive
+write-back cache: plain stores leave dirty lines there, written back to HBM
+when something evicts them (non-temporal stores leave none).  Back to back on the same buffers (the warm `value`), the receive
 rows and x that one step leaves in it are read by the combine from it and
 rewritten by the next step's dispatch before they ever reach HBM, so the
 warm figure counts up to ~256 MB of "HBM" writes per step that HBM never
@@ -180,6 +181,9 @@ def parse():
                          "pair count); or one row per (token, rank) with per-rank partials "
                          "(ep_dispatch_ranks / ep_combine_ranks)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--split-layout", action="store_true",
+                    help="token-major rows: time ep_dispatch_layout + ep_dispatch_from_layout (the plan reused) "
+                         "instead of one ep_dispatch_with_layout call")
     ap.add_argument("--no-cold", action="store_true",
                     help="skip the cold-cache step and per-call timings (graphs with a 512 MiB read flush "
                          "before each step)")
@@ -228,7 +232,8 @@ def main():
     if args.sweep:
         series = []
         for T in [2 ** i for i in range(14)]:
-            o = measure(args.workload, args.steps, args.warmup, not args.no_graph, args.layout, T=T)
+            o = measure(args.workload, args.steps, args.warmup, not args.no_graph, args.layout,
+                        split_layout=args.split_layout, T=T)
             o.pop("_inp")
             series.append({"tokens": T, "us_per_step": round(o["ms_per_step"] * 1000, 2),
                            "tokens_per_s": o["tokens_per_s"], "gbs": o["value"], "phase_us": o["phase_us"]})
@@ -237,7 +242,8 @@ def main():
                           "unit": "us", "series": series}), flush=True)
         return
     out = measure(args.workload, args.steps, args.warmup, not args.no_graph, args.layout,
-                  cold=not args.no_cold and not args.no_graph, ceilings=not args.no_ceilings)
+                  cold=not args.no_cold and not args.no_graph, ceilings=not args.no_ceilings,
+                  split_layout=args.split_layout)
     inp = out.pop("_inp")
     if not args.no_cpu_baseline:
         cfg = dict(inp, rank_rows=args.layout == "ranks", rank_capacity=out["config"]["rank_capacity"])
@@ -246,7 +252,7 @@ def main():
 
 
 def measure(workload: str, steps: int, warmup: int, graph: bool = False, layout_kind: str = "pairs",
-            cold: bool = False, ceilings: bool = False, **overrides) -> dict:
+            cold: bool = False, ceilings: bool = False, split_layout: bool = False, **overrides) -> dict:
     """Time `steps` steps of the path on `workload` (inputs resident in HBM);
     keyword overrides change the workload's shape (e.g. T=...).  layout_kind
     "ranks" times the (token, rank) path: layout, ep_dispatch_ranks,
@@ -362,8 +368,11 @@ def measure(workload: str, steps: int, warmup: int, graph: bool = False, layout_
     # and combine: it runs in warmup (its output does not change from step to
     # step, the inputs being the same) and stays out of the timed step
     phases = [("layout", layout), ("dispatch", dispatch), ("combine", combine)]
-    single_launch = M == 0 and T * k <= SINGLE_LAUNCH_PAIRS
-    if single_launch:   # the library runs layout + dispatch of such a batch as one kernel
+    # token-major rows: one ep_dispatch_with_layout call (a single launch up to
+    # 2048 pairs, else the count launch and the copy that scans the counts);
+    # split_layout times ep_dispatch_layout + ep_dispatch_from_layout instead
+    single_launch = M == 0 and (T * k <= SINGLE_LAUNCH_PAIRS or (not ranks and not split_layout))
+    if single_launch:
         phases = [("layout+dispatch", layout_dispatch), ("combine", combine)]
 
     def step():

@@ -87,6 +87,11 @@ struct CopyArgs {
     int32_t *per_rank, *per_expert, *per_node;
     uint8_t *in_rank;
     int64_t *algo;
+    // copy that rebuilds the plan (layout + dispatch in two launches): the
+    // raw tile counts (in tile_prefix) and, per expert e and tile u, {pairs
+    // of u with an expert below e, pairs of u with e} ([E][ntiles])
+    const int2 *tile_pairs;
+    int ntiles;
 };
 
 constexpr int kFusedPairs = 2048;   // pairs a single-launch batch may hold (32 ids per lane)
@@ -134,6 +139,86 @@ __device__ __forceinline__ int32_t counted_slot(const CopyArgs &a, int64_t t, in
     return lane < a.k ? slot_sm[lane] : -1;
 }
 
+// Sum over the 64 lanes (every lane active), returned wave-uniform: an
+// inclusive scan inside each 16-lane row by DPP row shifts, the rows' totals
+// carried on by row broadcasts, lane 63's value read back.
+__device__ __forceinline__ int32_t wave_sum(int32_t v) {
+    v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, false);   // row_shr:1
+    v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, false);   // row_shr:2
+    v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, false);   // row_shr:4
+    v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, false);   // row_shr:8
+    v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);   // row_bcast:15 into rows 1, 3
+    v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);   // row_bcast:31 into rows 2, 3
+    return __builtin_amdgcn_readlane(v, kWave - 1);
+}
+
+// Layout totals of a multi-tile batch from the tile counts, by one block of
+// the copy launch while the others copy: per column (experts, ranks, nodes)
+// the sum over tiles -> the layout outputs (when wanted), and the exclusive
+// scan of the expert totals -> the handle's segment starts.  Integer sums
+// only, so the results are those of the scan launch they replace.
+__device__ void plan_totals_block(const CopyArgs &a) {
+    extern __shared__ int32_t tot_sm[];   // [cols + 1 + waves + 1]
+    const int tid = threadIdx.x, nt = blockDim.x;
+    for (int c = tid; c < a.cols; c += nt) {
+        int32_t sum = 0;
+        for (int t0 = 0; t0 < a.ntiles; t0 += 8) {   // 8 loads in flight (clamped index)
+            int32_t v[8];
+#pragma unroll
+            for (int q = 0; q < 8; ++q) v[q] = a.tile_prefix[(size_t)min(t0 + q, a.ntiles - 1) * a.cols + c];
+#pragma unroll
+            for (int q = 0; q < 8; ++q) sum += (t0 + q < a.ntiles) ? v[q] : 0;
+        }
+        tot_sm[c] = sum;
+        if (c < a.E) {
+            if (a.per_expert) a.per_expert[c] = sum;
+        } else if (c < a.E + a.R) {
+            if (a.per_rank) a.per_rank[c - a.E] = sum;
+        } else if (a.per_node) {
+            a.per_node[c - a.E - a.R] = sum;
+        }
+    }
+    __syncthreads();
+    if (a.algo && tid == 0) {
+        int64_t al = 0;
+        for (int n = 0; n < a.N; ++n) al += tot_sm[a.E + a.R + n];
+        *a.algo = al;
+    }
+    block_exclusive_scan(tot_sm, a.expert_offset, a.E, tot_sm + a.cols + 1);
+}
+
+// Segment start of each of the token's valid slots plus the pairs of the same
+// expert in earlier tiles, rebuilt from the tile counts: for slot j with
+// expert e, the sum over tiles u of the pairs of u with smaller experts, plus,
+// for u before the token's tile, the pairs of u with e.  One tile per lane
+// (one 8-byte load of e's contiguous per-tile pairs) and one wave sum per
+// slot, eight slots at a time; lane j < k returns slot j's value.  em: lane
+// j's expert, -1 when masked.
+__device__ __forceinline__ int32_t slot_bases(const CopyArgs &a, int em, int tile, int lane) {
+    int32_t base = 0;
+    for (int j0 = 0; j0 < a.k; j0 += 8) {
+        int32_t v[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            const int e = readlane(em, j0 + q);   // lanes >= k hold -1 (j0 + q < 64)
+            const int es = e < 0 ? 0 : e;
+            int32_t acc = 0;
+            for (int u0 = 0; u0 < a.ntiles; u0 += kWave) {   // one pass up to 64 tiles
+                const int u = u0 + lane;
+                const int2 p = a.tile_pairs[(size_t)es * a.ntiles + min(u, a.ntiles - 1)];   // clamped
+                acc += (u < a.ntiles) ? p.x + (u < tile ? p.y : 0) : 0;
+            }
+            v[q] = e < 0 ? 0 : acc;
+        }
+#pragma unroll
+        for (int q = 0; q < 8; ++q) v[q] = wave_sum(v[q]);
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+            if (lane == j0 + q) base = v[q];
+    }
+    return base;
+}
+
 // Row t's vectors of this wave into the token's valid slots, VPL vectors per
 // lane per pass (the first pass is already in buf); NT: non-temporal stores.
 template <int VPL, bool NT>
@@ -169,9 +254,17 @@ __device__ __forceinline__ void store_rows(const CopyArgs &a, const char *src, i
 // The single-launch form runs one token per block (S waves of 64).  NT:
 // non-temporal row stores (a compile-time choice: a run-time test between
 // the two store kinds is merged by the compiler into plain stores).
-template <int VPL, int KEYS, bool NT>
+// SCAN: the copy of layout + dispatch in two launches -- block 0 writes the
+// layout totals and the handle's segment starts (plan_totals_block), and
+// every wave rebuilds its slots' segment starts from the tile counts
+// (slot_bases) instead of reading a scanned plan.
+template <int VPL, int KEYS, bool NT, bool SCAN = false>
 __global__ __launch_bounds__(KEYS ? 1024 : 256) void ep_dispatch_copy_kernel(CopyArgs a) {
     constexpr bool FUSED = KEYS > 0;
+    if (SCAN && blockIdx.x == 0) {
+        plan_totals_block(a);
+        return;
+    }
     if (FUSED && blockIdx.x == 0) {
         SmallLayout L{};
         L.topk_idx = a.topk_idx;
@@ -201,12 +294,12 @@ __global__ __launch_bounds__(KEYS ? 1024 : 256) void ep_dispatch_copy_kernel(Cop
         t = (int64_t)blockIdx.x - 1;   // < T: the grid has 1 + T blocks
         sub = threadIdx.x / kWave;
     } else {
-        const int64_t gw = (int64_t)blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
+        const int64_t gw = ((int64_t)blockIdx.x - (SCAN ? 1 : 0)) * (blockDim.x / kWave) + threadIdx.x / kWave;
         const int64_t pos = gw / a.S;
         sub = (int)(gw - pos * a.S);
         t = (EP_DISPATCH_ORDER && pos < a.T) ? interleaved_token(pos, a.T, a.plain_tokens) : pos;
         const int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-        if (!a.slots_in && g <= a.E) a.expert_offset[g] = a.plan_offset[g];   // handle copy of the segment starts
+        if (!SCAN && !a.slots_in && g <= a.E) a.expert_offset[g] = a.plan_offset[g];   // handle copy of the segment starts
     }
     if (t >= a.T) return;   // wave-uniform (never taken in the single-launch form)
 
@@ -251,6 +344,7 @@ __global__ __launch_bounds__(KEYS ? 1024 : 256) void ep_dispatch_copy_kernel(Cop
 
     // lanes 0..k-1: the token's slots
     int32_t slot = FUSED ? counted_slot<(KEYS > 0 ? KEYS : 1)>(a, t, lane, sub) : -1;
+    const int32_t base = SCAN ? slot_bases(a, (lane < a.k && lr >= 0) ? (int)eid : -1, (int)(t / a.TT), lane) : 0;
     if (lane < a.k) {
         const int64_t p = t * a.k + lane;
         if (!FUSED && a.slots_in) {   // cached: the slots of a previous dispatch's handle
@@ -259,7 +353,7 @@ __global__ __launch_bounds__(KEYS ? 1024 : 256) void ep_dispatch_copy_kernel(Cop
         }
         if (lr >= 0) {   // a valid pair (the plan's local rank is -1 for masked ones)
             const int e = (int)eid;
-            slot = a.plan_offset[e] + a.tile_prefix[(t / a.TT) * a.cols + e] + lr;
+            slot = SCAN ? base + lr : a.plan_offset[e] + a.tile_prefix[(t / a.TT) * a.cols + e] + lr;
             if (a.M > 0) {   // RANK_MAJOR: the same place inside the rank, at the rank's fixed block
                 const int r = a.epr_shift >= 0 ? e >> a.epr_shift : e / a.epr;
                 const int32_t in_rank = slot - a.plan_offset[r * a.epr];
@@ -373,37 +467,37 @@ CopyArgs copy_args(const Shape &s, const void *x, const float *x_scales, const i
     return a;
 }
 
-template <int KEYS, bool NT>
+template <int KEYS, bool NT, bool SCAN>
 void launch_copy_nt(const CopyArgs &a, const dim3 &grid, const dim3 &block, size_t lds, hipStream_t stream) {
     const int per_lane = (a.nvec + kWave * a.S - 1) / (kWave * a.S);
     if constexpr (KEYS == 0) {
         // hidden 7168 at one wave per token: exactly 14 (bf16) or 7 (e4m3)
         // vectors per lane, so no lane loads a vector past the row
         if (a.nvec == 14 * kWave * a.S) {
-            hipLaunchKernelGGL((ep_dispatch_copy_kernel<14, KEYS, NT>), grid, block, lds, stream, a);
+            hipLaunchKernelGGL((ep_dispatch_copy_kernel<14, KEYS, NT, SCAN>), grid, block, lds, stream, a);
             return;
         }
         if (a.nvec == 7 * kWave * a.S) {
-            hipLaunchKernelGGL((ep_dispatch_copy_kernel<7, KEYS, NT>), grid, block, lds, stream, a);
+            hipLaunchKernelGGL((ep_dispatch_copy_kernel<7, KEYS, NT, SCAN>), grid, block, lds, stream, a);
             return;
         }
     }
     if (per_lane <= 2) {
-        hipLaunchKernelGGL((ep_dispatch_copy_kernel<2, KEYS, NT>), grid, block, lds, stream, a);
+        hipLaunchKernelGGL((ep_dispatch_copy_kernel<2, KEYS, NT, SCAN>), grid, block, lds, stream, a);
     } else if (per_lane <= 4) {
-        hipLaunchKernelGGL((ep_dispatch_copy_kernel<4, KEYS, NT>), grid, block, lds, stream, a);
+        hipLaunchKernelGGL((ep_dispatch_copy_kernel<4, KEYS, NT, SCAN>), grid, block, lds, stream, a);
     } else if (per_lane <= 8 || KEYS) {   // the single-launch form has at most 8 (fused_dispatch_fits)
-        hipLaunchKernelGGL((ep_dispatch_copy_kernel<8, KEYS, NT>), grid, block, lds, stream, a);
+        hipLaunchKernelGGL((ep_dispatch_copy_kernel<8, KEYS, NT, SCAN>), grid, block, lds, stream, a);
     } else {
-        hipLaunchKernelGGL((ep_dispatch_copy_kernel<16, KEYS, NT>), grid, block, lds, stream, a);
+        hipLaunchKernelGGL((ep_dispatch_copy_kernel<16, KEYS, NT, SCAN>), grid, block, lds, stream, a);
     }
 }
 
-template <int KEYS>
+template <int KEYS, bool SCAN = false>
 void launch_copy(const CopyArgs &a, int64_t blocks, int threads, size_t lds, hipStream_t stream) {
     const dim3 grid((unsigned)blocks), block(threads);
-    if (a.nt_store) launch_copy_nt<KEYS, true>(a, grid, block, lds, stream);
-    else launch_copy_nt<KEYS, false>(a, grid, block, lds, stream);
+    if (a.nt_store) launch_copy_nt<KEYS, true, SCAN>(a, grid, block, lds, stream);
+    else launch_copy_nt<KEYS, false, SCAN>(a, grid, block, lds, stream);
 }
 
 }  // namespace
@@ -423,6 +517,35 @@ hipError_t launch_dispatch_copy(const Shape &s, const WsLayout &L, const void *x
     int64_t blocks = (s.T * a.S + 3) / 4;
     if (blocks * 256 < s.E + 1) blocks = (s.E + 1 + 255) / 256;   // threads to copy expert_offset
     launch_copy<0>(a, blocks, 256, 0, stream);
+    return hipGetLastError();
+}
+
+bool scan_in_copy_fits(const Shape &s, const WsLayout &L) {
+    return s.T > 0 && s.M == 0 && !s.rank_rows && L.tiles > 1 && L.tiles <= kScanCopyMaxTiles;
+}
+
+hipError_t launch_dispatch_scan_copy(const Shape &s, const WsLayout &L, const void *x,
+                                     const float *x_scales, const int64_t *topk_idx,
+                                     const float *topk_w, void *recv_x, float *recv_x_scales,
+                                     int32_t *recv_src_idx, float *recv_topk_w, int32_t *token_slot,
+                                     int32_t *expert_offset, int32_t *per_rank, int32_t *per_expert,
+                                     int32_t *per_node, int64_t *algo, char *ws, hipStream_t stream) {
+    CopyArgs a = copy_args(s, x, x_scales, topk_idx, topk_w, recv_x, recv_x_scales, recv_src_idx,
+                           recv_topk_w, token_slot, expert_offset);
+    a.tile_prefix = reinterpret_cast<const int32_t *>(ws + L.tile_count);   // raw tile counts
+    a.tile_pairs = reinterpret_cast<const int2 *>(ws + L.tile_pairs);
+    a.local_rank = reinterpret_cast<const int32_t *>(ws + L.local_rank);
+    a.ctrl = reinterpret_cast<uint32_t *>(ws + L.ctrl);
+    a.TT = L.tile_tokens;
+    a.ntiles = L.tiles;
+    a.per_rank = per_rank;
+    a.per_expert = per_expert;
+    a.per_node = per_node;
+    a.algo = algo;
+    // block 0: the totals; then the copy blocks (4 waves each)
+    const int64_t blocks = 1 + (s.T * a.S + 3) / 4;
+    const size_t lds = sizeof(int32_t) * ((size_t)a.cols + 1 + 256 / kWave + 1);
+    launch_copy<0, true>(a, blocks, 256, lds, stream);
     return hipGetLastError();
 }
 

@@ -101,6 +101,8 @@ WsLayout ws_layout(const Shape &s) {
     off = align256(off + (s.rank_rows ? sizeof(uint64_t) * (size_t)L.tiles * (size_t)s.R * L.tile_token_waves : 0));
     L.plan_rank_offset = off;
     off = align256(off + sizeof(int32_t) * (size_t)(s.R + 1));
+    L.tile_pairs = off;
+    off = align256(off + 2 * sizeof(int32_t) * (size_t)L.tiles * (size_t)s.E);
     L.total = off;
     return L;
 }
@@ -222,6 +224,15 @@ int dispatch_with_layout_impl(const Shape &s, const WsLayout &L, const void *x, 
                                                     recv_src_idx, recv_topk_w, token_slot, expert_offset,
                                                     per_rank, per_expert, in_rank, per_node, algo,
                                                     reinterpret_cast<uint32_t *>(w + L.ctrl), st));
+    if (ep::scan_in_copy_fits(s, L)) {   // two launches: counts, then the copy that scans them
+        hipError_t e = ep::launch_plan(s, L, topk_idx, per_rank, per_expert, in_rank, per_node, algo, w, st,
+                                       /*count_only=*/true);
+        if (e != hipSuccess) return EP_EHIP;
+        return hip_status(ep::launch_dispatch_scan_copy(s, L, x, x_scales, topk_idx, topk_w, recv_x,
+                                                        recv_x_scales, recv_src_idx, recv_topk_w, token_slot,
+                                                        expert_offset, per_rank, per_expert, per_node, algo, w,
+                                                        st));
+    }
     hipError_t e = ep::launch_plan(s, L, topk_idx, per_rank, per_expert, in_rank, per_node, algo, w, st);
     if (e != hipSuccess) return EP_EHIP;
     e = ep::launch_dispatch_copy(s, L, x, x_scales, topk_idx, topk_w, recv_x, recv_x_scales,
@@ -242,18 +253,11 @@ int ep_dispatch(const ep_shape *shape, const void *x, const float *x_scales,
     int rc = check_dispatch_args(shape, &s, x, x_scales, topk_idx, topk_w, recv_x, recv_x_scales,
                                  recv_src_idx, recv_topk_w, token_slot, expert_offset, ws, ws_bytes, &L);
     if (rc != EP_OK) return rc;
-    hipStream_t st = static_cast<hipStream_t>(stream);
-    char *w = static_cast<char *>(ws);
-    if (ep::fused_dispatch_fits(s))   // small batch: one launch, no plan in the workspace
-        return hip_status(ep::launch_dispatch_fused(s, x, x_scales, topk_idx, topk_w, recv_x, recv_x_scales,
-                                                    recv_src_idx, recv_topk_w, token_slot, expert_offset,
-                                                    nullptr, nullptr, nullptr, nullptr, nullptr,
-                                                    reinterpret_cast<uint32_t *>(w + L.ctrl), st));
-    hipError_t e = ep::launch_plan(s, L, topk_idx, nullptr, nullptr, nullptr, nullptr, nullptr, w, st);
-    if (e != hipSuccess) return EP_EHIP;
-    e = ep::launch_dispatch_copy(s, L, x, x_scales, topk_idx, topk_w, recv_x, recv_x_scales,
-                                 recv_src_idx, recv_topk_w, token_slot, expert_offset, w, st);
-    return hip_status(e);
+    // the plan itself (no layout outputs): one launch for a small batch, the
+    // count and copy launches for up to kScanCopyMaxTiles tiles, else three
+    return dispatch_with_layout_impl(s, L, x, x_scales, topk_idx, topk_w, nullptr, nullptr, nullptr, nullptr,
+                                     nullptr, recv_x, recv_x_scales, recv_src_idx, recv_topk_w, token_slot,
+                                     expert_offset, static_cast<char *>(ws), static_cast<hipStream_t>(stream));
 }
 
 int ep_dispatch_with_layout(const ep_shape *shape, const void *x, const float *x_scales,

@@ -22,10 +22,14 @@ namespace ep {
 //                                    ceil(tile_tokens / 64) waves), bit i set
 //                                    when the wave's token i reaches the rank
 //   plan_rank_offset : i32[R + 1]    (token, rank) region starts
+//   tile_pairs  : int2[E][tiles]     per expert e and tile u: {pairs of u with
+//                                    an expert below e, pairs of u with e}
+//                                    (layout + dispatch in one call,
+//                                    multi-tile batches)
 // A tile holds tile_tokens whole tokens (tile_tokens * k <= count_threads
 // pairs, one thread per pair).
 struct WsLayout {
-    size_t ctrl, tile_count, local_rank, plan_offset, rank_mask, plan_rank_offset, total;
+    size_t ctrl, tile_count, local_rank, plan_offset, rank_mask, plan_rank_offset, tile_pairs, total;
     int tiles;           // ceil(T / tile_tokens)
     int tile_tokens;
     int tile_waves;      // ceil(tile_tokens * k / 64): waves that own pair masks
@@ -54,15 +58,33 @@ WsLayout ws_layout(const Shape &s);
 hipError_t launch_ws_init(uint32_t *ws, size_t words, hipStream_t stream);
 
 // Layout counts (outputs may be null) and the dispatch plan in the workspace.
+// count_only: the count launch alone, which also writes tile_pairs (for
+// launch_dispatch_copy with scan_in_copy; multi-tile batches).
 hipError_t launch_plan(const Shape &s, const WsLayout &L, const int64_t *topk_idx,
                        int32_t *per_rank, int32_t *per_expert, uint8_t *in_rank,
-                       int32_t *per_node, int64_t *algo, char *ws, hipStream_t stream);
+                       int32_t *per_node, int64_t *algo, char *ws, hipStream_t stream,
+                       bool count_only = false);
 
 hipError_t launch_dispatch_copy(const Shape &s, const WsLayout &L, const void *x,
                                 const float *x_scales, const int64_t *topk_idx,
                                 const float *topk_w, void *recv_x, float *recv_x_scales,
                                 int32_t *recv_src_idx, float *recv_topk_w, int32_t *token_slot,
                                 int32_t *expert_offset, char *ws, hipStream_t stream);
+
+// Layout + dispatch of a multi-tile batch in two launches: the count launch
+// (launch_plan with count_only) and the copy, which rebuilds the segment
+// starts and prefixes over tiles from the tile counts (each wave for its own
+// slots) while one extra block writes the layout totals (outputs may be null)
+// and the handle's segment starts.  scan_in_copy_fits tells whether a shape
+// qualifies (compacted layout, no rank rows, 2 ... kScanCopyMaxTiles tiles).
+constexpr int kScanCopyMaxTiles = 256;
+bool scan_in_copy_fits(const Shape &s, const WsLayout &L);
+hipError_t launch_dispatch_scan_copy(const Shape &s, const WsLayout &L, const void *x,
+                                     const float *x_scales, const int64_t *topk_idx,
+                                     const float *topk_w, void *recv_x, float *recv_x_scales,
+                                     int32_t *recv_src_idx, float *recv_topk_w, int32_t *token_slot,
+                                     int32_t *expert_offset, int32_t *per_rank, int32_t *per_expert,
+                                     int32_t *per_node, int64_t *algo, char *ws, hipStream_t stream);
 
 // Cached dispatch: rows placed by a previous dispatch's handle (token_slot
 // [T][k], or token_rank_slot [T][R] for (token, rank) rows).

@@ -40,6 +40,11 @@
 //      are deterministic.
 //  A batch that fits one tile (T * k <= 1024 pairs at E <= 384) is planned by
 //  the count kernel alone: its block holds every count and scans them in LDS.
+//  For layout + dispatch in one call (count_only), the scan launch is left
+//  out: each count block also writes, per expert, its tile's count and the
+//  tile's pairs of smaller experts, and the dispatch rebuilds every segment
+//  start and prefix over tiles it needs from those (one sum over tiles per
+//  slot; dispatch.hip).
 #include "ep_device.h"
 #include "ep_internal.h"
 
@@ -65,6 +70,11 @@ struct CountArgs {
     int32_t *plan_rank_offset;   // [R + 1] (token, rank) region starts
     int32_t *per_expert, *per_rank, *per_node;   // layout outputs or null
     int64_t *algo;
+    // multi-tile batches, for a dispatch that rebuilds segment starts itself
+    // (or null): per expert e and tile u, {pairs of u whose expert is below
+    // e, pairs of u with expert e} ([E][ntiles], the tiles of one expert
+    // side by side)
+    int2 *tile_pairs;
 };
 
 __global__ __launch_bounds__(1024) void ep_plan_count_kernel(CountArgs a) {
@@ -125,10 +135,8 @@ __global__ __launch_bounds__(1024) void ep_plan_count_kernel(CountArgs a) {
             for (int q = 0; q < 4; ++q) c += (w0 + q < a.W) ? (int32_t)__popcll(m[q]) : 0;
         }
         tc[e2] = single ? 0 : c;          // single tile: no earlier tiles, prefix 0
-        if (single) {
-            cnt[e2] = c;
-            if (a.per_expert) a.per_expert[e2] = c;
-        }
+        if (single || a.tile_pairs) cnt[e2] = c;
+        if (single && a.per_expert) a.per_expert[e2] = c;
     }
 
     // ---- tokens: rank / node sets in registers, one token per thread (the
@@ -194,7 +202,14 @@ __global__ __launch_bounds__(1024) void ep_plan_count_kernel(CountArgs a) {
     // single tile: the rank columns hold the prefix over earlier tiles (0)
     // when (token, rank) rows are planned, else the counts
     for (int i = tid; i < a.R + a.N; i += nt) tc[E + i] = (single && a.rank_mask && i < a.R) ? 0 : rn[i];
-    if (!single) return;   // block-uniform
+    if (!single) {   // block-uniform
+        if (a.tile_pairs) {   // this tile's counts, prefixed over the experts (in place)
+            block_exclusive_scan(cnt, cnt, E, reinterpret_cast<int32_t *>(cnt + E + 1));
+            for (int e2 = tid; e2 < E; e2 += nt)
+                a.tile_pairs[(size_t)e2 * gridDim.x + blockIdx.x] = make_int2(cnt[e2], cnt[e2 + 1] - cnt[e2]);
+        }
+        return;
+    }
 
     // ---- single-tile batch: segment starts and layout outputs right here
     block_exclusive_scan(cnt, a.plan_offset, E, reinterpret_cast<int32_t *>(cnt + E));
@@ -345,7 +360,7 @@ __global__ __launch_bounds__(1024) void ep_plan_scan_kernel(ScanArgs a) {
 
 hipError_t launch_plan(const Shape &s, const WsLayout &L, const int64_t *topk_idx,
                        int32_t *per_rank, int32_t *per_expert, uint8_t *in_rank,
-                       int32_t *per_node, int64_t *algo, char *ws, hipStream_t stream) {
+                       int32_t *per_node, int64_t *algo, char *ws, hipStream_t stream, bool count_only) {
     CountArgs c{};
     c.topk_idx = topk_idx;
     c.T = s.T;
@@ -371,14 +386,15 @@ hipError_t launch_plan(const Shape &s, const WsLayout &L, const int64_t *topk_id
     c.per_rank = per_rank;
     c.per_node = per_node;
     c.algo = algo;
+    c.tile_pairs = count_only ? reinterpret_cast<int2 *>(ws + L.tile_pairs) : nullptr;
     if (s.T > 0) {
         // masks, staged ids, rank/node counts, and (single tile) expert counts + scan scratch
         const size_t lds = sizeof(uint64_t) * (size_t)L.tile_waves * s.E +
                            sizeof(int32_t) * ((size_t)L.tile_tokens * s.k + s.R + s.N + s.E + 1 +
-                                              1024 / kWave + 1);
+                                              1024 / kWave + 2);
         hipLaunchKernelGGL(ep_plan_count_kernel, dim3(L.tiles), dim3(L.count_threads), lds, stream, c);
         const hipError_t e = hipGetLastError();
-        if (e != hipSuccess || L.tiles == 1) return e;   // one tile: the plan is complete
+        if (e != hipSuccess || L.tiles == 1 || count_only) return e;   // one tile: the plan is complete
     }
     ScanArgs a{};
     a.E = s.E;

@@ -12,9 +12,10 @@
 //   write: a fixed pattern.
 //   copy : dst = src.
 // Plain (write-back) or non-temporal loads / stores.  Measured on MI355X:
-// both kinds of store allocate in the memory-side cache and leave dirty
-// lines there; a plain read of 512 MiB evicts everything it held (writing
-// back what was dirty) and leaves it clean.
+// plain stores leave dirty lines in the memory-side cache, written back to
+// HBM when something evicts them; non-temporal stores leave none; a plain
+// read of 512 MiB evicts everything the cache held (writing back what was
+// dirty) and leaves it clean.
 #include "ep_device.h"
 #include "ep_internal.h"
 

@@ -251,9 +251,43 @@ def test_with_layout_small_batches(kw):
     assert ndiff == 0
 
 
-@pytest.mark.parametrize("name", ["tiny", "decode"])
+@pytest.mark.parametrize("name", list(W.WORKLOADS))
 def test_with_layout_workloads(name):
+    """Full size: past 2048 pairs, the count launch and the copy that scans
+    the tile counts itself (no scan launch)."""
     _, _, ndiff = _run_both(W.make_inputs(name), with_layout=True)
+    assert ndiff == 0
+
+
+# Layout + dispatch in two launches (count, then the copy that rebuilds the
+# segment starts from the tile counts): one lane per tile and a wave sum per
+# slot, a second pass past 64 tiles, up to 256 tiles; 257 tiles and more take
+# the scan launch.  At E = 256, R = 16, N = 2, top-8 a tile holds 128 tokens.
+@pytest.mark.parametrize("tiles", [3, 63, 64, 65, 128, 255, 256, 257])
+def test_layout_in_copy_tile_edges(tiles):
+    inp = W.make_inputs("tiny", T=tiles * 128 - 3, H=64, E=256, R=16, N=2, k=8, mask_frac=0.05)
+    _, _, ndiff = _run_both(inp, with_layout=True)
+    assert ndiff == 0
+
+
+@pytest.mark.parametrize("kw", [
+    dict(T=300, H=64, E=4096, R=64, N=64, k=8),                 # tiles of 8 tokens (38 tiles)
+    dict(T=2049, H=64, E=256, R=8, N=1, k=1),                   # tiles of 1024 tokens
+    dict(T=65, H=64, E=256, R=16, N=2, k=32, routing="replace"),   # tiles of 32 tokens, repeated experts
+    dict(T=1000, H=256, E=64, R=8, N=4, k=6, mask_frac=0.3, mask_tokens=0.1),
+    dict(T=777, H=8, E=16, R=4, N=2, k=2),
+    dict(T=3000, H=128, E=96, R=12, N=3, k=8, routing="replace", mask_frac=0.1),   # experts not a power of two
+])
+def test_layout_in_copy_shapes(kw):
+    inp = W.make_inputs("tiny", **kw)
+    for with_layout, from_layout in ((True, True), (False, False)):   # layout + dispatch; standalone dispatch
+        _, _, ndiff = _run_both(inp, from_layout=from_layout, with_layout=with_layout)
+        assert ndiff == 0
+
+
+@pytest.mark.parametrize("name", ["quant", "nvfp4"])
+def test_layout_in_copy_quantized(name):
+    _, _, ndiff = _run_both(W.make_inputs(name, T=1500, H=1024, mask_frac=0.1), with_layout=True)
     assert ndiff == 0
 
 
@@ -265,11 +299,13 @@ def test_with_layout_quantized(kw):
     assert ndiff == 0
 
 
-def test_with_layout_flags_invalid_ids():
+@pytest.mark.parametrize("T", [100, 1000])   # one launch; count + copy launches
+def test_with_layout_flags_invalid_ids(T):
     import gpu_path
-    inp = W.make_inputs("decode", T=100, H=512, mask_frac=0.1)
+    inp = W.make_inputs("decode", T=T, H=512, mask_frac=0.1)
     bad = inp["topk_idx"].copy()
     bad[7, 3] = inp["E"] + 1
+    bad[T - 1, 0] = inp["E"] + 100
     inp["topk_idx"] = bad
     g = gpu_path.run(inp, check=False, with_layout=True)
     with pytest.raises(RuntimeError, match="flags 0x1"):
