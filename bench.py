@@ -6,12 +6,13 @@ in HBM, all on one stream: layout -> dispatch -> (the workload's expert
 stage, if any) -> combine.  Token-major rows: one ep_dispatch_with_layout
 call (layout counts, plan and row permutation; a single launch up to 2048
 (token, slot) pairs, else a count launch and the copy that scans the
-counts) -> ep_combine; phases "layout+dispatch" and "combine".
---split-layout times ep_dispatch_layout -> ep_dispatch_from_layout (the
-layout call's plan reused) -> ep_combine instead.  --layout ranks times the
-(token, rank) path: ep_dispatch_layout (planning one row per token per rank
-it reaches) -> ep_dispatch_ranks -> ep_combine_ranks, with
+counts) -> ep_combine; phases "layout+dispatch" and "combine".  --layout
+ranks times the (token, rank) path the same way: ep_dispatch_ranks_with_layout
+(one row per token per rank it reaches) -> ep_combine_ranks, with
 ep_expert_reduce_ranks (the weighted per-rank partials) as the expert stage.
+--split-layout times ep_dispatch_layout -> ep_dispatch_from_layout (or
+ep_dispatch_ranks; the layout call's plan reused) -> the combine instead,
+and --layout rank_major always does.
 The expert stage (identity, per-expert scaling, fp8 -> mxfp8 or bf16 ->
 nvfp4 re-encoding) runs during warmup and is not part of the timed step.
 W untimed warmup steps, then K timed steps bracketed by stream
@@ -182,8 +183,8 @@ def parse():
                          "(ep_dispatch_ranks / ep_combine_ranks)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--split-layout", action="store_true",
-                    help="token-major rows: time ep_dispatch_layout + ep_dispatch_from_layout (the plan reused) "
-                         "instead of one ep_dispatch_with_layout call")
+                    help="time ep_dispatch_layout + ep_dispatch_from_layout / ep_dispatch_ranks (the plan reused) "
+                         "instead of one ep_dispatch_with_layout / ep_dispatch_ranks_with_layout call")
     ap.add_argument("--no-cold", action="store_true",
                     help="skip the cold-cache step and per-call timings (graphs with a 512 MiB read flush "
                          "before each step)")
@@ -371,7 +372,7 @@ def measure(workload: str, steps: int, warmup: int, graph: bool = False, layout_
     # token-major rows: one ep_dispatch_with_layout call (a single launch up to
     # 2048 pairs, else the count launch and the copy that scans the counts);
     # split_layout times ep_dispatch_layout + ep_dispatch_from_layout instead
-    single_launch = M == 0 and (T * k <= SINGLE_LAUNCH_PAIRS or (not ranks and not split_layout))
+    single_launch = M == 0 and (T * k <= SINGLE_LAUNCH_PAIRS or not split_layout)
     if single_launch:
         phases = [("layout+dispatch", layout_dispatch), ("combine", combine)]
 

@@ -139,54 +139,6 @@ __device__ __forceinline__ int32_t counted_slot(const CopyArgs &a, int64_t t, in
     return lane < a.k ? slot_sm[lane] : -1;
 }
 
-// Sum over the 64 lanes (every lane active), returned wave-uniform: an
-// inclusive scan inside each 16-lane row by DPP row shifts, the rows' totals
-// carried on by row broadcasts, lane 63's value read back.
-__device__ __forceinline__ int32_t wave_sum(int32_t v) {
-    v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, false);   // row_shr:1
-    v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, false);   // row_shr:2
-    v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, false);   // row_shr:4
-    v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, false);   // row_shr:8
-    v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);   // row_bcast:15 into rows 1, 3
-    v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);   // row_bcast:31 into rows 2, 3
-    return __builtin_amdgcn_readlane(v, kWave - 1);
-}
-
-// Layout totals of a multi-tile batch from the tile counts, by one block of
-// the copy launch while the others copy: per column (experts, ranks, nodes)
-// the sum over tiles -> the layout outputs (when wanted), and the exclusive
-// scan of the expert totals -> the handle's segment starts.  Integer sums
-// only, so the results are those of the scan launch they replace.
-__device__ void plan_totals_block(const CopyArgs &a) {
-    extern __shared__ int32_t tot_sm[];   // [cols + 1 + waves + 1]
-    const int tid = threadIdx.x, nt = blockDim.x;
-    for (int c = tid; c < a.cols; c += nt) {
-        int32_t sum = 0;
-        for (int t0 = 0; t0 < a.ntiles; t0 += 8) {   // 8 loads in flight (clamped index)
-            int32_t v[8];
-#pragma unroll
-            for (int q = 0; q < 8; ++q) v[q] = a.tile_prefix[(size_t)min(t0 + q, a.ntiles - 1) * a.cols + c];
-#pragma unroll
-            for (int q = 0; q < 8; ++q) sum += (t0 + q < a.ntiles) ? v[q] : 0;
-        }
-        tot_sm[c] = sum;
-        if (c < a.E) {
-            if (a.per_expert) a.per_expert[c] = sum;
-        } else if (c < a.E + a.R) {
-            if (a.per_rank) a.per_rank[c - a.E] = sum;
-        } else if (a.per_node) {
-            a.per_node[c - a.E - a.R] = sum;
-        }
-    }
-    __syncthreads();
-    if (a.algo && tid == 0) {
-        int64_t al = 0;
-        for (int n = 0; n < a.N; ++n) al += tot_sm[a.E + a.R + n];
-        *a.algo = al;
-    }
-    block_exclusive_scan(tot_sm, a.expert_offset, a.E, tot_sm + a.cols + 1);
-}
-
 // Segment start of each of the token's valid slots plus the pairs of the same
 // expert in earlier tiles, rebuilt from the tile counts: for slot j with
 // expert e, the sum over tiles u of the pairs of u with smaller experts, plus,
@@ -199,17 +151,8 @@ __device__ __forceinline__ int32_t slot_bases(const CopyArgs &a, int em, int til
     for (int j0 = 0; j0 < a.k; j0 += 8) {
         int32_t v[8];
 #pragma unroll
-        for (int q = 0; q < 8; ++q) {
-            const int e = readlane(em, j0 + q);   // lanes >= k hold -1 (j0 + q < 64)
-            const int es = e < 0 ? 0 : e;
-            int32_t acc = 0;
-            for (int u0 = 0; u0 < a.ntiles; u0 += kWave) {   // one pass up to 64 tiles
-                const int u = u0 + lane;
-                const int2 p = a.tile_pairs[(size_t)es * a.ntiles + min(u, a.ntiles - 1)];   // clamped
-                acc += (u < a.ntiles) ? p.x + (u < tile ? p.y : 0) : 0;
-            }
-            v[q] = e < 0 ? 0 : acc;
-        }
+        for (int q = 0; q < 8; ++q)   // lanes >= k hold -1 (j0 + q < 64)
+            v[q] = tile_pair_sum_lane(a.tile_pairs, a.ntiles, readlane(em, j0 + q), tile, lane);
 #pragma unroll
         for (int q = 0; q < 8; ++q) v[q] = wave_sum(v[q]);
 #pragma unroll
@@ -262,7 +205,9 @@ template <int VPL, int KEYS, bool NT, bool SCAN = false>
 __global__ __launch_bounds__(KEYS ? 1024 : 256) void ep_dispatch_copy_kernel(CopyArgs a) {
     constexpr bool FUSED = KEYS > 0;
     if (SCAN && blockIdx.x == 0) {
-        plan_totals_block(a);
+        extern __shared__ int32_t tot_sm[];
+        plan_totals_block(a.tile_prefix, a.ntiles, a.E, a.R, a.N, a.per_expert, a.per_rank, a.per_node, a.algo,
+                          a.expert_offset, nullptr, tot_sm);
         return;
     }
     if (FUSED && blockIdx.x == 0) {

@@ -103,6 +103,8 @@ WsLayout ws_layout(const Shape &s) {
     off = align256(off + sizeof(int32_t) * (size_t)(s.R + 1));
     L.tile_pairs = off;
     off = align256(off + 2 * sizeof(int32_t) * (size_t)L.tiles * (size_t)s.E);
+    L.rank_pairs = off;
+    off = align256(off + (s.rank_rows ? 2 * sizeof(int32_t) * (size_t)L.tiles * (size_t)s.R : 0));
     L.total = off;
     return L;
 }
@@ -372,6 +374,16 @@ int ep_dispatch_ranks_with_layout(const ep_shape *shape, const void *x, const fl
             s, x, x_scales, topk_idx, topk_w, num_tokens_per_rank, num_tokens_per_expert, is_token_in_rank,
             num_tokens_per_node, rdma_algo_token_count, recv_x, recv_x_scales, recv_src_idx, recv_topk_idx,
             recv_topk_w, token_rank_slot, rank_offset, reinterpret_cast<uint32_t *>(w + L.ctrl), st));
+    if (ep::ranks_scan_fits(s, L)) {   // two launches: counts, then the copy that scans them
+        hipError_t e = ep::launch_plan(s, L, topk_idx, num_tokens_per_rank, num_tokens_per_expert,
+                                       is_token_in_rank, num_tokens_per_node, rdma_algo_token_count, w, st,
+                                       /*count_only=*/true);
+        if (e != hipSuccess) return EP_EHIP;
+        return hip_status(ep::launch_dispatch_ranks_scan(
+            s, L, x, x_scales, topk_idx, topk_w, recv_x, recv_x_scales, recv_src_idx, recv_topk_idx, recv_topk_w,
+            token_rank_slot, rank_offset, num_tokens_per_rank, num_tokens_per_expert, num_tokens_per_node,
+            rdma_algo_token_count, w, st));
+    }
     hipError_t e = ep::launch_plan(s, L, topk_idx, num_tokens_per_rank, num_tokens_per_expert,
                                    is_token_in_rank, num_tokens_per_node, rdma_algo_token_count, w, st);
     if (e != hipSuccess) return EP_EHIP;

@@ -229,4 +229,79 @@ __device__ __forceinline__ void wave_exclusive_scan(int32_t v, int n, int32_t *o
     if (lane == kWave - 1) out[n] = incl;
 }
 
+// Sum over the 64 lanes (every lane active), returned wave-uniform: an
+// inclusive scan inside each 16-lane row by DPP row shifts, the rows' totals
+// carried on by row broadcasts, lane 63's value read back.
+__device__ __forceinline__ int32_t wave_sum(int32_t v) {
+    v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, false);   // row_shr:1
+    v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, false);   // row_shr:2
+    v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, false);   // row_shr:4
+    v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, false);   // row_shr:8
+    v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);   // row_bcast:15 into rows 1, 3
+    v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);   // row_bcast:31 into rows 2, 3
+    return __builtin_amdgcn_readlane(v, kWave - 1);
+}
+
+// ---------------------------------------------------------------- plan totals
+
+// Layout totals of a multi-tile batch from the tile count matrix [ntiles][E +
+// R + N] (raw counts: experts, ranks, nodes), by one block of a copy launch
+// while its other blocks copy: per column the sum over tiles -> the layout
+// outputs (each may be null), the RDMA algo count (sum of the node totals),
+// and the exclusive scan of the expert totals into expert_offset [E + 1] and
+// / or of the rank totals into rank_offset [R + 1] (either may be null).
+// Integer sums only.  tot: LDS of E + R + N + 1 + blockDim / 64 + 1 ints.
+// Called by every thread of the block (blockDim <= 1024, a multiple of 64).
+__device__ inline void plan_totals_block(const int32_t *tile_count, int ntiles, int E, int R, int N,
+                                         int32_t *per_expert, int32_t *per_rank, int32_t *per_node,
+                                         int64_t *algo, int32_t *expert_offset, int32_t *rank_offset,
+                                         int32_t *tot) {
+    const int tid = threadIdx.x, nt = blockDim.x, cols = E + R + N;
+    for (int c = tid; c < cols; c += nt) {
+        int32_t sum = 0;
+        for (int t0 = 0; t0 < ntiles; t0 += 8) {   // 8 loads in flight (clamped index)
+            int32_t v[8];
+#pragma unroll
+            for (int q = 0; q < 8; ++q) v[q] = tile_count[(size_t)min(t0 + q, ntiles - 1) * cols + c];
+#pragma unroll
+            for (int q = 0; q < 8; ++q) sum += (t0 + q < ntiles) ? v[q] : 0;
+        }
+        tot[c] = sum;
+        if (c < E) {
+            if (per_expert) per_expert[c] = sum;
+        } else if (c < E + R) {
+            if (per_rank) per_rank[c - E] = sum;
+        } else if (per_node) {
+            per_node[c - E - R] = sum;
+        }
+    }
+    __syncthreads();
+    if (algo && tid == 0) {
+        int64_t al = 0;
+        for (int n = 0; n < N; ++n) al += tot[E + R + n];
+        *algo = al;
+    }
+    if (rank_offset && tid < kWave) wave_exclusive_scan(tid < R ? tot[E + tid] : 0, R, rank_offset);
+    if (expert_offset) block_exclusive_scan(tot, expert_offset, E, tot + cols + 1);
+}
+
+// Start of a region plus the earlier tiles' members of it, rebuilt from
+// per-tile pairs {members of tile u in earlier regions, members of tile u in
+// this region} stored region-major (pairs[region][ntiles], one region's tiles
+// side by side): the sum over tiles u of the first plus, for u before `tile`,
+// the second.  One tile per lane (an 8-byte load) and a wave sum; returns the
+// value for `region` (>= 0) to every lane, 0 for region < 0.  Called by the
+// whole wave.
+__device__ __forceinline__ int32_t tile_pair_sum_lane(const int2 *pairs, int ntiles, int region, int tile,
+                                                      int lane) {
+    const int rs = region < 0 ? 0 : region;
+    int32_t acc = 0;
+    for (int u0 = 0; u0 < ntiles; u0 += kWave) {   // one pass up to 64 tiles
+        const int u = u0 + lane;
+        const int2 p = pairs[(size_t)rs * ntiles + min(u, ntiles - 1)];   // clamped: always issued
+        acc += (u < ntiles) ? p.x + (u < tile ? p.y : 0) : 0;
+    }
+    return region < 0 ? 0 : acc;
+}
+
 }  // namespace ep

@@ -26,10 +26,14 @@ namespace ep {
 //                                    an expert below e, pairs of u with e}
 //                                    (layout + dispatch in one call,
 //                                    multi-tile batches)
+//   rank_pairs  : int2[R][tiles]     the same per rank for (token, rank) rows:
+//                                    {tokens of u reaching ranks below r,
+//                                    tokens of u reaching r}
 // A tile holds tile_tokens whole tokens (tile_tokens * k <= count_threads
 // pairs, one thread per pair).
 struct WsLayout {
-    size_t ctrl, tile_count, local_rank, plan_offset, rank_mask, plan_rank_offset, tile_pairs, total;
+    size_t ctrl, tile_count, local_rank, plan_offset, rank_mask, plan_rank_offset, tile_pairs, rank_pairs,
+        total;
     int tiles;           // ceil(T / tile_tokens)
     int tile_tokens;
     int tile_waves;      // ceil(tile_tokens * k / 64): waves that own pair masks
@@ -59,7 +63,8 @@ hipError_t launch_ws_init(uint32_t *ws, size_t words, hipStream_t stream);
 
 // Layout counts (outputs may be null) and the dispatch plan in the workspace.
 // count_only: the count launch alone, which also writes tile_pairs (for
-// launch_dispatch_copy with scan_in_copy; multi-tile batches).
+// launch_dispatch_scan_copy) or, with rank rows, rank_pairs (for
+// launch_dispatch_ranks_scan); multi-tile batches.
 hipError_t launch_plan(const Shape &s, const WsLayout &L, const int64_t *topk_idx,
                        int32_t *per_rank, int32_t *per_expert, uint8_t *in_rank,
                        int32_t *per_node, int64_t *algo, char *ws, hipStream_t stream,
@@ -121,6 +126,19 @@ hipError_t launch_dispatch_ranks(const Shape &s, const WsLayout &L, const void *
                                  int32_t *recv_src_idx, int32_t *recv_topk_idx, float *recv_topk_w,
                                  int32_t *token_rank_slot, int32_t *rank_offset, const char *ws,
                                  hipStream_t stream);
+
+// Layout + (token, rank) dispatch of a multi-tile batch in two launches:
+// launch_plan with count_only, then this copy, which rebuilds each region
+// start and prefix over tiles from rank_pairs while one extra block writes
+// the layout totals and the handle's region starts.  ranks_scan_fits: rank
+// rows, 2 ... kScanCopyMaxTiles tiles.
+bool ranks_scan_fits(const Shape &s, const WsLayout &L);
+hipError_t launch_dispatch_ranks_scan(const Shape &s, const WsLayout &L, const void *x,
+                                      const float *x_scales, const int64_t *topk_idx, const float *topk_w,
+                                      void *recv_x, float *recv_x_scales, int32_t *recv_src_idx,
+                                      int32_t *recv_topk_idx, float *recv_topk_w, int32_t *token_rank_slot,
+                                      int32_t *rank_offset, int32_t *per_rank, int32_t *per_expert,
+                                      int32_t *per_node, int64_t *algo, char *ws, hipStream_t stream);
 
 // Single-launch layout + (token, rank) dispatch (T * k <= 2048 pairs, rank
 // rows); the workspace plan is neither read nor written.

@@ -75,6 +75,10 @@ struct CountArgs {
     // e, pairs of u with expert e} ([E][ntiles], the tiles of one expert
     // side by side)
     int2 *tile_pairs;
+    // the same for (token, rank) rows: per rank r and tile u, {tokens of u
+    // reaching ranks below r (counted once per rank), tokens of u reaching r}
+    // ([R][ntiles]); or null
+    int2 *rank_pairs;
 };
 
 __global__ __launch_bounds__(1024) void ep_plan_count_kernel(CountArgs a) {
@@ -203,6 +207,15 @@ __global__ __launch_bounds__(1024) void ep_plan_count_kernel(CountArgs a) {
     // when (token, rank) rows are planned, else the counts
     for (int i = tid; i < a.R + a.N; i += nt) tc[E + i] = (single && a.rank_mask && i < a.R) ? 0 : rn[i];
     if (!single) {   // block-uniform
+        if (a.rank_pairs && tid < kWave) {   // wave 0: the tile's tokens per rank, prefixed over the ranks
+            const int32_t c = tid < a.R ? rn[tid] : 0;
+            int32_t incl = c;
+            for (int off = 1; off < kWave; off <<= 1) {
+                const int32_t u = __shfl_up(incl, off);
+                if (lane >= off) incl += u;
+            }
+            if (tid < a.R) a.rank_pairs[(size_t)tid * gridDim.x + blockIdx.x] = make_int2(incl - c, c);
+        }
         if (a.tile_pairs) {   // this tile's counts, prefixed over the experts (in place)
             block_exclusive_scan(cnt, cnt, E, reinterpret_cast<int32_t *>(cnt + E + 1));
             for (int e2 = tid; e2 < E; e2 += nt)
@@ -386,7 +399,8 @@ hipError_t launch_plan(const Shape &s, const WsLayout &L, const int64_t *topk_id
     c.per_rank = per_rank;
     c.per_node = per_node;
     c.algo = algo;
-    c.tile_pairs = count_only ? reinterpret_cast<int2 *>(ws + L.tile_pairs) : nullptr;
+    c.tile_pairs = (count_only && !s.rank_rows) ? reinterpret_cast<int2 *>(ws + L.tile_pairs) : nullptr;
+    c.rank_pairs = (count_only && s.rank_rows) ? reinterpret_cast<int2 *>(ws + L.rank_pairs) : nullptr;
     if (s.T > 0) {
         // masks, staged ids, rank/node counts, and (single tile) expert counts + scan scratch
         const size_t lds = sizeof(uint64_t) * (size_t)L.tile_waves * s.E +

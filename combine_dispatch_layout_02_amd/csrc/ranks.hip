@@ -81,7 +81,38 @@ struct RankCopyArgs {
     int64_t cap;                    // receive rows: T * min(k, R)
     int64_t row_bytes;
     int nvec, G, S;
+    // copy that rebuilds the plan (layout + dispatch in two launches): the raw
+    // tile counts (in tile_prefix), per rank and tile {tokens reaching lower
+    // ranks, tokens reaching the rank} ([R][ntiles]), the layout outputs
+    const int2 *rank_pairs;
+    int ntiles, N;
+    int32_t *per_rank, *per_expert, *per_node;
+    int64_t *algo;
 };
+
+// Start of each reached rank's region plus the tile's earlier-tile tokens of
+// it, rebuilt from rank_pairs: one sum over tiles per rank (eight ranks at a
+// time); lane r returns rank r's value.  reach: the uniform mask of ranks
+// the token reaches.
+__device__ __forceinline__ int32_t rank_bases(const RankCopyArgs &a, uint64_t reach, int tile, int lane) {
+    int32_t base = 0;
+    while (reach) {   // uniform: at most min(k, R) ranks
+        int rr[8];
+        int32_t v[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            rr[q] = reach ? (int)__builtin_ctzll(reach) : -1;
+            reach &= reach - 1;   // stays 0 once empty
+            v[q] = tile_pair_sum_lane(a.rank_pairs, a.ntiles, rr[q], tile, lane);
+        }
+#pragma unroll
+        for (int q = 0; q < 8; ++q) v[q] = wave_sum(v[q]);
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+            if (lane == rr[q]) base = v[q];
+    }
+    return base;
+}
 
 constexpr int kRankFusedPairs = 2048;   // pairs a single-launch batch may hold
 
@@ -139,12 +170,21 @@ __device__ __forceinline__ int32_t counted_rank_slot(const RankCopyArgs &a, int6
 
 // TOK > 0: the single-launch form (block 0 does the layout, every other block
 // holds one token in S waves and counts its rows); TOK == 0: rows from the
-// plan, or from a previous handle (cached form).
-template <int VPL, int TOK>
+// plan, or from a previous handle (cached form).  SCAN: the copy of layout +
+// dispatch in two launches -- block 0 writes the layout totals and the
+// handle's region starts, every wave rebuilds its region starts from the
+// tile counts (rank_bases).
+template <int VPL, int TOK, bool SCAN = false>
 __global__ __launch_bounds__(TOK ? 1024 : 256) void ep_dispatch_ranks_kernel(RankCopyArgs a, SmallLayout L) {
     constexpr bool FUSED = TOK > 0;
     if (FUSED && blockIdx.x == 0) {
         small_layout_block(L);
+        return;
+    }
+    if (SCAN && blockIdx.x == 0) {
+        extern __shared__ int32_t tot_sm[];
+        plan_totals_block(a.tile_prefix, a.ntiles, a.E, a.R, a.N, a.per_expert, a.per_rank, a.per_node, a.algo,
+                          nullptr, a.rank_offset, tot_sm);
         return;
     }
     const int lane = threadIdx.x & (kWave - 1);
@@ -154,11 +194,11 @@ __global__ __launch_bounds__(TOK ? 1024 : 256) void ep_dispatch_ranks_kernel(Ran
         t = (int64_t)blockIdx.x - 1;   // < T: the grid has 1 + T blocks
         sub = threadIdx.x / kWave;
     } else {
-        const int64_t gw = (int64_t)blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
+        const int64_t gw = ((int64_t)blockIdx.x - (SCAN ? 1 : 0)) * (blockDim.x / kWave) + threadIdx.x / kWave;
         t = gw / a.S;
         sub = (int)(gw - t * a.S);
         const int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-        if (!a.slots_in && g <= a.R) a.rank_offset[g] = a.plan_rank_offset[g];   // handle copy of the region starts
+        if (!SCAN && !a.slots_in && g <= a.R) a.rank_offset[g] = a.plan_rank_offset[g];   // handle copy of the region starts
     }
     if (t >= a.T) return;   // wave-uniform (never taken in the single-launch form)
 
@@ -186,26 +226,34 @@ __global__ __launch_bounds__(TOK ? 1024 : 256) void ep_dispatch_ranks_kernel(Ran
     } else if (lane < a.R && a.slots_in) {   // cached: the rows of a previous dispatch's handle
         slot = a.slots_in[t * a.R + lane];
         if ((uint64_t)slot >= (uint64_t)a.cap) slot = -1;
-    } else if (lane < a.R) {
+    } else if (!a.slots_in) {
         // t's place among its tile's tokens reaching rank `lane`: the set
         // bits before t's bit in the tile's mask of that rank
         const int64_t tile = t / a.TT;
         const int pos = (int)(t - tile * a.TT);
-        const uint64_t *m = a.rank_mask + ((size_t)tile * a.R + lane) * a.TW;
         const int wt = pos >> 6, bit = pos & 63;
-        // every lookup is independent of the others: one memory round trip
-        const uint64_t mw = m[wt];
-        const int32_t start = a.plan_rank_offset[lane] + a.tile_prefix[tile * a.cols + a.E + lane];
-        int32_t lr = (int32_t)__popcll(mw & ((1ull << bit) - 1ull));
-        for (int i = 0; i < wt; ++i) lr += (int32_t)__popcll(m[i]);
-        if ((mw >> bit) & 1u) {
-            slot = start + lr;
-            if ((uint64_t)slot >= (uint64_t)a.cap) {   // cannot happen; never write outside
-                atomicOr(&a.ctrl[0], kErrBadSlot);
-                slot = -1;
-            }
+        int32_t start = 0, lr = 0;
+        bool reached = false;
+        if (lane < a.R) {
+            const uint64_t *m = a.rank_mask + ((size_t)tile * a.R + lane) * a.TW;
+            // every lookup is independent of the others: one memory round trip
+            const uint64_t mw = m[wt];
+            if (!SCAN) start = a.plan_rank_offset[lane] + a.tile_prefix[tile * a.cols + a.E + lane];
+            lr = (int32_t)__popcll(mw & ((1ull << bit) - 1ull));
+            for (int i = 0; i < wt; ++i) lr += (int32_t)__popcll(m[i]);
+            reached = (mw >> bit) & 1u;
         }
-        if (sub == 0) a.token_rank_slot[t * a.R + lane] = slot;
+        if (SCAN) start = rank_bases(a, __ballot(reached), (int)tile, lane);
+        if (lane < a.R) {
+            if (reached) {
+                slot = start + lr;
+                if ((uint64_t)slot >= (uint64_t)a.cap) {   // cannot happen; never write outside
+                    atomicOr(&a.ctrl[0], kErrBadSlot);
+                    slot = -1;
+                }
+            }
+            if (sub == 0) a.token_rank_slot[t * a.R + lane] = slot;
+        }
     }
     const uint64_t live = __ballot(slot >= 0);
     if (live == 0) return;
@@ -439,18 +487,18 @@ __global__ __launch_bounds__(256) void ep_combine_ranks_kernel(RankCombineArgs a
     }
 }
 
-template <int TOK>
+template <int TOK, bool SCAN = false>
 void launch_ranks_copy(const RankCopyArgs &a, const SmallLayout &L, const dim3 &grid, const dim3 &block,
                        size_t lds, hipStream_t stream) {
     const int per_lane = (a.nvec + kWave * a.S - 1) / (kWave * a.S);
     if (per_lane <= 2) {
-        hipLaunchKernelGGL((ep_dispatch_ranks_kernel<2, TOK>), grid, block, lds, stream, a, L);
+        hipLaunchKernelGGL((ep_dispatch_ranks_kernel<2, TOK, SCAN>), grid, block, lds, stream, a, L);
     } else if (per_lane <= 4) {
-        hipLaunchKernelGGL((ep_dispatch_ranks_kernel<4, TOK>), grid, block, lds, stream, a, L);
+        hipLaunchKernelGGL((ep_dispatch_ranks_kernel<4, TOK, SCAN>), grid, block, lds, stream, a, L);
     } else if (per_lane <= 8 || TOK) {   // the single-launch form has at most 8 (fused_ranks_fits)
-        hipLaunchKernelGGL((ep_dispatch_ranks_kernel<8, TOK>), grid, block, lds, stream, a, L);
+        hipLaunchKernelGGL((ep_dispatch_ranks_kernel<8, TOK, SCAN>), grid, block, lds, stream, a, L);
     } else {
-        hipLaunchKernelGGL((ep_dispatch_ranks_kernel<16, TOK>), grid, block, lds, stream, a, L);
+        hipLaunchKernelGGL((ep_dispatch_ranks_kernel<16, TOK, SCAN>), grid, block, lds, stream, a, L);
     }
 }
 
@@ -532,12 +580,12 @@ hipError_t launch_dispatch_ranks_fused(const Shape &s, const void *x, const floa
     return hipGetLastError();
 }
 
-hipError_t launch_dispatch_ranks(const Shape &s, const WsLayout &L, const void *x,
-                                 const float *x_scales, const int64_t *topk_idx,
-                                 const float *topk_w, void *recv_x, float *recv_x_scales,
-                                 int32_t *recv_src_idx, int32_t *recv_topk_idx, float *recv_topk_w,
-                                 int32_t *token_rank_slot, int32_t *rank_offset, const char *ws,
-                                 hipStream_t stream) {
+namespace {
+
+RankCopyArgs plan_copy_args(const Shape &s, const WsLayout &L, const void *x, const float *x_scales,
+                            const int64_t *topk_idx, const float *topk_w, void *recv_x, float *recv_x_scales,
+                            int32_t *recv_src_idx, int32_t *recv_topk_idx, float *recv_topk_w,
+                            int32_t *token_rank_slot, int32_t *rank_offset, const char *ws) {
     RankCopyArgs a{};
     a.x = static_cast<const char *>(x);
     a.x_scales = x_scales;
@@ -559,6 +607,7 @@ hipError_t launch_dispatch_ranks(const Shape &s, const WsLayout &L, const void *
     a.k = s.k;
     a.E = s.E;
     a.R = s.R;
+    a.N = s.N;
     a.TT = L.tile_tokens;
     a.cols = s.E + s.R + s.N;
     a.epr = s.E / s.R;
@@ -569,10 +618,48 @@ hipError_t launch_dispatch_ranks(const Shape &s, const WsLayout &L, const void *
     a.nvec = (int)(a.row_bytes / 16);
     a.G = fp8 ? s.H / 128 : 0;
     a.S = waves_per_token(s.T, a.nvec, EP_RANKS_WAVES);
+    return a;
+}
+
+}  // namespace
+
+hipError_t launch_dispatch_ranks(const Shape &s, const WsLayout &L, const void *x,
+                                 const float *x_scales, const int64_t *topk_idx,
+                                 const float *topk_w, void *recv_x, float *recv_x_scales,
+                                 int32_t *recv_src_idx, int32_t *recv_topk_idx, float *recv_topk_w,
+                                 int32_t *token_rank_slot, int32_t *rank_offset, const char *ws,
+                                 hipStream_t stream) {
+    const RankCopyArgs a = plan_copy_args(s, L, x, x_scales, topk_idx, topk_w, recv_x, recv_x_scales, recv_src_idx,
+                                          recv_topk_idx, recv_topk_w, token_rank_slot, rank_offset, ws);
     int64_t blocks = (s.T * a.S + 3) / 4;
     if (blocks * 256 < s.R + 1) blocks = 1;   // threads to copy rank_offset (R <= 64)
     const dim3 grid((unsigned)blocks), block(256);
     launch_ranks_copy<0>(a, SmallLayout{}, grid, block, 0, stream);
+    return hipGetLastError();
+}
+
+bool ranks_scan_fits(const Shape &s, const WsLayout &L) {
+    return s.T > 0 && s.rank_rows && L.tiles > 1 && L.tiles <= kScanCopyMaxTiles;
+}
+
+hipError_t launch_dispatch_ranks_scan(const Shape &s, const WsLayout &L, const void *x,
+                                      const float *x_scales, const int64_t *topk_idx, const float *topk_w,
+                                      void *recv_x, float *recv_x_scales, int32_t *recv_src_idx,
+                                      int32_t *recv_topk_idx, float *recv_topk_w, int32_t *token_rank_slot,
+                                      int32_t *rank_offset, int32_t *per_rank, int32_t *per_expert,
+                                      int32_t *per_node, int64_t *algo, char *ws, hipStream_t stream) {
+    RankCopyArgs a = plan_copy_args(s, L, x, x_scales, topk_idx, topk_w, recv_x, recv_x_scales, recv_src_idx,
+                                    recv_topk_idx, recv_topk_w, token_rank_slot, rank_offset, ws);
+    a.rank_pairs = reinterpret_cast<const int2 *>(ws + L.rank_pairs);
+    a.ntiles = L.tiles;
+    a.per_rank = per_rank;
+    a.per_expert = per_expert;
+    a.per_node = per_node;
+    a.algo = algo;
+    // block 0: the totals; then the copy blocks (4 waves each)
+    const int64_t blocks = 1 + (s.T * a.S + 3) / 4;
+    const size_t lds = sizeof(int32_t) * ((size_t)a.cols + 1 + 256 / kWave + 1);
+    launch_ranks_copy<0, true>(a, SmallLayout{}, dim3((unsigned)blocks), dim3(256), lds, stream);
     return hipGetLastError();
 }
 

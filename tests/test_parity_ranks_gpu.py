@@ -154,9 +154,36 @@ def test_with_layout_small_batches(kw):
     assert ndiff == 0
 
 
-@pytest.mark.parametrize("name", ["tiny", "decode"])
+@pytest.mark.parametrize("name", ["tiny", "decode", "prefill2n", "skewed", "quant"])
 def test_with_layout_workloads(name):
+    """Full size: past 2048 pairs, the count launch and the copy that rebuilds
+    the region starts from the per-tile rank counts (no scan launch)."""
     _, _, ndiff = _run_both(W.make_inputs(name), with_layout=True)
+    assert ndiff == 0
+
+
+# Layout + (token, rank) dispatch in two launches: one lane per tile and a
+# wave sum per reached rank, a second pass past 64 tiles, up to 256 tiles;
+# 257 tiles take the scan launch.  At E = 256, R = 16, top-8 a tile holds 128
+# tokens.
+@pytest.mark.parametrize("tiles", [3, 63, 64, 65, 256, 257])
+def test_layout_in_copy_tile_edges(tiles):
+    inp = W.make_inputs("tiny", T=tiles * 128 - 3, H=64, E=256, R=16, N=2, k=8, mask_frac=0.05)
+    _, _, ndiff = _run_both(inp, with_layout=True)
+    assert ndiff == 0
+
+
+@pytest.mark.parametrize("kw", [
+    dict(T=300, H=64, E=4096, R=64, N=64, k=8),                 # 64 ranks, tiles of 8 tokens
+    dict(T=2049, H=64, E=256, R=8, N=1, k=1),
+    dict(T=65, H=64, E=256, R=16, N=2, k=32, routing="replace"),
+    dict(T=1000, H=256, E=64, R=8, N=4, k=6, mask_frac=0.3, mask_tokens=0.1),
+    dict(T=3000, H=128, E=96, R=12, N=3, k=8, routing="replace", mask_frac=0.1),
+    dict(T=900, H=128, E=32, R=1, N=1, k=4),                    # one rank
+    dict(T=1500, H=1024, x_fmt="fp8", E=256, R=8, N=1, k=8, mask_frac=0.1),
+])
+def test_layout_in_copy_shapes(kw):
+    _, _, ndiff = _run_both(W.make_inputs("tiny", **kw), with_layout=True)
     assert ndiff == 0
 
 
