@@ -489,8 +489,7 @@ hipError_t launch_dispatch_scan_copy(const Shape &s, const WsLayout &L, const vo
     a.algo = algo;
     // block 0: the totals; then the copy blocks (4 waves each)
     const int64_t blocks = 1 + (s.T * a.S + 3) / 4;
-    const size_t lds = sizeof(int32_t) * ((size_t)a.cols + 1 + 256 / kWave + 1);
-    launch_copy<0, true>(a, blocks, 256, lds, stream);
+    launch_copy<0, true>(a, blocks, 256, scan_copy_lds(s), stream);
     return hipGetLastError();
 }
 
@@ -558,11 +557,24 @@ hipError_t launch_dispatch_fused(const Shape &s, const void *x, const float *x_s
         a.nt_store = 1;
         a.plain_tokens = 0;
     }
-    const int threads = kWave * a.S;
-    const size_t lds = sizeof(int32_t) * ((size_t)s.T * s.k + s.E + s.R + s.N + threads / kWave + 1);
+    int threads = 0;
+    const size_t lds = fused_dispatch_lds(s, &threads);
     if (s.T * s.k <= 16 * kWave) launch_copy<16>(a, 1 + s.T, threads, lds, stream);
     else launch_copy<32>(a, 1 + s.T, threads, lds, stream);
     return hipGetLastError();
+}
+
+size_t fused_dispatch_lds(const Shape &s, int *threads) {
+    const int nvec = (int)((s.x_fmt == 1 ? (int64_t)s.H : 2 * (int64_t)s.H) / 16);
+    const int t = kWave * fused_waves(s, nvec);
+    if (threads) *threads = t;
+    // the layout block's staging (pair ids, counts, scan scratch), larger than
+    // the other blocks' pair ids
+    return sizeof(int32_t) * ((size_t)s.T * s.k + s.E + s.R + s.N + t / kWave + 1);
+}
+
+size_t scan_copy_lds(const Shape &s) {   // the totals block of a copy that scans the tile counts
+    return sizeof(int32_t) * ((size_t)s.E + s.R + s.N + 1 + 256 / kWave + 1);
 }
 
 }  // namespace ep

@@ -75,6 +75,8 @@ double row_bytes(int fmt, int H) {
 
 namespace ep {
 
+constexpr int kRegionCount = kWsRegions;
+
 WsLayout ws_layout(const Shape &s) {
     WsLayout L;
     // pair masks of one tile (tile_waves * E * 8 bytes) stay within 48 KiB
@@ -87,24 +89,28 @@ WsLayout ws_layout(const Shape &s) {
     L.tiles = (int)((s.T + L.tile_tokens - 1) / L.tile_tokens);
     if (L.tiles < 1) L.tiles = 1;
     const int64_t TK = s.T * s.k;
-    size_t off = 0;
-    L.ctrl = off;
-    off = align256(off + kCtrlWords * sizeof(uint32_t));
-    L.tile_count = off;
-    off = align256(off + sizeof(int32_t) * (size_t)L.tiles * (size_t)(s.E + s.R + s.N));
-    L.local_rank = off;
-    off = align256(off + sizeof(int32_t) * (size_t)(TK > 0 ? TK : 1));
-    L.plan_offset = off;
-    off = align256(off + sizeof(int32_t) * (size_t)(s.E + 1));
     L.tile_token_waves = (L.tile_tokens + 63) / 64;
-    L.rank_mask = off;
-    off = align256(off + (s.rank_rows ? sizeof(uint64_t) * (size_t)L.tiles * (size_t)s.R * L.tile_token_waves : 0));
-    L.plan_rank_offset = off;
-    off = align256(off + sizeof(int32_t) * (size_t)(s.R + 1));
-    L.tile_pairs = off;
-    off = align256(off + 2 * sizeof(int32_t) * (size_t)L.tiles * (size_t)s.E);
-    L.rank_pairs = off;
-    off = align256(off + (s.rank_rows ? 2 * sizeof(int32_t) * (size_t)L.tiles * (size_t)s.R : 0));
+    // the per-tile pairs serve the copies that scan the tile counts (2 ...
+    // kScanCopyMaxTiles tiles); other batches never touch them
+    const bool pairs = L.tiles > 1 && L.tiles <= kScanCopyMaxTiles;
+    const size_t need[kRegionCount] = {
+        kCtrlWords * sizeof(uint32_t),                                               // ctrl
+        sizeof(int32_t) * (size_t)L.tiles * (size_t)(s.E + s.R + s.N),               // tile_count
+        sizeof(int32_t) * (size_t)(TK > 0 ? TK : 1),                                 // local_rank
+        sizeof(int32_t) * (size_t)(s.E + 1),                                         // plan_offset
+        s.rank_rows ? sizeof(uint64_t) * (size_t)L.tiles * (size_t)s.R * L.tile_token_waves : 0,   // rank_mask
+        sizeof(int32_t) * (size_t)(s.R + 1),                                         // plan_rank_offset
+        (pairs && !s.rank_rows) ? 2 * sizeof(int32_t) * (size_t)L.tiles * (size_t)s.E : 0,   // tile_pairs
+        (pairs && s.rank_rows) ? 2 * sizeof(int32_t) * (size_t)L.tiles * (size_t)s.R : 0,    // rank_pairs
+    };
+    size_t *const field[kRegionCount] = {&L.ctrl, &L.tile_count, &L.local_rank, &L.plan_offset, &L.rank_mask,
+                                         &L.plan_rank_offset, &L.tile_pairs, &L.rank_pairs};
+    size_t off = 0;
+    for (int i = 0; i < kRegionCount; ++i) {
+        *field[i] = off;
+        L.region_bytes[i] = need[i];
+        off = align256(off + need[i]);
+    }
     L.total = off;
     return L;
 }
@@ -578,6 +584,39 @@ int ep_accounting(const ep_shape *shape, int32_t own_node, const int32_t *num_to
     out->hbm_combine_bytes = out->hbm_combine_read_bytes + out->hbm_combine_write_bytes;
     out->hbm_dispatch_ranks_bytes = out->hbm_dispatch_ranks_read_bytes + out->hbm_dispatch_ranks_write_bytes;
     out->hbm_combine_ranks_bytes = out->hbm_combine_ranks_read_bytes + out->hbm_combine_ranks_write_bytes;
+    return EP_OK;
+}
+
+int ep_plan_info(const ep_shape *shape, ep_plan_info_t *info) {
+    Shape s;
+    const int rc = check_shape(shape, &s);
+    if (rc != EP_OK) return rc;
+    if (!info) return EP_EINVAL;
+    const WsLayout L = ep::ws_layout(s);
+    *info = ep_plan_info_t{};
+    info->workspace_bytes = L.total;
+    const size_t offs[ep::kWsRegions] = {L.ctrl, L.tile_count, L.local_rank, L.plan_offset, L.rank_mask,
+                                         L.plan_rank_offset, L.tile_pairs, L.rank_pairs};
+    static_assert(ep::kWsRegions == EP_PLAN_REGIONS, "region count and header disagree");
+    for (int i = 0; i < ep::kWsRegions; ++i) {
+        info->region_offset[i] = offs[i];
+        info->region_bytes[i] = L.region_bytes[i];
+    }
+    info->tiles = L.tiles;
+    info->tile_tokens = L.tile_tokens;
+    info->tile_waves = L.tile_waves;
+    info->count_threads = L.count_threads;
+    info->count_lds_bytes = s.T > 0 ? ep::plan_count_lds(s, L) : 0;
+    int threads = 0;
+    if (ep::fused_dispatch_fits(s)) {
+        info->single_launch_lds_bytes = ep::fused_dispatch_lds(s, &threads);
+        info->single_launch_threads = threads;
+    } else if (ep::fused_ranks_fits(s)) {
+        info->single_launch_lds_bytes = ep::fused_ranks_lds(s, &threads);
+        info->single_launch_threads = threads;
+    }
+    const bool scan = s.rank_rows ? ep::ranks_scan_fits(s, L) : ep::scan_in_copy_fits(s, L);
+    info->scan_copy_lds_bytes = scan ? ep::scan_copy_lds(s) : 0;
     return EP_OK;
 }
 

@@ -31,9 +31,12 @@ namespace ep {
 //                                    tokens of u reaching r}
 // A tile holds tile_tokens whole tokens (tile_tokens * k <= count_threads
 // pairs, one thread per pair).
+constexpr int kWsRegions = 8;   // ctrl, tile_count, local_rank, plan_offset, rank_mask,
+                                // plan_rank_offset, tile_pairs, rank_pairs (in this order)
 struct WsLayout {
     size_t ctrl, tile_count, local_rank, plan_offset, rank_mask, plan_rank_offset, tile_pairs, rank_pairs,
         total;
+    size_t region_bytes[kWsRegions];   // bytes each region needs (its offset above, 256-aligned)
     int tiles;           // ceil(T / tile_tokens)
     int tile_tokens;
     int tile_waves;      // ceil(tile_tokens * k / 64): waves that own pair masks
@@ -57,6 +60,15 @@ struct Shape {
 };
 
 WsLayout ws_layout(const Shape &s);
+
+// Dynamic LDS bytes per workgroup of the launches that take it (the same
+// functions the launchers use): the count kernel; the single-launch layout +
+// dispatch forms (threads per block through *threads); the totals block of
+// the copies that scan the tile counts.
+size_t plan_count_lds(const Shape &s, const WsLayout &L);
+size_t fused_dispatch_lds(const Shape &s, int *threads);
+size_t fused_ranks_lds(const Shape &s, int *threads);
+size_t scan_copy_lds(const Shape &s);
 
 // Kernel launchers; every one enqueues on `stream` and returns the launch status.
 hipError_t launch_ws_init(uint32_t *ws, size_t words, hipStream_t stream);

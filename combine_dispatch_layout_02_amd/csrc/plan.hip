@@ -371,6 +371,13 @@ __global__ __launch_bounds__(1024) void ep_plan_scan_kernel(ScanArgs a) {
 
 }  // namespace
 
+size_t plan_count_lds(const Shape &s, const WsLayout &L) {
+    // pair masks [waves][E], staged ids, rank / node counts, expert counts
+    // and block-scan scratch (one slot more than the scan's 1024 / 64 + 1)
+    return sizeof(uint64_t) * (size_t)L.tile_waves * s.E +
+           sizeof(int32_t) * ((size_t)L.tile_tokens * s.k + s.R + s.N + s.E + 1 + 1024 / kWave + 2);
+}
+
 hipError_t launch_plan(const Shape &s, const WsLayout &L, const int64_t *topk_idx,
                        int32_t *per_rank, int32_t *per_expert, uint8_t *in_rank,
                        int32_t *per_node, int64_t *algo, char *ws, hipStream_t stream, bool count_only) {
@@ -402,11 +409,8 @@ hipError_t launch_plan(const Shape &s, const WsLayout &L, const int64_t *topk_id
     c.tile_pairs = (count_only && !s.rank_rows) ? reinterpret_cast<int2 *>(ws + L.tile_pairs) : nullptr;
     c.rank_pairs = (count_only && s.rank_rows) ? reinterpret_cast<int2 *>(ws + L.rank_pairs) : nullptr;
     if (s.T > 0) {
-        // masks, staged ids, rank/node counts, and (single tile) expert counts + scan scratch
-        const size_t lds = sizeof(uint64_t) * (size_t)L.tile_waves * s.E +
-                           sizeof(int32_t) * ((size_t)L.tile_tokens * s.k + s.R + s.N + s.E + 1 +
-                                              1024 / kWave + 2);
-        hipLaunchKernelGGL(ep_plan_count_kernel, dim3(L.tiles), dim3(L.count_threads), lds, stream, c);
+        hipLaunchKernelGGL(ep_plan_count_kernel, dim3(L.tiles), dim3(L.count_threads), plan_count_lds(s, L), stream,
+                           c);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess || L.tiles == 1 || count_only) return e;   // one tile: the plan is complete
     }

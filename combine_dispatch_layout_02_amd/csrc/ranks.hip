@@ -570,14 +570,22 @@ hipError_t launch_dispatch_ranks_fused(const Shape &s, const void *x, const floa
     L.in_rank = in_rank;
     L.algo = algo;
     L.rank_offset = rank_offset;
-    const int threads = kWave * a.S;
-    const size_t lds_layout = sizeof(int32_t) * ((size_t)s.T * s.k + s.E + s.R + s.N + threads / kWave + 1);
-    const size_t lds_masks = sizeof(uint64_t) * (size_t)s.T;
-    const size_t lds = lds_layout > lds_masks ? lds_layout : lds_masks;
+    int threads = 0;
+    const size_t lds = fused_ranks_lds(s, &threads);
     const dim3 grid((unsigned)(1 + s.T)), block(threads);
     if (s.T <= 8 * kWave) launch_ranks_copy<8>(a, L, grid, block, lds, stream);
     else launch_ranks_copy<32>(a, L, grid, block, lds, stream);
     return hipGetLastError();
+}
+
+size_t fused_ranks_lds(const Shape &s, int *threads) {
+    const int nvec = (int)((s.x_fmt == 1 ? (int64_t)s.H : 2 * (int64_t)s.H) / 16);
+    const int t = kWave * fused_rank_waves(s, nvec);
+    if (threads) *threads = t;
+    // block 0: the layout's staging; the other blocks: one rank mask per token
+    const size_t lds_layout = sizeof(int32_t) * ((size_t)s.T * s.k + s.E + s.R + s.N + t / kWave + 1);
+    const size_t lds_masks = sizeof(uint64_t) * (size_t)s.T;
+    return lds_layout > lds_masks ? lds_layout : lds_masks;
 }
 
 namespace {
@@ -658,8 +666,7 @@ hipError_t launch_dispatch_ranks_scan(const Shape &s, const WsLayout &L, const v
     a.algo = algo;
     // block 0: the totals; then the copy blocks (4 waves each)
     const int64_t blocks = 1 + (s.T * a.S + 3) / 4;
-    const size_t lds = sizeof(int32_t) * ((size_t)a.cols + 1 + 256 / kWave + 1);
-    launch_ranks_copy<0, true>(a, SmallLayout{}, dim3((unsigned)blocks), dim3(256), lds, stream);
+    launch_ranks_copy<0, true>(a, SmallLayout{}, dim3((unsigned)blocks), dim3(256), scan_copy_lds(s), stream);
     return hipGetLastError();
 }
 

@@ -19,7 +19,9 @@ from dataclasses import dataclass
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libep_hip.so")
+# EP_HIP_LIB: another build of the library to load (the CPU suite's
+# sanitizer run uses one built with host-side address / UB sanitizers)
+LIB_PATH = os.environ.get("EP_HIP_LIB") or os.path.join(_PKG, "libep_hip.so")
 
 EP_FMT_BF16, EP_FMT_FP8_S128, EP_FMT_MXFP8, EP_FMT_NVFP4 = 0, 1, 2, 3
 EP_OK, EP_EINVAL, EP_EALIGN, EP_EWORKSPACE, EP_EHIP, EP_EDEVICE = 0, -1, -2, -3, -4, -5
@@ -32,7 +34,7 @@ EXPORTED = (
     "ep_dispatch_ranks_cached", "ep_dispatch_ranks_with_layout", "ep_combine", "ep_check",
     "ep_dispatch_ranks", "ep_expert_reduce_ranks", "ep_combine_ranks", "ep_quant_fp8_s128",
     "ep_expert_scale_bf16", "ep_expert_requant_mxfp8", "ep_expert_requant_nvfp4", "ep_accounting",
-    "ep_calib_copy", "ep_stream", "ep_dispatch_with_layout_static",
+    "ep_calib_copy", "ep_stream", "ep_dispatch_with_layout_static", "ep_plan_info",
 )
 
 
@@ -88,6 +90,29 @@ class ep_accounting_t(ctypes.Structure):
         return {name: getattr(self, name) for name, _ in self._fields_}
 
 
+class ep_plan_info_t(ctypes.Structure):
+    _fields_ = [
+        ("workspace_bytes", ctypes.c_size_t),
+        ("region_offset", ctypes.c_size_t * 8),
+        ("region_bytes", ctypes.c_size_t * 8),
+        ("tiles", ctypes.c_int32),
+        ("tile_tokens", ctypes.c_int32),
+        ("tile_waves", ctypes.c_int32),
+        ("count_threads", ctypes.c_int32),
+        ("count_lds_bytes", ctypes.c_size_t),
+        ("single_launch_lds_bytes", ctypes.c_size_t),
+        ("single_launch_threads", ctypes.c_int32),
+        ("scan_copy_lds_bytes", ctypes.c_size_t),
+    ]
+
+    def as_dict(self):
+        out = {}
+        for name, _ in self._fields_:
+            v = getattr(self, name)
+            out[name] = list(v) if isinstance(v, ctypes.Array) else v
+        return out
+
+
 _lib = None
 
 
@@ -128,6 +153,7 @@ def load():
         "ep_calib_copy": (ctypes.c_int, [P, P, sz, P]),
         "ep_stream": (ctypes.c_int, [i32, P, P, sz, sz, i32, P]),
         "ep_dispatch_with_layout_static": (ctypes.c_int, [SP] + [P] * 15 + [P]),
+        "ep_plan_info": (ctypes.c_int, [SP, ctypes.POINTER(ep_plan_info_t)]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -137,6 +163,13 @@ def load():
         raise RuntimeError("libep_hip ABI version mismatch")
     _lib = lib
     return lib
+
+
+def plan_info(shape: ep_shape) -> dict:
+    """ep_plan_info: workspace regions, plan tiling and LDS per launch (host only)."""
+    info = ep_plan_info_t()
+    _ok(load().ep_plan_info(ctypes.byref(shape), ctypes.byref(info)), "ep_plan_info")
+    return info.as_dict()
 
 
 def strerror(rc: int) -> str:

@@ -466,6 +466,31 @@ int ep_accounting(const ep_shape *shape, int32_t own_node, const int32_t *num_to
                   const int32_t *num_tokens_per_node, int64_t rdma_algo_token_count,
                   int64_t valid_pairs, ep_accounting_t *out);
 
+/* ---- plan introspection (host only) --------------------------------------- */
+
+/* What the library will use for a shape, computed by the same functions its
+ * launchers use: the workspace regions (offset and bytes each needs; in this
+ * order: error word, tile counts, pair ranks inside their tiles, segment
+ * starts, (token, rank) masks, (token, rank) region starts, per-expert tile
+ * pairs, per-rank tile pairs -- a region a shape does not use has 0 bytes),
+ * the plan tiling, and the dynamic LDS bytes per workgroup of the launches
+ * that take it (0 where the shape does not use that launch): the count
+ * kernel, the single-launch layout + dispatch form (with its threads per
+ * workgroup) and the copy that scans the tile counts.  EP_EINVAL for a shape
+ * outside the supported range. */
+#define EP_PLAN_REGIONS 8
+typedef struct ep_plan_info_t {
+    size_t workspace_bytes;
+    size_t region_offset[EP_PLAN_REGIONS];
+    size_t region_bytes[EP_PLAN_REGIONS];
+    int32_t tiles, tile_tokens, tile_waves, count_threads;
+    size_t count_lds_bytes;
+    size_t single_launch_lds_bytes;
+    int32_t single_launch_threads;
+    size_t scan_copy_lds_bytes;
+} ep_plan_info_t;
+int ep_plan_info(const ep_shape *shape, ep_plan_info_t *info);
+
 /* ---- measurement helper --------------------------------------------------- */
 
 /* Plain device copy of `bytes` bytes (16-byte aligned pointers, bytes % 16

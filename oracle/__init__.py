@@ -39,6 +39,9 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "ep_oracle.c")
 _LIB_PATH = os.path.join(_HERE, "libep_oracle.so")
+# EP_ORACLE_LIB: load this build instead, as it is (the CPU suite's
+# sanitizer run builds one with address / UB sanitizers)
+_LIB_OVERRIDE = os.environ.get("EP_ORACLE_LIB")
 
 _lib = None
 
@@ -75,9 +78,12 @@ def _load():
     global _lib
     if _lib is not None:
         return _lib
-    if not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
-        build()
-    lib = ctypes.CDLL(_LIB_PATH)
+    if _LIB_OVERRIDE:
+        lib = ctypes.CDLL(_LIB_OVERRIDE)
+    else:
+        if not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
+            build()
+        lib = ctypes.CDLL(_LIB_PATH)
     P = ctypes.c_void_p
     i64, i32 = ctypes.c_int64, ctypes.c_int32
     sig = {
