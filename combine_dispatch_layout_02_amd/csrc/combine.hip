@@ -183,14 +183,20 @@ __global__ __launch_bounds__(256) void ep_combine_bf16_kernel(CombineArgs a) {
                     }
             }
         }
+        float flat[8 * C];
+#pragma unroll
+        for (int i = 0; i < C; ++i)
+#pragma unroll
+            for (int q = 0; q < 8; ++q) flat[8 * i + q] = acc[i][q];
+        uint32_t packed[4 * C];
+        pack_bf16(flat, packed);
 #pragma unroll
         for (int i = 0; i < C; ++i) {
             const int v = v0 + i * vstep;
             if (v >= vend) continue;
             vec16 o;
 #pragma unroll
-            for (int q = 0; q < 4; ++q)
-                o[q] = any_valid ? pack_bf16x2(acc[i][2 * q], acc[i][2 * q + 1]) : 0u;
+            for (int q = 0; q < 4; ++q) o[q] = any_valid ? packed[4 * i + q] : 0u;
             store_y<EP_COMBINE_Y_NT>(yrow + (int64_t)v * 16, o);
         }
     }
@@ -259,11 +265,13 @@ __global__ __launch_bounds__(256) void ep_combine_mxfp8_kernel(CombineArgs a) {
                 }
             }
         }
+        uint32_t packed[8];
+        pack_bf16(acc, packed);
         vec16 out[2];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-            out[0][q] = any_valid ? pack_bf16x2(acc[2 * q], acc[2 * q + 1]) : 0u;
-            out[1][q] = any_valid ? pack_bf16x2(acc[8 + 2 * q], acc[8 + 2 * q + 1]) : 0u;
+            out[0][q] = any_valid ? packed[q] : 0u;
+            out[1][q] = any_valid ? packed[4 + q] : 0u;
         }
         if (EP_COMBINE_Q_YT) {
             store_y_transposed<2>(ybuf[threadIdx.x / kWave], out, yrow, v0, a.nvec, lane);
@@ -340,12 +348,13 @@ __global__ __launch_bounds__(256) void ep_combine_nvfp4_kernel(CombineArgs a) {
                 }
             }
         }
+        uint32_t packed[16];
+        pack_bf16(acc, packed);
         vec16 out[4];
 #pragma unroll
         for (int o = 0; o < 4; ++o)
 #pragma unroll
-            for (int q = 0; q < 4; ++q)
-                out[o][q] = any_valid ? pack_bf16x2(acc[8 * o + 2 * q], acc[8 * o + 2 * q + 1]) : 0u;
+            for (int q = 0; q < 4; ++q) out[o][q] = any_valid ? packed[4 * o + q] : 0u;
         if (EP_COMBINE_Q_YT) {
             store_y_transposed<4>(ybuf[threadIdx.x / kWave], out, yrow, v0, a.nvec, lane);
         } else if (in_row) {

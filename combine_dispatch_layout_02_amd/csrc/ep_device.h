@@ -39,6 +39,39 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
     return f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
 }
 
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// The same two narrowings by gfx950's v_cvt_pk_bf16_f32 (one instruction):
+// round to nearest even, bit for bit f32_to_bf16 on every non-NaN binary32
+// (checked over all 2^32 patterns on MI355X); a NaN keeps its payload
+// (quieted) instead of becoming 0x7FC0, so it is used only where no input is
+// NaN (pack_bf16).
+__device__ __forceinline__ uint32_t pack_bf16x2_cvt(float lo, float hi) {
+    const f32x2_t v = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+}
+
+// M binary32 values of a lane (M even) -> M / 2 bf16 pairs, the even value in
+// the low half.  When no lane of the wave holds a NaN, by the packing
+// instruction; else by f32_to_bf16 (NaN -> 0x7FC0).  The test: the fp32 sum
+// of a lane's values is NaN when one of them is (and when +inf meets -inf,
+// which only sends the wave down the exact path).  Called by the whole wave:
+// the choice is wave-uniform.
+template <int M>
+__device__ __forceinline__ void pack_bf16(const float (&v)[M], uint32_t (&out)[M / 2]) {
+    float s = v[0];
+#pragma unroll
+    for (int i = 1; i < M; ++i) s += v[i];
+    if (__ballot(s != s) == 0) {
+#pragma unroll
+        for (int i = 0; i < M / 2; ++i) out[i] = pack_bf16x2_cvt(v[2 * i], v[2 * i + 1]);
+    } else {
+#pragma unroll
+        for (int i = 0; i < M / 2; ++i) out[i] = pack_bf16x2(v[2 * i], v[2 * i + 1]);
+    }
+}
+
 // ---------------------------------------------------------------- e4m3
 
 // binary32 -> e4m3 byte (RNE, saturating).
@@ -146,7 +179,7 @@ __device__ __forceinline__ float readlane<float>(float v, int lane) {
     return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
 }
 
-typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef f32x2_t f32x2;
 
 // 16-byte vector type used for every row copy (one global_load/store_dwordx4).
 typedef uint32_t vec16 __attribute__((ext_vector_type(4)));

@@ -474,13 +474,20 @@ __global__ __launch_bounds__(256) void ep_combine_ranks_kernel(RankCombineArgs a
                     }
             }
         }
+        float flat[8 * C];
+#pragma unroll
+        for (int i = 0; i < C; ++i)
+#pragma unroll
+            for (int q = 0; q < 8; ++q) flat[8 * i + q] = acc[i][q];
+        uint32_t packed[4 * C];
+        pack_bf16(flat, packed);
 #pragma unroll
         for (int i = 0; i < C; ++i) {
             const int v = v0 + i * stride;
             if (v >= a.nvec) continue;
             vec16 o;
 #pragma unroll
-            for (int q = 0; q < 4; ++q) o[q] = live ? pack_bf16x2(acc[i][2 * q], acc[i][2 * q + 1]) : 0u;
+            for (int q = 0; q < 4; ++q) o[q] = live ? packed[4 * i + q] : 0u;
             if (EP_RANKS_Y_NT) st16_nt(yrow + (int64_t)v * 16, o);
             else st16(yrow + (int64_t)v * 16, o);
         }
