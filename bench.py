@@ -650,45 +650,48 @@ def stream_ceilings(hev, stream, dev) -> dict:
     """The box's streaming read, write and copy rates (GB/s): CEIL_LAUNCHES
     back-to-back launches of ep_stream alternating over two sets of 1 GiB
     buffers, so the cache holds nothing a launch reuses and the dirty lines
-    each launch leaves are written back during the next one; best over the
-    launch shapes CEIL_SHAPES (chunk bytes x waves) and over plain /
-    non-temporal accesses."""
+    each launch leaves are written back during the next one.  Each of read,
+    write and copy is timed with plain and with non-temporal accesses, best
+    over the launch shapes CEIL_SHAPES (chunk bytes x waves); "read", "write"
+    and "copy" are the better of the two."""
     import torch
 
     from combine_dispatch_layout_02_amd import ep
 
     bufs = [torch.empty(CEIL_BYTES, dtype=torch.uint8, device=dev) for _ in range(4)]
     sink = torch.empty(256, dtype=torch.uint8, device=dev)
-    kinds = {"read": (ep.EP_STREAM_READ, ep.EP_STREAM_READ_NT), "write": (ep.EP_STREAM_WRITE, ep.EP_STREAM_WRITE_NT),
-             "copy": (ep.EP_STREAM_COPY, ep.EP_STREAM_COPY_NT)}
+    kinds = {"read": ep.EP_STREAM_READ, "read_nt": ep.EP_STREAM_READ_NT, "write": ep.EP_STREAM_WRITE,
+             "write_nt": ep.EP_STREAM_WRITE_NT, "copy": ep.EP_STREAM_COPY, "copy_nt": ep.EP_STREAM_COPY_NT}
     best = {}
-    for name, ks in kinds.items():
-        for kind in ks:
-            for chunk, waves in CEIL_SHAPES:
-                def launch(i):
-                    a, b = (bufs[0], bufs[1]) if i % 2 == 0 else (bufs[2], bufs[3])
-                    if name == "read":
-                        ep.ep_stream(kind, a, sink, CEIL_BYTES, chunk, waves)
-                    elif name == "write":
-                        ep.ep_stream(kind, None, a, CEIL_BYTES, chunk, waves)
-                    else:
-                        ep.ep_stream(kind, a, b, CEIL_BYTES, chunk, waves)
-                launch(1)
-                a0, a1 = hev.create(2)
-                torch.cuda.synchronize()
-                hev.record(a0, stream)
-                for i in range(CEIL_LAUNCHES):
-                    launch(i)
-                hev.record(a1, stream)
-                torch.cuda.synchronize()
-                moved = CEIL_BYTES * CEIL_LAUNCHES * (2 if name == "copy" else 1)
-                gbs = moved / (hev.ms(a0, a1) * 1e-3) / 1e9
-                hev.destroy([a0, a1])
-                if name not in best or gbs > best[name]["gbs"]:
-                    best[name] = {"gbs": round(gbs, 1), "chunk_bytes": chunk, "waves": waves,
-                                  "non_temporal": kind % 2 == 1}
+    for name, kind in kinds.items():
+        cls = name.split("_")[0]
+        for chunk, waves in CEIL_SHAPES:
+            def launch(i):
+                a, b = (bufs[0], bufs[1]) if i % 2 == 0 else (bufs[2], bufs[3])
+                if cls == "read":
+                    ep.ep_stream(kind, a, sink, CEIL_BYTES, chunk, waves)
+                elif cls == "write":
+                    ep.ep_stream(kind, None, a, CEIL_BYTES, chunk, waves)
+                else:
+                    ep.ep_stream(kind, a, b, CEIL_BYTES, chunk, waves)
+            launch(1)
+            a0, a1 = hev.create(2)
+            torch.cuda.synchronize()
+            hev.record(a0, stream)
+            for i in range(CEIL_LAUNCHES):
+                launch(i)
+            hev.record(a1, stream)
+            torch.cuda.synchronize()
+            moved = CEIL_BYTES * CEIL_LAUNCHES * (2 if cls == "copy" else 1)
+            gbs = moved / (hev.ms(a0, a1) * 1e-3) / 1e9
+            hev.destroy([a0, a1])
+            if name not in best or gbs > best[name]["gbs"]:
+                best[name] = {"gbs": round(gbs, 1), "chunk_bytes": chunk, "waves": waves}
     del bufs
-    return best
+    out = {cls: dict(max((best[cls], best[cls + "_nt"]), key=lambda v: v["gbs"]),
+                     non_temporal=best[cls + "_nt"]["gbs"] > best[cls]["gbs"]) for cls in ("read", "write", "copy")}
+    out["by_kind"] = best
+    return out
 
 
 def mix_ceiling(read_bytes: float, write_bytes: float, ceil: dict) -> float:

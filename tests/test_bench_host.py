@@ -87,3 +87,23 @@ def test_more_than_one_gpu_is_refused():
                        text=True, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stdout
+
+
+def test_mix_ceiling_weights_the_read_and_write_rates():
+    b = _bench()
+    ceil = {"read": {"gbs": 6000.0}, "write": {"gbs": 4000.0}}
+    assert b.mix_ceiling(1e9, 0.0, ceil) == 6000.0
+    assert b.mix_ceiling(0.0, 1e9, ceil) == 4000.0
+    # half and half: the bus time of each share, one after the other
+    mixed = b.mix_ceiling(1e9, 1e9, ceil)
+    assert abs(mixed - 2e9 / (1e9 / 6000.0 + 1e9 / 4000.0)) < 1e-6
+    assert 4000.0 < mixed < 6000.0
+    assert b.mix_ceiling(0.0, 0.0, ceil) == 0.0
+
+
+def test_host_cores_follows_the_job_share(monkeypatch):
+    b = _bench()
+    monkeypatch.setenv("OMP_NUM_THREADS", "3")
+    assert b.host_cores() == min(3, len(os.sched_getaffinity(0)))
+    monkeypatch.setenv("OMP_NUM_THREADS", "")
+    assert b.host_cores() == len(os.sched_getaffinity(0))
