@@ -199,8 +199,13 @@ int ep_dispatch(const ep_shape *shape, const void *x, const float *x_scales,
  * computes the layout counts and the segment starts while every other wave
  * finds its token's slots by counting the pairs that sort before them (the
  * stable counting sort's position); results are identical to the two calls.
- * Larger batches run the layout launches then the copy.  Afterwards the
- * workspace holds no plan that ep_dispatch_from_layout may reuse.
+ * Larger batches of up to 256 plan tiles (T * k <= 262144 pairs) run two
+ * launches: the count kernel, which also writes per (expert, tile) the
+ * tile's pairs of smaller experts and of the expert, and the copy, whose
+ * waves rebuild each slot's position from those sums and whose first block
+ * writes the layout totals.  Beyond that: the two layout launches, then the
+ * copy.  Afterwards the workspace holds no plan that ep_dispatch_from_layout
+ * may reuse.
  * Arguments: as ep_dispatch_layout and ep_dispatch.
  */
 int ep_dispatch_with_layout(const ep_shape *shape, const void *x, const float *x_scales,
@@ -331,8 +336,11 @@ int ep_dispatch_ranks(const ep_shape *shape, const void *x, const float *x_scale
  * computes the layout counts and the region starts while every other block
  * (one token) finds the token's rows by counting the tokens and ranks that
  * come before them; results are identical to the two calls.  Larger batches
- * run the layout launches, then the copy.  Afterwards the workspace holds no
- * plan that ep_dispatch_ranks may reuse.  Arguments: as ep_dispatch_layout
+ * of up to 256 plan tiles run two launches (the count kernel, which also
+ * writes per (rank, tile) the tile's tokens of smaller ranks and of the
+ * rank, then the copy, which sums them); beyond that, the two layout
+ * launches, then the copy.  Afterwards the workspace holds no plan that
+ * ep_dispatch_ranks may reuse.  Arguments: as ep_dispatch_layout
  * and ep_dispatch_ranks.
  */
 int ep_dispatch_ranks_with_layout(const ep_shape *shape, const void *x, const float *x_scales,
