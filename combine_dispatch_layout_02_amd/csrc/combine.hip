@@ -75,6 +75,17 @@ constexpr int kSlotBatch = 8;
                                // 2 cached tokens interleaved with the others
 #endif
 
+#ifndef EP_COMBINE_Q_OCC
+#define EP_COMBINE_Q_OCC 5     // mxfp8 / nvfp4: waves per SIMD the register allocation must allow (0: free)
+#endif
+#if EP_COMBINE_Q_OCC > 0
+#define EP_Q_OCC_ATTR __attribute__((amdgpu_waves_per_eu(EP_COMBINE_Q_OCC)))
+#else
+#define EP_Q_OCC_ATTR
+#endif
+#ifndef EP_COMBINE_Q_PIN
+#define EP_COMBINE_Q_PIN 1     // mxfp8 / nvfp4: where the batch's loads are pinned (pin_loads)
+#endif
 #ifndef EP_COMBINE_Q_YT
 #define EP_COMBINE_Q_YT 1      // mxfp8 / nvfp4: y through a per-wave LDS transpose, non-temporal
                                // (0: plain stores of each lane's pieces)
@@ -202,6 +213,68 @@ __global__ __launch_bounds__(256) void ep_combine_bf16_kernel(CombineArgs a) {
     }
 }
 
+// The token's unmasked slots, in slot order, as wave-uniform lane indices:
+// `m` holds the lanes (slots) not yet taken.  Skipping a masked slot is what
+// the fma chain does, so running over the unmasked slots alone, in order,
+// changes no result; the first of them starts the chain, where
+// fmaf(w, x, -0.0f) equals w * x, so no accumulator is set to -0.0 first.
+// Once `m` is empty it returns lane 63, whose slot is -1 (k <= 32).
+__device__ __forceinline__ int next_slot_lane(uint64_t &m) {
+    const int l = __builtin_ctzll(m | (1ull << 63));
+    m &= m - 1;
+    return l;
+}
+
+// An empty asm statement that uses every loaded value of a batch.  Without a
+// use outside the per-slot branches the compiler sinks each slot's loads into
+// that slot's branch, behind the previous slot's fmas, and the batch's loads
+// are no longer in flight together.  EP_COMBINE_Q_PIN 0 places the use before
+// the fmas (they wait for the whole batch), 1 after them (each waits for its
+// own slot; the loaded registers stay live to the end).
+template <int KB>
+__device__ __forceinline__ void pin_loads(const vec16 (&buf)[KB], const uint32_t (&sc)[KB]) {
+#pragma unroll
+    for (int jj = 0; jj < KB; ++jj) asm volatile("" ::"v"(buf[jj]), "v"(sc[jj]));
+}
+
+// One batch of up to KB unmasked slots of an mxfp8 row vector v: every load
+// first, then the fmas of the `live` slots in order.  The row and scale-row
+// bases are wave-uniform, so each load is a scalar base plus the lane's
+// 32-bit offset.
+template <int KB, bool FIRST>
+__device__ __forceinline__ void mxfp8_batch(const CombineArgs &a, int32_t slot, float wt, uint64_t &m, int live,
+                                            int v, float (&acc)[16]) {
+    const int G32 = a.H / 32;
+    vec16 buf[KB];
+    uint32_t sc[KB];
+    int ln[KB];
+#pragma unroll
+    for (int jj = 0; jj < KB; ++jj) {
+        ln[jj] = next_slot_lane(m);
+        const int64_t r = row_of(readlane(slot, ln[jj]));
+        buf[jj] = ld16_nt(a.eo + r * a.row_bytes + (uint32_t)v * 16u);
+        sc[jj] = (a.eo_scales + r * G32)[(uint32_t)v >> 1];
+    }
+    if (EP_COMBINE_Q_PIN == 0) pin_loads<KB>(buf, sc);
+#pragma unroll
+    for (int jj = 0; jj < KB; ++jj) {
+        if (jj >= live) break;
+        const float w = readlane(wt, ln[jj]);
+        const float scale = e8m0_to_f32(sc[jj]);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            // e4m3 bytes 0,1 and 2,3 of the dword, each times the scale
+            const f32x2 lo = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(buf[jj][q], scale, false);
+            const f32x2 hi = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(buf[jj][q], scale, true);
+            const float e[4] = {lo.x, lo.y, hi.x, hi.y};
+#pragma unroll
+            for (int b = 0; b < 4; ++b)
+                acc[4 * q + b] = (FIRST && jj == 0) ? w * e[b] : __builtin_fmaf(w, e[b], acc[4 * q + b]);
+        }
+    }
+    if (EP_COMBINE_Q_PIN == 1) pin_loads<KB>(buf, sc);
+}
+
 // mxfp8 rows: a 16-byte vector holds 16 e4m3 elements, half of a 32-element
 // scale group; the y row vectors for it are two 16-byte bf16 vectors.  The
 // element value e4m3(q) * 2^(e8m0 - 127) comes from gfx950's
@@ -210,7 +283,7 @@ __global__ __launch_bounds__(256) void ep_combine_bf16_kernel(CombineArgs a) {
 // subnormal codes and the subnormal scale 2^-127 included -- which the GPU
 // parity test over every (code, scale) pair checks through this kernel.
 template <int KC>
-__global__ __launch_bounds__(256) void ep_combine_mxfp8_kernel(CombineArgs a) {
+__global__ __launch_bounds__(256) EP_Q_OCC_ATTR void ep_combine_mxfp8_kernel(CombineArgs a) {
     constexpr int KB = KC > 0 ? KC : kSlotBatch;
     const int lane = threadIdx.x & (kWave - 1);
     const int64_t gw = (int64_t)blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
@@ -226,52 +299,33 @@ __global__ __launch_bounds__(256) void ep_combine_mxfp8_kernel(CombineArgs a) {
         wt = a.topk_w[t * k + lane];
         if ((uint64_t)slot >= (uint64_t)a.rows) slot = -1;   // outside the receive rows: masked
     }
-    const bool any_valid = __ballot(lane < k && slot >= 0) != 0;
+    const uint64_t valid = __ballot(lane < k && slot >= 0);
+    const int nvalid = __popcll(valid);
     char *yrow = a.y + t * (int64_t)a.H * 2;
     const int stride = kWave * a.S;
-    const int G32 = a.H / 32;
 
     __shared__ vec16 ybuf[4][2 * kWave];   // per wave of the block (EP_COMBINE_Q_YT)
     for (int v0 = kWave * sub; v0 < a.nvec; v0 += stride) {   // uniform passes
         // lanes past the row re-read its last vector and store nothing
         const bool in_row = v0 + lane < a.nvec;
         const int v = in_row ? v0 + lane : a.nvec - 1;
-        float acc[16];
-#pragma unroll
-        for (int q = 0; q < 16; ++q) acc[q] = -0.0f;
-        for (int jb = 0; jb < k; jb += KB) {
-            vec16 buf[KB];
-            uint32_t sc[KB];
-#pragma unroll
-            for (int jj = 0; jj < KB; ++jj) {
-                const int64_t r = row_of(readlane(slot, jb + jj));
-                buf[jj] = ld16_nt(a.eo + r * a.row_bytes + (int64_t)v * 16);
-                sc[jj] = a.eo_scales[r * G32 + (v >> 1)];
-            }
-#pragma unroll
-            for (int jj = 0; jj < KB; ++jj) {
-                if (readlane(slot, jb + jj) < 0) continue;
-                const float w = readlane(wt, jb + jj);
-                const float scale = e8m0_to_f32(sc[jj]);
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    // e4m3 bytes 0,1 and 2,3 of the dword, each times the scale
-                    const f32x2 lo = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(buf[jj][q], scale, false);
-                    const f32x2 hi = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(buf[jj][q], scale, true);
-                    acc[4 * q + 0] = __builtin_fmaf(w, lo.x, acc[4 * q + 0]);
-                    acc[4 * q + 1] = __builtin_fmaf(w, lo.y, acc[4 * q + 1]);
-                    acc[4 * q + 2] = __builtin_fmaf(w, hi.x, acc[4 * q + 2]);
-                    acc[4 * q + 3] = __builtin_fmaf(w, hi.y, acc[4 * q + 3]);
-                }
-            }
-        }
-        uint32_t packed[8];
-        pack_bf16(acc, packed);
         vec16 out[2];
+        if (nvalid == 0) {   // no valid slot: +0.0
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            out[0][q] = any_valid ? packed[q] : 0u;
-            out[1][q] = any_valid ? packed[4 + q] : 0u;
+            for (int q = 0; q < 4; ++q) out[0][q] = out[1][q] = 0u;
+        } else {
+            float acc[16];
+            uint64_t m = valid;
+            mxfp8_batch<KB, true>(a, slot, wt, m, min(nvalid, KB), v, acc);
+            if (KC == 0)   // k > KB is possible only for a run-time k
+                for (int jb = KB; jb < nvalid; jb += KB) mxfp8_batch<KB, false>(a, slot, wt, m, min(nvalid - jb, KB), v, acc);
+            uint32_t packed[8];
+            pack_bf16(acc, packed);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                out[0][q] = packed[q];
+                out[1][q] = packed[4 + q];
+            }
         }
         if (EP_COMBINE_Q_YT) {
             store_y_transposed<2>(ybuf[threadIdx.x / kWave], out, yrow, v0, a.nvec, lane);
@@ -282,6 +336,51 @@ __global__ __launch_bounds__(256) void ep_combine_mxfp8_kernel(CombineArgs a) {
     }
 }
 
+// One batch of up to KB unmasked slots of an nvfp4 row vector v (see
+// mxfp8_batch).  Element = e2m1 decoded at scale 1.0 (exact) times the
+// group's bf16 scale (exact: a 2-bit times an 8-bit significand); then one
+// fma by the weight.
+template <int KB, bool FIRST>
+__device__ __forceinline__ void nvfp4_batch(const CombineArgs &a, int32_t slot, float wt, uint64_t &m, int live,
+                                            int v, float (&acc)[32]) {
+    const int G16 = a.H / 16;
+    const uint16_t *scales = reinterpret_cast<const uint16_t *>(a.eo_scales);
+    vec16 buf[KB];
+    uint32_t sc[KB];
+    int ln[KB];
+#pragma unroll
+    for (int jj = 0; jj < KB; ++jj) {
+        ln[jj] = next_slot_lane(m);
+        const int64_t r = row_of(readlane(slot, ln[jj]));
+        buf[jj] = ld16_nt(a.eo + r * a.row_bytes + (uint32_t)v * 16u);
+        // the two bf16 scales of the vector's two 16-element groups
+        sc[jj] = *reinterpret_cast<const uint32_t *>(scales + r * G16 + 2u * (uint32_t)v);
+    }
+    if (EP_COMBINE_Q_PIN == 0) pin_loads<KB>(buf, sc);
+#pragma unroll
+    for (int jj = 0; jj < KB; ++jj) {
+        if (jj >= live) break;
+        const float w = readlane(wt, ln[jj]);
+        const float s_lo = bf16_lo(sc[jj]), s_hi = bf16_hi(sc[jj]);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const float s = q < 2 ? s_lo : s_hi;   // dwords 0-1: group 2v, 2-3: group 2v+1
+            // byte b of the dword holds elements 2b (low nibble) and 2b + 1
+            const f32x2 e0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(buf[jj][q], 1.0f, 0);
+            const f32x2 e1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(buf[jj][q], 1.0f, 1);
+            const f32x2 e2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(buf[jj][q], 1.0f, 2);
+            const f32x2 e3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(buf[jj][q], 1.0f, 3);
+            const float ev[8] = {e0.x, e0.y, e1.x, e1.y, e2.x, e2.y, e3.x, e3.y};
+#pragma unroll
+            for (int b = 0; b < 8; ++b) {
+                const float x = ev[b] * s;
+                acc[8 * q + b] = (FIRST && jj == 0) ? w * x : __builtin_fmaf(w, x, acc[8 * q + b]);
+            }
+        }
+    }
+    if (EP_COMBINE_Q_PIN == 1) pin_loads<KB>(buf, sc);
+}
+
 // nvfp4 rows: a 16-byte vector holds 32 e2m1 elements (two 16-element scale
 // groups, one bf16 scale each); the y row vectors for it are four 16-byte
 // bf16 vectors.  Elements decode with v_cvt_scalef32_pk_f32_fp4 at scale 1.0
@@ -290,7 +389,7 @@ __global__ __launch_bounds__(256) void ep_combine_mxfp8_kernel(CombineArgs a) {
 // used: it honours only the exponent of a scale, and these scales are not
 // powers of two.
 template <int KC>
-__global__ __launch_bounds__(256) void ep_combine_nvfp4_kernel(CombineArgs a) {
+__global__ __launch_bounds__(256) EP_Q_OCC_ATTR void ep_combine_nvfp4_kernel(CombineArgs a) {
     constexpr int KB = KC > 0 ? KC : kSlotBatch;
     const int lane = threadIdx.x & (kWave - 1);
     const int64_t gw = (int64_t)blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
@@ -306,55 +405,35 @@ __global__ __launch_bounds__(256) void ep_combine_nvfp4_kernel(CombineArgs a) {
         wt = a.topk_w[t * k + lane];
         if ((uint64_t)slot >= (uint64_t)a.rows) slot = -1;   // outside the receive rows: masked
     }
-    const bool any_valid = __ballot(lane < k && slot >= 0) != 0;
+    const uint64_t valid = __ballot(lane < k && slot >= 0);
+    const int nvalid = __popcll(valid);
     char *yrow = a.y + t * (int64_t)a.H * 2;
     const int stride = kWave * a.S;
-    const int G16 = a.H / 16;
-    const uint16_t *scales = reinterpret_cast<const uint16_t *>(a.eo_scales);
 
     __shared__ vec16 ybuf[4][4 * kWave];   // per wave of the block (EP_COMBINE_Q_YT)
     for (int v0 = kWave * sub; v0 < a.nvec; v0 += stride) {   // uniform passes
         // lanes past the row re-read its last vector and store nothing
         const bool in_row = v0 + lane < a.nvec;
         const int v = in_row ? v0 + lane : a.nvec - 1;
-        float acc[32];
-#pragma unroll
-        for (int q = 0; q < 32; ++q) acc[q] = -0.0f;
-        for (int jb = 0; jb < k; jb += KB) {
-            vec16 buf[KB];
-            uint32_t sc[KB];
-#pragma unroll
-            for (int jj = 0; jj < KB; ++jj) {
-                const int64_t r = row_of(readlane(slot, jb + jj));
-                buf[jj] = ld16_nt(a.eo + r * a.row_bytes + (int64_t)v * 16);
-                sc[jj] = *reinterpret_cast<const uint32_t *>(scales + r * G16 + 2 * v);   // two bf16
-            }
-#pragma unroll
-            for (int jj = 0; jj < KB; ++jj) {
-                if (readlane(slot, jb + jj) < 0) continue;
-                const float w = readlane(wt, jb + jj);
-                const float s_lo = bf16_lo(sc[jj]), s_hi = bf16_hi(sc[jj]);
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const float s = q < 2 ? s_lo : s_hi;   // dwords 0-1: group 2v, 2-3: group 2v+1
-                    // byte b of the dword holds elements 2b (low nibble) and 2b + 1
-                    const f32x2 e0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(buf[jj][q], 1.0f, 0);
-                    const f32x2 e1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(buf[jj][q], 1.0f, 1);
-                    const f32x2 e2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(buf[jj][q], 1.0f, 2);
-                    const f32x2 e3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(buf[jj][q], 1.0f, 3);
-                    const float ev[8] = {e0.x, e0.y, e1.x, e1.y, e2.x, e2.y, e3.x, e3.y};
-#pragma unroll
-                    for (int b = 0; b < 8; ++b) acc[8 * q + b] = __builtin_fmaf(w, ev[b] * s, acc[8 * q + b]);
-                }
-            }
-        }
-        uint32_t packed[16];
-        pack_bf16(acc, packed);
         vec16 out[4];
+        if (nvalid == 0) {   // no valid slot: +0.0
 #pragma unroll
-        for (int o = 0; o < 4; ++o)
+            for (int o = 0; o < 4; ++o)
 #pragma unroll
-            for (int q = 0; q < 4; ++q) out[o][q] = any_valid ? packed[4 * o + q] : 0u;
+                for (int q = 0; q < 4; ++q) out[o][q] = 0u;
+        } else {
+            float acc[32];
+            uint64_t m = valid;
+            nvfp4_batch<KB, true>(a, slot, wt, m, min(nvalid, KB), v, acc);
+            if (KC == 0)   // k > KB is possible only for a run-time k
+                for (int jb = KB; jb < nvalid; jb += KB) nvfp4_batch<KB, false>(a, slot, wt, m, min(nvalid - jb, KB), v, acc);
+            uint32_t packed[16];
+            pack_bf16(acc, packed);
+#pragma unroll
+            for (int o = 0; o < 4; ++o)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) out[o][q] = packed[4 * o + q];
+        }
         if (EP_COMBINE_Q_YT) {
             store_y_transposed<4>(ybuf[threadIdx.x / kWave], out, yrow, v0, a.nvec, lane);
         } else if (in_row) {
