@@ -83,6 +83,9 @@ constexpr int kSlotBatch = 8;
 #else
 #define EP_Q_OCC_ATTR
 #endif
+#ifndef EP_COMBINE_PIN
+#define EP_COMBINE_PIN 1       // bf16 rows: where the batch's loads are pinned (pin_loads)
+#endif
 #ifndef EP_COMBINE_Q_PIN
 #define EP_COMBINE_Q_PIN 1     // mxfp8 / nvfp4: where the batch's loads are pinned (pin_loads)
 #endif
@@ -132,87 +135,6 @@ __device__ __forceinline__ void store_y_transposed(vec16 *wbuf, const vec16 (&ou
 // FMAs are skipped, which keeps the masked-slot semantics exact.
 __device__ __forceinline__ int64_t row_of(int32_t s) { return s >= 0 ? (int64_t)s : 0; }
 
-// bf16 rows: a 16-byte vector holds 8 elements; C vectors per lane per pass,
-// KB slots per batch (k itself when k is a compile-time constant KC).
-template <int C, int KC>
-__global__ __launch_bounds__(256) void ep_combine_bf16_kernel(CombineArgs a) {
-    constexpr int KB = KC > 0 ? KC : kSlotBatch;
-    const int lane = threadIdx.x & (kWave - 1);
-    const int64_t gw = (int64_t)blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
-    const int64_t tw = gw / a.S;
-    const int sub = (int)(gw - tw * a.S);
-    if (tw >= a.T) return;
-    const int64_t t = EP_COMBINE_ORDER == 1 ? a.T - 1 - tw
-                      : EP_COMBINE_ORDER == 2 ? interleaved_token(tw, a.T, a.cached) : tw;
-    const int k = KC > 0 ? KC : a.k;
-
-    int32_t slot = -1;
-    float wt = 0.0f;
-    if (lane < k) {
-        slot = a.token_slot[t * k + lane];
-        wt = a.topk_w[t * k + lane];
-        if ((uint64_t)slot >= (uint64_t)a.rows) slot = -1;   // outside the receive rows: masked
-    }
-    const bool any_valid = __ballot(lane < k && slot >= 0) != 0;
-    char *yrow = a.y + t * (int64_t)a.H * 2;
-    const int stride = kWave * a.S;
-
-    // vectors of this wave: interleaved with the token's other waves, or one
-    // contiguous part of the row per wave
-    const int per = (a.nvec + a.S - 1) / a.S;
-    const int vbeg = EP_COMBINE_CONTIG ? sub * per + lane : lane + kWave * sub;
-    const int vend = EP_COMBINE_CONTIG ? min(a.nvec, (sub + 1) * per) : a.nvec;
-    const int vstep = EP_COMBINE_CONTIG ? kWave : stride;
-    for (int v0 = vbeg; v0 < vend; v0 += vstep * C) {
-        float acc[C][8];
-#pragma unroll
-        for (int i = 0; i < C; ++i)
-#pragma unroll
-            for (int q = 0; q < 8; ++q) acc[i][q] = -0.0f;
-
-        for (int jb = 0; jb < k; jb += KB) {
-            vec16 buf[KB][C];
-#pragma unroll
-            for (int jj = 0; jj < KB; ++jj) {
-                const char *row = a.eo + row_of(readlane(slot, jb + jj)) * a.row_bytes;
-#pragma unroll
-                for (int i = 0; i < C; ++i) {
-                    const int v = v0 + i * vstep;
-                    if (v < vend) buf[jj][i] = ld16_nt(row + (int64_t)v * 16);
-                }
-            }
-#pragma unroll
-            for (int jj = 0; jj < KB; ++jj) {
-                if (readlane(slot, jb + jj) < 0) continue;   // masked (or past k): uniform skip
-                const float w = readlane(wt, jb + jj);
-#pragma unroll
-                for (int i = 0; i < C; ++i)
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        acc[i][2 * q] = __builtin_fmaf(w, bf16_lo(buf[jj][i][q]), acc[i][2 * q]);
-                        acc[i][2 * q + 1] = __builtin_fmaf(w, bf16_hi(buf[jj][i][q]), acc[i][2 * q + 1]);
-                    }
-            }
-        }
-        float flat[8 * C];
-#pragma unroll
-        for (int i = 0; i < C; ++i)
-#pragma unroll
-            for (int q = 0; q < 8; ++q) flat[8 * i + q] = acc[i][q];
-        uint32_t packed[4 * C];
-        pack_bf16(flat, packed);
-#pragma unroll
-        for (int i = 0; i < C; ++i) {
-            const int v = v0 + i * vstep;
-            if (v >= vend) continue;
-            vec16 o;
-#pragma unroll
-            for (int q = 0; q < 4; ++q) o[q] = any_valid ? packed[4 * i + q] : 0u;
-            store_y<EP_COMBINE_Y_NT>(yrow + (int64_t)v * 16, o);
-        }
-    }
-}
-
 // The token's unmasked slots, in slot order, as wave-uniform lane indices:
 // `m` holds the lanes (slots) not yet taken.  Skipping a masked slot is what
 // the fma chain does, so running over the unmasked slots alone, in order,
@@ -235,6 +157,107 @@ template <int KB>
 __device__ __forceinline__ void pin_loads(const vec16 (&buf)[KB], const uint32_t (&sc)[KB]) {
 #pragma unroll
     for (int jj = 0; jj < KB; ++jj) asm volatile("" ::"v"(buf[jj]), "v"(sc[jj]));
+}
+template <int KB, int C>
+__device__ __forceinline__ void pin_loads2(const vec16 (&buf)[KB][C]) {
+#pragma unroll
+    for (int jj = 0; jj < KB; ++jj)
+#pragma unroll
+        for (int i = 0; i < C; ++i) asm volatile("" ::"v"(buf[jj][i]));
+}
+
+// One batch of up to KB unmasked slots of a bf16 pass (C vectors per lane,
+// v0 + i * vstep, those below vend): every load first, then the fmas of the
+// `live` slots in order (see next_slot_lane, pin_loads).
+template <int KB, int C, bool FIRST>
+__device__ __forceinline__ void bf16_batch(const CombineArgs &a, int32_t slot, float wt, uint64_t &m, int live,
+                                           int v0, int vstep, int vend, float (&acc)[8 * C]) {
+    vec16 buf[KB][C];
+    int ln[KB];
+#pragma unroll
+    for (int jj = 0; jj < KB; ++jj) {
+        ln[jj] = next_slot_lane(m);
+        const char *row = a.eo + row_of(readlane(slot, ln[jj])) * a.row_bytes;
+#pragma unroll
+        for (int i = 0; i < C; ++i) {
+            const int v = v0 + i * vstep;
+            if (v < vend) buf[jj][i] = ld16_nt(row + (uint32_t)v * 16u);
+        }
+    }
+    if (EP_COMBINE_PIN == 0) pin_loads2<KB, C>(buf);
+#pragma unroll
+    for (int jj = 0; jj < KB; ++jj) {
+        if (jj >= live) break;
+        const float w = readlane(wt, ln[jj]);
+#pragma unroll
+        for (int i = 0; i < C; ++i)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const float lo = bf16_lo(buf[jj][i][q]), hi = bf16_hi(buf[jj][i][q]);
+                float &a0 = acc[8 * i + 2 * q], &a1 = acc[8 * i + 2 * q + 1];
+                a0 = (FIRST && jj == 0) ? w * lo : __builtin_fmaf(w, lo, a0);
+                a1 = (FIRST && jj == 0) ? w * hi : __builtin_fmaf(w, hi, a1);
+            }
+    }
+    if (EP_COMBINE_PIN == 1) pin_loads2<KB, C>(buf);
+}
+
+// bf16 rows: a 16-byte vector holds 8 elements; C vectors per lane per pass,
+// KB slots per batch (k itself when k is a compile-time constant KC).
+template <int C, int KC>
+__global__ __launch_bounds__(256) void ep_combine_bf16_kernel(CombineArgs a) {
+    constexpr int KB = KC > 0 ? KC : kSlotBatch;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int64_t gw = (int64_t)blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
+    const int64_t tw = gw / a.S;
+    const int sub = (int)(gw - tw * a.S);
+    if (tw >= a.T) return;
+    const int64_t t = EP_COMBINE_ORDER == 1 ? a.T - 1 - tw
+                      : EP_COMBINE_ORDER == 2 ? interleaved_token(tw, a.T, a.cached) : tw;
+    const int k = KC > 0 ? KC : a.k;
+
+    int32_t slot = -1;
+    float wt = 0.0f;
+    if (lane < k) {
+        slot = a.token_slot[t * k + lane];
+        wt = a.topk_w[t * k + lane];
+        if ((uint64_t)slot >= (uint64_t)a.rows) slot = -1;   // outside the receive rows: masked
+    }
+    const uint64_t valid = __ballot(lane < k && slot >= 0);
+    const int nvalid = __popcll(valid);
+    char *yrow = a.y + t * (int64_t)a.H * 2;
+    const int stride = kWave * a.S;
+
+    // vectors of this wave: interleaved with the token's other waves, or one
+    // contiguous part of the row per wave
+    const int per = (a.nvec + a.S - 1) / a.S;
+    const int vbeg = EP_COMBINE_CONTIG ? sub * per + lane : lane + kWave * sub;
+    const int vend = EP_COMBINE_CONTIG ? min(a.nvec, (sub + 1) * per) : a.nvec;
+    const int vstep = EP_COMBINE_CONTIG ? kWave : stride;
+    for (int v0 = vbeg; v0 < vend; v0 += vstep * C) {
+        uint32_t packed[4 * C];
+        if (nvalid == 0) {   // no valid slot: +0.0
+#pragma unroll
+            for (int q = 0; q < 4 * C; ++q) packed[q] = 0u;
+        } else {
+            float acc[8 * C];
+            uint64_t m = valid;
+            bf16_batch<KB, C, true>(a, slot, wt, m, min(nvalid, KB), v0, vstep, vend, acc);
+            if (KC == 0)   // k > KB is possible only for a run-time k
+                for (int jb = KB; jb < nvalid; jb += KB)
+                    bf16_batch<KB, C, false>(a, slot, wt, m, min(nvalid - jb, KB), v0, vstep, vend, acc);
+            pack_bf16(acc, packed);
+        }
+#pragma unroll
+        for (int i = 0; i < C; ++i) {
+            const int v = v0 + i * vstep;
+            if (v >= vend) continue;
+            vec16 o;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) o[q] = packed[4 * i + q];
+            store_y<EP_COMBINE_Y_NT>(yrow + (int64_t)v * 16, o);
+        }
+    }
 }
 
 // One batch of up to KB unmasked slots of an mxfp8 row vector v: every load
