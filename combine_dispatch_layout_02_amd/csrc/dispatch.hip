@@ -253,7 +253,7 @@ __global__ __launch_bounds__(KEYS ? 1024 : 256) void ep_dispatch_copy_kernel(Cop
     // row t, which does not depend on them; the plan lookups that need the
     // inputs are issued as soon as those arrive, while the row is still in
     // flight, instead of queueing behind the whole row.
-    int32_t lr = -1, slot_in = -1;
+    int32_t pw = -1, slot_in = -1;
     int64_t eid = -1;
     float wv = 0.0f;
     if (lane < a.k) {
@@ -263,7 +263,7 @@ __global__ __launch_bounds__(KEYS ? 1024 : 256) void ep_dispatch_copy_kernel(Cop
         } else {
             wv = a.topk_w[p];
             if (!FUSED) {
-                lr = a.local_rank[p];
+                pw = a.local_rank[p];   // the plan word: expert and local rank, or -1
                 eid = a.topk_idx[p];
             }
         }
@@ -285,6 +285,19 @@ __global__ __launch_bounds__(KEYS ? 1024 : 256) void ep_dispatch_copy_kernel(Cop
     for (int i = 0; i < VPL; ++i) {
         const int v = min(v_first + i * stride, a.nvec - 1);
         buf[i] = ld16(src + (int64_t)v * 16);
+    }
+
+    // The plan was made for the pair's expert: a pair whose expert in
+    // topk_idx is not the planned one (a plan reused with other ids) gets no
+    // slot, and the call raises kErrStalePlan.
+    int32_t lr = -1;
+    if (!FUSED && lane < a.k && !a.slots_in) {
+        const bool now_valid = eid >= 0 && eid < a.E;
+        if (pw >= 0 && now_valid && (pw >> kPlanLrBits) == (int32_t)eid) {
+            lr = pw & ((1 << kPlanLrBits) - 1);
+        } else if (pw >= 0 || now_valid) {   // planned but not valid now, valid but not planned, or moved
+            atomicOr(&a.ctrl[0], kErrStalePlan);
+        }
     }
 
     // lanes 0..k-1: the token's slots

@@ -14,8 +14,11 @@ namespace ep {
 //                                    the scan, the exclusive prefix of expert e
 //                                    over earlier tiles), rank and node token
 //                                    counts
-//   local_rank  : i32[T * k]         rank of a pair among the same-expert pairs
-//                                    of its tile that precede it (-1: masked)
+//   local_rank  : i32[T * k]         plan word of a pair: (expert << kPlanLrBits)
+//                                    | rank of the pair among the same-expert
+//                                    pairs of its tile that precede it; -1:
+//                                    masked.  A copy that reuses the plan
+//                                    checks the expert against topk_idx.
 //   plan_offset : i32[E + 1]         expert segment starts
 //   rank_mask   : u64[tiles][R][TW]  (token, rank) rows only: per tile, rank
 //                                    and 64-token wave of the tile (TW =
@@ -48,6 +51,8 @@ constexpr int kCtrlWords = 64;
 constexpr uint32_t kErrBadExpert = 0x1u;
 constexpr uint32_t kErrBadSlot = 0x2u;   // internal consistency check of the plan
 constexpr uint32_t kErrRankOverflow = 0x4u;
+constexpr uint32_t kErrStalePlan = 0x8u;   // topk_idx differs from the planned one
+constexpr int kPlanLrBits = 16;            // local ranks < pairs per tile <= 2^16; experts < 2^15
 
 struct Shape {
     int64_t T;

@@ -124,7 +124,7 @@ __global__ __launch_bounds__(1024) void ep_plan_count_kernel(CountArgs a) {
                 for (int q = 0; q < 4; ++q) r += (w0 + q < w) ? (int32_t)__popcll(m[q]) : 0;
             }
         }
-        a.local_rank[t0 * k + tid] = r;
+        a.local_rank[t0 * k + tid] = r >= 0 ? (e << kPlanLrBits) | r : -1;   // the plan word
     }
     int32_t *tc = a.tile_count + (size_t)blockIdx.x * (E + a.R + a.N);
     const bool single = gridDim.x == 1;   // the whole batch is this tile

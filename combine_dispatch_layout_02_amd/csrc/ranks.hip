@@ -234,6 +234,11 @@ __global__ __launch_bounds__(TOK ? 1024 : 256) void ep_dispatch_ranks_kernel(Ran
         const int wt = pos >> 6, bit = pos & 63;
         int32_t start = 0, lr = 0;
         bool reached = false;
+        int re = -1;   // rank of slot `lane`'s expert by topk_idx (lanes < k)
+        if (lane < a.k) {
+            const int64_t e = a.topk_idx[t * a.k + lane];
+            if (e >= 0 && e < a.E) re = a.epr_shift >= 0 ? (int)(e >> a.epr_shift) : (int)(e / a.epr);
+        }
         if (lane < a.R) {
             const uint64_t *m = a.rank_mask + ((size_t)tile * a.R + lane) * a.TW;
             // every lookup is independent of the others: one memory round trip
@@ -243,7 +248,20 @@ __global__ __launch_bounds__(TOK ? 1024 : 256) void ep_dispatch_ranks_kernel(Ran
             for (int i = 0; i < wt; ++i) lr += (int32_t)__popcll(m[i]);
             reached = (mw >> bit) & 1u;
         }
-        if (SCAN) start = rank_bases(a, __ballot(reached), (int)tile, lane);
+        // The plan's rank set for t must be the one topk_idx gives now; a
+        // plan reused with other ids gets no rows for t, and the call raises
+        // kErrStalePlan.
+        uint64_t planned = __ballot(reached), now = 0;
+        for (int j = 0; j < a.k; ++j) {
+            const int rj = readlane(re, j);
+            if (rj >= 0) now |= 1ull << rj;
+        }
+        if (now != planned) {   // wave-uniform
+            if (lane == 0) atomicOr(&a.ctrl[0], kErrStalePlan);
+            reached = false;
+            planned = 0;
+        }
+        if (SCAN) start = rank_bases(a, planned, (int)tile, lane);
         if (lane < a.R) {
             if (reached) {
                 slot = start + lr;

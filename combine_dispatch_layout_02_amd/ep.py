@@ -26,6 +26,8 @@ LIB_PATH = os.environ.get("EP_HIP_LIB") or os.path.join(_PKG, "libep_hip.so")
 EP_FMT_BF16, EP_FMT_FP8_S128, EP_FMT_MXFP8, EP_FMT_NVFP4 = 0, 1, 2, 3
 EP_OK, EP_EINVAL, EP_EALIGN, EP_EWORKSPACE, EP_EHIP, EP_EDEVICE = 0, -1, -2, -3, -4, -5
 EP_STATIC_SCRATCH_BYTES = 16 << 20   # the static scratch of ep_dispatch_with_layout_static
+# device error flags (ep_check): bad expert id, internal slot check, RANK_MAJOR overflow, stale plan
+EP_ERRFLAG_BAD_EXPERT, EP_ERRFLAG_BAD_SLOT, EP_ERRFLAG_RANK_OVERFLOW, EP_ERRFLAG_STALE_PLAN = 0x1, 0x2, 0x4, 0x8
 
 # every symbol include/ep.h declares
 EXPORTED = (
@@ -159,7 +161,7 @@ def load():
         fn = getattr(lib, name)
         fn.restype = res
         fn.argtypes = args
-    if lib.ep_abi_version() != 6:
+    if lib.ep_abi_version() != 7:
         raise RuntimeError("libep_hip ABI version mismatch")
     _lib = lib
     return lib

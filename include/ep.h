@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define EP_ABI_VERSION 6
+#define EP_ABI_VERSION 7
 
 /* Status codes. */
 enum ep_status {
@@ -71,6 +71,8 @@ enum ep_status {
 #define EP_ERRFLAG_BAD_EXPERT 0x1u
 #define EP_ERRFLAG_BAD_SLOT   0x2u   /* internal: a computed slot fell outside the receive rows (skipped) */
 #define EP_ERRFLAG_RANK_OVERFLOW 0x4u /* RANK_MAJOR: a rank received more pairs than rank_capacity (dropped) */
+#define EP_ERRFLAG_STALE_PLAN 0x8u    /* a dispatch reusing the layout call's plan met a topk_idx that differs
+                                         from the planned one (the pairs / tokens concerned get no rows) */
 
 /* Payload formats. */
 enum ep_format {
@@ -252,7 +254,10 @@ int ep_dispatch_with_layout_static(const ep_shape *shape, const void *x, const f
  * launches.  The pages' cached dispatch ([PR860] cached_notify /
  * previous_handle) reuses a layout the same way.  Calling it without that
  * preceding layout call, or with a different topk_idx, gives unspecified
- * slots (the kernel still never writes outside [0, T*k) rows).
+ * slots (the kernel still never writes outside [0, T*k) rows).  The plan
+ * keeps each pair's expert, and the copy checks it against topk_idx: a pair
+ * whose expert (or validity) differs from the planned one gets slot -1 and
+ * no row, and the call raises EP_ERRFLAG_STALE_PLAN (ep_check).
  */
 int ep_dispatch_from_layout(const ep_shape *shape, const void *x, const float *x_scales,
                             const int64_t *topk_idx, const float *topk_w,
@@ -310,7 +315,10 @@ int ep_combine(const ep_shape *shape, const void *expert_out, const uint8_t *exp
  * ep_dispatch_layout call with the same shape, workspace and topk_idx left
  * in the workspace (stream-ordered before this call); without it the rows
  * are unspecified (the kernel still never writes outside the T*min(k,R)
- * receive rows).
+ * receive rows).  The copy checks each token's planned rank set against
+ * the one topk_idx gives: a token whose set differs gets no rows (its
+ * token_rank_slot entries are -1), and the call raises
+ * EP_ERRFLAG_STALE_PLAN (ep_check).
  *   x, x_scales, topk_idx, topk_w: as for ep_dispatch
  *   recv_x         [T*min(k,R), row] bf16 or e4m3 rows, 16-byte aligned; row
  *                  s < rank_offset[R] is a bitwise copy of x[recv_src_idx[s]]

@@ -35,10 +35,22 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_strerror(lib):
-    assert lib.ep_abi_version() == 6
+    assert lib.ep_abi_version() == 7
     for rc in (0, -1, -2, -3, -4, -5):
         assert ep.strerror(rc)
     assert "unknown" in ep.strerror(-99)
+
+
+def test_header_constants_match_binding():
+    """Status codes, formats and device error flags: the values ep.h defines
+    are the ones the binding uses."""
+    src = open(os.path.join(ROOT, "include", "ep.h")).read()
+    defines = {n: int(v, 0) for n, v in re.findall(r"#define (EP_ERRFLAG_[A-Z_]+)\s+(0x[0-9a-fA-F]+)u", src)}
+    enums = {n: int(v) for n, v in re.findall(r"\b(EP_(?:OK|E[A-Z]+|FMT_[A-Z0-9_]+))\s*=\s*(-?\d+)", src)}
+    assert len(defines) == 4 and len(enums) >= 10
+    for n, v in {**defines, **enums}.items():
+        assert getattr(ep, n) == v, n
+    assert len(set(defines.values())) == 4 and all(v & (v - 1) == 0 for v in defines.values())
 
 
 GOOD = dict(T=4096, H=7168, E=256, R=16, N=2, k=8)
