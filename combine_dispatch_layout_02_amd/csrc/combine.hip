@@ -47,7 +47,13 @@ struct CombineArgs {
     int64_t cached;             // tokens [0, cached) have their rows in the memory-side cache
 };
 
-constexpr int kSlotBatch = 8;
+#ifndef EP_COMBINE_BATCH
+#define EP_COMBINE_BATCH 8     // slots per batch of loads when k is not a compile-time constant
+#endif
+#ifndef EP_COMBINE_K8_GENERIC
+#define EP_COMBINE_K8_GENERIC 0   // 1: k = 8 takes the run-time-k kernels (batches of EP_COMBINE_BATCH)
+#endif
+constexpr int kSlotBatch = EP_COMBINE_BATCH;
 
 #ifndef EP_COMBINE_VECS
 #define EP_COMBINE_VECS 4      // 16-byte vectors per lane per pass (bf16 rows)
@@ -516,7 +522,7 @@ hipError_t launch_combine(const Shape &s, const void *expert_out, const uint8_t 
         } else {
             a.S = S;
             const dim3 g3((unsigned)((s.T * a.S + 3) / 4));
-            if (s.k == 8) hipLaunchKernelGGL((ep_combine_bf16_kernel<EP_COMBINE_VECS, 8>), g3, block, 0, stream, a);
+            if (s.k == 8 && !EP_COMBINE_K8_GENERIC) hipLaunchKernelGGL((ep_combine_bf16_kernel<EP_COMBINE_VECS, 8>), g3, block, 0, stream, a);
             else hipLaunchKernelGGL((ep_combine_bf16_kernel<EP_COMBINE_VECS, 0>), g3, block, 0, stream, a);
         }
     }

@@ -48,6 +48,10 @@
 #include "ep_device.h"
 #include "ep_internal.h"
 
+#ifndef EP_PLAN_ROTATE
+#define EP_PLAN_ROTATE 1   // 1: the count kernel's expert pass starts on the upper half of the block
+#endif
+
 namespace ep {
 namespace {
 
@@ -129,7 +133,9 @@ __global__ __launch_bounds__(1024) void ep_plan_count_kernel(CountArgs a) {
     int32_t *tc = a.tile_count + (size_t)blockIdx.x * (E + a.R + a.N);
     const bool single = gridDim.x == 1;   // the whole batch is this tile
     int32_t *cnt = rn + a.R + a.N;        // [E] tile counts (single-tile finish)
-    for (int e2 = tid; e2 < E; e2 += nt) {
+    // experts from the upper half of the block first: the token pass below
+    // runs on the lowest waves, so the two proceed side by side
+    for (int e2 = (tid + EP_PLAN_ROTATE * (nt >> 1)) % nt; e2 < E; e2 += nt) {
         int32_t c = 0;
         for (int w0 = 0; w0 < a.W; w0 += 4) {
             uint64_t m[4];
