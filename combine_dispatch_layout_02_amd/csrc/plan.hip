@@ -135,7 +135,15 @@ __global__ __launch_bounds__(1024) void ep_plan_count_kernel(CountArgs a) {
     int32_t *cnt = rn + a.R + a.N;        // [E] tile counts (single-tile finish)
     // experts from the upper half of the block first: the token pass below
     // runs on the lowest waves, so the two proceed side by side
-    for (int e2 = (tid + EP_PLAN_ROTATE * (nt >> 1)) % nt; e2 < E; e2 += nt) {
+    const int rot = EP_PLAN_ROTATE * (nt / kWave / 2) * kWave;   // whole waves: a wave's experts stay consecutive
+    // Tile pairs without a block scan when E <= blockDim: a thread then holds
+    // at most one expert and a wave 64 consecutive ones, so a wave prefix
+    // sum in registers plus the totals of the waves before it give each
+    // expert's pairs below it.
+    const bool wave_pairs = a.tile_pairs && !single && E <= nt;
+    const int e_wave = (w * kWave + rot) % nt;   // expert of lane 0 of this wave in the pass below
+    int32_t my_c = 0;
+    for (int e2 = (tid + rot) % nt; e2 < E; e2 += nt) {
         int32_t c = 0;
         for (int w0 = 0; w0 < a.W; w0 += 4) {
             uint64_t m[4];
@@ -145,8 +153,20 @@ __global__ __launch_bounds__(1024) void ep_plan_count_kernel(CountArgs a) {
             for (int q = 0; q < 4; ++q) c += (w0 + q < a.W) ? (int32_t)__popcll(m[q]) : 0;
         }
         tc[e2] = single ? 0 : c;          // single tile: no earlier tiles, prefix 0
-        if (single || a.tile_pairs) cnt[e2] = c;
+        if (single || (a.tile_pairs && !wave_pairs)) cnt[e2] = c;
         if (single && a.per_expert) a.per_expert[e2] = c;
+        my_c = c;
+    }
+    int32_t my_below = 0;                 // this expert's pairs below it within the wave
+    int32_t *wave_tot = cnt + E + 1;      // [blockDim / 64] pair totals of the expert waves
+    if (wave_pairs && e_wave < E) {       // wave-uniform
+        int32_t incl = my_c;              // 0 on lanes past E
+        for (int off = 1; off < kWave; off <<= 1) {
+            const int32_t u = __shfl_up(incl, off);
+            if (lane >= off) incl += u;
+        }
+        my_below = incl - my_c;
+        if (lane == kWave - 1) wave_tot[e_wave / kWave] = incl;
     }
 
     // ---- tokens: rank / node sets in registers, one token per thread (the
@@ -222,7 +242,14 @@ __global__ __launch_bounds__(1024) void ep_plan_count_kernel(CountArgs a) {
             }
             if (tid < a.R) a.rank_pairs[(size_t)tid * gridDim.x + blockIdx.x] = make_int2(incl - c, c);
         }
-        if (a.tile_pairs) {   // this tile's counts, prefixed over the experts (in place)
+        if (wave_pairs) {   // the wave totals were written before the barrier above
+            const int e2 = (tid + rot) % nt;
+            if (e2 < E) {
+                int32_t below = my_below;
+                for (int j = 0; j < e2 / kWave; ++j) below += wave_tot[j];
+                a.tile_pairs[(size_t)e2 * gridDim.x + blockIdx.x] = make_int2(below, my_c);
+            }
+        } else if (a.tile_pairs) {   // this tile's counts, prefixed over the experts (in place)
             block_exclusive_scan(cnt, cnt, E, reinterpret_cast<int32_t *>(cnt + E + 1));
             for (int e2 = tid; e2 < E; e2 += nt)
                 a.tile_pairs[(size_t)e2 * gridDim.x + blockIdx.x] = make_int2(cnt[e2], cnt[e2 + 1] - cnt[e2]);
