@@ -97,22 +97,20 @@ __global__ __launch_bounds__(1024) void ep_plan_count_kernel(CountArgs a) {
     const int ntok = (int)min<int64_t>(a.TT, a.T - t0);
     const int npairs = ntok * k;
 
-    for (int i = tid; i < a.W * E; i += nt) masks[i] = 0ull;
+    // Each wave clears its own mask row and sets its own pairs' bits in it,
+    // so only the barrier after the bits are set is needed (a wave's LDS
+    // operations are waited for before its atomics).  One pair per thread:
+    // the host sizes a tile to at most blockDim pairs.
+    int64_t v = -1;
+    if (tid < npairs) v = a.topk_idx[t0 * k + tid];   // in flight while the LDS is cleared
+    for (int i = lane; i < E; i += kWave) masks[w * E + i] = 0ull;
     for (int i = tid; i < a.R + a.N; i += nt) rn[i] = 0;
-    bool bad = false;
-    for (int q = tid; q < npairs; q += nt) {   // stage ids; invalid ids become masked
-        const int64_t v = a.topk_idx[t0 * k + q];
-        bad |= (v >= E);
-        ids[q] = (v >= 0 && v < E) ? (int32_t)v : -1;
-    }
-    __syncthreads();
-
+    const bool bad = v >= E;
+    const int e = (v >= 0 && v < E) ? (int32_t)v : -1;   // invalid ids become masked
+    if (tid < npairs) ids[tid] = e;
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): this wave's row is cleared
     // ---- pairs: ranks inside the tile
-    int e = -1;
-    if (tid < npairs) {
-        e = ids[tid];
-        if (e >= 0) atomicOr((unsigned long long *)&masks[w * E + e], 1ull << lane);
-    }
+    if (e >= 0) atomicOr((unsigned long long *)&masks[w * E + e], 1ull << lane);
     __syncthreads();
     if (tid < npairs) {
         int32_t r = -1;
