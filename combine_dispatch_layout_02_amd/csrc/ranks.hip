@@ -42,6 +42,9 @@ namespace {
 #ifndef EP_RANKS_COMBINE_WAVES
 #define EP_RANKS_COMBINE_WAVES 16384
 #endif
+#ifndef EP_RANKS_INPUTS_FIRST
+#define EP_RANKS_INPUTS_FIRST 1      // 1: the plan inputs are loaded ahead of the row (0: after it)
+#endif
 #ifndef EP_RANKS_NT_STORE
 #define EP_RANKS_NT_STORE 1          // non-temporal stores for the received rows
 #endif
@@ -205,11 +208,27 @@ __global__ __launch_bounds__(TOK ? 1024 : 256) void ep_dispatch_ranks_kernel(Ran
     const char *src = a.x + t * a.row_bytes;
     const int stride = kWave * a.S;
     const int v_first = lane + kWave * sub;
+    // With EP_RANKS_INPUTS_FIRST the plan path's inputs (t's ids and, per
+    // rank, the mask word of t's 64-token wave) are loaded ahead of the row,
+    // whose loads are then unconditional (a vector past the row re-reads the
+    // last one and is not stored), so the waits for the inputs do not cover
+    // the row.
+    const bool plan_path = !FUSED && !a.slots_in;
+    const int64_t tile = plan_path ? t / a.TT : 0;
+    const int pos = (int)(t - tile * a.TT);
+    const int wt = pos >> 6, bit = pos & 63;
+    int64_t eid_in = -1;
+    uint64_t mw_in = 0;
+    if (EP_RANKS_INPUTS_FIRST && plan_path) {
+        if (lane < a.k) eid_in = a.topk_idx[t * a.k + lane];
+        if (lane < a.R) mw_in = a.rank_mask[((size_t)tile * a.R + lane) * a.TW + wt];
+    }
     vec16 buf[VPL];
 #pragma unroll
     for (int i = 0; i < VPL; ++i) {
         const int v = v_first + i * stride;
-        if (v < a.nvec) buf[i] = ld16(src + (int64_t)v * 16);
+        if (EP_RANKS_INPUTS_FIRST) buf[i] = ld16(src + (int64_t)min(v, a.nvec - 1) * 16);
+        else if (v < a.nvec) buf[i] = ld16(src + (int64_t)v * 16);
     }
 
     // lanes 0..R-1: the token's row on each rank (-1: not reached)
@@ -229,20 +248,17 @@ __global__ __launch_bounds__(TOK ? 1024 : 256) void ep_dispatch_ranks_kernel(Ran
     } else if (!a.slots_in) {
         // t's place among its tile's tokens reaching rank `lane`: the set
         // bits before t's bit in the tile's mask of that rank
-        const int64_t tile = t / a.TT;
-        const int pos = (int)(t - tile * a.TT);
-        const int wt = pos >> 6, bit = pos & 63;
         int32_t start = 0, lr = 0;
         bool reached = false;
         int re = -1;   // rank of slot `lane`'s expert by topk_idx (lanes < k)
         if (lane < a.k) {
-            const int64_t e = a.topk_idx[t * a.k + lane];
+            const int64_t e = EP_RANKS_INPUTS_FIRST ? eid_in : a.topk_idx[t * a.k + lane];
             if (e >= 0 && e < a.E) re = a.epr_shift >= 0 ? (int)(e >> a.epr_shift) : (int)(e / a.epr);
         }
         if (lane < a.R) {
             const uint64_t *m = a.rank_mask + ((size_t)tile * a.R + lane) * a.TW;
             // every lookup is independent of the others: one memory round trip
-            const uint64_t mw = m[wt];
+            const uint64_t mw = EP_RANKS_INPUTS_FIRST ? mw_in : m[wt];
             if (!SCAN) start = a.plan_rank_offset[lane] + a.tile_prefix[tile * a.cols + a.E + lane];
             lr = (int32_t)__popcll(mw & ((1ull << bit) - 1ull));
             for (int i = 0; i < wt; ++i) lr += (int32_t)__popcll(m[i]);
