@@ -11,8 +11,9 @@ ranks times the (token, rank) path the same way: ep_dispatch_ranks_with_layout
 (one row per token per rank it reaches) -> ep_combine_ranks, with
 ep_expert_reduce_ranks (the weighted per-rank partials) as the expert stage.
 --split-layout times ep_dispatch_layout -> ep_dispatch_from_layout (or
-ep_dispatch_ranks; the layout call's plan reused) -> the combine instead,
-and --layout rank_major always does.
+ep_dispatch_ranks; the layout call's plan reused) -> the combine instead.
+--layout rank_major gives the token-major rows fixed per-rank blocks
+(rank_capacity).
 The expert stage (identity, per-expert scaling, fp8 -> mxfp8 or bf16 ->
 nvfp4 re-encoding) runs during warmup and is not part of the timed step.
 W untimed warmup steps, then K timed steps bracketed by stream
@@ -370,9 +371,10 @@ def measure(workload: str, steps: int, warmup: int, graph: bool = False, layout_
     # step, the inputs being the same) and stays out of the timed step
     phases = [("layout", layout), ("dispatch", dispatch), ("combine", combine)]
     # token-major rows: one ep_dispatch_with_layout call (a single launch up to
-    # 2048 pairs, else the count launch and the copy that scans the counts);
-    # split_layout times ep_dispatch_layout + ep_dispatch_from_layout instead
-    single_launch = M == 0 and (T * k <= SINGLE_LAUNCH_PAIRS or not split_layout)
+    # 2048 pairs of the compacted layout, else the count launch and the copy
+    # that scans the counts); split_layout times ep_dispatch_layout +
+    # ep_dispatch_from_layout instead, except for single-launch batches
+    single_launch = not split_layout or (M == 0 and T * k <= SINGLE_LAUNCH_PAIRS)
     if single_launch:
         phases = [("layout+dispatch", layout_dispatch), ("combine", combine)]
 

@@ -303,6 +303,16 @@ __global__ __launch_bounds__(KEYS ? 1024 : 256) void ep_dispatch_copy_kernel(Cop
     // lanes 0..k-1: the token's slots
     int32_t slot = FUSED ? counted_slot<(KEYS > 0 ? KEYS : 1)>(a, t, lane, sub) : -1;
     const int32_t base = SCAN ? slot_bases(a, (lane < a.k && lr >= 0) ? (int)eid : -1, (int)(t / a.TT), lane) : 0;
+    // RANK_MAJOR in the scanning copy: the compacted start of the slot's
+    // rank, i.e. the segment start of the rank's first expert (the sum of
+    // that expert's pairs below it over all tiles: tile 0 adds no earlier
+    // tiles)
+    int32_t rank_start = 0;
+    if (SCAN && a.M > 0) {   // uniform
+        const int r0 = (lane < a.k && lr >= 0)
+                           ? (a.epr_shift >= 0 ? (int)eid >> a.epr_shift : (int)eid / a.epr) * a.epr : -1;
+        rank_start = slot_bases(a, r0, 0, lane);
+    }
     if (lane < a.k) {
         const int64_t p = t * a.k + lane;
         if (!FUSED && a.slots_in) {   // cached: the slots of a previous dispatch's handle
@@ -314,7 +324,7 @@ __global__ __launch_bounds__(KEYS ? 1024 : 256) void ep_dispatch_copy_kernel(Cop
             slot = SCAN ? base + lr : a.plan_offset[e] + a.tile_prefix[(t / a.TT) * a.cols + e] + lr;
             if (a.M > 0) {   // RANK_MAJOR: the same place inside the rank, at the rank's fixed block
                 const int r = a.epr_shift >= 0 ? e >> a.epr_shift : e / a.epr;
-                const int32_t in_rank = slot - a.plan_offset[r * a.epr];
+                const int32_t in_rank = slot - (SCAN ? rank_start : a.plan_offset[r * a.epr]);
                 if (in_rank < a.M) {
                     slot = r * a.M + in_rank;
                 } else {
@@ -479,7 +489,7 @@ hipError_t launch_dispatch_copy(const Shape &s, const WsLayout &L, const void *x
 }
 
 bool scan_in_copy_fits(const Shape &s, const WsLayout &L) {
-    return s.T > 0 && s.M == 0 && !s.rank_rows && L.tiles > 1 && L.tiles <= kScanCopyMaxTiles;
+    return s.T > 0 && !s.rank_rows && L.tiles > 1 && L.tiles <= kScanCopyMaxTiles;
 }
 
 hipError_t launch_dispatch_scan_copy(const Shape &s, const WsLayout &L, const void *x,

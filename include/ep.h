@@ -201,13 +201,14 @@ int ep_dispatch(const ep_shape *shape, const void *x, const float *x_scales,
  * computes the layout counts and the segment starts while every other wave
  * finds its token's slots by counting the pairs that sort before them (the
  * stable counting sort's position); results are identical to the two calls.
- * Larger batches of up to 256 plan tiles (T * k <= 262144 pairs) run two
- * launches: the count kernel, which also writes per (expert, tile) the
- * tile's pairs of smaller experts and of the expert, and the copy, whose
- * waves rebuild each slot's position from those sums and whose first block
- * writes the layout totals.  Beyond that: the two layout launches, then the
- * copy.  Afterwards the workspace holds no plan that ep_dispatch_from_layout
- * may reuse.
+ * Other batches of 2 to 256 plan tiles (up to T * k = 262144 pairs; either
+ * layout) run two launches: the count kernel, which also writes per (expert,
+ * tile) the tile's pairs of smaller experts and of the expert, and the copy,
+ * whose waves rebuild each slot's position from those sums (and, for
+ * RANK_MAJOR, the start of the slot's rank from those of the rank's first
+ * expert) and whose first block writes the layout totals.  One tile, or
+ * more than 256: the layout launches, then the copy.  Afterwards the
+ * workspace holds no plan that ep_dispatch_from_layout may reuse.
  * Arguments: as ep_dispatch_layout and ep_dispatch.
  */
 int ep_dispatch_with_layout(const ep_shape *shape, const void *x, const float *x_scales,

@@ -270,6 +270,51 @@ def test_layout_in_copy_tile_edges(tiles):
     assert ndiff == 0
 
 
+def _rank_capacity(inp, slack=0):
+    """The largest rank's pair count (plus slack): no pair is dropped."""
+    off = oracle.slots(inp["topk_idx"], inp["topk_w"], inp["E"])["expert_offset"]
+    return int(max(np.diff(off[:: inp["E"] // inp["R"]]))) + slack
+
+
+# RANK_MAJOR through the one-call form: from 2 to 256 plan tiles the copy
+# also rebuilds each rank's compacted start from the tile pairs of the
+# rank's first expert; 1 tile and 257 tiles take the launches of the plan.
+@pytest.mark.parametrize("tiles", [1, 2, 3, 64, 65, 256, 257])
+def test_rank_major_with_layout_tile_edges(tiles):
+    inp = W.make_inputs("tiny", T=tiles * 128 - 3, H=64, E=256, R=16, N=2, k=8, mask_frac=0.05)
+    inp["rank_capacity"] = _rank_capacity(inp, 5)
+    _, _, ndiff = _run_both(inp, with_layout=True)
+    assert ndiff == 0
+
+
+@pytest.mark.parametrize("slack", [0, 37])
+def test_rank_major_with_layout_full_size(slack):
+    """The prefill shape in one call: parity with the oracle, and y equal to
+    the compacted layout's y bit for bit."""
+    import gpu_path
+    inp = W.make_inputs("prefill2n")
+    g_tm = gpu_path.run(inp, with_layout=True)
+    g, r, ndiff = _run_both(dict(inp, rank_capacity=_rank_capacity(inp, slack)), with_layout=True)
+    assert ndiff == 0
+    np.testing.assert_array_equal(g["y"], g_tm["y"])
+
+
+@pytest.mark.parametrize("kw", [dict(T=500, H=256), dict(T=3000, H=64, E=96, R=8, N=2, k=8)])   # 1 tile; 24 tiles, 12 experts per rank
+def test_rank_major_with_layout_overflow(kw):
+    """Capacity below the largest rank's count: the overflowing pairs are
+    dropped and flagged in both the plan's copy and the one-call form."""
+    import gpu_path
+    inp = W.make_inputs("tiny", **kw)
+    inp["rank_capacity"] = _rank_capacity(inp) - 7
+    for with_layout in (False, True):
+        g = gpu_path.run(inp, check=False, with_layout=with_layout)
+        with pytest.raises(RuntimeError, match="flags 0x4"):
+            g["ws"].check()
+        r = oracle.run_path(inp)
+        assert r["slots"]["dropped"] > 0
+        assert gpu_path.compare(g, r, False) == 0
+
+
 @pytest.mark.parametrize("kw", [
     dict(T=300, H=64, E=4096, R=64, N=64, k=8),                 # tiles of 8 tokens (38 tiles)
     dict(T=2049, H=64, E=256, R=8, N=1, k=1),                   # tiles of 1024 tokens
