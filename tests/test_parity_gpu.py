@@ -328,6 +328,10 @@ def test_layout_in_copy_shapes(kw):
     for with_layout, from_layout in ((True, True), (False, False)):   # layout + dispatch; standalone dispatch
         _, _, ndiff = _run_both(inp, from_layout=from_layout, with_layout=with_layout)
         assert ndiff == 0
+    # the same shapes in RANK_MAJOR blocks, through the one-call form
+    inp = dict(inp, rank_capacity=_rank_capacity(inp, 3))
+    _, _, ndiff = _run_both(inp, with_layout=True)
+    assert ndiff == 0
 
 
 @pytest.mark.parametrize("name", ["quant", "nvfp4"])
