@@ -5,7 +5,8 @@ Each case draws (from its seed) the token count, hidden size, experts /
 ranks / nodes, top-k, routing with or without repeats, masked slots and
 tokens, and runs the token-major path through ep_dispatch_from_layout,
 ep_dispatch and ep_dispatch_with_layout, the RANK_MAJOR layout (a capacity
-that fits, and one that drops pairs), and the (token, rank) path.  The bar
+that fits, and one that drops pairs; from the plan and in one call), and the
+(token, rank) path.  The bar
 is the parity bar of the other GPU tests: integer outputs and rows bit-exact,
 y within 1 bf16 ulp, and no differing element at all.
 """
@@ -62,16 +63,16 @@ def test_random_shapes_all_paths(seed):
     top = int(per_rank.max()) if per_rank.size else 0
     for M in (max(1, top), max(1, top // 2)):
         rm = dict(inp, rank_capacity=M)
-        g = gpu_path.run(rm, check=False)
-        flags = g["ws"].check() if M >= top else None
         r = oracle.run_path(rm)
-        if M < top:
-            with pytest.raises(RuntimeError, match="flags 0x4"):
-                g["ws"].check()
-            assert r["slots"]["dropped"] > 0
-        else:
-            assert flags == 0
-        assert gpu_path.compare(g, r, False) == 0, f"rank_major M={M}"
+        for with_layout in (False, True):   # from the layout call's plan; layout + dispatch in one call
+            g = gpu_path.run(rm, check=False, with_layout=with_layout)
+            if M < top:
+                with pytest.raises(RuntimeError, match="flags 0x4"):
+                    g["ws"].check()
+                assert r["slots"]["dropped"] > 0
+            else:
+                assert g["ws"].check() == 0
+            assert gpu_path.compare(g, r, False) == 0, f"rank_major M={M} with_layout={with_layout}"
 
     # (token, rank) rows, from the layout call's plan and in one call
     r = oracle.run_path(dict(inp, rank_rows=True))
