@@ -94,6 +94,8 @@ def test_regions_fit_and_cover_what_the_kernels_address(lib):
         assert threads >= tt, d
         assert tw * E * 8 <= 48 * KIB or tw == 1, d
         assert tiles <= MAX_GRID, d
+        # the plan word of a pair, (expert << 16) | local rank, stays a non-negative int32
+        assert tt * k <= 1 << 16 and ((E - 1) << 16 | (tt * k - 1)) < 1 << 31, d
         # what the kernels address (4-byte counts, 8-byte masks / pairs)
         ctrl, tile_count, local_rank, plan_offset, rank_mask, rank_start, tile_pairs, rank_pairs = size
         assert ctrl >= 4, d
