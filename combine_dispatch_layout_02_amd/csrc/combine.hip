@@ -12,12 +12,13 @@
 // (exact in binary32).
 //
 // How: one wave per (token, row part).  Lanes 0..k-1 read the token's slots
-// and weights, which readlane moves into scalar registers, so every decision
-// on a slot is uniform.  Each lane owns 16-byte column vectors of the row;
-// per batch of slots (all k when k is a compile-time constant) it issues
-// every load of the batch before the first FMA, then applies v_fma_f32 in
-// slot order.  Nothing is reduced across lanes, so the result does not depend on
-// the launch shape.  The gathered rows are read once: the loads carry the
+// and weights; a ballot gives the unmasked ones, which readlane moves into
+// scalar registers in slot order, so every decision on a slot is uniform.
+// Each lane owns 16-byte column vectors of the row; per batch of slots (all
+// k when k is a compile-time constant) it issues every load of the batch
+// before the first FMA, then applies v_fma_f32 in slot order, the first
+// unmasked slot as a multiply.  Nothing is reduced across lanes, so the
+// result does not depend on the launch shape.  The gathered rows are read once: the loads carry the
 // non-temporal hint so they do not evict what the caches still hold.
 // bf16 rows: the tokens are taken last to first and y is stored
 // non-temporal.  The dispatch leaves the first tokens' receive rows in the
