@@ -461,9 +461,10 @@ def measure(workload: str, steps: int, warmup: int, graph: bool = False, layout_
 
     # (4) cold: the memory-side cache flushed (512 MiB plain read: evicts
     # everything, writes back what was dirty, leaves the cache clean) before
-    # every step; graphs of [flush, calls 0..i] minus graphs of [flush, calls
-    # 0..i-1], so the write-back of what the calls leave dirty in the cache
-    # (it happens during the next flush) is charged to them
+    # every step; graphs of [flush, step] (and of [flush, one call]) minus
+    # graphs of [flush] alone, so the write-back of what the step or call
+    # leaves dirty in the cache (it happens during the next flush) is
+    # charged to it
     cold_res = None
     if cold and graph_ms is not None:
         cold_res = cold_timing(phases, steps, G, hev, stream, dev)
