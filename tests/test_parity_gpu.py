@@ -3,9 +3,12 @@
 Bar: layout counts, slots, index maps, dispatched rows, fp8 rows / scales and
 mxfp8 payloads bit-exact; combine within 1 bf16 ulp per element (the fp32
 fma chain in slot order is reproduced exactly, so the tests also report the
-count of differing elements, expected 0).  The five workloads run at their
-full sizes, in the launch configuration the benchmark uses; the edge cases
-cover ragged and empty inputs, masked slots, duplicate experts, invalid ids
+count of differing elements, expected 0).  Every workload (the five
+configurations and the nvfp4 payload) runs at its full size, in the launch
+configuration the benchmark uses, with the plan reused, planned again and
+in one call; the RANK_MAJOR layout runs at the prefill shape in both forms.
+The edge cases cover ragged and empty inputs, masked slots, duplicate
+experts, invalid ids, plan-tile counts on both sides of every path's limits
 and the shape limits.
 """
 import numpy as np
