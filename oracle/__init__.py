@@ -13,12 +13,24 @@ Parity status per function (what pins it, all in ``tests/test_oracle_*.py``):
   layout / algo count       worked example 8166 (MORI "Why ... equivalent",
                             Step 4), three independent dedup formulations,
                             closed-form expectations, brute force
+  accounting                the worked example's byte counts and the fp8
+                            factor (1 + 4/128) / 2
   slots / dispatch rows     brute-force lexicographic sort, bijection and
                             stability invariants
-  combine bf16 / mxfp8      identity round trip (y == x), fp64 bound
-  formats / quantization    exhaustive e4m3 / e8m0 tables against exact
-                            rational arithmetic, torch's bf16 and fp8 casts
+  RANK_MAJOR slots          brute force per rank; the combine over them equal
+                            bit for bit to the token-major one
+  (token, rank) slots,      brute force on small cases, regions equal to the
+  partials and combine      layout's per-rank counts, one rank reducing to
+                            the token-major combine, exact small integers,
+                            the two-rounding bound, +0.0 for an empty token
+  combine bf16 / mxfp8      identity round trip (y == x), fp64 bound, the
+                            slot order that is computed
+  combine nvfp4             fp64 bound and exactly representable rows
+  formats / quantization    exhaustive e4m3 / e8m0 / e2m1 tables against
+                            exact rational arithmetic and brute force, torch's
+                            bf16 and fp8 casts, the formats' error on N(0,1)
   expert stage              same format pins (it is a composition of them)
+  threads() mode            bytes equal to one thread on every workload
 
 Timing only: inside ``with oracle.threads(n):`` the row-level wrappers
 (dispatch rows, combines, expert stages, fp8 input quantisation) split their
