@@ -7,7 +7,10 @@ The library never allocates, synchronises or records a memset inside a call,
 so a step can be captured once and replayed.  Each case captures two steps,
 replays the graph three times with eager steps and synchronisations in
 between, and checks every replay bit for bit against the eager result and the
-eager result against the CPU oracle.
+eager result against the CPU oracle.  A second test captures one step and
+replays it over new batches written into the captured input tensors (other
+routing, masks, repeated experts, an all-masked batch), each replay checked
+against the oracle for its batch.
 """
 import numpy as np
 import pytest
@@ -27,11 +30,11 @@ def _gpu():
     ep.load()
 
 
-def _pairs_step(inp, one_call):
+def _pairs_step(inp, one_call, rank_capacity=0):
     import gpu_path
     from combine_dispatch_layout_02_amd import ep
     T, H, E, R, N, k = (inp[n] for n in ("T", "H", "E", "R", "N", "k"))
-    shape = ep.make_shape(T, H, E, R, N, k)
+    shape = ep.make_shape(T, H, E, R, N, k, rank_capacity=rank_capacity)
     ws = ep.Workspace(shape)
     x = gpu_path.to_dev_bf16(inp["x"])
     idx = torch.from_numpy(inp["topk_idx"]).cuda()
@@ -39,9 +42,10 @@ def _pairs_step(inp, one_call):
     lay = dict(r=torch.empty(R, dtype=torch.int32, device="cuda"), e=torch.empty(E, dtype=torch.int32, device="cuda"),
                m=torch.empty((T, R), dtype=torch.uint8, device="cuda"),
                n=torch.empty(N, dtype=torch.int32, device="cuda"), a=torch.empty(1, dtype=torch.int64, device="cuda"))
-    recv = torch.empty((T * k, H), dtype=torch.bfloat16, device="cuda")
-    src = torch.empty(T * k, dtype=torch.int32, device="cuda")
-    rw = torch.empty(T * k, dtype=torch.float32, device="cuda")
+    rows = shape.rows
+    recv = torch.empty((rows, H), dtype=torch.bfloat16, device="cuda")
+    src = torch.empty(rows, dtype=torch.int32, device="cuda")
+    rw = torch.empty(rows, dtype=torch.float32, device="cuda")
     slot = torch.empty((T, k), dtype=torch.int32, device="cuda")
     off = torch.empty(E + 1, dtype=torch.int32, device="cuda")
     y = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
@@ -55,7 +59,8 @@ def _pairs_step(inp, one_call):
             ep.ep_dispatch(shape, x, None, idx, w, recv, None, src, rw, slot, off, ws, from_layout=True)
         ep.ep_combine(shape, recv, None, slot, w, y)
 
-    return step, ws, lambda: (gpu_path.bf16_bits(y), slot.cpu().numpy(), lay["r"].cpu().numpy())
+    return step, ws, lambda: (gpu_path.bf16_bits(y), slot.cpu().numpy(), lay["r"].cpu().numpy()), \
+        dict(x=x, idx=idx, w=w)
 
 
 def _cached_step(inp, x2):
@@ -86,7 +91,7 @@ def _cached_step(inp, x2):
         ep.ep_dispatch_cached(shape, xb, None, slot, recv)
         ep.ep_combine(shape, recv, None, slot, w, y)
 
-    return step, ws, lambda: (gpu_path.bf16_bits(y), slot.cpu().numpy(), lay["r"].cpu().numpy())
+    return step, ws, lambda: (gpu_path.bf16_bits(y), slot.cpu().numpy(), lay["r"].cpu().numpy()), None
 
 
 def _ranks_step(inp):
@@ -117,7 +122,8 @@ def _ranks_step(inp):
         ep.ep_expert_reduce_ranks(shape, recv, None, roff, r_idx, r_w, None, part)
         ep.ep_combine_ranks(shape, part, trs, y)
 
-    return step, ws, lambda: (gpu_path.bf16_bits(y), trs.cpu().numpy(), lay["r"].cpu().numpy())
+    return step, ws, lambda: (gpu_path.bf16_bits(y), trs.cpu().numpy(), lay["r"].cpu().numpy()), \
+        dict(x=x, idx=idx, w=w)
 
 
 def _quantized_step(inp):
@@ -158,7 +164,8 @@ def _quantized_step(inp):
             ep.ep_expert_requant_mxfp8(shape, off, None, recv, recv_s, eq, es)
         ep.ep_combine(shape, eq, es, slot, w, y)
 
-    return step, ws, lambda: (gpu_path.bf16_bits(y), slot.cpu().numpy(), lay["r"].cpu().numpy())
+    ins = dict(x=xq, idx=idx, w=w) if nv else dict(xq=xq, xs=xs, idx=idx, w=w)
+    return step, ws, lambda: (gpu_path.bf16_bits(y), slot.cpu().numpy(), lay["r"].cpu().numpy()), ins
 
 
 @pytest.mark.parametrize("case", ["pairs", "pairs_full_size", "pairs_one_call_small", "pairs_one_call_large", "cached",
@@ -166,32 +173,32 @@ def _quantized_step(inp):
 def test_graph_replays_match_eager(case):
     if case == "pairs":
         inp = W.make_inputs("prefill2n", T=1000, H=1024, mask_frac=0.05)
-        step, ws, read = _pairs_step(inp, one_call=False)
+        step, ws, read, _ = _pairs_step(inp, one_call=False)
         ref = oracle.run_path(inp)
     elif case == "pairs_full_size":   # receive rows beyond the cache budget: interleaved dispatch order
         inp = W.make_inputs("prefill2n")
-        step, ws, read = _pairs_step(inp, one_call=False)
+        step, ws, read, _ = _pairs_step(inp, one_call=False)
         ref = oracle.run_path(inp)
     elif case == "pairs_one_call_small":   # a single launch for layout + dispatch
         inp = W.make_inputs("prefill2n", T=128, H=1024, mask_frac=0.05)
-        step, ws, read = _pairs_step(inp, one_call=True)
+        step, ws, read, _ = _pairs_step(inp, one_call=True)
         ref = oracle.run_path(inp)
     elif case == "pairs_one_call_large":
         inp = W.make_inputs("prefill2n", T=700, H=1024)
-        step, ws, read = _pairs_step(inp, one_call=True)
+        step, ws, read, _ = _pairs_step(inp, one_call=True)
         ref = oracle.run_path(inp)
     elif case == "cached":   # another tensor of the same tokens through a previous handle
         inp = W.make_inputs("prefill2n", T=1000, H=1024, mask_frac=0.05)
         x2 = np.ascontiguousarray(inp["x"][::-1])
-        step, ws, read = _cached_step(inp, x2)
+        step, ws, read, _ = _cached_step(inp, x2)
         ref = oracle.run_path(dict(inp, x=x2))
     elif case in ("quant_mxfp8", "nvfp4"):
         inp = W.make_inputs("quant" if case == "quant_mxfp8" else "nvfp4", T=1000, H=1024, mask_frac=0.05)
-        step, ws, read = _quantized_step(inp)
+        step, ws, read, _ = _quantized_step(inp)
         ref = oracle.run_path(inp)
     else:
         inp = W.make_inputs("prefill2n", T=1000, H=1024, mask_frac=0.05)
-        step, ws, read = _ranks_step(inp)
+        step, ws, read, _ = _ranks_step(inp)
         ref = oracle.run_path(dict(inp, rank_rows=True))
     print(f"graph case {case} T={inp['T']}", flush=True)
     step()
@@ -214,3 +221,59 @@ def test_graph_replays_match_eager(case):
         step()   # eager work between replays
         torch.cuda.synchronize()
     ws.check()
+
+
+def _load(ins, inp):
+    """Write a new batch into the tensors the graph was captured with."""
+    import gpu_path
+    from combine_dispatch_layout_02_amd import ep
+    x = gpu_path.to_dev_bf16(inp["x"])
+    if "xs" in ins:   # fp8 rows: the captured step reads the quantized copy
+        q, s = ep.quant_fp8_s128(x)
+        ins["xq"].copy_(q)
+        ins["xs"].copy_(s)
+    else:
+        ins["x"].copy_(x)
+    ins["idx"].copy_(torch.from_numpy(inp["topk_idx"]))
+    ins["w"].copy_(torch.from_numpy(inp["topk_w"]))
+
+
+# A serving loop captures one step and replays it for every batch of the same
+# shape, writing each batch into the captured input tensors: the routing, the
+# rows and the weights change between replays, nothing else does.
+@pytest.mark.parametrize("case", ["split", "one_call_small", "one_call_large", "rank_major", "ranks", "quant_mxfp8"])
+def test_graph_replays_follow_new_inputs(case):
+    name = "quant" if case == "quant_mxfp8" else "prefill2n"
+    T = {"one_call_small": 128, "one_call_large": 700}.get(case, 1000)
+    batches = [W.make_inputs(name, seed=0, T=T, H=1024),
+               W.make_inputs(name, seed=1, T=T, H=1024, mask_frac=0.2, mask_tokens=0.05),
+               W.make_inputs(name, seed=2, T=T, H=1024, routing="replace"),   # repeated experts in a row
+               W.make_inputs(name, seed=3, T=T, H=1024, mask_tokens=1.0)]     # every slot masked
+    M = 0
+    if case == "rank_major":   # one capacity that holds every batch's largest rank
+        M = max(int(max(np.diff(oracle.slots(b["topk_idx"], b["topk_w"], b["E"])["expert_offset"][:: b["E"] // b["R"]])))
+                for b in batches) + 3
+    if case == "ranks":
+        step, ws, read, ins = _ranks_step(batches[0])
+    elif case == "quant_mxfp8":
+        step, ws, read, ins = _quantized_step(batches[0])
+    else:
+        step, ws, read, ins = _pairs_step(batches[0], one_call=case != "split", rank_capacity=M)
+    print(f"graph new-inputs case {case} T={T} M={M}", flush=True)
+    step()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for i in [1, 2, 3, 0, 2]:
+        inp = dict(batches[i], rank_rows=case == "ranks", rank_capacity=M)
+        _load(ins, inp)
+        g.replay()
+        torch.cuda.synchronize()
+        assert ws.check() == 0
+        ref = oracle.run_path(inp)
+        y, slots, ranks = read()
+        np.testing.assert_array_equal(y, ref["y"])
+        np.testing.assert_array_equal(ranks, ref["layout"]["num_tokens_per_rank"])
+        want = ref["slots"]["token_rank_slot"] if case == "ranks" else ref["slots"]["token_slot"]
+        np.testing.assert_array_equal(slots, want)

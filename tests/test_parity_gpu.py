@@ -87,6 +87,28 @@ def test_scaled_expert_with_masks():
     assert ndiff == 0
 
 
+# Every slot masked (T > 0): nothing is counted or dispatched and every y row
+# is +0.0, through the plan's copy, the standalone dispatch and the one-call
+# form (a single launch at T = 100, count + copy at T = 1000).
+@pytest.mark.parametrize("T", [100, 1000])
+@pytest.mark.parametrize("name", ["prefill2n", "decode", "quant", "nvfp4"])
+def test_all_slots_masked(name, T):
+    inp = W.make_inputs(name, T=T, H=1024, mask_tokens=1.0)
+    assert (inp["topk_idx"] < 0).all()
+    forms = [dict(from_layout=True), dict(from_layout=False), dict(with_layout=True)]
+    for kw in forms:
+        g, _, ndiff = _run_both(inp, **kw)
+        assert ndiff == 0
+        assert not g["y"].any()
+        assert g["layout"]["rdma_algo_token_count"] == 0
+        assert (g["slots"]["expert_offset"] == 0).all()
+    if name == "prefill2n":   # RANK_MAJOR blocks of one row per rank
+        for kw in forms:
+            g, _, ndiff = _run_both(dict(inp, rank_capacity=1), **kw)
+            assert ndiff == 0
+            assert not g["y"].any()
+
+
 @pytest.mark.parametrize("from_layout", [True, False])
 def test_empty_batch(from_layout):
     import gpu_path

@@ -46,6 +46,19 @@ def test_workload_full_size(name):
     assert g["slots"]["rank_offset"][-1] == g["layout"]["num_tokens_per_rank"].sum()
 
 
+# Every slot masked (T > 0): no (token, rank) row, every y row +0.0, through
+# the layout call's plan and the one-call form (one launch at T = 100).
+@pytest.mark.parametrize("T", [100, 1000])
+@pytest.mark.parametrize("name", ["decode", "quant"])
+def test_all_slots_masked(name, T):
+    inp = W.make_inputs(name, T=T, H=1024, mask_tokens=1.0)
+    for with_layout in (False, True):
+        g, _, ndiff = _run_both(inp, with_layout)
+        assert ndiff == 0
+        assert not g["y"].any()
+        assert g["slots"]["rank_offset"][-1] == 0
+
+
 @pytest.mark.parametrize("T", [1, 63, 129, 257, 1000, 1025])
 def test_ragged_token_counts(T):
     _, _, ndiff = _run_both(W.make_inputs("decode", T=T, H=1024))
