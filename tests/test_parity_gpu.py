@@ -87,6 +87,18 @@ def test_scaled_expert_with_masks():
     assert ndiff == 0
 
 
+# Every pair on one or two experts: one expert segment holds (nearly) every
+# receive row, and every token reaches every rank and node.
+@pytest.mark.parametrize("kw", [dict(E=1, R=1, N=1, k=1, T=700),
+                                dict(E=2, R=1, N=1, k=4, T=3000, routing="replace"),
+                                dict(E=2, R=2, N=2, k=2, T=300)])
+def test_one_or_two_experts(kw):
+    inp = W.make_inputs("tiny", H=256, **kw)
+    for form in (dict(from_layout=True), dict(from_layout=False), dict(with_layout=True)):
+        _, _, ndiff = _run_both(inp, **form)
+        assert ndiff == 0
+
+
 # Every slot masked (T > 0): nothing is counted or dispatched and every y row
 # is +0.0, through the plan's copy, the standalone dispatch and the one-call
 # form (a single launch at T = 100, count + copy at T = 1000).

@@ -46,6 +46,17 @@ def test_workload_full_size(name):
     assert g["slots"]["rank_offset"][-1] == g["layout"]["num_tokens_per_rank"].sum()
 
 
+# Every pair on one or two experts (one or two ranks).
+@pytest.mark.parametrize("kw", [dict(E=1, R=1, N=1, k=1, T=700),
+                                dict(E=2, R=1, N=1, k=4, T=3000, routing="replace"),
+                                dict(E=2, R=2, N=2, k=2, T=300)])
+def test_one_or_two_experts(kw):
+    inp = W.make_inputs("tiny", H=256, **kw)
+    for with_layout in (False, True):
+        _, _, ndiff = _run_both(inp, with_layout)
+        assert ndiff == 0
+
+
 # Every slot masked (T > 0): no (token, rank) row, every y row +0.0, through
 # the layout call's plan and the one-call form (one launch at T = 100).
 @pytest.mark.parametrize("T", [100, 1000])
