@@ -18,6 +18,10 @@ namespace {
 using ep::Shape;
 using ep::WsLayout;
 
+// The current device's static scratch (ep_dispatch_with_layout_static), or
+// null if no call has used it on that device yet; defined with the array.
+int static_scratch_if_used(void **out);
+
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -460,7 +464,16 @@ int ep_dispatch_ranks_cached(const ep_shape *shape, const void *x, const float *
 }
 
 int ep_check(void *ws, size_t ws_bytes, void *stream, uint32_t *flags) {
-    if (!ws || ws_bytes < 256) return EP_EINVAL;
+    if (!ws) {   // the error word of ep_dispatch_with_layout_static's scratch on the current device
+        const int rc = static_scratch_if_used(&ws);
+        if (rc != EP_OK) return rc;
+        if (!ws) {   // no allocation-free call on this device yet: nothing flagged
+            if (flags) *flags = 0;
+            return EP_OK;
+        }
+        ws_bytes = 256;
+    }
+    if (ws_bytes < 256) return EP_EINVAL;
     hipStream_t st = static_cast<hipStream_t>(stream);
     if (hipStreamSynchronize(st) != hipSuccess) return EP_EHIP;
     uint32_t word = 0;
@@ -673,6 +686,14 @@ int static_scratch(void **out, hipStream_t st) {
         if (ep::launch_ws_init(static_cast<uint32_t *>(p), ep::kCtrlWords, st) != hipSuccess) return EP_EHIP;
         g_scratch_ptr[dev] = p;
     }
+    *out = g_scratch_ptr[dev];
+    return EP_OK;
+}
+
+int static_scratch_if_used(void **out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return EP_EHIP;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
     *out = g_scratch_ptr[dev];
     return EP_OK;
 }

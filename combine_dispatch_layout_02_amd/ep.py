@@ -161,7 +161,7 @@ def load():
         fn = getattr(lib, name)
         fn.restype = res
         fn.argtypes = args
-    if lib.ep_abi_version() != 7:
+    if lib.ep_abi_version() != 8:
         raise RuntimeError("libep_hip ABI version mismatch")
     _lib = lib
     return lib
@@ -352,6 +352,17 @@ def ep_dispatch_with_layout_static(shape, x, x_scales, topk_idx, topk_w, num_tok
         _ptr(num_tokens_per_expert), _ptr(is_token_in_rank), _ptr(num_tokens_per_node),
         _ptr(rdma_algo_token_count), _ptr(recv_x), _ptr(recv_x_scales), _ptr(recv_src_idx), _ptr(recv_topk_w),
         _ptr(token_slot), _ptr(expert_offset), _stream(stream)), "ep_dispatch_with_layout_static")
+
+
+def check_static(stream=None) -> int:
+    """Synchronize and read/clear the error word of the current device's
+    static scratch (ep_check with no workspace; raises on a flag)."""
+    flags = ctypes.c_uint32()
+    rc = load().ep_check(None, 0, _stream(stream), ctypes.byref(flags))
+    if rc == EP_EDEVICE:
+        raise RuntimeError(f"ep_check: {strerror(rc)} (flags {flags.value:#x})")
+    _ok(rc, "ep_check")
+    return flags.value
 
 
 def ep_dispatch_cached(shape, x, x_scales, token_slot, recv_x, recv_x_scales=None, stream=None):

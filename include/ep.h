@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define EP_ABI_VERSION 7
+#define EP_ABI_VERSION 8
 
 /* Status codes. */
 enum ep_status {
@@ -236,9 +236,9 @@ int ep_dispatch_with_layout(const ep_shape *shape, const void *x, const float *x
  *   - Every call on one GPU shares that GPU's array, which keeps the last
  *     call's plan: calls that overlap on one GPU (other streams, other host
  *     threads) race and must be ordered by the caller.
- *   - Invalid expert ids are treated as masked, as everywhere; their error
- *     flag stays in the array and is not reported (use ep_check with a
- *     workspace call to see it).
+ *   - Invalid expert ids are treated as masked and RANK_MAJOR overflows are
+ *     dropped, as everywhere; their flags collect in the array's error word,
+ *     which ep_check(NULL, 0, stream, &flags) reads and clears.
  */
 #define EP_STATIC_SCRATCH_BYTES ((size_t)16 << 20)
 int ep_dispatch_with_layout_static(const ep_shape *shape, const void *x, const float *x_scales,
@@ -406,7 +406,10 @@ int ep_combine_ranks(const ep_shape *shape, const uint16_t *partial,
 
 /* Synchronize `stream`, read and clear the workspace error word; returns
  * EP_EDEVICE if any kernel flagged bad input (e.g. an expert id >= E), and
- * writes the flags to *flags (host) when flags is not NULL. */
+ * writes the flags to *flags (host) when flags is not NULL.  ws = NULL
+ * (ws_bytes ignored) reads and clears the error word of the current
+ * device's static scratch, the one ep_dispatch_with_layout_static uses
+ * (flags 0 and EP_OK if no such call has run on that device). */
 int ep_check(void *ws, size_t ws_bytes, void *stream, uint32_t *flags);
 
 /* ---- payload conversion and the workloads' expert stage ------------------ */

@@ -3,7 +3,8 @@ ep_dispatch_with_layout (the same call with a caller-owned workspace): every
 output bit-identical, on consecutive calls that share the GPU's static
 scratch -- a full-size batch, then smaller ones (several plan tiles, a
 single-launch batch, fp8 rows), so the plan the previous call left in the
-scratch must not leak into the next.  Both calls go through the C ABI."""
+scratch must not leak into the next.  Both calls go through the C ABI.
+The static entry's error flags are read with ep_check and no workspace."""
 import ctypes
 
 import numpy as np
@@ -96,3 +97,48 @@ def test_static_rejects_shapes_beyond_the_scratch(ep):
     rc = lib.ep_dispatch_with_layout_static(ctypes.byref(big), fake, None, fake, fake, *([fake] * 5), fake, None,
                                             fake, fake, fake, fake, None)
     assert rc == ep.EP_EWORKSPACE
+
+
+def test_static_flags_read_by_ep_check_without_workspace(ep):
+    """The static entry's device error flags: an invalid expert id and a
+    RANK_MAJOR overflow raise them in the scratch's error word, and
+    ep_check(NULL, ...) reads and clears it; the outputs equal the workspace
+    call's, which raises the same flags."""
+    import oracle
+    dev = torch.device("cuda:0")
+    ep.check_static()   # whatever an earlier call left
+    for case in ("bad_expert", "rank_overflow"):
+        inp = W.make_inputs("tiny", T=300, H=256, E=64, R=8, N=2, k=4)
+        T, H, E, R, N, k = (inp[n] for n in ("T", "H", "E", "R", "N", "k"))
+        M, want = 0, ep.EP_ERRFLAG_BAD_EXPERT
+        if case == "bad_expert":
+            inp["topk_idx"][5, 1] = E + 3
+            inp["topk_idx"][77, 0] = E
+        else:
+            off = oracle.slots(inp["topk_idx"], inp["topk_w"], E)["expert_offset"]
+            M, want = int(max(np.diff(off[:: E // R]))) - 5, ep.EP_ERRFLAG_RANK_OVERFLOW
+        print(f"case static flags {case} M={M}", flush=True)
+        shape = ep.make_shape(T, H, E, R, N, k, rank_capacity=M)
+        x = torch.from_numpy(inp["x"].view(np.int16)).to(dev).view(torch.bfloat16)
+        idx = torch.from_numpy(inp["topk_idx"]).to(dev)
+        w = torch.from_numpy(inp["topk_w"]).to(dev)
+        ref, got = _outputs(ep, shape, inp, dev), _outputs(ep, shape, inp, dev)
+        ws = ep.Workspace(shape, dev)
+        ep.ep_dispatch_with_layout(shape, x, None, idx, w, *_args(ref), ws)
+        ep.ep_dispatch_with_layout_static(shape, x, None, idx, w, *_args(got))
+        with pytest.raises(RuntimeError, match=f"flags {want:#x}"):
+            ws.check()
+        with pytest.raises(RuntimeError, match=f"flags {want:#x}"):
+            ep.check_static()
+        assert ep.check_static() == 0   # read and cleared
+        for key in ref:
+            if ref[key] is not None:
+                assert torch.equal(ref[key].view(torch.uint8), got[key].view(torch.uint8)), f"{case}: {key}"
+    # a clean call raises nothing
+    inp = W.make_inputs("tiny", T=100)
+    shape = ep.make_shape(inp["T"], inp["H"], inp["E"], inp["R"], inp["N"], inp["k"])
+    x = torch.from_numpy(inp["x"].view(np.int16)).to(dev).view(torch.bfloat16)
+    got = _outputs(ep, shape, inp, dev)
+    ep.ep_dispatch_with_layout_static(shape, x, None, torch.from_numpy(inp["topk_idx"]).to(dev),
+                                      torch.from_numpy(inp["topk_w"]).to(dev), *_args(got))
+    assert ep.check_static() == 0
