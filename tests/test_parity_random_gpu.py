@@ -6,7 +6,8 @@ ranks / nodes, top-k, routing with or without repeats, masked slots and
 tokens, and runs the token-major path through ep_dispatch_from_layout,
 ep_dispatch and ep_dispatch_with_layout, the RANK_MAJOR layout (a capacity
 that fits, and one that drops pairs; from the plan and in one call), and the
-(token, rank) path.  The bar
+(token, rank) path; a second draw widens the shapes (T up to 9000, k up to
+32, E up to 4096, R and N up to 64).  The bar
 is the parity bar of the other GPU tests: integer outputs and rows bit-exact,
 y within 1 bf16 ulp, and no differing element at all.
 """
@@ -75,6 +76,59 @@ def test_random_shapes_all_paths(seed):
             assert gpu_path.compare(g, r, False) == 0, f"rank_major M={M} with_layout={with_layout}"
 
     # (token, rank) rows, from the layout call's plan and in one call
+    r = oracle.run_path(dict(inp, rank_rows=True))
+    for with_layout in (False, True):
+        g = gpu_path.run_ranks(inp, with_layout=with_layout)
+        assert gpu_path.compare_ranks(g, r, False) == 0, f"ranks with_layout={with_layout}"
+
+
+def _draw_wide(seed):
+    """Larger batches and wider shapes than _draw: T up to 9000 (many plan
+    tiles), k up to 32, E up to 4096, R and N up to 64, small rows."""
+    rng = np.random.default_rng(90000 + seed)
+    N = int(rng.choice([1, 2, 4, 8, 16, 64]))
+    R = min(N * int(rng.choice([1, 2, 4])), 64)
+    E = R * int(rng.choice([1, 2, 3, 5, 8, 16, 64]))
+    E = min(E, 4096 - 4096 % R)
+    k = int(rng.integers(1, min(E, 32) + 1))
+    T = min(int(rng.choice([300, 1000, 2049, 4097, 9000])), 200000 // k)
+    H = int(rng.choice([8, 16, 72, 136]))
+    kw = dict(T=T, H=H, E=E, R=R, N=N, k=k, routing="replace" if rng.random() < 0.3 else "uniform")
+    if rng.random() < 0.5:
+        kw["mask_frac"] = float(rng.choice([0.05, 0.5]))
+    if rng.random() < 0.3:
+        kw["mask_tokens"] = float(rng.choice([0.1, 0.9]))
+    return W.make_inputs("tiny", seed=seed, **kw)
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_random_wide_shapes_all_paths(seed):
+    """_draw_wide through every token-major form, RANK_MAJOR at a capacity
+    that fits and one that drops pairs, and the (token, rank) path."""
+    import gpu_path
+    inp = _draw_wide(seed)
+    E, R = inp["E"], inp["R"]
+    print(f"random wide case seed={seed} T={inp['T']} H={inp['H']} E={E} R={R} N={inp['N']} "
+          f"k={inp['k']} routing={inp['routing']}", flush=True)
+    ref = oracle.run_path(inp)
+    for mode in ("from_layout", "standalone", "with_layout"):
+        g = gpu_path.run(inp, from_layout=(mode == "from_layout"), with_layout=(mode == "with_layout"))
+        assert gpu_path.compare(g, ref, False) == 0, mode
+    ids = inp["topk_idx"]
+    ok = (ids >= 0) & (ids < E)
+    per_rank = np.bincount(ids[ok] // (E // R), minlength=R)
+    top = int(per_rank.max()) if per_rank.size else 0
+    for M in (max(1, top), max(1, top // 2)):
+        rm = dict(inp, rank_capacity=M)
+        r = oracle.run_path(rm)
+        for with_layout in (False, True):
+            g = gpu_path.run(rm, check=False, with_layout=with_layout)
+            if M < top:
+                with pytest.raises(RuntimeError, match="flags 0x4"):
+                    g["ws"].check()
+            else:
+                assert g["ws"].check() == 0
+            assert gpu_path.compare(g, r, False) == 0, f"rank_major M={M} with_layout={with_layout}"
     r = oracle.run_path(dict(inp, rank_rows=True))
     for with_layout in (False, True):
         g = gpu_path.run_ranks(inp, with_layout=with_layout)
