@@ -7,9 +7,10 @@ count of differing elements, expected 0).  Every workload (the five
 configurations and the nvfp4 payload) runs at its full size, in the launch
 configuration the benchmark uses, with the plan reused, planned again and
 in one call; the RANK_MAJOR layout runs at the prefill shape in both forms.
-The edge cases cover ragged and empty inputs, masked slots, duplicate
-experts, invalid ids, plan-tile counts on both sides of every path's limits
-and the shape limits.
+The edge cases cover ragged, empty and all-masked inputs, masked slots,
+duplicate experts, one or two experts, invalid ids, plan-tile counts on both
+sides of every path's limits, the shape limits, and receive buffers past 2
+and 4 GiB.
 """
 import numpy as np
 import pytest
@@ -513,3 +514,90 @@ def test_cached_rank_dispatch_reuses_a_handle(kw):
     if fp8:
         refs = oracle.dispatch_rows(s2.cpu().numpy(), trs, rows=cap)
         np.testing.assert_array_equal(rs2.cpu().numpy()[used].view(np.uint32), refs[used].view(np.uint32))
+
+
+# Receive buffers past 2^31 and 2^32 bytes, so any 32-bit byte offset would
+# show: every count, slot and source index in full; receive rows sampled
+# (every ~500th used row and the last 64, which lie past 4 GiB in the
+# token-major cases); y of sampled tokens against the oracle run on those
+# tokens alone (a token's y depends only on its own row, ids and weights).
+@pytest.mark.parametrize("case", ["one_call_256_tiles", "plan_313_tiles", "ranks"])
+def test_receive_buffer_past_4_gib(case):
+    import gpu_path
+    from combine_dispatch_layout_02_amd import ep
+    T, H = (40000, 7168) if case == "plan_313_tiles" else (32768, 8704)
+    inp = W.make_inputs("prefill2n", T=T, H=H)
+    E, R, N, k = inp["E"], inp["R"], inp["N"], inp["k"]
+    ranks = case == "ranks"
+    shape = ep.make_shape(T, H, E, R, N, k, rank_rows=int(ranks))
+    row_bytes = 2 * H
+    print(f"case large receive buffer {case} T={T} H={H} rows {shape.rows} x {row_bytes} B", flush=True)
+    ws = ep.Workspace(shape)
+    x = gpu_path.to_dev_bf16(inp["x"])
+    idx = torch.from_numpy(inp["topk_idx"]).cuda()
+    w = torch.from_numpy(inp["topk_w"]).cuda()
+    if ranks:
+        lay, d = ep.dispatch_ranks_with_layout(x, idx, w, shape, ws)
+        y = ep.combine_ranks(ep.expert_reduce_ranks(d), d["handle"])
+        recv, src = d["recv_x"], d["recv_src_idx"]
+        ref = oracle.slots_ranks(inp["topk_idx"], inp["topk_w"], E, R)
+        np.testing.assert_array_equal(d["handle"].token_rank_slot.cpu().numpy(), ref["token_rank_slot"])
+        np.testing.assert_array_equal(d["handle"].rank_offset.cpu().numpy(), ref["rank_offset"])
+        nrows = int(ref["rank_offset"][-1])
+    else:
+        if case == "one_call_256_tiles":
+            lay, recv, _, src, rw, h = ep.dispatch_with_layout(x, idx, w, shape, ws)
+        else:
+            lay = ep.dispatch_layout(idx, shape, ws)
+            recv, _, src, rw, h = ep.dispatch(x, idx, w, shape, ws, from_layout=True)
+        y = ep.combine(recv, h)
+        ref = oracle.slots(inp["topk_idx"], inp["topk_w"], E)
+        np.testing.assert_array_equal(h.token_slot.cpu().numpy(), ref["token_slot"])
+        np.testing.assert_array_equal(h.expert_offset.cpu().numpy(), ref["expert_offset"])
+        nrows = int(ref["expert_offset"][-1])
+        np.testing.assert_array_equal(rw.cpu().numpy()[:nrows].view(np.uint32), ref["recv_topk_w"][:nrows].view(np.uint32))
+    assert ws.check() == 0
+    assert nrows * row_bytes > (1 << 31) and (ranks or nrows * row_bytes > (1 << 32))
+    lr = oracle.layout(inp["topk_idx"], E, R, N)
+    for key in ("num_tokens_per_rank", "num_tokens_per_expert", "is_token_in_rank", "num_tokens_per_node"):
+        np.testing.assert_array_equal(lay[key].cpu().numpy(), lr[key], err_msg=key)
+    np.testing.assert_array_equal(src.cpu().numpy()[:nrows], ref["recv_src_idx"][:nrows])
+    rows = np.unique(np.concatenate([np.arange(0, nrows, 499), np.arange(nrows - 64, nrows)]))
+    got = gpu_path.bf16_bits(recv[torch.from_numpy(rows).cuda()])
+    np.testing.assert_array_equal(got, inp["x"][ref["recv_src_idx"][rows]])
+    toks = np.unique(np.concatenate([np.arange(0, T, 211), np.arange(T - 16, T)]))
+    sub = dict(inp, T=len(toks), x=inp["x"][toks], topk_idx=inp["topk_idx"][toks], topk_w=inp["topk_w"][toks],
+               rank_rows=ranks)
+    np.testing.assert_array_equal(gpu_path.bf16_bits(y[torch.from_numpy(toks).cuda()]), oracle.run_path(sub)["y"])
+
+
+# The same for the quantized payloads: fp8 rows (2.3 GB of receive rows and
+# as many of mxfp8 expert rows) and bf16 rows with an nvfp4 payload (4.6 GB
+# of receive rows), through the one-call dispatch, the expert stage and the
+# combine.
+@pytest.mark.parametrize("name", ["quant", "nvfp4"])
+def test_quantized_receive_buffer_past_2_gib(name):
+    import gpu_path
+    T = 40000
+    inp = W.make_inputs(name, T=T)
+    E, H = inp["E"], inp["H"]
+    fp8 = name == "quant"
+    print(f"case large quantized receive buffer {name} T={T} H={H}", flush=True)
+    g = gpu_path.run(inp, with_layout=True)
+    ref = oracle.slots(inp["topk_idx"], inp["topk_w"], E)
+    np.testing.assert_array_equal(g["slots"]["token_slot"], ref["token_slot"])
+    np.testing.assert_array_equal(g["slots"]["expert_offset"], ref["expert_offset"])
+    nrows = int(ref["expert_offset"][-1])
+    assert nrows * (H if fp8 else 2 * H) > (1 << 31)
+    np.testing.assert_array_equal(g["slots"]["recv_src_idx"][:nrows], ref["recv_src_idx"][:nrows])
+    rows = np.unique(np.concatenate([np.arange(0, nrows, 499), np.arange(nrows - 64, nrows)]))
+    src = ref["recv_src_idx"][rows]
+    if fp8:
+        q, s = oracle.quant_fp8_s128(inp["x"][src])
+        np.testing.assert_array_equal(g["recv_x"][rows], q)
+        np.testing.assert_array_equal(g["recv_x_scales"][rows].view(np.uint32), s.view(np.uint32))
+    else:
+        np.testing.assert_array_equal(g["recv_x"][rows], inp["x"][src])
+    toks = np.unique(np.concatenate([np.arange(0, T, 211), np.arange(T - 16, T)]))
+    sub = dict(inp, T=len(toks), x=inp["x"][toks], topk_idx=inp["topk_idx"][toks], topk_w=inp["topk_w"][toks])
+    np.testing.assert_array_equal(g["y"][toks], oracle.run_path(sub)["y"])
