@@ -9,8 +9,8 @@ configuration the benchmark uses, with the plan reused, planned again and
 in one call; the RANK_MAJOR layout runs at the prefill shape in both forms.
 The edge cases cover ragged, empty and all-masked inputs, masked slots,
 duplicate experts, one or two experts, invalid ids, plan-tile counts on both
-sides of every path's limits, the shape limits, and receive buffers past 2
-and 4 GiB.
+sides of every path's limits, the shape limits, rows of 64 K elements, and
+receive buffers past 2 and 4 GiB.
 """
 import numpy as np
 import pytest
@@ -86,6 +86,22 @@ def test_edge_cases_quantized(kw):
 def test_scaled_expert_with_masks():
     _, _, ndiff = _run_both(W.make_inputs("decode", T=200, mask_frac=0.2))
     assert ndiff == 0
+
+
+# Wide rows: 64 K elements (128 KB bf16 rows), so every kernel loops over
+# several passes per wave and the dispatch and combine run 16 to 64 waves
+# per token; bf16 at a hidden size that is no multiple of 128, fp8 rows with
+# 512 scales each, and the nvfp4 payload.
+@pytest.mark.parametrize("name,T,H", [("tiny", 100, 65536), ("tiny", 700, 65528), ("quant", 100, 65536),
+                                      ("quant", 300, 65536), ("nvfp4", 300, 65536)])
+def test_wide_rows(name, T, H):
+    inp = W.make_inputs(name, T=T, H=H, E=64, R=8, N=2, k=8, mask_frac=0.1)
+    forms = [dict(from_layout=True), dict(with_layout=True)]
+    if name == "tiny":
+        forms.append(dict(from_layout=False))
+    for form in forms:
+        _, _, ndiff = _run_both(inp, **form)
+        assert ndiff == 0
 
 
 # Every pair on one or two experts: one expert segment holds (nearly) every

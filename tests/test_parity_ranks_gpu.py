@@ -46,6 +46,15 @@ def test_workload_full_size(name):
     assert g["slots"]["rank_offset"][-1] == g["layout"]["num_tokens_per_rank"].sum()
 
 
+# Wide rows (64 K elements): several passes per wave in every kernel.
+@pytest.mark.parametrize("name,T,H", [("tiny", 100, 65536), ("tiny", 700, 65528), ("quant", 300, 65536)])
+def test_wide_rows(name, T, H):
+    inp = W.make_inputs(name, T=T, H=H, E=64, R=8, N=2, k=8, mask_frac=0.1)
+    for with_layout in (False, True):
+        _, _, ndiff = _run_both(inp, with_layout)
+        assert ndiff == 0
+
+
 # Every pair on one or two experts (one or two ranks).
 @pytest.mark.parametrize("kw", [dict(E=1, R=1, N=1, k=1, T=700),
                                 dict(E=2, R=1, N=1, k=4, T=3000, routing="replace"),
