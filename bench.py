@@ -24,8 +24,9 @@ durations in phase_us: median over steps).
 
 Warm and cold.  The 256 MB memory-side cache (MALL) of MI355X is a
 write-back cache: plain stores leave dirty lines there, written back to HBM
-when something evicts them (non-temporal stores leave none).  Back to back on the same buffers (the warm `value`), the receive
-rows and x that one step leaves in it are read by the combine from it and
+when something evicts them (non-temporal stores leave none).  Back to back
+on the same buffers (the warm `value`), the receive rows and x that one
+step leaves in it are read by the combine from it and
 rewritten by the next step's dispatch before they ever reach HBM, so the
 warm figure counts up to ~256 MB of "HBM" writes per step that HBM never
 sees.  The cold figures charge them: `cold` times HIP graphs of [a 512 MiB
@@ -56,7 +57,8 @@ Prints one JSON line:
                 buffers (so write-backs are charged), best over a few launch
                 shapes
   cpu_baseline  the CPU oracle on the same workload, one thread and all cores
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--layout pairs|ranks]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                       [--layout pairs|rank_major|ranks] [--split-layout] [--sweep]
 """
 from __future__ import annotations
 
