@@ -57,6 +57,8 @@ Prints one JSON line:
                 buffers (so write-backs are charged), best over a few launch
                 shapes
   cpu_baseline  the CPU oracle on the same workload, one thread and all cores
+  kernel_sources_sha256  hash of the step kernels' code (comments and
+                whitespace removed), as stated in the profiles/ summaries
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                        [--layout pairs|rank_major|ranks] [--split-layout] [--sweep]
 """
@@ -575,6 +577,7 @@ def measure(workload: str, steps: int, warmup: int, graph: bool = False, layout_
         "step_algorithmic_bytes": int(step_bytes),
         "eager_ms_per_step": round(eager_ms, 4),
         "timing": ("steps replayed from a HIP graph of %d steps" % G) if graph_ms is not None else "eager",
+        "kernel_sources_sha256": kernel_source_hash(),
         "roofline": roofline,
         "ceilings": ceil,
         "pages_accounting": {"rdma_algo_tokens": acc["rdma_algo_tokens"],
