@@ -92,7 +92,7 @@ def test_scaled_expert_with_masks():
 # several passes per wave and the dispatch and combine run 16 to 64 waves
 # per token; bf16 at a hidden size that is no multiple of 128, fp8 rows with
 # 512 scales each, and the nvfp4 payload.
-@pytest.mark.parametrize("name,T,H", [("tiny", 100, 65536), ("tiny", 700, 65528), ("quant", 100, 65536),
+@pytest.mark.parametrize("name,T,H", [("tiny", 100, 65536), ("tiny", 300, 65528), ("quant", 100, 65536),
                                       ("quant", 300, 65536), ("nvfp4", 300, 65536)])
 def test_wide_rows(name, T, H):
     inp = W.make_inputs(name, T=T, H=H, E=64, R=8, N=2, k=8, mask_frac=0.1)
